@@ -1,0 +1,237 @@
+"""CPU oracle for the NVFP4 W4A16 gated FFN -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The GPU library never calls it, and it
+shares no code with the GPU library.
+
+The arithmetic lives in ``ffn_oracle.c`` (plain C, double precision, sums in
+ascending index order); this module only compiles it with gcc and marshals
+numpy arrays into it. Every function here takes an ``ffn_inputs.FfnCase`` or
+plain numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ffn_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libffn_oracle.so")
+
+
+def build(force: bool = True, src: str = _SRC, out: str = LIB_PATH) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, OpenMP over outputs)."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+               src, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+class Oracle:
+    """ctypes view of one compiled copy of ffn_oracle.c."""
+
+    def __init__(self, lib_path: str = LIB_PATH):
+        if not os.path.exists(lib_path):
+            build(force=False, out=lib_path)
+        lib = ctypes.CDLL(lib_path)
+        lib.oracle_e2m1_value.restype = ctypes.c_double
+        lib.oracle_e2m1_value.argtypes = [_I]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_value.argtypes = [_I]
+        lib.oracle_bf16_value.restype = ctypes.c_double
+        lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        lib.oracle_act.restype = ctypes.c_double
+        lib.oracle_act.argtypes = [_I, ctypes.c_double]
+        lib.oracle_dequant.restype = None
+        lib.oracle_dequant.argtypes = [_P, _P, _F, _I, _I, _P]
+        lib.oracle_linear_f64.restype = None
+        lib.oracle_linear_f64.argtypes = [_P, _I, _I, _I, _P, _P, _F, _P]
+        lib.oracle_dual.restype = _I
+        lib.oracle_dual.argtypes = [_P, _I, _I, _I, _P, _P, _F, _P, _P, _F, _P, _P]
+        lib.oracle_gated_act.restype = None
+        lib.oracle_gated_act.argtypes = [_I, _P, _P, ctypes.c_size_t, _P]
+        lib.oracle_down.restype = None
+        lib.oracle_down.argtypes = [_P, _I, _I, _I, _P, _P, _F, _P]
+        lib.oracle_ffn.restype = _I
+        lib.oracle_ffn.argtypes = [_P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _F, _P, _P, _F, _P]
+        lib.oracle_num_threads.restype = _I
+        lib.oracle_num_threads.argtypes = []
+        self.lib = lib
+        self.path = lib_path
+
+    def e2m1_value(self, code: int) -> float:
+        return self.lib.oracle_e2m1_value(int(code))
+
+    def e4m3_value(self, byte: int) -> float:
+        return self.lib.oracle_e4m3_value(int(byte))
+
+    def bf16_value(self, bits: int) -> float:
+        return self.lib.oracle_bf16_value(int(bits))
+
+    def act(self, kind: int, g: float) -> float:
+        return self.lib.oracle_act(int(kind), float(g))
+
+    def e2m1_table(self) -> np.ndarray:
+        return np.array([self.e2m1_value(i) for i in range(16)], dtype=np.float64)
+
+    def e4m3_table(self) -> np.ndarray:
+        return np.array([self.e4m3_value(i) for i in range(256)], dtype=np.float64)
+
+    def dequant(self, w) -> np.ndarray:
+        """Dequantised weight [rows, cols] in double."""
+        codes = _c(w.codes, np.uint8)
+        scales = _c(w.scales, np.uint8)
+        rows, cols = codes.shape[0], codes.shape[1] * 2
+        out = np.empty((rows, cols), dtype=np.float64)
+        self.lib.oracle_dequant(_ptr(codes), _ptr(scales), float(w.scale2), rows, cols, _ptr(out))
+        return out
+
+    def linear(self, a: np.ndarray, w) -> np.ndarray:
+        """y[m, r] = sum_c W[r, c] a[m, c] with a in double."""
+        a = _c(a, np.float64)
+        codes = _c(w.codes, np.uint8)
+        scales = _c(w.scales, np.uint8)
+        M, cols = a.shape
+        rows = codes.shape[0]
+        assert codes.shape[1] * 2 == cols
+        y = np.empty((M, rows), dtype=np.float64)
+        self.lib.oracle_linear_f64(_ptr(a), M, cols, rows, _ptr(codes), _ptr(scales),
+                                   float(w.scale2), _ptr(y))
+        return y
+
+    def dual(self, case) -> Tuple[np.ndarray, np.ndarray]:
+        """(gate, up), each [M, N] in double."""
+        x = _c(case.x_bits, np.uint16)
+        g, u = case.gate, case.up
+        gate = np.empty((case.M, case.N), dtype=np.float64)
+        up = np.empty((case.M, case.N), dtype=np.float64)
+        gc, gs, uc, us = (_c(a, np.uint8) for a in (g.codes, g.scales, u.codes, u.scales))
+        rc = self.lib.oracle_dual(_ptr(x), case.M, case.K, case.N,
+                                  _ptr(gc), _ptr(gs), float(g.scale2),
+                                  _ptr(uc), _ptr(us), float(u.scale2), _ptr(gate), _ptr(up))
+        if rc != 0:
+            raise MemoryError("oracle_dual")
+        return gate, up
+
+    def gated_act(self, kind: int, gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+        gate = _c(gate, np.float64)
+        up = _c(up, np.float64)
+        h = np.empty_like(gate)
+        self.lib.oracle_gated_act(int(kind), _ptr(gate), _ptr(up), gate.size, _ptr(h))
+        return h
+
+    def down(self, h: np.ndarray, w) -> np.ndarray:
+        """out[m, j] = sum_n W_d[j, n] h[m, n]."""
+        h = _c(h, np.float64)
+        codes = _c(w.codes, np.uint8)
+        scales = _c(w.scales, np.uint8)
+        M, N = h.shape
+        K = codes.shape[0]
+        out = np.empty((M, K), dtype=np.float64)
+        self.lib.oracle_down(_ptr(h), M, N, K, _ptr(codes), _ptr(scales), float(w.scale2), _ptr(out))
+        return out
+
+    def ffn(self, case, rows: Optional[np.ndarray] = None) -> np.ndarray:
+        """out [M, K] in double; with ``rows`` only those rows of x are
+        computed (rows of the FFN are independent): [len(rows), K]."""
+        x = _c(case.x_bits if rows is None else case.x_bits[np.asarray(rows)], np.uint16)
+        M = x.shape[0]
+        g, u, d = case.gate, case.up, case.down
+        arrs = [_c(a, np.uint8) for a in (g.codes, g.scales, u.codes, u.scales, d.codes, d.scales)]
+        out = np.empty((M, case.K), dtype=np.float64)
+        rc = self.lib.oracle_ffn(_ptr(x), M, case.K, case.N, int(case.act),
+                                 _ptr(arrs[0]), _ptr(arrs[1]), float(g.scale2),
+                                 _ptr(arrs[2]), _ptr(arrs[3]), float(u.scale2),
+                                 _ptr(arrs[4]), _ptr(arrs[5]), float(d.scale2), _ptr(out))
+        if rc != 0:
+            raise MemoryError("oracle_ffn")
+        return out
+
+    def num_threads(self) -> int:
+        return self.lib.oracle_num_threads()
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle(LIB_PATH)
+    return _default
+
+
+def e2m1_table() -> np.ndarray:
+    return default().e2m1_table()
+
+
+def e4m3_table() -> np.ndarray:
+    return default().e4m3_table()
+
+
+def dequant(w) -> np.ndarray:
+    return default().dequant(w)
+
+
+def linear(a: np.ndarray, w) -> np.ndarray:
+    return default().linear(a, w)
+
+
+def dual(case):
+    return default().dual(case)
+
+
+def gated_act(kind: int, gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    return default().gated_act(kind, gate, up)
+
+
+def down(h: np.ndarray, w) -> np.ndarray:
+    return default().down(h, w)
+
+
+def ffn(case, rows=None) -> np.ndarray:
+    return default().ffn(case, rows)
+
+
+def num_threads() -> int:
+    return default().num_threads()
+
+
+def ulp_bf16(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |v|: 2^(floor(log2|v|) - 7), floored at the
+    smallest bf16 subnormal 2^-133."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    u = np.ldexp(1.0, (e - 7).astype(np.int64))
+    u = np.where(a > 0, u, 0.0)
+    return np.maximum(u, 2.0 ** -133)
+
+
+def parity_bound(out_ref: np.ndarray, rms_ref: Optional[float] = None,
+                 rel: float = 1e-2) -> np.ndarray:
+    """Per-element bound for a bf16 GPU output against the double reference:
+    rel * rms(out_ref) + one bf16 ulp of the reference value."""
+    if rms_ref is None:
+        rms_ref = float(np.sqrt(np.mean(np.square(out_ref))))
+    return rel * rms_ref + ulp_bf16(out_ref)

@@ -1,0 +1,226 @@
+/*
+ * ffn_oracle.c -- CPU oracle for the NVFP4 W4A16 gated FFN.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the plain, slow, obviously correct
+ * definition of what the GPU library computes; only the tests, the smoke check
+ * and the benchmark's CPU-baseline leg may load it. It shares no code, header,
+ * table or constant with the GPU library.
+ *
+ * Everything is computed in double precision, element by element, with sums
+ * taken in ascending index order. OpenMP, when enabled, only spreads
+ * independent output elements over threads: each element is still one
+ * sequential sum, so results do not depend on the thread count.
+ *
+ * Sources (web pages of the Atlas inference engine API docs):
+ *  - dense_ffn.rs page, module doc comment: the gated FFN dataflow
+ *    gate = gate_proj(x), up = up_proj(x), out = down_proj(act(gate) * up).
+ *  - dense_ffn.rs page, FfnActivation enum: SiLU (Qwen/Llama) or GELU (Gemma).
+ *  - dense_ffn.rs page, DenseFfnLayer::ensure_int8_weight doc comment: an NVFP4
+ *    weight is packed E2M1 codes [N, K/2], one E4M3 scale per 16 elements
+ *    [N, K/16], and one per-tensor F32 weight_scale_2.
+ *  - dense_ffn.rs page, DenseFfnLayer::forward_prefill_inner, FP4-MMQ branch:
+ *    weight_scale_2 multiplies each projection's output and, for gate and up,
+ *    is applied before the nonlinearity.
+ *  - qwen35_dense.rs page, load of the SSM FP8 prefill copies: E4M3 magnitudes
+ *    are bounded by 448, i.e. the OCP "E4M3FN" variant (no infinities).
+ *  - The E2M1 and E4M3 bit layouts follow the OCP Microscaling Formats (MX)
+ *    v1.0 specification.
+ *
+ * Readings taken where the pages are silent (each is listed in the design
+ * notes): the even column of a byte is its low nibble; GELU is the tanh form;
+ * there is no clamp on the SwiGLU product; scale bytes may be negative and
+ * NaN scale bytes propagate as NaN.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_ACT_SILU 0
+#define ORACLE_ACT_GELU_TANH 1
+
+/* E2M1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa.
+ * Exponent field 0 encodes the subnormal m * 0.5; otherwise the value is
+ * 2^(e-1) * (1 + m/2). */
+double oracle_e2m1_value(int code)
+{
+    int s = (code >> 3) & 1;
+    int e = (code >> 1) & 3;
+    int m = code & 1;
+    double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* E4M3FN: bit 7 sign, bits 6..3 exponent (bias 7), bits 2..0 mantissa.
+ * Exponent field 0 is subnormal: (m/8) * 2^-6. The all-ones magnitude
+ * S.1111.111 is NaN; there are no infinities, so 1111.110 = 448 is the max. */
+double oracle_e4m3_value(int byte)
+{
+    int s = (byte >> 7) & 1;
+    int e = (byte >> 3) & 15;
+    int m = byte & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp(m / 8.0, -6);
+    else
+        mag = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* bf16 is the upper half of an IEEE fp32; widening to double is exact. */
+double oracle_bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* SiLU(g) = g * sigmoid(g) = g / (1 + e^-g). */
+double oracle_silu(double g)
+{
+    return g / (1.0 + exp(-g));
+}
+
+/* GELU, tanh form: 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))). */
+double oracle_gelu_tanh(double g)
+{
+    const double k = sqrt(2.0 / 3.14159265358979323846);
+    return 0.5 * g * (1.0 + tanh(k * (g + 0.044715 * g * g * g)));
+}
+
+double oracle_act(int act, double g)
+{
+    return act == ORACLE_ACT_GELU_TANH ? oracle_gelu_tanh(g) : oracle_silu(g);
+}
+
+/* Lookup tables built from the two definitions above. */
+static void build_tables(double e2m1[16], double e4m3[256])
+{
+    for (int i = 0; i < 16; ++i)
+        e2m1[i] = oracle_e2m1_value(i);
+    for (int i = 0; i < 256; ++i)
+        e4m3[i] = oracle_e4m3_value(i);
+}
+
+/* Element (r, c) of a dequantised NVFP4 weight of logical shape [rows, cols]:
+ * code(r, c) * scale(r, c/16) * scale2. Codes are packed two per byte along a
+ * row, column 2j in the low nibble of byte j and column 2j+1 in the high one. */
+static double weight_at(const double e2m1[16], const double e4m3[256],
+                        const uint8_t *codes, const uint8_t *scales, double scale2,
+                        int cols, int r, int c)
+{
+    uint8_t byte = codes[(size_t)r * (size_t)(cols / 2) + (size_t)(c / 2)];
+    int code = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+    uint8_t sb = scales[(size_t)r * (size_t)(cols / 16) + (size_t)(c / 16)];
+    return e2m1[code] * e4m3[sb] * scale2;
+}
+
+void oracle_dequant(const uint8_t *codes, const uint8_t *scales, float scale2,
+                    int rows, int cols, double *w_out)
+{
+    double e2m1[16], e4m3[256];
+    build_tables(e2m1, e4m3);
+    for (int r = 0; r < rows; ++r)
+        for (int c = 0; c < cols; ++c)
+            w_out[(size_t)r * cols + c] = weight_at(e2m1, e4m3, codes, scales, scale2, cols, r, c);
+}
+
+/* y[m, r] = sum_c W[r, c] * a[m, c] over a [rows, cols] NVFP4 weight and a
+ * double-precision input a[M, cols]; y is [M, rows]. */
+void oracle_linear_f64(const double *a, int M, int cols, int rows,
+                       const uint8_t *codes, const uint8_t *scales, float scale2,
+                       double *y)
+{
+    double e2m1[16], e4m3[256];
+    build_tables(e2m1, e4m3);
+    long total = (long)M * rows;
+#pragma omp parallel for schedule(static)
+    for (long idx = 0; idx < total; ++idx) {
+        int m = (int)(idx / rows);
+        int r = (int)(idx % rows);
+        double acc = 0.0;
+        for (int c = 0; c < cols; ++c)
+            acc += weight_at(e2m1, e4m3, codes, scales, scale2, cols, r, c) * a[(size_t)m * cols + c];
+        y[idx] = acc;
+    }
+}
+
+/* gate = W_g x and up = W_u x for bf16 x[M, K]; W_g, W_u are [N, K];
+ * gate and up are [M, N]. Returns 0, or -1 if memory runs out. */
+int oracle_dual(const uint16_t *x_bits, int M, int K, int N,
+                const uint8_t *g_codes, const uint8_t *g_scales, float g_scale2,
+                const uint8_t *u_codes, const uint8_t *u_scales, float u_scale2,
+                double *gate, double *up)
+{
+    double *x = (double *)malloc(sizeof(double) * (size_t)M * (size_t)K);
+    if (!x)
+        return -1;
+    for (size_t i = 0; i < (size_t)M * (size_t)K; ++i)
+        x[i] = oracle_bf16_value(x_bits[i]);
+    oracle_linear_f64(x, M, K, N, g_codes, g_scales, g_scale2, gate);
+    oracle_linear_f64(x, M, K, N, u_codes, u_scales, u_scale2, up);
+    free(x);
+    return 0;
+}
+
+/* h[m, n] = act(gate[m, n]) * up[m, n]. */
+void oracle_gated_act(int act, const double *gate, const double *up, size_t count, double *h)
+{
+    for (size_t i = 0; i < count; ++i)
+        h[i] = oracle_act(act, gate[i]) * up[i];
+}
+
+/* out[m, j] = sum_n W_d[j, n] * h[m, n] with W_d of shape [K, N]. */
+void oracle_down(const double *h, int M, int N, int K,
+                 const uint8_t *d_codes, const uint8_t *d_scales, float d_scale2,
+                 double *out)
+{
+    oracle_linear_f64(h, M, N, K, d_codes, d_scales, d_scale2, out);
+}
+
+/* The whole gated FFN: out = W_d (act(W_g x) * (W_u x)), all in double.
+ * out is [M, K]. Returns 0, or -1 if memory runs out. */
+int oracle_ffn(const uint16_t *x_bits, int M, int K, int N, int act,
+               const uint8_t *g_codes, const uint8_t *g_scales, float g_scale2,
+               const uint8_t *u_codes, const uint8_t *u_scales, float u_scale2,
+               const uint8_t *d_codes, const uint8_t *d_scales, float d_scale2,
+               double *out)
+{
+    size_t mn = (size_t)M * (size_t)N;
+    double *gate = (double *)malloc(sizeof(double) * mn);
+    double *up = (double *)malloc(sizeof(double) * mn);
+    int rc = -1;
+    if (gate && up &&
+        oracle_dual(x_bits, M, K, N, g_codes, g_scales, g_scale2,
+                    u_codes, u_scales, u_scale2, gate, up) == 0) {
+        oracle_gated_act(act, gate, up, mn, gate); /* h overwrites gate */
+        oracle_down(gate, M, N, K, d_codes, d_scales, d_scale2, out);
+        rc = 0;
+    }
+    free(gate);
+    free(up);
+    return rc;
+}
+
+/* Number of threads an OpenMP region would use (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,404 @@
+"""Pins of the CPU oracle to facts outside itself (no GPU needed).
+
+Each ``pin_*`` function checks the oracle against something it does not
+contain: the OCP format tables, torch's own float8 decoder, closed forms of
+the activations, exact rational arithmetic, numpy's float64 matmul on cases
+where every sum is exact, and the generator's closed-form moments. The
+mutation test at the end compiles deliberately broken copies of the oracle
+source (on the CPU) and checks that some pin catches each one.
+"""
+import math
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import ffn_inputs as fi
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                a, b = line.split()
+                rows.append((a, float(b)))
+    return rows
+
+
+def _same_float(a, b):
+    if math.isnan(a) or math.isnan(b):
+        return math.isnan(a) and math.isnan(b)
+    return a == b and math.copysign(1.0, a) == math.copysign(1.0, b)
+
+
+# ---------------------------------------------------------------- formats
+
+
+def pin_e2m1_table(orc):
+    table = orc.e2m1_table()
+    for code, val in _read_table("e2m1_values.txt"):
+        assert _same_float(table[int(code)], val), (code, table[int(code)], val)
+    assert table.sum() == 0.0
+    assert np.sum(table ** 2) == 137.0
+
+
+def pin_e4m3_vs_torch(orc):
+    table = orc.e4m3_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for b in range(256):
+        assert _same_float(table[b], ref[b]) or (table[b] == 0 and ref[b] == 0 and
+                                                 math.copysign(1, table[b]) == math.copysign(1, ref[b])), \
+            (hex(b), table[b], ref[b])
+
+
+def pin_e4m3_anchors_and_order(orc):
+    table = orc.e4m3_table()
+    for hx, val in _read_table("e4m3_anchors.txt"):
+        assert _same_float(table[int(hx, 16)], val), (hx, table[int(hx, 16)], val)
+    pos = table[:0x7F]
+    assert np.all(np.diff(pos) > 0), "E4M3 magnitudes must increase with the byte"
+    assert np.isfinite(table).sum() == 254
+    assert np.nanmax(np.abs(table)) == 448.0
+    for b in range(0x7F):
+        assert _same_float(table[b | 0x80], -table[b])
+
+
+def pin_byte_nibble_order(orc):
+    """Bytes 0..255 as one row of codes: every ordered pair of E2M1 values
+    appears once, and byte 0x21 decodes to (0.5, 1.0): the even column is
+    the low nibble."""
+    codes = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    scales = np.full((1, 32), 0x38, dtype=np.uint8)  # 1.0
+    w = orc.dequant(fi.Nvfp4Weight(codes, scales, 1.0))[0]
+    e2 = [v for _, v in _read_table("e2m1_values.txt")]
+    pairs = {(float(w[2 * j]), math.copysign(1, w[2 * j]), float(w[2 * j + 1]), math.copysign(1, w[2 * j + 1]))
+             for j in range(256)}
+    assert len(pairs) == 256
+    assert (w[2 * 0x21], w[2 * 0x21 + 1]) == (0.5, 1.0)
+    assert (w[2 * 0x7F], w[2 * 0x7F + 1]) == (-6.0, 6.0)
+    assert (w[2 * 0xF0], w[2 * 0xF0 + 1]) == (0.0, -6.0)
+    assert sorted(set(float(v) for v in w)) == sorted(set(e2)), "value set is the E2M1 set"
+
+
+def pin_scale_blocks(orc):
+    """Scale byte j of a row applies to columns 16j..16j+15 of that row."""
+    rng = np.random.default_rng(3)
+    rows, cols = 4, 64
+    codes = np.full((rows, cols // 2), 0x22, dtype=np.uint8)  # every element 1.0
+    scales = rng.choice(fi.finite_e4m3_bytes(), size=(rows, cols // 16)).astype(np.uint8)
+    w = orc.dequant(fi.Nvfp4Weight(codes, scales, 1.0))
+    ref = torch.from_numpy(scales.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(w, np.repeat(ref, 16, axis=1))
+
+
+def _independent_dequant(w):
+    """Dequantise with a separate route: nibble unpack by numpy, the E2M1
+    values from the OCP table fixture, E4M3 scales decoded by torch."""
+    e2 = np.array([v for _, v in _read_table("e2m1_values.txt")])
+    lo = w.codes & 0x0F
+    hi = w.codes >> 4
+    idx = np.stack([lo, hi], axis=-1).reshape(w.codes.shape[0], -1)
+    sc = torch.from_numpy(np.ascontiguousarray(w.scales)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return e2[idx] * np.repeat(sc, 16, axis=1) * float(np.float32(w.scale2))
+
+
+def pin_dequant_independent(orc):
+    case = fi.make_format_coverage()
+    for w in (case.gate, case.up, case.down):
+        np.testing.assert_array_equal(orc.dequant(w), _independent_dequant(w))
+
+
+# ------------------------------------------------------------ activations
+
+
+def pin_activations(orc):
+    S, G = fi.ACT_SILU, fi.ACT_GELU_TANH
+    assert orc.act(S, 0.0) == 0.0 and orc.act(G, 0.0) == 0.0
+    xs = np.concatenate([np.linspace(-12, 12, 97), [1e-8, -1e-8, 0.5, -3.7, 30.0, -30.0]])
+    for x in xs:
+        # Odd-part identities f(x) - f(-x) = x hold for both gates.
+        assert abs(orc.act(S, x) - orc.act(S, -x) - x) <= 1e-13 * max(1.0, abs(x))
+        assert abs(orc.act(G, x) - orc.act(G, -x) - x) <= 1e-13 * max(1.0, abs(x))
+        # Library routines: x * expit(x); torch's tanh-approximate GELU in float64.
+        assert abs(orc.act(S, x) - x * scipy.special.expit(x)) <= 1e-14 * max(1.0, abs(x))
+        tg = torch.nn.functional.gelu(torch.tensor(x, dtype=torch.float64), approximate="tanh").item()
+        assert abs(orc.act(G, x) - tg) <= 1e-14 * max(1.0, abs(x))
+    assert abs(orc.act(S, 50.0) - 50.0) < 1e-15 * 50 + 1e-18
+    assert abs(orc.act(S, -50.0)) < 1e-19
+    assert orc.act(G, 10.0) == 10.0 and abs(orc.act(G, -10.0)) < 1e-30
+    assert orc.act(S, 1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+
+
+def pin_gated_act(orc):
+    rng = np.random.default_rng(5)
+    g = rng.normal(size=64) * 4
+    u = rng.normal(size=64)
+    for kind in (fi.ACT_SILU, fi.ACT_GELU_TANH):
+        h = orc.gated_act(kind, g, u)
+        for i in range(64):
+            assert h[i] == orc.act(kind, g[i]) * u[i]
+    # The product is act(gate) * up, not act(up) * gate.
+    h = orc.gated_act(fi.ACT_SILU, np.array([2.0]), np.array([-1.0]))
+    assert h[0] == pytest.approx(-2.0 * scipy.special.expit(2.0), rel=1e-15)
+
+
+# ------------------------------------------------------------ linear part
+
+
+def _one_hot_weight(rows, cols, pick, value_code=0x2):
+    """Row r holds code `value_code` at column pick[r]; scale 1.0; scale2 1."""
+    codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    for r, c in enumerate(pick):
+        codes[r, c // 2] |= (value_code << 4) if c % 2 else value_code
+    scales = np.full((rows, cols // 16), 0x38, dtype=np.uint8)
+    return fi.Nvfp4Weight(codes, scales, 1.0)
+
+
+def pin_one_hot_selects(orc):
+    rng = np.random.default_rng(11)
+    K, N, M = 96, 40, 3
+    pick = rng.integers(0, K, size=N)
+    wg = _one_hot_weight(N, K, pick)
+    wu = _one_hot_weight(N, K, rng.integers(0, K, size=N), value_code=0xA)  # -1.0
+    x_bits = fi.f32_to_bf16_bits(rng.normal(size=(M, K)).astype(np.float32))
+    x = fi.bf16_bits_to_f32(x_bits).astype(np.float64)
+    case = fi.FfnCase("onehot", M, K, N, fi.ACT_SILU, x_bits, wg, wu, wg)
+    gate, up = orc.dual(case)
+    np.testing.assert_array_equal(gate, x[:, pick])
+    # Doubling scale2 doubles the output exactly.
+    case2 = fi.FfnCase("onehot2", M, K, N, fi.ACT_SILU, x_bits,
+                       fi.Nvfp4Weight(wg.codes, wg.scales, 2.0), wu, wg)
+    g2, _ = orc.dual(case2)
+    np.testing.assert_array_equal(g2, 2.0 * gate)
+
+
+def pin_down_orientation(orc):
+    """W_d is [K, N]: out[m, j] = h[m, pick[j]] for a one-hot W_d."""
+    rng = np.random.default_rng(12)
+    K, N, M = 64, 96, 2
+    pick = rng.integers(0, N, size=K)
+    wd = _one_hot_weight(K, N, pick)
+    h = rng.normal(size=(M, N))
+    out = orc.down(h, wd)
+    np.testing.assert_array_equal(out, h[:, pick])
+
+
+def pin_ternary_exact_vs_numpy(orc):
+    """Codes in {0, +1, -1} with unit scales: every partial sum of bf16
+    inputs is exact in double, so the oracle must equal numpy's matmul
+    bit for bit."""
+    rng = np.random.default_rng(21)
+    M, K, N = 3, 512, 64
+    tern = np.array([0x0, 0x2, 0xA], dtype=np.uint8)
+    lo = rng.choice(tern, size=(N, K // 2))
+    hi = rng.choice(tern, size=(N, K // 2))
+    w = fi.Nvfp4Weight((lo | (hi << 4)).astype(np.uint8), np.full((N, K // 16), 0x38, np.uint8), 1.0)
+    x_bits = fi.f32_to_bf16_bits(rng.normal(size=(M, K)).astype(np.float32))
+    x = fi.bf16_bits_to_f32(x_bits).astype(np.float64)
+    wd = np.where(lo == 0x2, 1.0, np.where(lo == 0xA, -1.0, 0.0))
+    wdh = np.where(hi == 0x2, 1.0, np.where(hi == 0xA, -1.0, 0.0))
+    dense = np.stack([wd, wdh], axis=-1).reshape(N, K)
+    ref = x @ dense.T
+    np.testing.assert_array_equal(orc.linear(x, w), ref)
+
+
+def pin_matches_numpy_matmul(orc):
+    """General weights: the oracle agrees with numpy's float64 matmul over an
+    independently dequantised matrix to double rounding."""
+    case = fi.make_format_coverage(M=2)
+    x = fi.bf16_bits_to_f32(case.x_bits).astype(np.float64)
+    for w in (case.gate, case.up):
+        ref = x @ _independent_dequant(w).T
+        got = orc.linear(x, w)
+        scale = np.abs(x) @ np.abs(_independent_dequant(w)).T
+        assert np.all(np.abs(got - ref) <= 1e-12 * scale + 1e-300)
+
+
+def _exact_x_bits(rng, shape):
+    """bf16 values k/64 with |k| < 256: all partial sums stay exact in double."""
+    k = rng.integers(-255, 256, size=shape)
+    return fi.f32_to_bf16_bits((k / 64.0).astype(np.float32))
+
+
+def pin_fraction_brute_force(orc):
+    """Exact rational gate/up for tiny shapes; the double result must be exact."""
+    rng = np.random.default_rng(31)
+    M, K, N = 2, 64, 16
+    fin = fi.finite_e4m3_bytes()
+    # keep scales >= 2^-6 so every product and sum is exact in double
+    fin = fin[(fin & 0x78) != 0]
+
+    def weight(rows, cols):
+        return fi.Nvfp4Weight(rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8),
+                              rng.choice(fin, size=(rows, cols // 16)).astype(np.uint8), 0.375)
+
+    wg, wu = weight(N, K), weight(N, K)
+    x_bits = _exact_x_bits(rng, (M, K))
+    case = fi.FfnCase("frac", M, K, N, fi.ACT_SILU, x_bits, wg, wu, weight(K, N))
+    gate, up = orc.dual(case)
+    e2 = [Fraction(v) for _, v in _read_table("e2m1_values.txt")]
+    e4 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    xf = [[Fraction(float(v)) for v in row] for row in fi.bf16_bits_to_f32(x_bits)]
+    for w, got in ((wg, gate), (wu, up)):
+        for m in range(M):
+            for n in range(N):
+                acc = Fraction(0)
+                for k in range(K):
+                    byte = int(w.codes[n, k // 2])
+                    code = byte & 15 if k % 2 == 0 else byte >> 4
+                    acc += e2[code] * Fraction(float(e4[w.scales[n, k // 16]])) * xf[m][k]
+                acc *= Fraction(0.375)
+                assert Fraction(got[m, n]) == acc, (m, n)
+
+
+def pin_down_fraction_bound(orc):
+    """Down projection over double inputs: within the standard bound
+    n*u*sum|w h| of the exact rational result."""
+    rng = np.random.default_rng(41)
+    K, N, M = 8, 48, 2
+    wd = fi.Nvfp4Weight(rng.integers(0, 256, size=(K, N // 2), dtype=np.uint8),
+                        rng.choice(fi.finite_e4m3_bytes(), size=(K, N // 16)).astype(np.uint8), 0.7)
+    h = rng.normal(size=(M, N)) * 3
+    out = orc.down(h, wd)
+    dense = _independent_dequant(wd)
+    u = 2.0 ** -53
+    for m in range(M):
+        for j in range(K):
+            exact = sum(Fraction(float(dense[j, n])) * Fraction(float(h[m, n])) for n in range(N))
+            bound = N * u * float(np.sum(np.abs(dense[j] * h[m]))) * 1.01
+            assert abs(float(Fraction(out[m, j]) - exact)) <= bound
+
+
+def pin_ffn_composition(orc):
+    """The whole FFN equals down(act(gate) * up) assembled from library
+    routines (numpy matmul, scipy expit, torch gelu) to double rounding."""
+    for act in (fi.ACT_SILU, fi.ACT_GELU_TANH):
+        case = fi.make_small(2, 128, 96, act=act, seed=51, scale2=0.25)
+        out = orc.ffn(case)
+        x = fi.bf16_bits_to_f32(case.x_bits).astype(np.float64)
+        g = x @ _independent_dequant(case.gate).T
+        u = x @ _independent_dequant(case.up).T
+        if act == fi.ACT_SILU:
+            h = g * scipy.special.expit(g) * u
+        else:
+            h = torch.nn.functional.gelu(torch.from_numpy(g), approximate="tanh").numpy() * u
+        ref = h @ _independent_dequant(case.down).T
+        scale = np.abs(h) @ np.abs(_independent_dequant(case.down)).T
+        assert np.all(np.abs(out - ref) <= 1e-10 * scale)
+        # row subset gives the same rows
+        np.testing.assert_array_equal(orc.ffn(case, rows=np.array([1])), out[1:2])
+
+
+PINS = [pin_e2m1_table, pin_e4m3_vs_torch, pin_e4m3_anchors_and_order, pin_byte_nibble_order,
+        pin_scale_blocks, pin_dequant_independent, pin_activations, pin_gated_act,
+        pin_one_hot_selects, pin_down_orientation, pin_ternary_exact_vs_numpy,
+        pin_matches_numpy_matmul, pin_fraction_brute_force, pin_down_fraction_bound,
+        pin_ffn_composition]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(pin):
+    pin(oracle.default())
+
+
+# ------------------------------------------------------------ generator
+
+
+def test_generator_moments():
+    """rms(gate) follows from the draw: E[e2m1^2] = 137/16, E[scale^2] over
+    2^u, u uniform on {-6..0}, is (1/7) sum 4^u; so rms = sqrt(K * 137/16 *
+    E[s^2]) * scale2 * sigma."""
+    case = fi.make_small(4, 1024, 2048, seed=61, scale2=0.5)
+    gate, up = oracle.dual(case)
+    es2 = sum(4.0 ** u for u in range(-6, 1)) / 7.0
+    x = fi.bf16_bits_to_f32(case.x_bits).astype(np.float64)
+    expect = math.sqrt(case.K * (137 / 16) * es2 * np.mean(x ** 2)) * 0.5
+    for a in (gate, up):
+        got = math.sqrt(np.mean(a ** 2))
+        assert abs(got / expect - 1) < 0.05, (got, expect)
+    # codes uniform over all 16 nibbles, scales over exactly 7 bytes
+    assert set(np.unique(case.gate.scales)) == {(u + 7) << 3 for u in range(-6, 1)}
+    nib = np.concatenate([(case.gate.codes & 15).ravel(), (case.gate.codes >> 4).ravel()])
+    counts = np.bincount(nib, minlength=16) / nib.size
+    assert np.all(np.abs(counts - 1 / 16) < 0.01)
+
+
+def test_generator_deterministic_and_shapes():
+    a = fi.make_config(0)
+    b = fi.make_config(0)
+    np.testing.assert_array_equal(a.gate.codes, b.gate.codes)
+    np.testing.assert_array_equal(a.x_bits, b.x_bits)
+    assert a.gate.codes.shape == (512, 128) and a.gate.scales.shape == (512, 16)
+    assert a.down.codes.shape == (256, 256) and a.down.scales.shape == (256, 32)
+    assert a.weight_bytes == 221184
+
+
+def test_format_coverage_case():
+    c = fi.make_format_coverage()
+    allsc = np.concatenate([c.gate.scales.ravel(), c.up.scales.ravel(), c.down.scales.ravel()])
+    assert set(np.unique(allsc)) == set(fi.finite_e4m3_bytes().tolist())
+    nib = np.concatenate([(c.gate.codes & 15).ravel(), (c.gate.codes >> 4).ravel()])
+    assert set(np.unique(nib)) == set(range(16))
+
+
+def test_golden_tiny_config():
+    """Regression pin of the oracle on the tiny config, written by
+    tests/golden/make_golden.py (which calls only the oracle)."""
+    path = os.path.join(GOLDEN, "tiny_silu_m1_out.txt")
+    ref = np.loadtxt(path, dtype=np.float64).reshape(1, -1)
+    out = oracle.ffn(fi.make_config(0))
+    np.testing.assert_allclose(out, ref, rtol=1e-15, atol=0)
+
+
+# ------------------------------------------------------------ mutations
+
+
+MUTANTS = {
+    "nibble_order": ("(c % 2 == 0) ? (byte & 0x0F) : (byte >> 4)", "(c % 2 == 0) ? (byte >> 4) : (byte & 0x0F)"),
+    "e2m1_bias": ("ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e)"),
+    "e2m1_sign": ("return s ? -mag : mag;\n}\n\n/* E4M3FN", "return mag;\n}\n\n/* E4M3FN"),
+    "e4m3_bias": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    "e4m3_subnormal": ("ldexp(m / 8.0, -6)", "ldexp(1.0 + m / 8.0, -6)"),
+    "e4m3_nan": ("if (e == 15 && m == 7)\n        return NAN;", "if (0)\n        return NAN;"),
+    "scale_block": ("(size_t)(c / 16)]", "(size_t)(c / 32)]"),
+    "scale2_dropped": ("e2m1[code] * e4m3[sb] * scale2", "e2m1[code] * e4m3[sb]"),
+    "silu_sign": ("g / (1.0 + exp(-g))", "g / (1.0 + exp(g))"),
+    "gelu_coeff": ("0.044715 * g * g * g", "0.044715 * g * g"),
+    "gate_up_swapped": ("h[i] = oracle_act(act, gate[i]) * up[i];", "h[i] = oracle_act(act, up[i]) * gate[i];"),
+    "dropped_last_term": ("for (int c = 0; c < cols; ++c)\n            acc +=", "for (int c = 0; c < cols - 1; ++c)\n            acc +="),
+    "row_index": ("codes[(size_t)r * (size_t)(cols / 2)", "codes[(size_t)(r / 2) * (size_t)(cols / 2)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    """A plausible mistake planted in a copy of the oracle (CPU only) must make
+    at least one pin fail."""
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "ffn_oracle.c")).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not found once"
+    mpath = tmp_path / f"mut_{name}.c"
+    mpath.write_text(src.replace(old, new))
+    lib = oracle.build(force=True, src=str(mpath), out=str(tmp_path / f"mut_{name}.so"))
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught mutant {name}"
