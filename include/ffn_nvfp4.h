@@ -1,0 +1,141 @@
+/*
+ * ffn_nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 W4A16 gated-FFN library.
+ *
+ * The library computes the dense gated FFN of a decoding transformer layer,
+ *     gate = W_g x,   up = W_u x,   h = act(gate) * up,   out = W_d h,
+ * with NVFP4 weights and bf16 activations (dense_ffn.rs page, module doc
+ * comment and DenseFfnLayer::forward: a dual gate+up GEMV over one activation
+ * row, the activation, then the down GEMV).
+ *
+ * Weight format (dense_ffn.rs page, DenseFfnLayer::ensure_int8_weight doc
+ * comment): a weight of logical shape [rows, cols] is
+ *   - codes : uint8 [rows, cols/2], two E2M1 codes per byte; the code of the
+ *             even column is the low nibble, the odd column the high nibble;
+ *   - scales: uint8 [rows, cols/16], one E4M3FN scale per 16 consecutive
+ *             columns of a row;
+ *   - scale2: one fp32 per-tensor multiplier applied to the projection's
+ *             output (dense_ffn.rs page, forward_prefill_inner FP4-MMQ branch:
+ *             for gate and up it is applied before the nonlinearity).
+ * Element (r, c) is e2m1(code) * e4m3(scale[r][c/16]) * scale2.
+ * Shapes: W_g, W_u are [N, K]; W_d is [K, N]; K = hidden, N = intermediate.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are device memory owned by the caller; the
+ *     library never allocates, frees or keeps them past the call. Host structs
+ *     are read during the call only.
+ *   - Matrices are row-major and dense (no strides); x, h and out are
+ *     [M, width] with row m at offset m*width.
+ *   - Every call is asynchronous on `stream` (0 = the null stream): the
+ *     library enqueues kernels and returns without synchronising. Inputs must
+ *     stay valid and unmodified until the work completes.
+ *   - M = 0 is an empty call: the weights, K, N and act are still validated,
+ *     x / out / workspace may be NULL, nothing is launched, 0 is returned.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     error nothing is launched and a negative status is returned. Faults
+ *     during execution surface at the caller's next synchronisation, as for
+ *     any HIP kernel.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ *     Row m of a batched call is bit-identical to an M=1 call on that row for
+ *     every M <= 8.
+ *   - The functions hold no global mutable state and may be called from
+ *     several host threads (on distinct output buffers).
+ */
+#ifndef FFN_NVFP4_H
+#define FFN_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define FFN_NVFP4_OK 0
+#define FFN_NVFP4_ERR_NULL (-1)          /* a required pointer is NULL */
+#define FFN_NVFP4_ERR_ALIGN (-2)         /* codes / x / out / workspace not 16-byte aligned;
+                                            scales not 2-byte aligned */
+#define FFN_NVFP4_ERR_SHAPE (-3)         /* K or N not a positive multiple of 32, or too large */
+#define FFN_NVFP4_ERR_BATCH (-4)         /* M outside the supported set (see below) */
+#define FFN_NVFP4_ERR_ACT (-5)           /* unknown activation */
+#define FFN_NVFP4_ERR_WORKSPACE (-6)     /* workspace smaller than ffn_nvfp4_workspace_bytes() */
+#define FFN_NVFP4_ERR_LAUNCH (-7)        /* HIP reported an error when launching */
+#define FFN_NVFP4_ERR_SCALE2 (-8)        /* scale2 is not finite */
+
+/* Activation of the gate. SiLU(g) = g / (1 + e^-g) (Qwen/Llama);
+ * GELU-tanh(g) = 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))) (Gemma).
+ * dense_ffn.rs page, FfnActivation enum. */
+typedef enum ffn_nvfp4_act {
+    FFN_NVFP4_ACT_SILU = 0,
+    FFN_NVFP4_ACT_GELU_TANH = 1
+} ffn_nvfp4_act;
+
+/* One NVFP4 weight (see the format above). codes: device, 16-byte aligned;
+ * scales: device, 2-byte aligned; scale2: host value. */
+typedef struct ffn_nvfp4_weight {
+    const uint8_t *codes;
+    const uint8_t *scales;
+    float scale2;
+} ffn_nvfp4_weight;
+
+/* Supported batch sizes: M = 0 (empty), 1 <= M <= 8 runs the weight-streaming GEMV arm
+ * (each weight byte read once for all M rows; dense_ffn.rs page,
+ * forward_k2 / forward_k3 / forward_km). Other M: ERR_BATCH.
+ * K and N: positive multiples of 32, at most 65536. */
+
+/* Bytes of device workspace ffn_nvfp4_forward needs for (M, K, N);
+ * 0 if M = 0 or the shape is unsupported. */
+size_t ffn_nvfp4_workspace_bytes(int M, int K, int N);
+
+/* The whole FFN: out[M, K] (bf16) = W_d (act(W_g x) * (W_u x)) for
+ * x[M, K] (bf16).
+ *   x          device, bf16 [M, K], 16-byte aligned
+ *   gate, up   host structs describing [N, K] weights
+ *   down       host struct describing a [K, N] weight
+ *   act        ffn_nvfp4_act
+ *   workspace  device, >= ffn_nvfp4_workspace_bytes(M, K, N) bytes, 16-byte
+ *              aligned; holds gate and up (fp32) between the two GEMVs;
+ *              clobbered by the call
+ *   out        device, bf16 [M, K], 16-byte aligned; may not alias x
+ * The intermediate h = act(gate) * up is rounded to bf16 once; gate and up
+ * are kept in fp32 up to that point. */
+int ffn_nvfp4_forward(const void *x, int M, int K, int N,
+                      const ffn_nvfp4_weight *gate, const ffn_nvfp4_weight *up,
+                      const ffn_nvfp4_weight *down, int act,
+                      void *workspace, size_t workspace_bytes,
+                      void *out, hipStream_t stream);
+
+/* Dual GEMV (one pass over x for both projections; dense_ffn.rs page,
+ * DenseFfnLayer::forward, w4a16_gemv_dual):
+ *   gate_out[m, n] = scale2_g * sum_k W_g[n, k] x[m, k]
+ *   up_out[m, n]   = scale2_u * sum_k W_u[n, k] x[m, k]
+ *   x          device, bf16 [M, K], 16-byte aligned
+ *   gate_out   device, fp32 [M, N], 16-byte aligned
+ *   up_out     device, fp32 [M, N], 16-byte aligned */
+int ffn_nvfp4_dual_gemv(const void *x, int M, int K, int N,
+                        const ffn_nvfp4_weight *gate, const ffn_nvfp4_weight *up,
+                        float *gate_out, float *up_out, hipStream_t stream);
+
+/* Down GEMV with the activation fused into its input load (dense_ffn.rs
+ * page, DenseFfnLayer::forward, w4a16_gemv_silu_input / gelu_mul):
+ *   out[m, j] = bf16(scale2_d * sum_n W_d[j, n] * bf16(act(gate[m, n]) * up[m, n]))
+ *   gate_in, up_in   device, fp32 [M, N] (as written by the dual GEMV),
+ *                    16-byte aligned
+ *   down             host struct describing a [K, N] weight
+ *   out              device, bf16 [M, K], 16-byte aligned */
+int ffn_nvfp4_down_gemv(const float *gate_in, const float *up_in, int M, int N, int K,
+                        const ffn_nvfp4_weight *down, int act,
+                        void *out, hipStream_t stream);
+
+/* Static text for a status code. */
+const char *ffn_nvfp4_strerror(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int ffn_nvfp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFN_NVFP4_H */

@@ -1,0 +1,125 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every
+function the header declares, and rejects invalid arguments before anything
+is launched. Every call here fails validation (or is the empty M = 0 call),
+so no HIP work is ever enqueued; fake device addresses are never touched.
+"""
+import ctypes
+
+import pytest
+
+import w4a16_nvfp4_dense_amd as ffn
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def W(codes=FAKE, scales=FAKE + 0x10000, scale2=1.0):
+    return ffn.WeightStruct(codes, scales, scale2)
+
+
+def fwd(x=FAKE, M=1, K=256, N=512, g=None, u=None, d=None, act=0, ws=FAKE + 0x200000, wsb=1 << 20,
+        out=FAKE + 0x400000):
+    g = g or W()
+    u = u or W()
+    d = d or W()
+    return ffn.load().ffn_nvfp4_forward(x, M, K, N, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), act,
+                                        ws, wsb, out, 0)
+
+
+def dual(x=FAKE, M=1, K=256, N=512, g=None, u=None, go=FAKE + 0x200000, uo=FAKE + 0x400000):
+    g = g or W()
+    u = u or W()
+    return ffn.load().ffn_nvfp4_dual_gemv(x, M, K, N, ctypes.byref(g), ctypes.byref(u), go, uo, 0)
+
+
+def down(gi=FAKE, ui=FAKE + 0x200000, M=1, N=512, K=256, d=None, act=0, out=FAKE + 0x400000):
+    d = d or W()
+    return ffn.load().ffn_nvfp4_down_gemv(gi, ui, M, N, K, ctypes.byref(d), act, out, 0)
+
+
+def test_exports_every_header_symbol():
+    lib = ffn.load()
+    names = ffn.header_functions()
+    assert set(names) == {"ffn_nvfp4_forward", "ffn_nvfp4_dual_gemv", "ffn_nvfp4_down_gemv",
+                          "ffn_nvfp4_workspace_bytes", "ffn_nvfp4_strerror", "ffn_nvfp4_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_strerror_workspace():
+    assert ffn.version() >= 100
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+        assert ffn.strerror(s) and ffn.strerror(s) != "unknown status"
+    assert ffn.strerror(-99) == "unknown status"
+    assert ffn.workspace_bytes(1, 5120, 17408) == 2 * 17408 * 4
+    assert ffn.workspace_bytes(8, 5120, 17408) == 2 * 8 * 17408 * 4
+    assert ffn.workspace_bytes(0, 256, 512) == 0
+    assert ffn.workspace_bytes(9, 256, 512) == 0
+    assert ffn.workspace_bytes(1, 250, 512) == 0
+    assert ffn.workspace_bytes(3, 96, 160) % 256 == 0
+
+
+@pytest.mark.parametrize("call", [fwd, dual, down])
+def test_null_pointers(call):
+    if call is fwd:
+        assert fwd(x=0) == ffn.ERR_NULL
+        assert fwd(out=0) == ffn.ERR_NULL
+        assert fwd(ws=0) == ffn.ERR_NULL
+        assert fwd(g=W(codes=0)) == ffn.ERR_NULL
+        assert fwd(d=W(scales=0)) == ffn.ERR_NULL
+    elif call is dual:
+        assert dual(x=0) == ffn.ERR_NULL
+        assert dual(go=0) == ffn.ERR_NULL
+        assert dual(u=W(codes=0)) == ffn.ERR_NULL
+    else:
+        assert down(gi=0) == ffn.ERR_NULL
+        assert down(out=0) == ffn.ERR_NULL
+        assert down(d=W(codes=0)) == ffn.ERR_NULL
+
+
+def test_misaligned():
+    assert fwd(x=FAKE + 2) == ffn.ERR_ALIGN
+    assert fwd(out=FAKE + 0x400008) == ffn.ERR_ALIGN
+    assert fwd(ws=FAKE + 4) == ffn.ERR_ALIGN
+    assert fwd(g=W(codes=FAKE + 8)) == ffn.ERR_ALIGN
+    assert fwd(u=W(scales=FAKE + 1)) == ffn.ERR_ALIGN
+    assert dual(go=FAKE + 4) == ffn.ERR_ALIGN
+    assert down(ui=FAKE + 0x200004) == ffn.ERR_ALIGN
+    # scales only need 2-byte alignment: this one fails later, on M
+    assert fwd(g=W(scales=FAKE + 2), M=9) == ffn.ERR_BATCH
+
+
+@pytest.mark.parametrize("K,N", [(0, 512), (256, 0), (250, 512), (256, 500), (-32, 512), (65568, 512),
+                                 (256, 70000)])
+def test_bad_shapes(K, N):
+    assert fwd(K=K, N=N) == ffn.ERR_SHAPE
+    assert dual(K=K, N=N) == ffn.ERR_SHAPE
+    assert down(K=K, N=N) == ffn.ERR_SHAPE
+
+
+@pytest.mark.parametrize("M", [-1, 9, 16, 100])
+def test_unsupported_batch(M):
+    assert fwd(M=M) == ffn.ERR_BATCH
+    assert dual(M=M) == ffn.ERR_BATCH
+    assert down(M=M) == ffn.ERR_BATCH
+
+
+def test_bad_act_and_workspace_and_scale2():
+    assert fwd(act=2) == ffn.ERR_ACT
+    assert fwd(act=-1) == ffn.ERR_ACT
+    assert down(act=7) == ffn.ERR_ACT
+    assert fwd(wsb=ffn.workspace_bytes(1, 256, 512) - 1) == ffn.ERR_WORKSPACE
+    assert fwd(M=2, wsb=ffn.workspace_bytes(1, 256, 512)) == ffn.ERR_WORKSPACE
+    assert fwd(g=W(scale2=float("nan"))) == ffn.ERR_SCALE2
+    assert dual(u=W(scale2=float("inf"))) == ffn.ERR_SCALE2
+    assert down(d=W(scale2=float("-inf"))) == ffn.ERR_SCALE2
+
+
+def test_empty_batch_is_a_noop():
+    # M = 0: nothing to compute; output/workspace pointers may be NULL.
+    assert fwd(M=0, x=0, out=0, ws=0, wsb=0) == ffn.OK
+    assert dual(M=0, x=0, go=0, uo=0) == ffn.OK
+    assert down(M=0, gi=0, ui=0, out=0) == ffn.OK
+    # ...but the rest is still validated
+    assert fwd(M=0, K=100) == ffn.ERR_SHAPE
+    assert fwd(M=0, act=5) == ffn.ERR_ACT
+    assert dual(M=0, g=W(codes=0)) == ffn.ERR_NULL

@@ -1,0 +1,228 @@
+"""Python binding of libffn_nvfp4 (MI355X / gfx950 NVFP4 W4A16 gated FFN).
+
+Argument marshalling only: every step of the FFN runs in the HIP kernels of
+``lib/libffn_nvfp4.so`` through its C ABI (``include/ffn_nvfp4.h``). PyTorch
+is used for device memory and streams. There is no fallback: if the library
+is missing or a call fails, an exception is raised.
+
+The functions mirror the C entry points:
+
+* :func:`forward`    -- ``ffn_nvfp4_forward``   out = W_d (act(W_g x) * (W_u x))
+* :func:`dual_gemv`  -- ``ffn_nvfp4_dual_gemv`` gate, up = W_g x, W_u x (fp32)
+* :func:`down_gemv`  -- ``ffn_nvfp4_down_gemv`` out = W_d bf16(act(gate) * up)
+* :func:`workspace_bytes` -- ``ffn_nvfp4_workspace_bytes``
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "lib", "libffn_nvfp4.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "ffn_nvfp4.h")
+
+ACT_SILU = 0
+ACT_GELU_TANH = 1
+
+OK = 0
+ERR_NULL = -1
+ERR_ALIGN = -2
+ERR_SHAPE = -3
+ERR_BATCH = -4
+ERR_ACT = -5
+ERR_WORKSPACE = -6
+ERR_LAUNCH = -7
+ERR_SCALE2 = -8
+
+
+class FfnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({strerror(status)})")
+
+
+class WeightStruct(ctypes.Structure):
+    """ffn_nvfp4_weight: device codes, device scales, host fp32 scale2."""
+
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("scale2", ctypes.c_float)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_WP = ctypes.POINTER(WeightStruct)
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m w4a16_nvfp4_dense_amd.build` "
+                           "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    lib.ffn_nvfp4_version.restype = _I
+    lib.ffn_nvfp4_version.argtypes = []
+    lib.ffn_nvfp4_strerror.restype = ctypes.c_char_p
+    lib.ffn_nvfp4_strerror.argtypes = [_I]
+    lib.ffn_nvfp4_workspace_bytes.restype = ctypes.c_size_t
+    lib.ffn_nvfp4_workspace_bytes.argtypes = [_I, _I, _I]
+    lib.ffn_nvfp4_forward.restype = _I
+    lib.ffn_nvfp4_forward.argtypes = [_P, _I, _I, _I, _WP, _WP, _WP, _I, _P, ctypes.c_size_t, _P, _P]
+    lib.ffn_nvfp4_dual_gemv.restype = _I
+    lib.ffn_nvfp4_dual_gemv.argtypes = [_P, _I, _I, _I, _WP, _WP, _P, _P, _P]
+    lib.ffn_nvfp4_down_gemv.restype = _I
+    lib.ffn_nvfp4_down_gemv.argtypes = [_P, _P, _I, _I, _I, _WP, _I, _P, _P]
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER_PATH) -> Sequence[str]:
+    """Names of the functions the public header declares."""
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ffn_nvfp4_[a-z_0-9]+)\s*\(", text)))
+
+
+def version() -> int:
+    return load().ffn_nvfp4_version()
+
+
+def strerror(status: int) -> str:
+    return load().ffn_nvfp4_strerror(int(status)).decode()
+
+
+def workspace_bytes(M: int, K: int, N: int) -> int:
+    return int(load().ffn_nvfp4_workspace_bytes(int(M), int(K), int(N)))
+
+
+# ------------------------------------------------------------ torch marshalling
+
+
+@dataclasses.dataclass
+class DeviceWeight:
+    """An NVFP4 weight resident on the GPU: codes uint8 [rows, cols/2],
+    scales uint8 [rows, cols/16] (both torch tensors on the device) and the
+    per-tensor scale2 (host float)."""
+
+    codes: "object"
+    scales: "object"
+    scale2: float
+
+    @property
+    def rows(self) -> int:
+        return int(self.codes.shape[0])
+
+    @property
+    def cols(self) -> int:
+        return int(self.codes.shape[1]) * 2
+
+    def struct(self) -> WeightStruct:
+        return WeightStruct(self.codes.data_ptr(), self.scales.data_ptr(), float(self.scale2))
+
+    @classmethod
+    def from_host(cls, w, device="cuda") -> "DeviceWeight":
+        """From an object with numpy ``codes``, ``scales`` and ``scale2``."""
+        import torch
+        return cls(torch.from_numpy(w.codes).to(device), torch.from_numpy(w.scales).to(device),
+                   float(w.scale2))
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_tensor(t, dtype, shape, name):
+    import torch
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise FfnError(status, what)
+
+
+def forward(x, gate: DeviceWeight, up: DeviceWeight, down: DeviceWeight, act: int = ACT_SILU,
+            out=None, workspace=None, stream=None):
+    """out[M, K] (bf16) = W_d (act(W_g x) * (W_u x)) for x bf16 [M, K]."""
+    import torch
+    M, K = x.shape
+    N = gate.rows
+    _check_tensor(x, torch.bfloat16, (M, K), "x")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
+    _check_tensor(out, torch.bfloat16, (M, K), "out")
+    need = workspace_bytes(M, K, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    g, u, d = gate.struct(), up.struct(), down.struct()
+    rc = load().ffn_nvfp4_forward(x.data_ptr(), M, K, N, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                                  int(act), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  out.data_ptr(), _stream_handle(stream))
+    _check(rc, "ffn_nvfp4_forward")
+    return out
+
+
+def dual_gemv(x, gate: DeviceWeight, up: DeviceWeight, gate_out=None, up_out=None, stream=None):
+    """(gate, up) fp32 [M, N] = (scale2_g W_g x, scale2_u W_u x)."""
+    import torch
+    M, K = x.shape
+    N = gate.rows
+    _check_tensor(x, torch.bfloat16, (M, K), "x")
+    if gate_out is None:
+        gate_out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if up_out is None:
+        up_out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check_tensor(gate_out, torch.float32, (M, N), "gate_out")
+    _check_tensor(up_out, torch.float32, (M, N), "up_out")
+    g, u = gate.struct(), up.struct()
+    rc = load().ffn_nvfp4_dual_gemv(x.data_ptr(), M, K, N, ctypes.byref(g), ctypes.byref(u),
+                                    gate_out.data_ptr(), up_out.data_ptr(), _stream_handle(stream))
+    _check(rc, "ffn_nvfp4_dual_gemv")
+    return gate_out, up_out
+
+
+def down_gemv(gate_in, up_in, down: DeviceWeight, act: int = ACT_SILU, out=None, stream=None):
+    """out[M, K] (bf16) = W_d bf16(act(gate) * up) with the activation fused
+    into the down GEMV's input load."""
+    import torch
+    M, N = gate_in.shape
+    K = down.rows
+    _check_tensor(gate_in, torch.float32, (M, N), "gate_in")
+    _check_tensor(up_in, torch.float32, (M, N), "up_in")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=gate_in.device)
+    _check_tensor(out, torch.bfloat16, (M, K), "out")
+    d = down.struct()
+    rc = load().ffn_nvfp4_down_gemv(gate_in.data_ptr(), up_in.data_ptr(), M, N, K, ctypes.byref(d), int(act),
+                                    out.data_ptr(), _stream_handle(stream))
+    _check(rc, "ffn_nvfp4_down_gemv")
+    return out
+
+
+def bf16_from_bits(bits, device="cuda"):
+    """A bf16 torch tensor on ``device`` from a numpy uint16 array of bf16 bits."""
+    import numpy as np
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def bf16_to_f64(t):
+    """A bf16 torch tensor as a float64 numpy array (exact)."""
+    return t.float().cpu().double().numpy()

@@ -1,0 +1,40 @@
+// kernels.h -- internal launchers of the NVFP4 FFN kernels (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ffn {
+
+struct WeightArg {
+    const uint8_t *codes;   // [rows, cols/2]
+    const uint8_t *scales;  // [rows, cols/16]
+    float scale2;
+};
+
+// Kinds of input staged into LDS along the reduction dimension.
+enum InKind : int {
+    IN_BF16 = 0,         // bf16 [M, cols] (x for the dual GEMV, h for the down GEMV)
+    IN_GATEUP_SILU = 1,  // fp32 gate, up [M, cols]; staged h = bf16(SiLU(gate) * up)
+    IN_GATEUP_GELU = 2,  // same with GELU-tanh
+};
+
+// What the row results are turned into.
+enum OutKind : int {
+    OUT_F32_PAIR = 0,  // two projections: out0 = s2_0 * y0, out1 = s2_1 * y1 (fp32 [M, rows])
+    OUT_BF16 = 1,      // one projection: out0 = bf16(s2_0 * y0) [M, rows]
+    OUT_H_SILU = 2,    // two projections: out0 = bf16(SiLU(s2_0 y0) * s2_1 y1) [M, rows]
+    OUT_H_GELU = 3,    // same with GELU-tanh
+};
+
+// Streaming GEMV over NVFP4 weights for 1 <= M <= 8 activation rows:
+// y_t[m, r] = sum_c W_t[r, c] * a[m, c] for one (nmat = 1) or two (nmat = 2)
+// weights of shape [rows, cols] sharing the same input a. Returns a HIP error
+// code (hipSuccess on launch).
+hipError_t launch_gemv(int M, int nmat, InKind in, OutKind out,
+                       const void *in0, const float *in1,
+                       const WeightArg &w0, const WeightArg &w1,
+                       void *out0, void *out1, int rows, int cols, hipStream_t stream);
+
+}  // namespace ffn

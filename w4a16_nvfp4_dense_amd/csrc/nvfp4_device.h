@@ -1,0 +1,116 @@
+// nvfp4_device.h -- gfx950 device helpers for NVFP4 (E2M1 codes + E4M3 scales)
+// dequantisation, bf16 dot products, wave-level reductions and the gate
+// activations of the gated FFN.
+//
+// Format (dense_ffn.rs page, DenseFfnLayer::ensure_int8_weight doc comment):
+// packed E2M1 codes [rows, cols/2], one E4M3 scale per 16 columns
+// [rows, cols/16], one fp32 per-tensor scale2. The even column of a byte is its
+// low nibble.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ffn {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Byte SEL of `word` holds two E2M1 codes; returns them as a bf16 pair with
+// element 0 = low nibble. The hardware conversion takes an fp32 scale of which
+// it only uses the power-of-two exponent, so it is called with 1.0 and the
+// E4M3 block scale is applied separately. E2M1 values are exact in bf16.
+template <int SEL>
+__device__ __forceinline__ bf16x2_t fp4x2_to_bf16x2(uint32_t word)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, SEL);
+}
+
+// Byte SEL of `word` as an OCP E4M3FN value (gfx950 decodes the OCP variant:
+// bias 7, no infinities, S.1111.111 = NaN). Exact in fp32.
+template <int SEL>
+__device__ __forceinline__ float e4m3_to_f32(uint32_t word)
+{
+    return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word), SEL);
+}
+
+// c + a.x*b.x + a.y*b.y with bf16 pairs and an fp32 accumulator.
+__device__ __forceinline__ float dot2_bf16(bf16x2_t a, bf16x2_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u)
+{
+    return __builtin_bit_cast(bf16x2_t, u);
+}
+
+// Round two fp32 values to bf16 (nearest even) and pack lo | hi << 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float f)
+{
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16)
+{
+    return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// ---------------------------------------------------------------- activations
+// SiLU(g) = g / (1 + e^-g). GELU with the tanh approximation,
+// 0.5 g (1 + tanh(s (g + 0.044715 g^3))), s = sqrt(2/pi), is written in the
+// equivalent form g / (1 + e^(-2 s (g + 0.044715 g^3))) so both gates cost one
+// exponential and one reciprocal. Large |g| saturate to g or -0 without NaN.
+enum Act : int { ACT_SILU = 0, ACT_GELU_TANH = 1 };
+
+template <int ACT>
+__device__ __forceinline__ float gate_act(float g)
+{
+    float z;
+    if constexpr (ACT == ACT_SILU) {
+        z = -g;
+    } else {
+        constexpr float two_s = 1.5957691216057308f;  // 2 * sqrt(2/pi)
+        z = -two_s * (g + 0.044715f * g * g * g);
+    }
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(z));
+}
+
+// ------------------------------------------------------ wave-level reductions
+// DPP lane moves (GFX9 encodings): quad_perm, row (16-lane) mirrors and row
+// broadcasts. `update_dpp(old, src, ...)` writes `old` in lanes whose row is
+// masked off, so masked rows add zero.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_move(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum of v over each aligned segment of LPR lanes (LPR = 8, 16, 32 or 64),
+// in a fixed tree order; the total is valid in the segment's last lane
+// (lane % LPR == LPR - 1). Every lane of the wave must execute this.
+template <int LPR>
+__device__ __forceinline__ float segment_sum(float v)
+{
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "segment width");
+    v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]: pairs
+    v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]: quads
+    v += dpp_move<0x141>(v);  // row_half_mirror: 8 lanes
+    if constexpr (LPR >= 16)
+        v += dpp_move<0x140>(v);  // row_mirror: 16 lanes
+    if constexpr (LPR >= 32)
+        v += dpp_move<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3: 32 lanes in rows 1, 3
+    if constexpr (LPR >= 64)
+        v += dpp_move<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3: 64 lanes in row 3
+    return v;
+}
+
+}  // namespace ffn
