@@ -1,0 +1,227 @@
+"""Benchmark of the NVFP4 W4A16 gated FFN on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one FFN forward (dual gate+up GEMV, then the down GEMV with the
+activation fused into its input load) over one batch of synthetic input. The
+default workload is the M=1 SwiGLU decode FFN (hidden 5120, intermediate
+17408). Weights are rotated over several byte-identical copies so the 256 MB
+Infinity Cache cannot serve repeated reads; all inputs are resident in HBM
+before the timed region.
+
+Prints ONE JSON line on stdout. `value` is the achieved algorithmic HBM
+bandwidth of the whole forward (bytes the method must move / time), with
+`us_per_forward` beside it; `roofline` reports the dominant kernel (the dual
+GEMV, 2/3 of the bytes) timed with HIP events around each of its launches on
+the stream it runs on; `cpu_baseline` times the CPU oracle on a bounded sample
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "µs/FFN forward + achieved HBM GB/s (% of peak), NVFP4 SwiGLU decode M=1"
+
+WORKLOADS = {
+    # name: (config index, M)
+    "tiny_silu_m1": (0, 1),
+    "decode_silu_m1": (1, 1),
+    "decode_gelu_m1": (2, 1),
+    "verify_silu_m2": (3, 2),
+    "verify_silu_m3": (3, 3),
+    "verify_silu_m8": (3, 8),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(M, K, N):
+    """Bytes each launch must move at minimum: NVFP4 codes + E4M3 scales of
+    the weights it streams, its activation input and its output. The forward
+    passes h = act(gate) * up between its two kernels as bf16 [M, N]."""
+    w1 = N * K // 2 + N * K // 16          # one [N, K] (or [K, N]) NVFP4 weight
+    return {
+        "weights": 3 * w1,
+        "forward": 3 * w1 + 2 * M * K + 2 * M * N + 2 * M * N + 2 * M * K,
+        # the dual GEMV entry as timed for the roofline: fp32 gate and up out
+        "dual_f32": 2 * w1 + 2 * M * K + 2 * M * N * 4,
+        "down_h": w1 + 2 * M * N + 2 * M * K,
+    }
+
+
+def cpu_baseline(case, seconds):
+    import numpy as np
+    import oracle
+
+    orc = oracle.default()
+    b = algorithmic_bytes(case.M, case.K, case.N)["forward"]
+    orc.ffn(case)  # warm
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.ffn(case)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    us = el / n * 1e6
+    return {"value": round(b / (us * 1e-6) / 1e9, 3), "unit": "GB/s", "us_per_forward": round(us, 1),
+            "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"{n} full forwards of the same workload (fp64 C oracle, OpenMP over output rows), "
+                      f"{el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="decode_silu_m1", choices=sorted(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=4, help="weight copies rotated over")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import ffn_inputs as fi
+    import w4a16_nvfp4_dense_amd as ffn
+
+    lib = ffn.load()
+    idx, M = WORKLOADS[args.workload]
+    case = fi.make_config(idx, M=M) if idx == 3 else fi.make_config(idx)
+    K, N = case.K, case.N
+    nbytes = algorithmic_bytes(M, K, N)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    copies = []
+    for _ in range(args.copies):
+        copies.append((ffn.DeviceWeight.from_host(case.gate, dev), ffn.DeviceWeight.from_host(case.up, dev),
+                       ffn.DeviceWeight.from_host(case.down, dev)))
+    x = ffn.bf16_from_bits(case.x_bits, dev)
+    out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    ws_bytes = ffn.workspace_bytes(M, K, N)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    gate_out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    up_out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    structs = [(g.struct(), u.struct(), d.struct()) for g, u, d in copies]
+    refs = [(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d)) for g, u, d in structs]
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    xp, op, wp = x.data_ptr(), out.data_ptr(), ws.data_ptr()
+    gp, upp = gate_out.data_ptr(), up_out.data_ptr()
+    fwd = lib.ffn_nvfp4_forward
+    dual = lib.ffn_nvfp4_dual_gemv
+    act = case.act
+    nc = len(refs)
+
+    def step(i):
+        g, u, d = refs[i % nc]
+        rc = fwd(xp, M, K, N, g, u, d, act, wp, ws_bytes, op, sh)
+        if rc:
+            raise ffn.FfnError(rc, "ffn_nvfp4_forward")
+
+    # copies are byte-identical, so every copy must give the same output
+    outs = []
+    for i in range(nc):
+        step(i)
+        outs.append(out.clone())
+    torch.cuda.synchronize()
+    assert all(torch.equal(o, outs[0]) for o in outs), "weight copies disagree"
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    us = ms_per_step * 1e3
+    gbs = nbytes["forward"] / (us * 1e-6) / 1e9
+    log(f"[bench] {args.workload}: {us:.2f} us/forward, {gbs:.1f} GB/s algorithmic "
+        f"({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f}); host wall {wall * 1e3 / args.steps * 1e3:.2f} us/step")
+
+    # Dominant kernel: the dual GEMV, each launch bracketed by events on its stream.
+    nk = min(args.steps, 1000)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nk)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(nk)]
+    for i in range(args.warmup):
+        g, u, _ = refs[i % nc]
+        dual(xp, M, K, N, g, u, gp, upp, sh)
+    for i in range(nk):
+        g, u, _ = refs[i % nc]
+        starts[i].record(stream)
+        rc = dual(xp, M, K, N, g, u, gp, upp, sh)
+        ends[i].record(stream)
+        if rc:
+            raise ffn.FfnError(rc, "ffn_nvfp4_dual_gemv")
+    torch.cuda.synchronize()
+    dual_us = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / nk * 1e3
+    dual_gbs = nbytes["dual_f32"] / (dual_us * 1e-6) / 1e9
+    log(f"[bench] dual GEMV: {dual_us:.2f} us/launch, {dual_gbs:.1f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "us_per_forward": round(us, 3),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{case.name}: gated FFN forward, M={M}, hidden K={K}, intermediate N={N}, "
+                        f"act={fi.ACT_NAMES[act]}, NVFP4 weights rotated over {nc} copies",
+            "M": M, "K": K, "N": N, "act": fi.ACT_NAMES[act],
+            "algorithmic_bytes_per_forward": nbytes["forward"],
+        },
+        "roofline": {
+            "kernel": "dual gate+up GEMV (ffn_nvfp4_dual_gemv: gate, up fp32 out)",
+            "bound": "hbm",
+            "achieved": round(dual_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dual_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "us_per_launch": round(dual_us, 3),
+            "algorithmic_bytes_per_launch": nbytes["dual_f32"],
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -95,8 +95,8 @@ size_t ffn_nvfp4_workspace_bytes(int M, int K, int N);
  *   down       host struct describing a [K, N] weight
  *   act        ffn_nvfp4_act
  *   workspace  device, >= ffn_nvfp4_workspace_bytes(M, K, N) bytes, 16-byte
- *              aligned; holds gate and up (fp32) between the two GEMVs;
- *              clobbered by the call
+ *              aligned; holds h = bf16(act(gate) * up) [M, N] between the
+ *              two GEMVs; clobbered by the call
  *   out        device, bf16 [M, K], 16-byte aligned; may not alias x
  * The intermediate h = act(gate) * up is rounded to bf16 once; gate and up
  * are kept in fp32 up to that point. */

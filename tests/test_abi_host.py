@@ -50,8 +50,8 @@ def test_version_strerror_workspace():
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert ffn.strerror(s) and ffn.strerror(s) != "unknown status"
     assert ffn.strerror(-99) == "unknown status"
-    assert ffn.workspace_bytes(1, 5120, 17408) == 2 * 17408 * 4
-    assert ffn.workspace_bytes(8, 5120, 17408) == 2 * 8 * 17408 * 4
+    assert ffn.workspace_bytes(1, 5120, 17408) == 17408 * 2
+    assert ffn.workspace_bytes(8, 5120, 17408) == 8 * 17408 * 2
     assert ffn.workspace_bytes(0, 256, 512) == 0
     assert ffn.workspace_bytes(9, 256, 512) == 0
     assert ffn.workspace_bytes(1, 250, 512) == 0

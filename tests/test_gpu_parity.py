@@ -81,6 +81,12 @@ SMALL = [
     (7, 256, 3072, fi.ACT_SILU, 10),
     (8, 5120, 2048, fi.ACT_SILU, 11),       # several LDS pieces for M = 8
     (8, 1056, 8224, fi.ACT_GELU_TANH, 12),  # 33 and 257 chunks: ragged, several pieces
+    # row-streaming kernels (M <= 2, 33 or more chunks per row)
+    (1, 1056, 2080, fi.ACT_SILU, 13),       # 33 / 65 chunks: partly masked last lane chunk
+    (2, 2080, 1056, fi.ACT_GELU_TANH, 14),
+    (1, 4096, 96, fi.ACT_SILU, 15),         # fewer rows than compute units
+    (2, 2048, 20000, fi.ACT_SILU, 16),      # 79 rows per CU; 625-chunk down rows from LDS
+    (1, 12288, 4096, fi.ACT_GELU_TANH, 17), # 6 chunks per lane
 ]
 
 

@@ -49,6 +49,26 @@ int launch_status(hipError_t e)
     return e == hipSuccess ? FFN_NVFP4_OK : FFN_NVFP4_ERR_LAUNCH;
 }
 
+// Dual GEMV: the LDS-ring kernels where they apply (M <= 2), else the
+// general LDS-staged kernel.
+hipError_t run_dual(int M, ffn::OutKind out, const void *x, const ffn::WeightArg &g, const ffn::WeightArg &u,
+                    void *out0, void *out1, int N, int K, hipStream_t stream)
+{
+    hipError_t e = ffn::launch_ring_dual(M, out, x, g, u, out0, out1, N, K, stream);
+    if (e != hipErrorNotSupported)
+        return e;
+    return ffn::launch_gemv(M, 2, ffn::IN_BF16, out, x, nullptr, g, u, out0, out1, N, K, stream);
+}
+
+hipError_t run_down(int M, ffn::InKind in, const void *in0, const float *in1, const ffn::WeightArg &d,
+                    void *out, int K, int N, hipStream_t stream)
+{
+    hipError_t e = ffn::launch_ring_down(M, in, in0, in1, d, out, K, N, stream);
+    if (e != hipErrorNotSupported)
+        return e;
+    return ffn::launch_gemv(M, 1, in, ffn::OUT_BF16, in0, in1, d, d, out, nullptr, K, N, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -80,8 +100,8 @@ size_t ffn_nvfp4_workspace_bytes(int M, int K, int N)
         return 0;
     if (M == 0)
         return 0;
-    // gate and up in fp32, [M, N] each, one after the other
-    size_t bytes = 2 * static_cast<size_t>(M) * static_cast<size_t>(N) * 4;
+    // h = act(gate) * up in bf16, [M, N]
+    size_t bytes = static_cast<size_t>(M) * static_cast<size_t>(N) * 2;
     return (bytes + 255) & ~static_cast<size_t>(255);
 }
 
@@ -101,8 +121,7 @@ int ffn_nvfp4_dual_gemv(const void *x, int M, int K, int N, const ffn_nvfp4_weig
         return FFN_NVFP4_ERR_NULL;
     if (!aligned(x, 16) || !aligned(gate_out, 16) || !aligned(up_out, 16))
         return FFN_NVFP4_ERR_ALIGN;
-    return launch_status(ffn::launch_gemv(M, 2, ffn::IN_BF16, ffn::OUT_F32_PAIR, x, nullptr, warg(gate),
-                                          warg(up), gate_out, up_out, N, K, stream));
+    return launch_status(run_dual(M, ffn::OUT_F32_PAIR, x, warg(gate), warg(up), gate_out, up_out, N, K, stream));
 }
 
 int ffn_nvfp4_down_gemv(const float *gate_in, const float *up_in, int M, int N, int K,
@@ -124,8 +143,7 @@ int ffn_nvfp4_down_gemv(const float *gate_in, const float *up_in, int M, int N, 
     if (!aligned(gate_in, 16) || !aligned(up_in, 16) || !aligned(out, 16))
         return FFN_NVFP4_ERR_ALIGN;
     const ffn::InKind in = act == FFN_NVFP4_ACT_SILU ? ffn::IN_GATEUP_SILU : ffn::IN_GATEUP_GELU;
-    return launch_status(ffn::launch_gemv(M, 1, in, ffn::OUT_BF16, gate_in, up_in, warg(down), warg(down), out,
-                                          nullptr, K, N, stream));
+    return launch_status(run_down(M, in, gate_in, up_in, warg(down), out, K, N, stream));
 }
 
 int ffn_nvfp4_forward(const void *x, int M, int K, int N, const ffn_nvfp4_weight *gate,
@@ -149,17 +167,15 @@ int ffn_nvfp4_forward(const void *x, int M, int K, int N, const ffn_nvfp4_weight
         return FFN_NVFP4_ERR_ALIGN;
     if (workspace_bytes < ffn_nvfp4_workspace_bytes(M, K, N))
         return FFN_NVFP4_ERR_WORKSPACE;
-    // Dual GEMV writes gate and up (fp32) to the workspace; the down GEMV
-    // stages bf16(act(gate) * up) into LDS as it loads them.
-    float *gate_ws = static_cast<float *>(workspace);
-    float *up_ws = gate_ws + static_cast<size_t>(M) * N;
-    hipError_t e = ffn::launch_gemv(M, 2, ffn::IN_BF16, ffn::OUT_F32_PAIR, x, nullptr, warg(gate), warg(up),
-                                    gate_ws, up_ws, N, K, stream);
+    // The dual GEMV's epilogue computes h = bf16(act(s2_g gate) * (s2_u up))
+    // once per element (64 rows per instruction); the down GEMV streams W_d
+    // against h staged in LDS or registers. Bit-identical to the dual GEMV
+    // followed by the down GEMV with the activation in its input load.
+    const ffn::OutKind epi = act == FFN_NVFP4_ACT_SILU ? ffn::OUT_H_SILU : ffn::OUT_H_GELU;
+    hipError_t e = run_dual(M, epi, x, warg(gate), warg(up), workspace, nullptr, N, K, stream);
     if (e != hipSuccess)
         return FFN_NVFP4_ERR_LAUNCH;
-    const ffn::InKind in = act == FFN_NVFP4_ACT_SILU ? ffn::IN_GATEUP_SILU : ffn::IN_GATEUP_GELU;
-    return launch_status(ffn::launch_gemv(M, 1, in, ffn::OUT_BF16, gate_ws, up_ws, warg(down), warg(down), out,
-                                          nullptr, K, N, stream));
+    return launch_status(run_down(M, ffn::IN_BF16, workspace, nullptr, warg(down), out, K, N, stream));
 }
 
 }  // extern "C"

@@ -263,15 +263,22 @@ hipError_t launch_m(int M, int lpr, const GemvParams &p, size_t lds_bytes, hipSt
     }
 }
 
-// Lanes per row: the widest of 64/32/16/8 that divides the chunk count, else 8
-// (the last iteration of a row is then partly masked).
-int pick_lpr(int cpr)
+}  // namespace
+
+// Lanes per row as a function of the reduction length only: the smallest of
+// 8/16/32/64 covering the row's chunks, 64 for rows of 33 chunks or more. Every
+// kernel that computes a row with a given reduction length uses this split and
+// the same per-lane order, so a row's result does not depend on M or on which
+// kernel ran it.
+int lanes_per_row(int cpr)
 {
-    for (int l : {64, 32, 16, 8})
-        if (cpr % l == 0)
-            return l;
-    return 8;
+    int l = 8;
+    while (l < 64 && l < cpr)
+        l *= 2;
+    return l;
 }
+
+namespace {
 
 }  // namespace
 
@@ -293,7 +300,7 @@ hipError_t launch_gemv(int M, int nmat, InKind in, OutKind out, const void *in0,
     p.rows = rows;
     p.cols = cols;
     p.cpr = cols / 32;
-    const int lpr = pick_lpr(p.cpr);
+    const int lpr = lanes_per_row(p.cpr);
     // Largest piece (in chunks) whose staged copy fits the budget.
     const size_t unit = static_cast<size_t>(M) * 4 * 16;
     int piece = static_cast<int>(kLdsBudget / unit) - 1;

@@ -38,3 +38,32 @@ hipError_t launch_gemv(int M, int nmat, InKind in, OutKind out,
                        void *out0, void *out1, int rows, int cols, hipStream_t stream);
 
 }  // namespace ffn
+
+namespace ffn {
+
+// Row-streaming GEMV (M = 1 or 2, reduction length up to 64 * 32 * kStreamMaxIt
+// columns): one workgroup per compute unit, whole-wave rows, activations in
+// registers. Returns hipErrorNotSupported for shapes it does not cover.
+constexpr int kStreamMaxIt = 12;
+hipError_t launch_stream_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1,
+                              void *out0, void *out1, int rows, int cols, hipStream_t stream);
+hipError_t launch_stream_down(int M, InKind in, const void *in0, const float *in1, const WeightArg &w,
+                              void *out, int rows, int cols, hipStream_t stream);
+
+// LDS-ring GEMV (M = 1 or 2; rows of 33 or more chunks, an even number of
+// them, at most 64 * 32 * kStreamMaxIt columns): weights streamed into LDS by
+// direct global->LDS loads, activations in registers. Returns
+// hipErrorNotSupported for shapes it does not cover.
+hipError_t launch_ring_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1,
+                            void *out0, void *out1, int rows, int cols, hipStream_t stream);
+hipError_t launch_ring_down(int M, InKind in, const void *in0, const float *in1, const WeightArg &w, void *out,
+                            int rows, int cols, hipStream_t stream);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// Lanes that share one weight row for a reduction of `cpr` 32-column chunks
+// (8, 16, 32 or 64); the row-streaming kernels require 64.
+int lanes_per_row(int cpr);
+
+}  // namespace ffn
