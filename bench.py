@@ -12,9 +12,9 @@ before the timed region.
 Prints ONE JSON line on stdout. `value` is the achieved algorithmic HBM
 bandwidth of the whole forward (bytes the method must move / time), with
 `us_per_forward` beside it; `roofline` reports the dominant kernel (the dual
-GEMV, 2/3 of the bytes) timed with HIP events around each of its launches on
-the stream it runs on; `cpu_baseline` times the CPU oracle on a bounded sample
-of the same workload.
+GEMV, 2/3 of the bytes) timed with HIP events on the stream it runs on, around
+a batch of back-to-back launches; `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -61,6 +61,22 @@ def algorithmic_bytes(M, K, N):
     }
 
 
+def measured_traffic(workload):
+    """HBM bytes per launch of the dual GEMV from the committed counter
+    summary (profiles/traffic_dual_gemv_<workload>.json), or None when there is
+    none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_dual_gemv_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    from w4a16_nvfp4_dense_amd import profiling
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != profiling.source_digest():
+        log(f"[bench] {path} was measured on other kernel sources: traffic not reported")
+        return None
+    return t
+
+
 def cpu_baseline(case, seconds):
     import numpy as np
     import oracle
@@ -92,6 +108,9 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated over")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 64 MiB device-to-device copy (untimed), the reference "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -147,6 +166,14 @@ def main():
     torch.cuda.synchronize()
     assert all(torch.equal(o, outs[0]) for o in outs), "weight copies disagree"
 
+    if args.calibrate_copy:
+        src = torch.empty(64 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -166,25 +193,31 @@ def main():
     log(f"[bench] {args.workload}: {us:.2f} us/forward, {gbs:.1f} GB/s algorithmic "
         f"({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f}); host wall {wall * 1e3 / args.steps * 1e3:.2f} us/step")
 
-    # Dominant kernel: the dual GEMV, each launch bracketed by events on its stream.
+    # Dominant kernel: the dual GEMV, timed with events on its stream around a
+    # batch of back-to-back launches (rotating the weight copies); the average
+    # includes the short gaps between dependent launches.
     nk = min(args.steps, 1000)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(nk)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(nk)]
     for i in range(args.warmup):
         g, u, _ = refs[i % nc]
         dual(xp, M, K, N, g, u, gp, upp, sh)
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
     for i in range(nk):
         g, u, _ = refs[i % nc]
-        starts[i].record(stream)
         rc = dual(xp, M, K, N, g, u, gp, upp, sh)
-        ends[i].record(stream)
         if rc:
             raise ffn.FfnError(rc, "ffn_nvfp4_dual_gemv")
+    d1.record(stream)
     torch.cuda.synchronize()
-    dual_us = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / nk * 1e3
+    dual_us = d0.elapsed_time(d1) / nk * 1e3
     dual_gbs = nbytes["dual_f32"] / (dual_us * 1e-6) / 1e9
     log(f"[bench] dual GEMV: {dual_us:.2f} us/launch, {dual_gbs:.1f} GB/s")
 
+    traffic = measured_traffic(args.workload)
+    if traffic is not None:
+        log(f"[bench] measured HBM traffic of the dual GEMV: {traffic['bytes'] / 1e6:.2f} MB per launch "
+            f"({traffic['bytes'] / nbytes['dual_f32']:.4f} x algorithmic)")
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -213,7 +246,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dual_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else round(traffic["bytes"]),
             "us_per_launch": round(dual_us, 3),
             "algorithmic_bytes_per_launch": nbytes["dual_f32"],
         },

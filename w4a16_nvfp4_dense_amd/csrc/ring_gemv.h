@@ -102,7 +102,9 @@ __global__ __launch_bounds__(64 * W) void ring_gemv_kernel(const RingParams p)
     // generic -> LDS address space (a C-style cast is the only way to spell it)
     FFN_LDS uint8_t *lds = (FFN_LDS uint8_t *)lds_raw;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // The wave index is uniform across the wave; saying so keeps row
+    // addresses in scalar registers (scalar base + per-lane offset loads).
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Rows are interleaved over all waves of the grid (wave g takes rows g,
     // g + G, g + 2G, ...), so at any moment the whole GPU streams one window
     // of consecutive rows, which HBM serves far better than scattered blocks.

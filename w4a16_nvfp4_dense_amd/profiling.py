@@ -1,0 +1,119 @@
+"""Summaries of rocprofv3 output for the library's kernels.
+
+    python -m w4a16_nvfp4_dense_amd.profiling stats   TRACE_DIR  > summary.txt
+    python -m w4a16_nvfp4_dense_amd.profiling traffic FETCH_DIR WRITE_DIR KERNEL_SUBSTR OUT.json
+
+``stats`` reads the ``*_kernel_stats.csv`` of a ``rocprofv3 --kernel-trace
+--stats --output-format csv`` run. ``traffic`` reads two ``rocprofv3 --pmc``
+runs (``FETCH_SIZE``, then ``WRITE_SIZE``, both in KiB per dispatch) of
+``bench.py --calibrate-copy``: the 64 MiB device copy in that run is the
+reference that scales each counter to bytes (on MI355X ``FETCH_SIZE`` reads
+about half the copied bytes, ``WRITE_SIZE`` all of them). The JSON records a
+digest of the kernel sources, so ``bench.py`` only reports the traffic while
+the kernels are the ones that were measured.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+from typing import Dict, List
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG_DIR, "csrc")
+COPY_BYTES = 64 << 20  # the calibration copy of bench.py --calibrate-copy
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources (csrc/*), in name order."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _one(pattern: str) -> str:
+    found = sorted(glob.glob(pattern, recursive=True))
+    if not found:
+        raise FileNotFoundError(pattern)
+    return found[0]
+
+
+def stats_summary(trace_dir: str, top: int = 8) -> str:
+    path = _one(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
+    rows = list(csv.DictReader(open(path)))
+    out = ["kernel | calls | average us | min us | max us | share %"]
+    for r in rows[:top]:
+        name = r["Name"].replace("void ", "")
+        name = name.split("(")[0] if "ffn::" in name else name[:60]
+        out.append(f"{name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                   f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.2f}")
+    return "\n".join(out)
+
+
+def _counter_rows(run_dir: str, counter: str) -> List[dict]:
+    path = _one(os.path.join(run_dir, "**", "*counter_collection.csv"))
+    return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+
+
+def _per_dispatch(rows: List[dict]) -> Dict[int, dict]:
+    out: Dict[int, dict] = {}
+    for r in rows:
+        d = int(r["Dispatch_Id"])
+        e = out.setdefault(d, {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]), "value": 0.0})
+        e["value"] += float(r["Counter_Value"])
+    return out
+
+
+def counter_bytes(run_dir: str, counter: str, kernel_substr: str) -> dict:
+    """Median KiB per dispatch of `counter` for the matching kernel, and the
+    same counter for the calibration copy (the largest copy kernel)."""
+    disp = _per_dispatch(_counter_rows(run_dir, counter))
+    ker = [e["value"] for e in disp.values() if kernel_substr in e["name"]]
+    copies = [e["value"] for e in disp.values()
+              if ("copyBuffer" in e["name"] or "copy" in e["name"].lower()) and e["grid"] >= 65536]
+    if not ker or not copies:
+        raise ValueError(f"no dispatches for {kernel_substr!r} or no calibration copy in {run_dir}")
+    return {"kernel_kib": statistics.median(ker), "copy_kib": max(copies), "n": len(ker)}
+
+
+def traffic(fetch_dir: str, write_dir: str, kernel_substr: str) -> dict:
+    f = counter_bytes(fetch_dir, "FETCH_SIZE", kernel_substr)
+    w = counter_bytes(write_dir, "WRITE_SIZE", kernel_substr)
+    f_scale = COPY_BYTES / (f["copy_kib"] * 1024.0)
+    w_scale = COPY_BYTES / (w["copy_kib"] * 1024.0)
+    fetch_b = f["kernel_kib"] * 1024.0 * f_scale
+    write_b = w["kernel_kib"] * 1024.0 * w_scale
+    return {
+        "kernel": kernel_substr,
+        "fetch_kib_raw": f["kernel_kib"], "write_kib_raw": w["kernel_kib"],
+        "copy_fetch_kib_raw": f["copy_kib"], "copy_write_kib_raw": w["copy_kib"],
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "fetch_bytes": fetch_b, "write_bytes": write_b, "bytes": fetch_b + write_b,
+        "dispatches": f["n"],
+        "source_digest": source_digest(),
+    }
+
+
+def main(argv: List[str]) -> int:
+    if len(argv) >= 2 and argv[0] == "stats":
+        print(stats_summary(argv[1]))
+        return 0
+    if len(argv) >= 5 and argv[0] == "traffic":
+        t = traffic(argv[1], argv[2], argv[3])
+        with open(argv[4], "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t, indent=1))
+        return 0
+    print(__doc__)
+    return 2
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
