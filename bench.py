@@ -40,7 +40,9 @@ WORKLOADS = {
     "verify_silu_m2": (3, 2),
     "verify_silu_m3": (3, 3),
     "verify_silu_m8": (3, 8),
+    "prefill_silu_m128": (4, 128),
 }
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 
 
 def log(*a):
@@ -125,7 +127,7 @@ def main():
 
     lib = ffn.load()
     idx, M = WORKLOADS[args.workload]
-    case = fi.make_config(idx, M=M) if idx == 3 else fi.make_config(idx)
+    case = fi.make_config(idx, M=M) if idx in (3, 4) else fi.make_config(idx)
     K, N = case.K, case.N
     nbytes = algorithmic_bytes(M, K, N)
     dev = torch.device("cuda:0")
@@ -192,6 +194,32 @@ def main():
     gbs = nbytes["forward"] / (us * 1e-6) / 1e9
     log(f"[bench] {args.workload}: {us:.2f} us/forward, {gbs:.1f} GB/s algorithmic "
         f"({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f}); host wall {wall * 1e3 / args.steps * 1e3:.2f} us/step")
+
+    if M > 8:
+        # Matrix-core arm: bound by the bf16 MFMA rate; the whole forward's
+        # flops (three [M, K] x [K, N]-sized products) over its time.
+        flops = 2.0 * 3 * M * K * N
+        tflops = flops / (us * 1e-6) / 1e12
+        log(f"[bench] {args.workload}: {tflops:.1f} TFLOP/s ({100 * tflops / MFMA_BF16_PEAK_TFLOPS:.1f}% of "
+            f"{MFMA_BF16_PEAK_TFLOPS:.0f})")
+        result = {
+            "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "us_per_forward": round(us, 3),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"{case.name}: gated FFN forward, M={M}, hidden K={K}, intermediate N={N}, "
+                                   f"act={fi.ACT_NAMES[act]}, NVFP4 weights rotated over {nc} copies",
+                       "M": M, "K": K, "N": N, "act": fi.ACT_NAMES[act],
+                       "algorithmic_bytes_per_forward": nbytes["forward"]},
+            "roofline": {"kernel": "whole forward (dual GEMM + down GEMM on bf16 matrix cores)", "bound": "mfma",
+                         "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "flops_per_forward": flops},
+        }
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        print(json.dumps(result), flush=True)
+        return
 
     # Dominant kernel: the dual GEMV, timed with events on its stream around a
     # batch of back-to-back launches (rotating the weight copies); the average

@@ -235,3 +235,15 @@ def parity_bound(out_ref: np.ndarray, rms_ref: Optional[float] = None,
     if rms_ref is None:
         rms_ref = float(np.sqrt(np.mean(np.square(out_ref))))
     return rel * rms_ref + ulp_bf16(out_ref)
+
+
+def h_rounding_bound(case) -> np.ndarray:
+    """First-order bound [M, K] of what rounding h = act(gate) * up to bf16
+    (once, to nearest) can move out = W_d h: 2^-8 * sum_n |W_d[j, n]| |h[m, n]|
+    (bf16 keeps 8 significant bits, so one rounding is off by at most 2^-8 of
+    the value). It only matters for weights with extreme dynamic range, where
+    out is a small difference of large terms."""
+    g, u = default().dual(case)
+    h = default().gated_act(case.act, g, u)
+    wd = np.abs(default().dequant(case.down))
+    return (2.0 ** -8) * (np.abs(h) @ wd.T)

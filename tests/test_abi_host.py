@@ -53,8 +53,14 @@ def test_version_strerror_workspace():
     assert ffn.workspace_bytes(1, 5120, 17408) == 17408 * 2
     assert ffn.workspace_bytes(8, 5120, 17408) == 8 * 17408 * 2
     assert ffn.workspace_bytes(0, 256, 512) == 0
-    assert ffn.workspace_bytes(9, 256, 512) == 0
     assert ffn.workspace_bytes(1, 250, 512) == 0
+    # matrix-core arm (M > 8): h for one block of 128 rows, counters, partial slots
+    ws9 = ffn.workspace_bytes(9, 256, 512)
+    assert ws9 > 9 * 512 * 2 and ws9 % 256 == 0
+    assert ffn.workspace_bytes(128, 5120, 17408) == ffn.workspace_bytes(4096, 5120, 17408)
+    assert ffn.workspace_bytes(128, 5120, 17408) >= 128 * 17408 * 2
+    assert ffn.workspace_bytes(9, 96, 512) == 0   # the arm needs K, N multiples of 64
+    assert ffn.workspace_bytes(65537, 256, 512) == 0
     assert ffn.workspace_bytes(3, 96, 160) % 256 == 0
 
 
@@ -84,8 +90,12 @@ def test_misaligned():
     assert fwd(u=W(scales=FAKE + 1)) == ffn.ERR_ALIGN
     assert dual(go=FAKE + 4) == ffn.ERR_ALIGN
     assert down(ui=FAKE + 0x200004) == ffn.ERR_ALIGN
-    # scales only need 2-byte alignment: this one fails later, on M
-    assert fwd(g=W(scales=FAKE + 2), M=9) == ffn.ERR_BATCH
+    # scales need 2-byte alignment up to M = 8 (this one fails later, on M),
+    # 4-byte alignment on the matrix-core arm
+    assert fwd(g=W(scales=FAKE + 2), M=-1) == ffn.ERR_BATCH
+    assert fwd(g=W(scales=FAKE + 2), M=9, wsb=1 << 30) == ffn.ERR_ALIGN
+    assert dual(u=W(scales=FAKE + 6), M=64) == ffn.ERR_ALIGN
+    assert down(d=W(scales=FAKE + 2), M=128) == ffn.ERR_ALIGN
 
 
 @pytest.mark.parametrize("K,N", [(0, 512), (256, 0), (250, 512), (256, 500), (-32, 512), (65568, 512),
@@ -96,11 +106,19 @@ def test_bad_shapes(K, N):
     assert down(K=K, N=N) == ffn.ERR_SHAPE
 
 
-@pytest.mark.parametrize("M", [-1, 9, 16, 100])
+@pytest.mark.parametrize("M", [-1, -100, 65537, 1 << 24])
 def test_unsupported_batch(M):
     assert fwd(M=M) == ffn.ERR_BATCH
     assert dual(M=M) == ffn.ERR_BATCH
     assert down(M=M) == ffn.ERR_BATCH
+
+
+@pytest.mark.parametrize("K,N", [(96, 512), (256, 480), (320, 96)])
+def test_prefill_needs_multiples_of_64(K, N):
+    # M <= 8 takes any multiple of 32; the matrix-core arm (M > 8) needs 64
+    assert fwd(M=9, K=K, N=N, wsb=1 << 30) == ffn.ERR_SHAPE
+    assert dual(M=16, K=K, N=N) == ffn.ERR_SHAPE
+    assert down(M=128, K=K, N=N) == ffn.ERR_SHAPE
 
 
 def test_bad_act_and_workspace_and_scale2():
@@ -109,6 +127,7 @@ def test_bad_act_and_workspace_and_scale2():
     assert down(act=7) == ffn.ERR_ACT
     assert fwd(wsb=ffn.workspace_bytes(1, 256, 512) - 1) == ffn.ERR_WORKSPACE
     assert fwd(M=2, wsb=ffn.workspace_bytes(1, 256, 512)) == ffn.ERR_WORKSPACE
+    assert fwd(M=9, wsb=ffn.workspace_bytes(9, 256, 512) - 256) == ffn.ERR_WORKSPACE
     assert fwd(g=W(scale2=float("nan"))) == ffn.ERR_SCALE2
     assert dual(u=W(scale2=float("inf"))) == ffn.ERR_SCALE2
     assert down(d=W(scale2=float("-inf"))) == ffn.ERR_SCALE2

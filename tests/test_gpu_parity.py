@@ -44,9 +44,13 @@ def loaded(key, make):
     return _cache[key]
 
 
-def assert_ffn_close(out_gpu, out_ref, what):
+def assert_ffn_close(out_gpu, out_ref, what, extra=None):
+    """`extra` (elementwise) widens the bound, for the format-coverage weights
+    only: see oracle.h_rounding_bound."""
     got = ffn.bf16_to_f64(out_gpu) if torch.is_tensor(out_gpu) else out_gpu
     bound = oracle.parity_bound(out_ref)
+    if extra is not None:
+        bound = bound + extra
     err = np.abs(got - out_ref)
     bad = ~(err <= bound)
     if bad.any():
@@ -122,7 +126,10 @@ def test_dual_and_down_entries(M, K, N, act, seed):
 @pytest.mark.parametrize("M", [1, 3, 8])
 def test_format_coverage(act, M):
     """All 16 E2M1 codes, all 254 finite E4M3 scales (negative, subnormal,
-    448), scale2 not a power of two."""
+    448), scale2 not a power of two. The decoding is checked through the dual
+    entry at the fp32 bound; the FFN output bound adds the propagated bound of
+    the one bf16 rounding of h, which these weights (E4M3 scales spanning
+    2^-9 .. 448 in W_d) can blow up through cancellation."""
     case = fi.make_format_coverage(act=act, M=M)
     L = loaded(case.name, lambda: case)
     out = L.forward()
@@ -131,7 +138,7 @@ def test_format_coverage(act, M):
     g_ref, u_ref = oracle.dual(case)
     assert_dual_close(g, g_ref, "gate")
     assert_dual_close(u, u_ref, "up")
-    assert_ffn_close(out, oracle.ffn(case), case.name)
+    assert_ffn_close(out, oracle.ffn(case), case.name, extra=oracle.h_rounding_bound(case))
 
 
 def test_determinism_and_entry_composition():

@@ -402,3 +402,21 @@ def test_pins_catch_mutant(name, tmp_path):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin caught mutant {name}"
+
+
+@pytest.mark.parametrize("act", [fi.ACT_SILU, fi.ACT_GELU_TANH])
+def test_h_rounding_bound_covers_bf16_h(act):
+    """The format-coverage FFN bound: storing h = act(gate) * up in bf16 (with
+    gate and up in fp32) stays within parity_bound + h_rounding_bound of the
+    exact result, here simulated with torch's bf16 rounding."""
+    import torch
+
+    case = fi.make_format_coverage(act=act, M=128)
+    g, u = oracle.dual(case)
+    h = oracle.gated_act(act, g.astype(np.float32).astype(np.float64), u.astype(np.float32).astype(np.float64))
+    hb = torch.from_numpy(h).to(torch.bfloat16).double().numpy()
+    staged = oracle.down(hb, case.down)
+    ref = oracle.ffn(case)
+    extra = oracle.h_rounding_bound(case)
+    assert np.all(np.abs(staged - ref) <= oracle.parity_bound(ref) + extra)
+    assert np.all(extra >= 0) and np.all(np.isfinite(extra))

@@ -7,11 +7,13 @@
 #include <cstdint>
 
 #include "kernels.h"
+#include "mfma_launch.h"
 
 namespace {
 
 constexpr int kMaxDim = 65536;
 constexpr int kMaxGemvM = 8;
+constexpr int kMaxM = 65536;
 
 bool aligned(const void *p, uintptr_t a)
 {
@@ -36,7 +38,50 @@ int check_weight(const ffn_nvfp4_weight *w)
 
 int check_batch(int M)
 {
-    return (M >= 0 && M <= kMaxGemvM) ? FFN_NVFP4_OK : FFN_NVFP4_ERR_BATCH;
+    return (M >= 0 && M <= kMaxM) ? FFN_NVFP4_OK : FFN_NVFP4_ERR_BATCH;
+}
+
+// Batches above kMaxGemvM rows run on the matrix-core arm, which needs K and
+// N in multiples of 64.
+int check_prefill_shape(int M, int K, int N)
+{
+    if (M > kMaxGemvM && (K % 64 != 0 || N % 64 != 0))
+        return FFN_NVFP4_ERR_SHAPE;
+    return FFN_NVFP4_OK;
+}
+
+// ... and scales aligned to 4 bytes.
+int check_prefill_scales(int M, const ffn_nvfp4_weight *a, const ffn_nvfp4_weight *b = nullptr,
+                         const ffn_nvfp4_weight *c = nullptr)
+{
+    if (M <= kMaxGemvM)
+        return FFN_NVFP4_OK;
+    for (const ffn_nvfp4_weight *w : {a, b, c})
+        if (w && !aligned(w->scales, 4))
+            return FFN_NVFP4_ERR_ALIGN;
+    return FFN_NVFP4_OK;
+}
+
+size_t round256(size_t b)
+{
+    return (b + 255) & ~static_cast<size_t>(255);
+}
+
+// Workspace of the matrix-core arm: h for one block of up to kMfmaMaxM rows,
+// the per-tile counters, and the stream-K partial slots.
+struct PrefillLayout {
+    size_t h, counters, partials, total;
+};
+
+PrefillLayout prefill_layout(int M, int N)
+{
+    PrefillLayout l{};
+    const int mb = M < ffn::kMfmaMaxM ? M : ffn::kMfmaMaxM;
+    l.h = 0;
+    l.counters = round256(static_cast<size_t>(mb) * N * 2);
+    l.partials = l.counters + round256(static_cast<size_t>(ffn::mfma_max_tiles(N)) * sizeof(int));
+    l.total = l.partials + round256(ffn::mfma_partials_floats() * sizeof(float));
+    return l;
 }
 
 ffn::WeightArg warg(const ffn_nvfp4_weight *w)
@@ -51,22 +96,84 @@ int launch_status(hipError_t e)
 
 // Dual GEMV: the LDS-ring kernels where they apply (M <= 2), else the
 // general LDS-staged kernel.
+// The LDS-ring and matrix-core kernels move scales 4 bytes at a time.
+bool scales_dma_ok(const ffn::WeightArg &w)
+{
+    return aligned(w.scales, 4);
+}
+
 hipError_t run_dual(int M, ffn::OutKind out, const void *x, const ffn::WeightArg &g, const ffn::WeightArg &u,
                     void *out0, void *out1, int N, int K, hipStream_t stream)
 {
-    hipError_t e = ffn::launch_ring_dual(M, out, x, g, u, out0, out1, N, K, stream);
-    if (e != hipErrorNotSupported)
-        return e;
+    if (scales_dma_ok(g) && scales_dma_ok(u)) {
+        hipError_t e = ffn::launch_ring_dual(M, out, x, g, u, out0, out1, N, K, stream);
+        if (e != hipErrorNotSupported)
+            return e;
+    }
     return ffn::launch_gemv(M, 2, ffn::IN_BF16, out, x, nullptr, g, u, out0, out1, N, K, stream);
 }
 
 hipError_t run_down(int M, ffn::InKind in, const void *in0, const float *in1, const ffn::WeightArg &d,
                     void *out, int K, int N, hipStream_t stream)
 {
-    hipError_t e = ffn::launch_ring_down(M, in, in0, in1, d, out, K, N, stream);
-    if (e != hipErrorNotSupported)
-        return e;
+    if (scales_dma_ok(d)) {
+        hipError_t e = ffn::launch_ring_down(M, in, in0, in1, d, out, K, N, stream);
+        if (e != hipErrorNotSupported)
+            return e;
+    }
     return ffn::launch_gemv(M, 1, in, ffn::OUT_BF16, in0, in1, d, d, out, nullptr, K, N, stream);
+}
+
+// Matrix-core arm, in blocks of up to kMfmaMaxM rows.
+hipError_t run_prefill_dual(int M, const void *x, const ffn::WeightArg &g, const ffn::WeightArg &u, float *gate_out,
+                            float *up_out, int N, int K, hipStream_t stream)
+{
+    for (int m0 = 0; m0 < M; m0 += ffn::kMfmaMaxM) {
+        const int mb = M - m0 < ffn::kMfmaMaxM ? M - m0 : ffn::kMfmaMaxM;
+        const size_t xo = static_cast<size_t>(m0) * K, oo = static_cast<size_t>(m0) * N;
+        hipError_t e = ffn::launch_mfma_dual(mb, ffn::OUT_F32_PAIR, static_cast<const uint16_t *>(x) + xo, g, u,
+                                             gate_out + oo, up_out + oo, N, K, nullptr, stream);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t run_prefill_down(int M, ffn::InKind in, const float *gate_in, const float *up_in,
+                            const ffn::WeightArg &d, void *out, int K, int N, hipStream_t stream)
+{
+    for (int m0 = 0; m0 < M; m0 += ffn::kMfmaMaxM) {
+        const int mb = M - m0 < ffn::kMfmaMaxM ? M - m0 : ffn::kMfmaMaxM;
+        const size_t io = static_cast<size_t>(m0) * N, oo = static_cast<size_t>(m0) * K;
+        hipError_t e = ffn::launch_mfma_down(mb, in, gate_in + io, up_in + io, d,
+                                             static_cast<uint16_t *>(out) + oo, K, N, nullptr, stream);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t run_prefill_forward(int M, ffn::OutKind epi, const void *x, const ffn::WeightArg &g,
+                               const ffn::WeightArg &u, const ffn::WeightArg &d, void *workspace, void *out, int K,
+                               int N, hipStream_t stream)
+{
+    const PrefillLayout l = prefill_layout(M, N);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    ffn::MfmaScratch scratch{reinterpret_cast<float *>(ws + l.partials), reinterpret_cast<int *>(ws + l.counters),
+                             ffn::mfma_max_tiles(N)};
+    void *h = ws + l.h;
+    for (int m0 = 0; m0 < M; m0 += ffn::kMfmaMaxM) {
+        const int mb = M - m0 < ffn::kMfmaMaxM ? M - m0 : ffn::kMfmaMaxM;
+        hipError_t e = ffn::launch_mfma_dual(mb, epi, static_cast<const uint16_t *>(x) + static_cast<size_t>(m0) * K,
+                                             g, u, h, nullptr, N, K, &scratch, stream);
+        if (e != hipSuccess)
+            return e;
+        e = ffn::launch_mfma_down(mb, ffn::IN_BF16, h, nullptr, d,
+                                  static_cast<uint16_t *>(out) + static_cast<size_t>(m0) * K, K, N, &scratch, stream);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -83,8 +190,10 @@ const char *ffn_nvfp4_strerror(int status)
     switch (status) {
     case FFN_NVFP4_OK: return "ok";
     case FFN_NVFP4_ERR_NULL: return "a required pointer is NULL";
-    case FFN_NVFP4_ERR_ALIGN: return "pointer misaligned (codes/x/out/workspace need 16 bytes, scales 2)";
-    case FFN_NVFP4_ERR_SHAPE: return "K and N must be positive multiples of 32, at most 65536";
+    case FFN_NVFP4_ERR_ALIGN:
+        return "pointer misaligned (codes/x/out/workspace need 16 bytes, scales 2, or 4 when M > 8)";
+    case FFN_NVFP4_ERR_SHAPE:
+        return "K and N must be positive multiples of 32 (of 64 when M > 8), at most 65536";
     case FFN_NVFP4_ERR_BATCH: return "unsupported batch size M";
     case FFN_NVFP4_ERR_ACT: return "unknown activation";
     case FFN_NVFP4_ERR_WORKSPACE: return "workspace too small";
@@ -98,11 +207,12 @@ size_t ffn_nvfp4_workspace_bytes(int M, int K, int N)
 {
     if (check_batch(M) != FFN_NVFP4_OK || !dim_ok(K) || !dim_ok(N))
         return 0;
-    if (M == 0)
+    if (M == 0 || check_prefill_shape(M, K, N) != FFN_NVFP4_OK)
         return 0;
+    if (M > kMaxGemvM)
+        return prefill_layout(M, N).total;
     // h = act(gate) * up in bf16, [M, N]
-    size_t bytes = static_cast<size_t>(M) * static_cast<size_t>(N) * 2;
-    return (bytes + 255) & ~static_cast<size_t>(255);
+    return round256(static_cast<size_t>(M) * static_cast<size_t>(N) * 2);
 }
 
 int ffn_nvfp4_dual_gemv(const void *x, int M, int K, int N, const ffn_nvfp4_weight *gate,
@@ -113,7 +223,7 @@ int ffn_nvfp4_dual_gemv(const void *x, int M, int K, int N, const ffn_nvfp4_weig
         return rc;
     if (!dim_ok(K) || !dim_ok(N))
         return FFN_NVFP4_ERR_SHAPE;
-    if ((rc = check_batch(M)))
+    if ((rc = check_batch(M)) || (rc = check_prefill_shape(M, K, N)))
         return rc;
     if (M == 0)
         return FFN_NVFP4_OK;
@@ -121,6 +231,10 @@ int ffn_nvfp4_dual_gemv(const void *x, int M, int K, int N, const ffn_nvfp4_weig
         return FFN_NVFP4_ERR_NULL;
     if (!aligned(x, 16) || !aligned(gate_out, 16) || !aligned(up_out, 16))
         return FFN_NVFP4_ERR_ALIGN;
+    if ((rc = check_prefill_scales(M, gate, up)))
+        return rc;
+    if (M > kMaxGemvM)
+        return launch_status(run_prefill_dual(M, x, warg(gate), warg(up), gate_out, up_out, N, K, stream));
     return launch_status(run_dual(M, ffn::OUT_F32_PAIR, x, warg(gate), warg(up), gate_out, up_out, N, K, stream));
 }
 
@@ -132,7 +246,7 @@ int ffn_nvfp4_down_gemv(const float *gate_in, const float *up_in, int M, int N, 
         return rc;
     if (!dim_ok(K) || !dim_ok(N))
         return FFN_NVFP4_ERR_SHAPE;
-    if ((rc = check_batch(M)))
+    if ((rc = check_batch(M)) || (rc = check_prefill_shape(M, K, N)))
         return rc;
     if (act != FFN_NVFP4_ACT_SILU && act != FFN_NVFP4_ACT_GELU_TANH)
         return FFN_NVFP4_ERR_ACT;
@@ -142,7 +256,11 @@ int ffn_nvfp4_down_gemv(const float *gate_in, const float *up_in, int M, int N, 
         return FFN_NVFP4_ERR_NULL;
     if (!aligned(gate_in, 16) || !aligned(up_in, 16) || !aligned(out, 16))
         return FFN_NVFP4_ERR_ALIGN;
+    if ((rc = check_prefill_scales(M, down)))
+        return rc;
     const ffn::InKind in = act == FFN_NVFP4_ACT_SILU ? ffn::IN_GATEUP_SILU : ffn::IN_GATEUP_GELU;
+    if (M > kMaxGemvM)
+        return launch_status(run_prefill_down(M, in, gate_in, up_in, warg(down), out, K, N, stream));
     return launch_status(run_down(M, in, gate_in, up_in, warg(down), out, K, N, stream));
 }
 
@@ -155,7 +273,7 @@ int ffn_nvfp4_forward(const void *x, int M, int K, int N, const ffn_nvfp4_weight
         return rc;
     if (!dim_ok(K) || !dim_ok(N))
         return FFN_NVFP4_ERR_SHAPE;
-    if ((rc = check_batch(M)))
+    if ((rc = check_batch(M)) || (rc = check_prefill_shape(M, K, N)))
         return rc;
     if (act != FFN_NVFP4_ACT_SILU && act != FFN_NVFP4_ACT_GELU_TANH)
         return FFN_NVFP4_ERR_ACT;
@@ -165,6 +283,8 @@ int ffn_nvfp4_forward(const void *x, int M, int K, int N, const ffn_nvfp4_weight
         return FFN_NVFP4_ERR_NULL;
     if (!aligned(x, 16) || !aligned(out, 16) || !aligned(workspace, 16))
         return FFN_NVFP4_ERR_ALIGN;
+    if ((rc = check_prefill_scales(M, gate, up, down)))
+        return rc;
     if (workspace_bytes < ffn_nvfp4_workspace_bytes(M, K, N))
         return FFN_NVFP4_ERR_WORKSPACE;
     // The dual GEMV's epilogue computes h = bf16(act(s2_g gate) * (s2_u up))
@@ -172,6 +292,9 @@ int ffn_nvfp4_forward(const void *x, int M, int K, int N, const ffn_nvfp4_weight
     // against h staged in LDS or registers. Bit-identical to the dual GEMV
     // followed by the down GEMV with the activation in its input load.
     const ffn::OutKind epi = act == FFN_NVFP4_ACT_SILU ? ffn::OUT_H_SILU : ffn::OUT_H_GELU;
+    if (M > kMaxGemvM)
+        return launch_status(run_prefill_forward(M, epi, x, warg(gate), warg(up), warg(down), workspace, out, K, N,
+                                                 stream));
     hipError_t e = run_dual(M, epi, x, warg(gate), warg(up), workspace, nullptr, N, K, stream);
     if (e != hipSuccess)
         return FFN_NVFP4_ERR_LAUNCH;

@@ -1,0 +1,452 @@
+// mfma_gemm.h -- the prefill arm of the NVFP4 gated FFN (dense_ffn.rs page,
+// DenseFfnLayer::forward_prefill / forward_prefill_inner): the two projections
+// and the down projection as GEMMs over up to 128 token rows, on bf16 matrix
+// cores (v_mfma_f32_32x32x16_bf16) with the weights dequantised on the fly.
+//
+// Product. For a weight W [rows, cols] (NVFP4) and an activation block
+// A [M, cols] (bf16, M <= 32 * MT), every wave computes
+//     D[m, r] = sum_c A[m, c] * W[r, c]
+// for all M token rows and 32 (two projections) or 64 (one projection) weight
+// rows. The activation fragment is the MFMA's A operand (rows = tokens), the
+// dequantised weight fragment its B operand (columns = weight rows), so a
+// lane's accumulators cover 16 tokens of one weight row and output rows are
+// written 32 consecutive elements at a time.
+//
+// Dequantisation. Each weight element is dequantised exactly once per launch,
+// in registers, by the one wave that owns its row: FP4 pair -> fp32 pair
+// (v_cvt_scalef32_pk_f32_fp4 with unit scale), times the E4M3 block scale,
+// rounded to bf16. E2M1 x E4M3 has at most 6 significant bits, so the bf16
+// weight is exact and the only rounding in the product is the fp32
+// accumulation inside the matrix core. scale2 multiplies in the epilogue.
+//
+// K order. The reduction runs over units of 64 columns. In a unit, lane half
+// h (lane / 32) of a wave holds columns [32 h, 32 h + 32) of its row (16 code
+// bytes), and MFMA step s (of 4) takes columns 32 h + 8 s .. + 7 from each
+// half; the activation fragment is read with the same column map.
+//
+// Data movement. Per unit, a workgroup (4 waves, one per SIMD) stages into
+// one LDS ring stage: the activation block [32 MT rows, 64 cols] bf16, with
+// its 16-byte pieces XOR-swizzled by row (conflict-free ds_read_b128 of 32
+// rows at one column), and each wave's raw codes (1 KB per 32 rows) and
+// scales. All of it moves with gfx950 direct global->LDS loads (no
+// registers), S - 1 units ahead of the math. The loads complete in order on
+// the vector memory counter, which the compiler does not tie to the LDS they
+// fill: each iteration waits explicitly for its unit and then meets the other
+// waves at a barrier, after which the stage of the previous unit is free.
+//
+// Work split (stream-K). The reduction of every 128- (or 256-) row tile is cut
+// into units; the T x KU units of the launch are dealt out to the G
+// workgroups as G contiguous, equal ranges (workgroup g takes
+// [floor(g U / G), floor((g + 1) U / G))), so all compute units finish
+// together whatever the tile count. A tile whose units span several
+// workgroups is finished by the last of them to arrive: each writes its
+// fp32 partial tile to its own slot of the workspace, bumps the tile's
+// counter, and the one that completes the count adds the pieces in k order
+// (always the same order, whoever arrives last) and runs the epilogue. No
+// workgroup ever waits for another. With G = T every workgroup owns exactly
+// one whole tile and neither slots nor counters are touched.
+#pragma once
+
+#include "kernels.h"
+#include "nvfp4_device.h"
+#include "ring_gemv.h"  // FFN_LDS, wait_vmcnt
+
+namespace ffn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kMfmaWaves = 4;
+constexpr int kUnitCols = 64;  // reduction columns per unit
+
+struct MfmaParams {
+    const void *in0;   // bf16 [M, cols], or fp32 gate [M, cols] (gate/up input)
+    const float *in1;  // fp32 up [M, cols] (gate/up input)
+    const uint8_t *codes0;
+    const uint8_t *scales0;
+    const uint8_t *codes1;
+    const uint8_t *scales1;
+    float s2_0;
+    float s2_1;
+    void *out0;
+    void *out1;
+    float *partials;   // 2 G slots of partial tiles (stream-K only)
+    int *counters;     // one per tile, zero at launch (stream-K, not deferred)
+    int defer;         // 1: leave split tiles as pieces for mfma_reduce_kernel
+    int M;             // token rows, 1 <= M <= 32 * MT
+    int rows;          // weight rows (output columns)
+    int cols;          // reduction length, a multiple of 64
+    int tiles;         // T
+    int units_per_tile;  // KU = cols / 64
+    int units;           // U = T * KU
+};
+
+template <int MT>
+constexpr int mfma_stage_bytes()
+{
+    return MT * 4096 + 8192 + 1024;  // activations, codes (4 waves x 2 x 1 KB), scales (4 x 256 B)
+}
+
+// Weight rows per wave / per workgroup tile: two projections share 32 rows,
+// one projection takes 64 rows as two 32-row fragments.
+template <int NMAT>
+constexpr int mfma_rows_per_tile()
+{
+    return kMfmaWaves * (NMAT == 2 ? 32 : 64);
+}
+
+// Floats of one partial slot: 4 waves x 2 x MT accumulator tiles x 16 x 64.
+template <int MT>
+constexpr int mfma_slot_floats()
+{
+    return kMfmaWaves * 2 * MT * 16 * 64;
+}
+
+// First unit of workgroup g, and the workgroup that owns unit u.
+__host__ __device__ inline int sk_begin(long long g, long long U, long long G)
+{
+    return static_cast<int>(g * U / G);
+}
+__host__ __device__ inline int sk_owner(long long u, long long U, long long G)
+{
+    // the largest g with floor(g U / G) <= u
+    return static_cast<int>(((u + 1) * G + U - 1) / U) - 1;
+}
+
+// Wait until at most `ahead` units (of L loads each) issued after the one to
+// be consumed are outstanding; `ahead` is wave-uniform and in [0, S - 2].
+template <int S, int L>
+__device__ __forceinline__ void wait_units_ahead(int ahead)
+{
+    if constexpr (S >= 6) { if (ahead >= 4) { wait_vmcnt<4 * L>(); return; } }
+    if constexpr (S >= 5) { if (ahead >= 3) { wait_vmcnt<3 * L>(); return; } }
+    if constexpr (S >= 4) { if (ahead >= 2) { wait_vmcnt<2 * L>(); return; } }
+    if constexpr (S >= 3) { if (ahead >= 1) { wait_vmcnt<1 * L>(); return; } }
+    wait_vmcnt<0>();
+}
+
+// Hides a wave-uniform value from the optimiser, so that what is derived from
+// it inside a rarely taken branch is computed there and not hoisted out of the
+// main loop (where it would hold registers for the whole kernel).
+__device__ __forceinline__ int opaque_uniform(int x)
+{
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
+// Workgroup barrier for LDS only: waits for this wave's LDS traffic and meets
+// the other waves, without the vector-memory drain of __syncthreads() (which
+// would also wait for the direct loads still in flight for later units).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt untouched
+    __builtin_amdgcn_s_barrier();
+}
+
+// Eight codes (one dword) times one block scale, as eight bf16 (exact).
+__device__ __forceinline__ bf16x8_t dequant8(uint32_t d, float sc)
+{
+    const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+    const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+    const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+    const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+    bf16x8_t w;
+    w[0] = static_cast<__bf16>(p0[0] * sc);
+    w[1] = static_cast<__bf16>(p0[1] * sc);
+    w[2] = static_cast<__bf16>(p1[0] * sc);
+    w[3] = static_cast<__bf16>(p1[1] * sc);
+    w[4] = static_cast<__bf16>(p2[0] * sc);
+    w[5] = static_cast<__bf16>(p2[1] * sc);
+    w[6] = static_cast<__bf16>(p3[0] * sc);
+    w[7] = static_cast<__bf16>(p3[1] * sc);
+    return w;
+}
+
+// Epilogue of one accumulator position. Accumulator (f, mt, v) of lane
+// `lane` of wave `wave` holds D[m, row] with m = 32 mt + 8 (v / 4) + 4 (lane /
+// 32) + v % 4 and row = row lane % 32 of fragment f. (y0, y1) are fragments 0
+// and 1 at (mt, v): gate and up of one row (two projections, written as the
+// fp32 pair or as h = bf16(act(s2_0 y0) * (s2_1 y1))), or two rows 32 apart
+// (one projection, bf16(s2_0 y)).
+template <int NMAT, int OUT, int ROWS_TILE>
+__device__ __forceinline__ void emit_pair(const MfmaParams &p, int rows, int M, int t, int wave, int lane, int mt,
+                                          int v, float y0, float y1)
+{
+    const int m = 32 * mt + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    if (m >= M)
+        return;
+    if constexpr (NMAT == 2) {
+        const int row = t * ROWS_TILE + wave * 32 + (lane & 31);
+        if (row >= rows)
+            return;
+        const float gv = y0 * p.s2_0;
+        const float uv = y1 * p.s2_1;
+        const size_t o = static_cast<size_t>(m) * rows + row;
+        if constexpr (OUT == OUT_F32_PAIR) {
+            static_cast<float *>(p.out0)[o] = gv;
+            static_cast<float *>(p.out1)[o] = uv;
+        } else {
+            constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
+            static_cast<uint16_t *>(p.out0)[o] = to_bf16_bits(gate_act<A>(gv) * uv);
+        }
+    } else {
+        const int row = t * ROWS_TILE + wave * 64 + (lane & 31);
+        uint16_t *out = static_cast<uint16_t *>(p.out0) + static_cast<size_t>(m) * rows;
+        if (row < rows)
+            out[row] = to_bf16_bits(y0 * p.s2_0);
+        if (row + 32 < rows)
+            out[row + 32] = to_bf16_bits(y1 * p.s2_0);
+    }
+}
+
+template <int MT, int NMAT, int IN, int OUT, int S>
+__global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaParams p)
+{
+    static_assert(MT >= 1 && MT <= 4, "token tiles");
+    static_assert(S >= 2 && S <= 6, "ring stages");
+    constexpr int STAGE = mfma_stage_bytes<MT>();
+    constexpr int XB = MT * 4096;                           // activation bytes per stage
+    constexpr int L = (IN == IN_BF16 ? MT : 0) + 3;         // direct loads per unit per wave
+    static_assert((S - 2) * L < 64, "outstanding loads must fit the vmcnt counter");
+    constexpr int ROWS_WAVE = NMAT == 2 ? 32 : 64;
+    constexpr int ROWS_TILE = kMfmaWaves * ROWS_WAVE;
+    constexpr int SLOT = mfma_slot_floats<MT>();
+
+    extern __shared__ u32x4_t lds_raw[];
+    FFN_LDS uint8_t *lds = (FFN_LDS uint8_t *)lds_raw;
+    __shared__ int s_arrivals;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5;
+    const int r = lane & 31;
+    const long long U = p.units;
+    const long long G = gridDim.x;
+    const int g = blockIdx.x;
+    const int u_begin = sk_begin(g, U, G);
+    const int n = sk_begin(g + 1, U, G) - u_begin;
+    const int KU = p.units_per_tile;
+    const int cols = p.cols;
+    const int M = p.M;
+    const size_t row_codes = static_cast<size_t>(cols) / 2;
+    const size_t row_scales = static_cast<size_t>(cols) / 16;
+
+    // Weight row of fragment f, row r of this wave, in tile t (clamped: rows
+    // past the end load row rows - 1 and are never stored).
+    auto wrow = [&](int t, int f, int rr) {
+        const int row = t * ROWS_TILE + wave * ROWS_WAVE + (NMAT == 2 ? 0 : f * 32) + rr;
+        return min(row, p.rows - 1);
+    };
+
+    // Activation slot P (16 bytes) of a stage holds row P / 8, 16-byte piece
+    // (P % 8) ^ (row % 8) of the unit.
+    auto issue = [&](int v, int st) {
+        const int t = v / KU;
+        const int k0 = (v - t * KU) * kUnitCols;
+        FFN_LDS uint8_t *base = lds + st * STAGE;
+        if constexpr (IN == IN_BF16) {
+            const uint16_t *X = static_cast<const uint16_t *>(p.in0);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const int P = (wave * MT + i) * 64 + lane;
+                const int m = P >> 3;
+                const int c = (P & 7) ^ (m & 7);
+                const int ms = min(m, M - 1);
+                __builtin_amdgcn_global_load_lds(
+                    reinterpret_cast<const void *>(X + static_cast<size_t>(ms) * cols + k0 + 8 * c),
+                    reinterpret_cast<FFN_LDS void *>(base + (wave * MT + i) * 1024), 16, 0, 0);
+            }
+        } else {
+            // h = bf16(act(gate) * up) computed while staging (gate, up fp32).
+            constexpr int A = (IN == IN_GATEUP_SILU) ? ACT_SILU : ACT_GELU_TANH;
+            const float *Gp = static_cast<const float *>(p.in0);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const int P = (wave * MT + i) * 64 + lane;
+                const int m = P >> 3;
+                const int c = (P & 7) ^ (m & 7);
+                const size_t off = static_cast<size_t>(min(m, M - 1)) * cols + k0 + 8 * c;
+                const f32x4_t g0 = *reinterpret_cast<const f32x4_t *>(Gp + off);
+                const f32x4_t g1 = *reinterpret_cast<const f32x4_t *>(Gp + off + 4);
+                const f32x4_t u0 = *reinterpret_cast<const f32x4_t *>(p.in1 + off);
+                const f32x4_t u1 = *reinterpret_cast<const f32x4_t *>(p.in1 + off + 4);
+                u32x4_t hv;
+                hv[0] = pack_bf16x2(gate_act<A>(g0[0]) * u0[0], gate_act<A>(g0[1]) * u0[1]);
+                hv[1] = pack_bf16x2(gate_act<A>(g0[2]) * u0[2], gate_act<A>(g0[3]) * u0[3]);
+                hv[2] = pack_bf16x2(gate_act<A>(g1[0]) * u1[0], gate_act<A>(g1[1]) * u1[1]);
+                hv[3] = pack_bf16x2(gate_act<A>(g1[2]) * u1[2], gate_act<A>(g1[3]) * u1[3]);
+                *reinterpret_cast<FFN_LDS u32x4_t *>(base + P * 16) = hv;
+            }
+        }
+        // codes: lane (r, h) -> row r, bytes [16 h, 16 h + 16) of the unit
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const uint8_t *cb = (f == 0 || NMAT == 1) ? p.codes0 : p.codes1;
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const void *>(cb + static_cast<size_t>(wrow(t, f, r)) * row_codes + k0 / 2 + 16 * h),
+                reinterpret_cast<FFN_LDS void *>(base + XB + (wave * 2 + f) * 1024), 16, 0, 0);
+        }
+        // scales: lane (f = h, r) -> the unit's 4 scale bytes of row r of fragment f
+        {
+            const uint8_t *sb = (h == 0 || NMAT == 1) ? p.scales0 : p.scales1;
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const void *>(sb + static_cast<size_t>(wrow(t, h, r)) * row_scales + k0 / 16),
+                reinterpret_cast<FFN_LDS void *>(base + XB + 8192 + wave * 256), 4, 0, 0);
+        }
+    };
+
+    f32x16_t acc[2][MT];
+
+    auto compute = [&](int st) {
+        const FFN_LDS uint8_t *base = lds + st * STAGE;
+        bf16x8_t w[2][4];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const u32x4_t cw = *reinterpret_cast<const FFN_LDS u32x4_t *>(base + XB + (wave * 2 + f) * 1024 + lane * 16);
+            const uint32_t sw = *reinterpret_cast<const FFN_LDS uint16_t *>(base + XB + 8192 + wave * 256 + f * 128 +
+                                                                           r * 4 + h * 2);
+            const float sc0 = e4m3_to_f32<0>(sw);
+            const float sc1 = e4m3_to_f32<1>(sw);
+            w[f][0] = dequant8(cw[0], sc0);
+            w[f][1] = dequant8(cw[1], sc0);
+            w[f][2] = dequant8(cw[2], sc1);
+            w[f][3] = dequant8(cw[3], sc1);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int m = 32 * mt + r;
+                const bf16x8_t a = *reinterpret_cast<const FFN_LDS bf16x8_t *>(
+                    base + m * 128 + (((4 * h + s) ^ (m & 7)) * 16));
+                acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w[0][s], acc[0][mt], 0, 0, 0);
+                acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w[1][s], acc[1][mt], 0, 0, 0);
+            }
+        }
+    };
+
+    auto store_out = [&](int t) {
+        const int rows = opaque_uniform(p.rows);
+        const int M = opaque_uniform(p.M);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                emit_pair<NMAT, OUT, ROWS_TILE>(p, rows, M, t, wave, lane, mt, v, acc[0][mt][v], acc[1][mt][v]);
+    };
+
+    auto slot_ptr = [&](int gg, int t) {
+        const int slot = 2 * gg + (t == sk_begin(gg, U, G) / KU ? 0 : 1);
+        return p.partials + static_cast<size_t>(slot) * SLOT + static_cast<size_t>(wave) * (SLOT / kMfmaWaves);
+    };
+
+    const int npre = min(n, S - 1);
+    for (int j = 0; j < npre; ++j)
+        issue(u_begin + j, j);
+
+    // Pieces: maximal runs of this workgroup's units inside one tile. The
+    // ring runs on across pieces; the accumulators only live inside one.
+    int j = 0;
+    while (j < n) {
+        const int t = (u_begin + j) / KU;
+        const int ku0 = u_begin + j - t * KU;
+        const int len = min(KU - ku0, n - j);
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[f][mt] = f32x16_t{};
+        for (const int jend = j + len; j < jend; ++j) {
+            wait_units_ahead<S, L>(min(S - 2, n - 1 - j));
+            lds_barrier();
+            if (j + S - 1 < n)
+                issue(u_begin + j + S - 1, (j + S - 1) % S);
+            compute(j % S);
+        }
+        if (ku0 == 0 && len == KU) {
+            store_out(t);
+            continue;
+        }
+        // A piece of a tile shared with other workgroups: to its slot.
+        float *mine = slot_ptr(g, t);
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    mine[((f * MT + mt) * 16 + q) * 64 + lane] = acc[f][mt][q];
+        if (p.defer)
+            continue;  // a later reduction launch finishes every tile
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_arrivals = atomicAdd(p.counters + t, 1);
+        __syncthreads();
+        const int g_lo = sk_owner(static_cast<long long>(t) * KU, U, G);
+        const int g_hi = sk_owner(static_cast<long long>(t) * KU + KU - 1, U, G);
+        if (s_arrivals != g_hi - g_lo)
+            continue;
+        // Last piece in: fold all pieces in k order (own one included, read
+        // back), one whole piece per step with all of its loads in flight.
+        __threadfence();
+        for (int gg = g_lo; gg <= g_hi; ++gg) {
+            const float *src = slot_ptr(gg, t) + lane;
+            float x[2][MT][16];
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        x[f][mt][q] = src[((f * MT + mt) * 16 + q) * 64];
+            const bool first = gg == g_lo;
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        acc[f][mt][q] = first ? x[f][mt][q] : acc[f][mt][q] + x[f][mt][q];
+        }
+        store_out(t);
+    }
+}
+
+// Finishes the tiles a deferred launch left as pieces: every element sums its
+// pieces in k order (the slot order) and goes through the same epilogue.
+// Grid: (tiles, ceil(4 * MT * 16 * 64 / 256)), 256 threads.
+template <int MT, int NMAT, int OUT>
+__global__ __launch_bounds__(256) void mfma_reduce_kernel(const MfmaParams p, int G)
+{
+    constexpr int ROWS_TILE = mfma_rows_per_tile<NMAT>();
+    constexpr int SLOT = mfma_slot_floats<MT>();
+    constexpr int PER_WAVE = MT * 16 * 64;  // positions of one fragment of one wave
+    const int t = blockIdx.x;
+    const int e = blockIdx.y * 256 + threadIdx.x;
+    if (e >= kMfmaWaves * PER_WAVE)
+        return;
+    const long long U = p.units;
+    const int KU = p.units_per_tile;
+    const int g_lo = sk_owner(static_cast<long long>(t) * KU, U, G);
+    const int g_hi = sk_owner(static_cast<long long>(t) * KU + KU - 1, U, G);
+    if (g_lo == g_hi)
+        return;  // one workgroup held the whole tile and stored it
+    const int wave = e / PER_WAVE;
+    const int rem = e - wave * PER_WAVE;
+    const int q = rem >> 6;
+    const int lane = rem & 63;
+    float y0 = 0.0f, y1 = 0.0f;
+    for (int gg = g_lo; gg <= g_hi; ++gg) {
+        const int slot = 2 * gg + (t == sk_begin(gg, U, G) / KU ? 0 : 1);
+        const float *src = p.partials + static_cast<size_t>(slot) * SLOT + wave * (SLOT / kMfmaWaves) + rem;
+        const float x0 = src[0];
+        const float x1 = src[PER_WAVE];
+        y0 = gg == g_lo ? x0 : y0 + x0;
+        y1 = gg == g_lo ? x1 : y1 + x1;
+    }
+    emit_pair<NMAT, OUT, ROWS_TILE>(p, p.rows, p.M, t, wave, lane, q >> 4, q & 15, y0, y1);
+}
+
+}  // namespace ffn
