@@ -67,10 +67,10 @@ size_t round256(size_t b)
     return (b + 255) & ~static_cast<size_t>(255);
 }
 
-// Workspace of the matrix-core arm: h for one block of up to kMfmaMaxM rows,
-// the per-tile counters, and the stream-K partial slots.
+// Workspace of the matrix-core arm: h for one block of up to kMfmaMaxM rows
+// and the stream-K partial slots.
 struct PrefillLayout {
-    size_t h, counters, partials, total;
+    size_t h, partials, total;
 };
 
 PrefillLayout prefill_layout(int M, int N)
@@ -78,8 +78,7 @@ PrefillLayout prefill_layout(int M, int N)
     PrefillLayout l{};
     const int mb = M < ffn::kMfmaMaxM ? M : ffn::kMfmaMaxM;
     l.h = 0;
-    l.counters = round256(static_cast<size_t>(mb) * N * 2);
-    l.partials = l.counters + round256(static_cast<size_t>(ffn::mfma_max_tiles(N)) * sizeof(int));
+    l.partials = round256(static_cast<size_t>(mb) * N * 2);
     l.total = l.partials + round256(ffn::mfma_partials_floats() * sizeof(float));
     return l;
 }
@@ -159,8 +158,7 @@ hipError_t run_prefill_forward(int M, ffn::OutKind epi, const void *x, const ffn
 {
     const PrefillLayout l = prefill_layout(M, N);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    ffn::MfmaScratch scratch{reinterpret_cast<float *>(ws + l.partials), reinterpret_cast<int *>(ws + l.counters),
-                             ffn::mfma_max_tiles(N)};
+    ffn::MfmaScratch scratch{reinterpret_cast<float *>(ws + l.partials)};
     void *h = ws + l.h;
     for (int m0 = 0; m0 < M; m0 += ffn::kMfmaMaxM) {
         const int mb = M - m0 < ffn::kMfmaMaxM ? M - m0 : ffn::kMfmaMaxM;

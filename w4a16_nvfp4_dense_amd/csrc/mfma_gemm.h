@@ -38,13 +38,13 @@
 // into units; the T x KU units of the launch are dealt out to the G
 // workgroups as G contiguous, equal ranges (workgroup g takes
 // [floor(g U / G), floor((g + 1) U / G))), so all compute units finish
-// together whatever the tile count. A tile whose units span several
-// workgroups is finished by the last of them to arrive: each writes its
-// fp32 partial tile to its own slot of the workspace, bumps the tile's
-// counter, and the one that completes the count adds the pieces in k order
-// (always the same order, whoever arrives last) and runs the epilogue. No
-// workgroup ever waits for another. With G = T every workgroup owns exactly
-// one whole tile and neither slots nor counters are touched.
+// together whatever the tile count. A workgroup that holds a whole tile runs
+// the epilogue itself; the pieces of a tile split between workgroups go to
+// fp32 slots of the workspace, and mfma_reduce_kernel, launched next, adds
+// them in k order and runs the same epilogue. No workgroup waits for or
+// signals another (device-scope fences inside the GEMM would write back and
+// invalidate the L2 that keeps the activation block resident). With G = T
+// every workgroup owns exactly one whole tile and no slot is touched.
 #pragma once
 
 #include "kernels.h"
@@ -72,8 +72,6 @@ struct MfmaParams {
     void *out0;
     void *out1;
     float *partials;   // 2 G slots of partial tiles (stream-K only)
-    int *counters;     // one per tile, zero at launch (stream-K, not deferred)
-    int defer;         // 1: leave split tiles as pieces for mfma_reduce_kernel
     int M;             // token rows, 1 <= M <= 32 * MT
     int rows;          // weight rows (output columns)
     int cols;          // reduction length, a multiple of 64
@@ -115,14 +113,16 @@ __host__ __device__ inline int sk_owner(long long u, long long U, long long G)
 }
 
 // Wait until at most `ahead` units (of L loads each) issued after the one to
-// be consumed are outstanding; `ahead` is wave-uniform and in [0, S - 2].
-template <int S, int L>
-__device__ __forceinline__ void wait_units_ahead(int ahead)
+// be consumed are outstanding; `ahead` is wave-uniform and in [0, MAXA].
+template <int MAXA, int L>
+__device__ __forceinline__ void wait_units(int ahead)
 {
-    if constexpr (S >= 6) { if (ahead >= 4) { wait_vmcnt<4 * L>(); return; } }
-    if constexpr (S >= 5) { if (ahead >= 3) { wait_vmcnt<3 * L>(); return; } }
-    if constexpr (S >= 4) { if (ahead >= 2) { wait_vmcnt<2 * L>(); return; } }
-    if constexpr (S >= 3) { if (ahead >= 1) { wait_vmcnt<1 * L>(); return; } }
+    static_assert(MAXA <= 5 && MAXA * L < 64, "vmcnt range");
+    if constexpr (MAXA >= 5) { if (ahead >= 5) { wait_vmcnt<5 * L>(); return; } }
+    if constexpr (MAXA >= 4) { if (ahead >= 4) { wait_vmcnt<4 * L>(); return; } }
+    if constexpr (MAXA >= 3) { if (ahead >= 3) { wait_vmcnt<3 * L>(); return; } }
+    if constexpr (MAXA >= 2) { if (ahead >= 2) { wait_vmcnt<2 * L>(); return; } }
+    if constexpr (MAXA >= 1) { if (ahead >= 1) { wait_vmcnt<1 * L>(); return; } }
     wait_vmcnt<0>();
 }
 
@@ -132,6 +132,13 @@ __device__ __forceinline__ void wait_units_ahead(int ahead)
 __device__ __forceinline__ int opaque_uniform(int x)
 {
     asm volatile("" : "+s"(x));
+    return x;
+}
+
+// The same for a per-lane value.
+__device__ __forceinline__ int opaque_lane(int x)
+{
+    asm volatile("" : "+v"(x));
     return x;
 }
 
@@ -204,18 +211,17 @@ template <int MT, int NMAT, int IN, int OUT, int S>
 __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaParams p)
 {
     static_assert(MT >= 1 && MT <= 4, "token tiles");
-    static_assert(S >= 2 && S <= 6, "ring stages");
+    static_assert(S <= 6, "ring stages");
     constexpr int STAGE = mfma_stage_bytes<MT>();
     constexpr int XB = MT * 4096;                           // activation bytes per stage
     constexpr int L = (IN == IN_BF16 ? MT : 0) + 3;         // direct loads per unit per wave
-    static_assert((S - 2) * L < 64, "outstanding loads must fit the vmcnt counter");
+    static_assert(S >= 3 && (S - 2) * L < 64, "ring stages / vmcnt range");
     constexpr int ROWS_WAVE = NMAT == 2 ? 32 : 64;
     constexpr int ROWS_TILE = kMfmaWaves * ROWS_WAVE;
     constexpr int SLOT = mfma_slot_floats<MT>();
 
     extern __shared__ u32x4_t lds_raw[];
     FFN_LDS uint8_t *lds = (FFN_LDS uint8_t *)lds_raw;
-    __shared__ int s_arrivals;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -298,9 +304,12 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaPa
 
     f32x16_t acc[2][MT];
 
-    auto compute = [&](int st) {
-        const FFN_LDS uint8_t *base = lds + st * STAGE;
+    // The dequantised weight fragments of one unit (register double buffer).
+    struct Frags {
         bf16x8_t w[2][4];
+    };
+    auto load_weights = [&](int st, Frags &F) {
+        const FFN_LDS uint8_t *base = lds + st * STAGE;
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
             const u32x4_t cw = *reinterpret_cast<const FFN_LDS u32x4_t *>(base + XB + (wave * 2 + f) * 1024 + lane * 16);
@@ -308,32 +317,36 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaPa
                                                                            r * 4 + h * 2);
             const float sc0 = e4m3_to_f32<0>(sw);
             const float sc1 = e4m3_to_f32<1>(sw);
-            w[f][0] = dequant8(cw[0], sc0);
-            w[f][1] = dequant8(cw[1], sc0);
-            w[f][2] = dequant8(cw[2], sc1);
-            w[f][3] = dequant8(cw[3], sc1);
+            F.w[f][0] = dequant8(cw[0], sc0);
+            F.w[f][1] = dequant8(cw[1], sc0);
+            F.w[f][2] = dequant8(cw[2], sc1);
+            F.w[f][3] = dequant8(cw[3], sc1);
         }
+    };
+    // The unit's products: activation fragments straight from the stage.
+    auto mfma_unit = [&](int st, const Frags &F) {
+        const FFN_LDS uint8_t *base = lds + st * STAGE;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int m = 32 * mt + r;
-                const bf16x8_t a = *reinterpret_cast<const FFN_LDS bf16x8_t *>(
-                    base + m * 128 + (((4 * h + s) ^ (m & 7)) * 16));
-                acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w[0][s], acc[0][mt], 0, 0, 0);
-                acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w[1][s], acc[1][mt], 0, 0, 0);
+                const bf16x8_t a =
+                    *reinterpret_cast<const FFN_LDS bf16x8_t *>(base + m * 128 + (((4 * h + s) ^ (m & 7)) * 16));
+                acc[0][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, F.w[0][s], acc[0][mt], 0, 0, 0);
+                acc[1][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, F.w[1][s], acc[1][mt], 0, 0, 0);
             }
-        }
     };
 
     auto store_out = [&](int t) {
         const int rows = opaque_uniform(p.rows);
         const int M = opaque_uniform(p.M);
+        const int ln = opaque_lane(lane);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-                emit_pair<NMAT, OUT, ROWS_TILE>(p, rows, M, t, wave, lane, mt, v, acc[0][mt][v], acc[1][mt][v]);
+                emit_pair<NMAT, OUT, ROWS_TILE>(p, rows, M, t, wave, ln, mt, v, acc[0][mt][v], acc[1][mt][v]);
     };
 
     auto slot_ptr = [&](int gg, int t) {
@@ -341,9 +354,41 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaPa
         return p.partials + static_cast<size_t>(slot) * SLOT + static_cast<size_t>(wave) * (SLOT / kMfmaWaves);
     };
 
+    // Software pipeline: up to S - 1 units in flight in the LDS ring. In the
+    // step for unit j the weights of unit j + 1 are read and dequantised into
+    // the other register set while the matrix cores work on unit j (whose
+    // activation fragments are read from its stage as they are needed).
+    // F0 holds the weights of the next unit to multiply.
     const int npre = min(n, S - 1);
     for (int j = 0; j < npre; ++j)
         issue(u_begin + j, j);
+    Frags F0, F1;
+    wait_units<S - 2, L>(min(S - 2, n - 1));
+    lds_barrier();
+    load_weights(0, F0);
+    auto step = [&](Frags &cur, Frags &nxt, int j) {
+        // unit j + 1 has landed (past the end: nothing outstanding) ...
+        wait_units<S - 3, L>(max(0, min(S - 3, n - 2 - j)));
+        // ... in every wave, and every wave is done with unit j - 1's stage
+        lds_barrier();
+        if (j + S - 1 < n)
+            issue(u_begin + j + S - 1, (j + S - 1) % S);
+        load_weights((j + 1) % S, nxt);  // past the end: a harmless re-read
+        mfma_unit(j % S, cur);
+        // Interleave: the next unit's code/scale reads and the first two
+        // activation fragments up front, then per fragment its two products,
+        // a share of the dequantisation, and the read two fragments ahead.
+        constexpr int NF = 4 * MT;
+        constexpr int VPF = (2 * 4 * 16 + NF - 1) / NF;  // dequant VALU per fragment
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VPF, 0);
+            if (i < NF - 2)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
 
     // Pieces: maximal runs of this workgroup's units inside one tile. The
     // ring runs on across pieces; the accumulators only live inside one.
@@ -357,19 +402,25 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaPa
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 acc[f][mt] = f32x16_t{};
-        for (const int jend = j + len; j < jend; ++j) {
-            wait_units_ahead<S, L>(min(S - 2, n - 1 - j));
-            lds_barrier();
-            if (j + S - 1 < n)
-                issue(u_begin + j + S - 1, (j + S - 1) % S);
-            compute(j % S);
+        // Two units per trip so the register sets swap roles without copies;
+        // an odd piece ends with one step and a copy of the next unit's set.
+        const int jend = j + len;
+        for (; j + 1 < jend; j += 2) {
+            step(F0, F1, j);
+            step(F1, F0, j + 1);
+        }
+        if (j < jend) {
+            step(F0, F1, j);
+            F0 = F1;
+            ++j;
         }
         if (ku0 == 0 && len == KU) {
             store_out(t);
             continue;
         }
-        // A piece of a tile shared with other workgroups: to its slot.
-        float *mine = slot_ptr(g, t);
+        // A piece of a tile shared with other workgroups: to its slot, for
+        // mfma_reduce_kernel.
+        float *mine = slot_ptr(g, t) + (opaque_lane(lane) - lane);
 #pragma unroll
         for (int f = 0; f < 2; ++f)
 #pragma unroll
@@ -377,44 +428,10 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaPa
 #pragma unroll
                 for (int q = 0; q < 16; ++q)
                     mine[((f * MT + mt) * 16 + q) * 64 + lane] = acc[f][mt][q];
-        if (p.defer)
-            continue;  // a later reduction launch finishes every tile
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0)
-            s_arrivals = atomicAdd(p.counters + t, 1);
-        __syncthreads();
-        const int g_lo = sk_owner(static_cast<long long>(t) * KU, U, G);
-        const int g_hi = sk_owner(static_cast<long long>(t) * KU + KU - 1, U, G);
-        if (s_arrivals != g_hi - g_lo)
-            continue;
-        // Last piece in: fold all pieces in k order (own one included, read
-        // back), one whole piece per step with all of its loads in flight.
-        __threadfence();
-        for (int gg = g_lo; gg <= g_hi; ++gg) {
-            const float *src = slot_ptr(gg, t) + lane;
-            float x[2][MT][16];
-#pragma unroll
-            for (int f = 0; f < 2; ++f)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int q = 0; q < 16; ++q)
-                        x[f][mt][q] = src[((f * MT + mt) * 16 + q) * 64];
-            const bool first = gg == g_lo;
-#pragma unroll
-            for (int f = 0; f < 2; ++f)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int q = 0; q < 16; ++q)
-                        acc[f][mt][q] = first ? x[f][mt][q] : acc[f][mt][q] + x[f][mt][q];
-        }
-        store_out(t);
     }
 }
 
-// Finishes the tiles a deferred launch left as pieces: every element sums its
+// Finishes the tiles a stream-K launch left as pieces: every element sums its
 // pieces in k order (the slot order) and goes through the same epilogue.
 // Grid: (tiles, ceil(4 * MT * 16 * 64 / 256)), 256 threads.
 template <int MT, int NMAT, int OUT>

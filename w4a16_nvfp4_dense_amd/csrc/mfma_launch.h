@@ -11,18 +11,12 @@ namespace ffn {
 constexpr int kMfmaMaxM = 128;     // token rows per launch (larger batches are cut into blocks)
 constexpr int kMfmaMaxGrid = 256;  // workgroups of a stream-K launch
 
-// Stream-K scratch: partial tiles and per-tile arrival counters. The counters
-// must be zero when a launch starts (launch_zero_counters).
+// Stream-K scratch: the partial-tile slots (contents need no initialisation).
 struct MfmaScratch {
     float *partials;  // mfma_partials_floats() floats
-    int *counters;    // max_tiles ints
-    int max_tiles;
 };
 
 size_t mfma_partials_floats();
-// Tiles of the largest launch over `rows` weight rows (two-projection tiling).
-int mfma_max_tiles(int rows);
-hipError_t launch_zero_counters(int *counters, int n, hipStream_t stream);
 
 // Dual GEMM (gate and up, rows = N, cols = K) and down GEMM (rows = K,
 // cols = N) for 1 <= M <= kMfmaMaxM token rows; cols must be a multiple of 64.

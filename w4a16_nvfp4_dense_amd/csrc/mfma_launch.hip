@@ -11,13 +11,7 @@ namespace ffn {
 
 namespace {
 
-constexpr int kStages = 4;
-
-__global__ void zero_i32_kernel(int *p, int n)
-{
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
-        p[i] = 0;
-}
+constexpr int kStages = 5;
 
 template <int MT, int NMAT, int IN, int OUT>
 hipError_t launch_t(MfmaParams p, int G, hipStream_t stream)
@@ -32,12 +26,12 @@ hipError_t launch_t(MfmaParams p, int G, hipStream_t stream)
     return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(G), dim3(kMfmaWaves * 64), args, lds, stream);
 }
 
-// The GEMM, then (deferred stream-K) the reduction of the split tiles.
+// The GEMM, then (stream-K) the reduction of the split tiles.
 template <int MT, int NMAT, int IN, int OUT>
 hipError_t launch_gemm_reduce(const MfmaParams &p, int G, hipStream_t stream)
 {
     hipError_t e = launch_t<MT, NMAT, IN, OUT>(p, G, stream);
-    if (e != hipSuccess || !p.defer)
+    if (e != hipSuccess || p.partials == nullptr)
         return e;
     constexpr int per_tile = kMfmaWaves * MT * 16 * 64;
     hipLaunchKernelGGL((mfma_reduce_kernel<MT, NMAT, OUT>), dim3(p.tiles, (per_tile + 255) / 256), dim3(256), 0,
@@ -58,36 +52,23 @@ hipError_t launch_mt(const MfmaParams &p, int G, hipStream_t stream)
 }
 
 // Grid and stream-K bookkeeping for one GEMM. With a workspace the grid is
-// one workgroup per compute unit (capped at kMfmaMaxGrid) and split tiles are
-// finished either in the kernel by their last piece (counters zeroed first by
-// a small fill launch) or, with `defer`, by a reduction launch after it.
-// Without a workspace the grid is one workgroup per tile.
-hipError_t plan(MfmaParams &p, int nmat, const MfmaScratch *ws, bool defer, int &G, hipStream_t stream)
+// one workgroup per compute unit (capped at kMfmaMaxGrid) and a reduction
+// launch finishes the split tiles; without one it is one workgroup per tile.
+void plan(MfmaParams &p, int nmat, const MfmaScratch *ws, int &G)
 {
     const int rows_tile = nmat == 2 ? mfma_rows_per_tile<2>() : mfma_rows_per_tile<1>();
     p.tiles = (p.rows + rows_tile - 1) / rows_tile;
     p.units_per_tile = p.cols / kUnitCols;
     p.units = p.tiles * p.units_per_tile;
+    p.partials = nullptr;
     if (ws == nullptr) {
         G = p.tiles;
-        p.partials = nullptr;
-        p.counters = nullptr;
-        return hipSuccess;
+        return;
     }
     G = std::max(1, std::min({device_cu_count(), kMfmaMaxGrid, p.units}));
-    if (G <= p.tiles && p.units % G == 0 && (p.units / G) % p.units_per_tile == 0) {
-        p.partials = nullptr;  // every workgroup owns whole tiles
-        p.counters = nullptr;
-        return hipSuccess;
-    }
+    if (G <= p.tiles && p.units % G == 0 && (p.units / G) % p.units_per_tile == 0)
+        return;  // every workgroup owns whole tiles
     p.partials = ws->partials;
-    p.counters = ws->counters;
-    p.defer = defer ? 1 : 0;
-    if (defer)
-        return hipSuccess;
-    if (p.tiles > ws->max_tiles)
-        return hipErrorInvalidValue;
-    return launch_zero_counters(p.counters, p.tiles, stream);
 }
 
 MfmaParams params(int M, const void *in0, const float *in1, const WeightArg &w0, const WeightArg &w1, void *out0,
@@ -117,19 +98,6 @@ size_t mfma_partials_floats()
     return static_cast<size_t>(2) * kMfmaMaxGrid * mfma_slot_floats<4>();
 }
 
-hipError_t launch_zero_counters(int *counters, int n, hipStream_t stream)
-{
-    const int threads = 256;
-    const int blocks = std::max(1, std::min(64, (n + threads - 1) / threads));
-    hipLaunchKernelGGL(zero_i32_kernel, dim3(blocks), dim3(threads), 0, stream, counters, n);
-    return hipGetLastError();
-}
-
-int mfma_max_tiles(int rows)
-{
-    return (rows + mfma_rows_per_tile<2>() - 1) / mfma_rows_per_tile<2>();
-}
-
 hipError_t launch_mfma_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1,
                             void *out0, void *out1, int rows, int cols, const MfmaScratch *ws,
                             hipStream_t stream)
@@ -138,9 +106,7 @@ hipError_t launch_mfma_dual(int M, OutKind out, const void *x, const WeightArg &
         return hipErrorNotSupported;
     MfmaParams p = params(M, x, nullptr, w0, w1, out0, out1, rows, cols);
     int G = 0;
-    hipError_t e = plan(p, 2, ws, false, G, stream);
-    if (e != hipSuccess)
-        return e;
+    plan(p, 2, ws, G);
     switch (out) {
     case OUT_F32_PAIR: return launch_mt<2, IN_BF16, OUT_F32_PAIR>(p, G, stream);
     case OUT_H_SILU: return launch_mt<2, IN_BF16, OUT_H_SILU>(p, G, stream);
@@ -156,9 +122,7 @@ hipError_t launch_mfma_down(int M, InKind in, const void *in0, const float *in1,
         return hipErrorNotSupported;
     MfmaParams p = params(M, in0, in1, w, w, out, nullptr, rows, cols);
     int G = 0;
-    hipError_t e = plan(p, 1, ws, true, G, stream);
-    if (e != hipSuccess)
-        return e;
+    plan(p, 1, ws, G);
     switch (in) {
     case IN_BF16: return launch_mt<1, IN_BF16, OUT_BF16>(p, G, stream);
     case IN_GATEUP_SILU: return launch_mt<1, IN_GATEUP_SILU, OUT_BF16>(p, G, stream);
