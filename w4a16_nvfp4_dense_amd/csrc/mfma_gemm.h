@@ -117,13 +117,16 @@ __host__ __device__ inline int sk_owner(long long u, long long U, long long G)
 template <int MAXA, int L>
 __device__ __forceinline__ void wait_units(int ahead)
 {
-    static_assert(MAXA <= 5 && MAXA * L < 64, "vmcnt range");
-    if constexpr (MAXA >= 5) { if (ahead >= 5) { wait_vmcnt<5 * L>(); return; } }
-    if constexpr (MAXA >= 4) { if (ahead >= 4) { wait_vmcnt<4 * L>(); return; } }
-    if constexpr (MAXA >= 3) { if (ahead >= 3) { wait_vmcnt<3 * L>(); return; } }
-    if constexpr (MAXA >= 2) { if (ahead >= 2) { wait_vmcnt<2 * L>(); return; } }
-    if constexpr (MAXA >= 1) { if (ahead >= 1) { wait_vmcnt<1 * L>(); return; } }
-    wait_vmcnt<0>();
+    static_assert(MAXA >= 0 && MAXA * L < 64, "vmcnt range");
+    if constexpr (MAXA == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= MAXA) {
+            wait_vmcnt<MAXA * L>();
+            return;
+        }
+        wait_units<MAXA - 1, L>(ahead);
+    }
 }
 
 // Hides a wave-uniform value from the optimiser, so that what is derived from
@@ -211,7 +214,7 @@ template <int MT, int NMAT, int IN, int OUT, int S>
 __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaParams p)
 {
     static_assert(MT >= 1 && MT <= 4, "token tiles");
-    static_assert(S <= 6, "ring stages");
+    static_assert(S <= 16, "ring stages");
     constexpr int STAGE = mfma_stage_bytes<MT>();
     constexpr int XB = MT * 4096;                           // activation bytes per stage
     constexpr int L = (IN == IN_BF16 ? MT : 0) + 3;         // direct loads per unit per wave

@@ -11,13 +11,21 @@ namespace ffn {
 
 namespace {
 
-constexpr int kStages = 5;
+// Ring stages: as many as fit in ~150 KB of LDS (the loads in flight per
+// compute unit are what bounds the streaming rate), at most 12.
+template <int MT>
+constexpr int stages()
+{
+    constexpr int s = (150 * 1024) / mfma_stage_bytes<MT>();
+    return s > 12 ? 12 : s;
+}
 
 template <int MT, int NMAT, int IN, int OUT>
 hipError_t launch_t(MfmaParams p, int G, hipStream_t stream)
 {
-    auto kern = mfma_gemm_kernel<MT, NMAT, IN, OUT, kStages>;
-    const int lds = kStages * mfma_stage_bytes<MT>();
+    constexpr int S = stages<MT>();
+    auto kern = mfma_gemm_kernel<MT, NMAT, IN, OUT, S>;
+    const int lds = S * mfma_stage_bytes<MT>();
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess)
