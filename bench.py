@@ -268,7 +268,7 @@ def main():
             "algorithmic_bytes_per_forward": nbytes["forward"],
         },
         "roofline": {
-            "kernel": "dual gate+up GEMV (ffn_nvfp4_dual_gemv: gate, up fp32 out)",
+            "kernel": "dual gate+up GEMV (ffn_nvfp4_dual_gemv entry point: wave_gemv_kernel, gate and up fp32 out)",
             "bound": "hbm",
             "achieved": round(dual_gbs, 2),
             "peak": HBM_PEAK_GBS,

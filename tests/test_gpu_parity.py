@@ -85,7 +85,7 @@ SMALL = [
     (7, 256, 3072, fi.ACT_SILU, 10),
     (8, 5120, 2048, fi.ACT_SILU, 11),       # several LDS pieces for M = 8
     (8, 1056, 8224, fi.ACT_GELU_TANH, 12),  # 33 and 257 chunks: ragged, several pieces
-    # row-streaming kernels (M <= 2, 33 or more chunks per row)
+    # many-wave kernel (M <= 2, 33 or more chunks per row; down rows from LDS)
     (1, 1056, 2080, fi.ACT_SILU, 13),       # 33 / 65 chunks: partly masked last lane chunk
     (2, 2080, 1056, fi.ACT_GELU_TANH, 14),
     (1, 4096, 96, fi.ACT_SILU, 15),         # fewer rows than compute units
@@ -180,6 +180,28 @@ def test_degenerate_weights():
     # zero activations
     z = torch.zeros_like(L.x)
     assert torch.count_nonzero(ffn.forward(z, L.gate, L.up, L.down)) == 0
+
+
+def _scales_at_offset(w, off):
+    """The same scales in a buffer that starts `off` bytes past an aligned
+    allocation (the ABI only asks for 2-byte alignment for M <= 8)."""
+    buf = torch.zeros(w.scales.numel() + 16, dtype=torch.uint8, device=DEV)
+    view = buf[off:off + w.scales.numel()].view(w.scales.shape)
+    view.copy_(w.scales)
+    return ffn.DeviceWeight(w.codes, view, w.scale2)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3])
+def test_scales_two_byte_aligned(M):
+    case = fi.make_small(M, 1056, 2080, act=fi.ACT_GELU_TANH, seed=26)
+    L = loaded(case.name, lambda: case)
+    ref = L.forward()
+    g, u, d = (_scales_at_offset(w, 2) for w in (L.gate, L.up, L.down))
+    assert g.scales.data_ptr() % 4 == 2
+    out = ffn.forward(L.x, g, u, d, case.act)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert_ffn_close(out, oracle.ffn(case), case.name)
 
 
 def test_nan_scale_propagates():

@@ -93,33 +93,24 @@ int launch_status(hipError_t e)
     return e == hipSuccess ? FFN_NVFP4_OK : FFN_NVFP4_ERR_LAUNCH;
 }
 
-// Dual GEMV: the LDS-ring kernels where they apply (M <= 2), else the
-// general LDS-staged kernel.
-// The LDS-ring and matrix-core kernels move scales 4 bytes at a time.
-bool scales_dma_ok(const ffn::WeightArg &w)
-{
-    return aligned(w.scales, 4);
-}
-
+// M = 1, 2: the many-wave GEMV for rows of 33 chunks or more, else (and for
+// 3 <= M <= 8) the general LDS-staged kernel. All of them share one per-row
+// arithmetic, so a row's result does not depend on which one ran.
 hipError_t run_dual(int M, ffn::OutKind out, const void *x, const ffn::WeightArg &g, const ffn::WeightArg &u,
                     void *out0, void *out1, int N, int K, hipStream_t stream)
 {
-    if (scales_dma_ok(g) && scales_dma_ok(u)) {
-        hipError_t e = ffn::launch_ring_dual(M, out, x, g, u, out0, out1, N, K, stream);
-        if (e != hipErrorNotSupported)
-            return e;
-    }
+    hipError_t e = ffn::launch_wave_dual(M, out, x, g, u, out0, out1, N, K, stream);
+    if (e != hipErrorNotSupported)
+        return e;
     return ffn::launch_gemv(M, 2, ffn::IN_BF16, out, x, nullptr, g, u, out0, out1, N, K, stream);
 }
 
 hipError_t run_down(int M, ffn::InKind in, const void *in0, const float *in1, const ffn::WeightArg &d,
                     void *out, int K, int N, hipStream_t stream)
 {
-    if (scales_dma_ok(d)) {
-        hipError_t e = ffn::launch_ring_down(M, in, in0, in1, d, out, K, N, stream);
-        if (e != hipErrorNotSupported)
-            return e;
-    }
+    hipError_t e = ffn::launch_wave_down(M, in, in0, in1, d, out, K, N, stream);
+    if (e != hipErrorNotSupported)
+        return e;
     return ffn::launch_gemv(M, 1, in, ffn::OUT_BF16, in0, in1, d, d, out, nullptr, K, N, stream);
 }
 

@@ -265,6 +265,22 @@ hipError_t launch_m(int M, int lpr, const GemvParams &p, size_t lds_bytes, hipSt
 
 }  // namespace
 
+// Compute units of the current device, cached per device.
+int device_cu_count()
+{
+    static int counts[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int n = __atomic_load_n(&counts[dev], __ATOMIC_RELAXED);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        __atomic_store_n(&counts[dev], n, __ATOMIC_RELAXED);
+    }
+    return n;
+}
+
 // Lanes per row as a function of the reduction length only: the smallest of
 // 8/16/32/64 covering the row's chunks, 64 for rows of 33 chunks or more. Every
 // kernel that computes a row with a given reduction length uses this split and

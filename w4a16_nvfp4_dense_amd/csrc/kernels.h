@@ -41,22 +41,12 @@ hipError_t launch_gemv(int M, int nmat, InKind in, OutKind out,
 
 namespace ffn {
 
-// Row-streaming GEMV (M = 1 or 2, reduction length up to 64 * 32 * kStreamMaxIt
-// columns): one workgroup per compute unit, whole-wave rows, activations in
-// registers. Returns hipErrorNotSupported for shapes it does not cover.
-constexpr int kStreamMaxIt = 12;
-hipError_t launch_stream_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1,
-                              void *out0, void *out1, int rows, int cols, hipStream_t stream);
-hipError_t launch_stream_down(int M, InKind in, const void *in0, const float *in1, const WeightArg &w,
-                              void *out, int rows, int cols, hipStream_t stream);
-
-// LDS-ring GEMV (M = 1 or 2; rows of 33 or more chunks, an even number of
-// them, at most 64 * 32 * kStreamMaxIt columns): weights streamed into LDS by
-// direct global->LDS loads, activations in registers. Returns
-// hipErrorNotSupported for shapes it does not cover.
-hipError_t launch_ring_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1,
+// Many-wave GEMV (M = 1 or 2; rows of 33 to 768 chunks): one whole row per
+// wave at a time, many waves per compute unit, activations staged in LDS.
+// Returns hipErrorNotSupported for shapes it does not cover.
+hipError_t launch_wave_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1,
                             void *out0, void *out1, int rows, int cols, hipStream_t stream);
-hipError_t launch_ring_down(int M, InKind in, const void *in0, const float *in1, const WeightArg &w, void *out,
+hipError_t launch_wave_down(int M, InKind in, const void *in0, const float *in1, const WeightArg &w, void *out,
                             int rows, int cols, hipStream_t stream);
 
 // Number of compute units of the current device (cached per device).

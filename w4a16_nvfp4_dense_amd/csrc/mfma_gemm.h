@@ -49,7 +49,6 @@
 
 #include "kernels.h"
 #include "nvfp4_device.h"
-#include "ring_gemv.h"  // FFN_LDS, wait_vmcnt
 
 namespace ffn {
 

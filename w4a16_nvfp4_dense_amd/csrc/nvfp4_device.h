@@ -63,6 +63,18 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16)
     return __builtin_bit_cast(float, bits16 << 16);
 }
 
+// LDS address space (a C-style cast is the only way to spell a pointer into it).
+#define FFN_LDS __attribute__((address_space(3)))
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt low bits [3:0], high bits [15:14]; expcnt [6:4] = 7; lgkmcnt [11:8] = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // ---------------------------------------------------------------- activations
 // SiLU(g) = g / (1 + e^-g). GELU with the tanh approximation,
 // 0.5 g (1 + tanh(s (g + 0.044715 g^3))), s = sqrt(2/pi), is written in the
