@@ -85,12 +85,16 @@ SMALL = [
     (7, 256, 3072, fi.ACT_SILU, 10),
     (8, 5120, 2048, fi.ACT_SILU, 11),       # several LDS pieces for M = 8
     (8, 1056, 8224, fi.ACT_GELU_TANH, 12),  # 33 and 257 chunks: ragged, several pieces
-    # many-wave kernel (M <= 2, 33 or more chunks per row; down rows from LDS)
+    # many-wave kernel (33 or more chunks per row, activations in LDS)
     (1, 1056, 2080, fi.ACT_SILU, 13),       # 33 / 65 chunks: partly masked last lane chunk
     (2, 2080, 1056, fi.ACT_GELU_TANH, 14),
     (1, 4096, 96, fi.ACT_SILU, 15),         # fewer rows than compute units
     (2, 2048, 20000, fi.ACT_SILU, 16),      # 79 rows per CU; 625-chunk down rows from LDS
     (1, 12288, 4096, fi.ACT_GELU_TANH, 17), # 6 chunks per lane
+    (5, 1056, 12288, fi.ACT_GELU_TANH, 18), # down: 6 chunks per lane, launches of 4 + 1 rows
+    (7, 4096, 18432, fi.ACT_SILU, 19),      # down: 9 chunks per lane, launches of 4 + 3 rows
+    (6, 12288, 1056, fi.ACT_SILU, 20),      # dual: 6 chunks per lane, launches of 4 + 2 rows
+    (3, 24576, 1056, fi.ACT_GELU_TANH, 21), # dual: 12 chunks per lane, 8-wave workgroups
 ]
 
 

@@ -93,9 +93,9 @@ int launch_status(hipError_t e)
     return e == hipSuccess ? FFN_NVFP4_OK : FFN_NVFP4_ERR_LAUNCH;
 }
 
-// M = 1, 2: the many-wave GEMV for rows of 33 chunks or more, else (and for
-// 3 <= M <= 8) the general LDS-staged kernel. All of them share one per-row
-// arithmetic, so a row's result does not depend on which one ran.
+// 1 <= M <= 8: the many-wave GEMV for rows of 33 chunks or more, else the
+// general LDS-staged kernel. Both share one per-row arithmetic, so a row's
+// result does not depend on which one ran.
 hipError_t run_dual(int M, ffn::OutKind out, const void *x, const ffn::WeightArg &g, const ffn::WeightArg &u,
                     void *out0, void *out1, int N, int K, hipStream_t stream)
 {

@@ -41,8 +41,9 @@ hipError_t launch_gemv(int M, int nmat, InKind in, OutKind out,
 
 namespace ffn {
 
-// Many-wave GEMV (M = 1 or 2; rows of 33 to 768 chunks): one whole row per
-// wave at a time, many waves per compute unit, activations staged in LDS.
+// Many-wave GEMV (1 <= M <= 8; rows of 33 to 768 chunks): one whole row per
+// wave at a time, many waves per compute unit, activations staged in LDS
+// (in several launches of up to 8 activation rows when they do not fit).
 // Returns hipErrorNotSupported for shapes it does not cover.
 hipError_t launch_wave_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1,
                             void *out0, void *out1, int rows, int cols, hipStream_t stream);

@@ -1,6 +1,8 @@
-// wave_gemv.h -- many-wave NVFP4 GEMV for decode batches (M = 1, 2): the dual
-// gate+up GEMV and the down GEMV (dense_ffn.rs page, DenseFfnLayer::forward
-// and forward_k2) for rows of 33 chunks (1056 columns) or more.
+// wave_gemv.h -- many-wave NVFP4 GEMV for decode and verify batches
+// (1 <= M <= 8 activation rows, launched in groups whose activations fit in
+// LDS): the dual gate+up GEMV and the down GEMV (dense_ffn.rs page,
+// DenseFfnLayer::forward, forward_k2 / forward_k3 / forward_km) for rows of
+// 33 chunks (1056 columns) or more.
 //
 // Why. One wave per SIMD issues a VALU instruction at best every ~7.5 cycles,
 // and the FP4 conversions are slow instructions, so a GEMV that keeps one
@@ -86,15 +88,20 @@ __global__ __launch_bounds__(64 * W) void wave_gemv_kernel(const WaveParams p)
         }
     };
 
-    // Activations into LDS. Their global loads go out before the first row's
-    // weight loads, so waiting for them does not wait for the weights (loads
-    // complete in order).
+    // Activations into LDS, in batches of SU 16-byte units per thread. The
+    // first row's weight loads go out right after the last batch's global
+    // loads: waiting for the activations then does not wait for the weights
+    // (loads complete in order), and the weight registers are not live while
+    // earlier batches are in flight.
     {
-        constexpr int SU = 4;  // 16-byte units per thread and batch
-        const int total = M * IT * 64 * 4;
-        const int nthr = 64 * W;
-        bool first = true;
-        for (int base = 0; base < total; base += SU * nthr) {
+        constexpr int total = M * IT * 64 * 4;
+        constexpr int nthr = 64 * W;
+        constexpr int need = (total + nthr - 1) / nthr;
+        constexpr int SU = (IN == IN_BF16) ? (need < 8 ? need : 8) : 2;
+        constexpr int nbatch = (total + SU * nthr - 1) / (SU * nthr);
+#pragma unroll
+        for (int bi = 0; bi < nbatch; ++bi) {
+            const int base = bi * SU * nthr;
             u32x4_t v[SU];
 #pragma unroll
             for (int k = 0; k < SU; ++k) {
@@ -117,9 +124,8 @@ __global__ __launch_bounds__(64 * W) void wave_gemv_kernel(const WaveParams p)
                     v[k][3] = pack_bf16x2(gate_act<A>(g1[2]) * u1[2], gate_act<A>(g1[3]) * u1[3]);
                 }
             }
-            if (first && g < p.rows)
+            if (bi == nbatch - 1 && g < p.rows)
                 load_row(g);
-            first = false;
 #pragma unroll
             for (int k = 0; k < SU; ++k) {
                 const int u = base + k * nthr + static_cast<int>(threadIdx.x);
@@ -132,8 +138,6 @@ __global__ __launch_bounds__(64 * W) void wave_gemv_kernel(const WaveParams p)
                 }
             }
         }
-        if (first && g < p.rows)
-            load_row(g);
         __syncthreads();
     }
 
@@ -152,54 +156,55 @@ __global__ __launch_bounds__(64 * W) void wave_gemv_kernel(const WaveParams p)
                 acc[t][m] = 0.0f;
 #pragma unroll
         for (int i = 0; i < IT; ++i) {
-            u32x4_t a[M][4];
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    a[m][q] = ar[((m * IT + i) * 4 + q) * 64];
+            // this chunk's weights of every matrix as bf16 pairs, and scales
+            bf16x2_t wp[NMAT][16];
+            float s0[NMAT], s1[NMAT];
 #pragma unroll
             for (int t = 0; t < NMAT; ++t) {
                 const u32x4_t w = wc[t][i];
                 // past the row end: zero activations, and a zero scale so that
                 // a NaN scale of the clamped duplicate chunk cannot leak in
                 const uint32_t sw = (i < IT - 1 || oklast) ? ws[t][i] : 0u;
-                bf16x2_t wp[16];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    wp[4 * q + 0] = fp4x2_to_bf16x2<0>(w[q]);
-                    wp[4 * q + 1] = fp4x2_to_bf16x2<1>(w[q]);
-                    wp[4 * q + 2] = fp4x2_to_bf16x2<2>(w[q]);
-                    wp[4 * q + 3] = fp4x2_to_bf16x2<3>(w[q]);
+                    wp[t][4 * q + 0] = fp4x2_to_bf16x2<0>(w[q]);
+                    wp[t][4 * q + 1] = fp4x2_to_bf16x2<1>(w[q]);
+                    wp[t][4 * q + 2] = fp4x2_to_bf16x2<2>(w[q]);
+                    wp[t][4 * q + 3] = fp4x2_to_bf16x2<3>(w[q]);
                 }
-                const float s0 = e4m3_to_f32<0>(sw);
-                const float s1 = e4m3_to_f32<1>(sw);
+                s0[t] = e4m3_to_f32<0>(sw);
+                s1[t] = e4m3_to_f32<1>(sw);
+            }
 #pragma unroll
-                for (int m = 0; m < M; ++m) {
+            for (int m = 0; m < M; ++m) {
+                u32x4_t a[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    a[q] = ar[((m * IT + i) * 4 + q) * 64];
+#pragma unroll
+                for (int t = 0; t < NMAT; ++t) {
                     float t0 = 0.0f, t1 = 0.0f;
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
-                        t0 = dot2_bf16(wp[b], as_bf16x2(a[m][0][b]), t0);
-                        t1 = dot2_bf16(wp[8 + b], as_bf16x2(a[m][2][b]), t1);
+                        t0 = dot2_bf16(wp[t][b], as_bf16x2(a[0][b]), t0);
+                        t1 = dot2_bf16(wp[t][8 + b], as_bf16x2(a[2][b]), t1);
                     }
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
-                        t0 = dot2_bf16(wp[4 + b], as_bf16x2(a[m][1][b]), t0);
-                        t1 = dot2_bf16(wp[12 + b], as_bf16x2(a[m][3][b]), t1);
+                        t0 = dot2_bf16(wp[t][4 + b], as_bf16x2(a[1][b]), t0);
+                        t1 = dot2_bf16(wp[t][12 + b], as_bf16x2(a[3][b]), t1);
                     }
-                    acc[t][m] = __builtin_fmaf(t0, s0, acc[t][m]);
-                    acc[t][m] = __builtin_fmaf(t1, s1, acc[t][m]);
+                    acc[t][m] = __builtin_fmaf(t0, s0[t], acc[t][m]);
+                    acc[t][m] = __builtin_fmaf(t1, s1[t], acc[t][m]);
                 }
-            }
-            // One chunk at a time: the accumulators pass through an empty asm
-            // that also orders memory, so this chunk's arithmetic completes
-            // before the next chunk's activation reads (otherwise all of them
-            // are issued first and pinned in registers).
+                // One activation row at a time: its accumulators pass through
+                // an empty asm that also orders memory, so its arithmetic is
+                // done before the next activation reads (otherwise all of them
+                // are issued first and pinned in registers).
 #pragma unroll
-            for (int t = 0; t < NMAT; ++t)
-#pragma unroll
-                for (int m = 0; m < M; ++m)
+                for (int t = 0; t < NMAT; ++t)
                     asm volatile("" : "+v"(acc[t][m])::"memory");
+            }
         }
         // the next row's loads go out before this row's reduction and store
         if (r + G < p.rows)

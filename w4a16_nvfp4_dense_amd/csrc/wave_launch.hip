@@ -1,4 +1,4 @@
-// wave_launch.hip -- host-side launch of the many-wave GEMV (M = 1, 2) and
+// wave_launch.hip -- host-side launch of the many-wave GEMV (1 <= M <= 8) and
 // its instantiations.
 #include <hip/hip_runtime.h>
 
@@ -10,49 +10,108 @@ namespace ffn {
 
 namespace {
 
-constexpr int kWaveMaxIt = 12;  // chunks per lane: reduction length up to 24576
+constexpr int kWaveMaxIt = 12;        // chunks per lane: reduction length up to 24576
+constexpr int kWaveLdsMax = 144 * 1024;  // of the 160 KB per compute unit
 
-// Waves per workgroup and workgroups per compute unit (measured on MI355X at
-// the decode shapes): the dual GEMV runs 2 x 8 waves per CU, the down GEMV
-// 16 waves in one workgroup per CU.
-template <int NMAT>
+// Activation rows one launch stages in LDS (M x IT x 4 KB).
+template <int M, int IT>
+constexpr bool wave_fits()
+{
+    return M * IT * 4096 <= kWaveLdsMax;
+}
+
+// Waves per workgroup: 16 (at most 128 registers per lane) while the
+// weight registers of one row (5 per chunk and matrix), the converted chunk
+// (16 per matrix) and the accumulators fit in that with room to spare,
+// otherwise 8 (up to 256 registers).
+template <int M, int IT, int NMAT>
+constexpr int wave_w_regs()
+{
+    return (NMAT * IT * 5 + NMAT * 16 + M * NMAT + 30 <= 120) ? 16 : 8;
+}
+
+// Measured on MI355X at the decode shapes: the dual GEMV runs best as 2 x 8
+// waves per compute unit while two workgroups' activations fit in LDS; the
+// down GEMV as 16 waves in one workgroup.
+template <int M, int IT, int NMAT>
 constexpr int wave_w()
 {
-    return NMAT == 2 ? 8 : 16;
+    return (NMAT == 2 && 2 * M * IT * 4096 <= kWaveLdsMax) ? 8 : wave_w_regs<M, IT, NMAT>();
 }
-template <int NMAT>
+
+template <int M, int IT, int NMAT>
 constexpr int wave_blocks_per_cu()
 {
-    return NMAT == 2 ? 2 : 1;
+    return (wave_w<M, IT, NMAT>() == 8 && 2 * M * IT * 4096 <= kWaveLdsMax) ? 2 : 1;
 }
 
 template <int M, int IT, int NMAT, int IN, int OUT>
 hipError_t launch_one(const WaveParams &p, hipStream_t stream)
 {
-    constexpr int W = wave_w<NMAT>();
-    auto kern = wave_gemv_kernel<M, IT, NMAT, IN, OUT, W>;
-    const int lds = M * IT * 4096;
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess)
-            return e;
+    if constexpr (!wave_fits<M, IT>()) {
+        return hipErrorNotSupported;
+    } else {
+        constexpr int W = wave_w<M, IT, NMAT>();
+        auto kern = wave_gemv_kernel<M, IT, NMAT, IN, OUT, W>;
+        const int lds = M * IT * 4096;
+        if (lds > 64 * 1024) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (e != hipSuccess)
+                return e;
+        }
+        const int want = device_cu_count() * wave_blocks_per_cu<M, IT, NMAT>();
+        const int blocks = std::max(1, std::min(want, (p.rows + W - 1) / W));
+        WaveParams q = p;
+        void *args[] = {&q};
+        return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(blocks), dim3(W * 64), args, lds,
+                               stream);
     }
-    const int want = device_cu_count() * wave_blocks_per_cu<NMAT>();
-    const int blocks = std::max(1, std::min(want, (p.rows + W - 1) / W));
-    WaveParams q = p;
-    void *args[] = {&q};
-    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(blocks), dim3(W * 64), args, lds, stream);
 }
 
-template <int NMAT, int IN, int OUT>
-hipError_t launch_it(int M, int it, const WaveParams &p, hipStream_t stream)
+template <int IT, int NMAT, int IN, int OUT>
+hipError_t launch_m(int M, const WaveParams &p, hipStream_t stream)
 {
-#define FFN_WAVE_CASE(IT_)                                                   \
-    case IT_:                                                                \
-        return M == 1 ? launch_one<1, IT_, NMAT, IN, OUT>(p, stream)         \
-                      : launch_one<2, IT_, NMAT, IN, OUT>(p, stream);
-    switch (it) {
+    switch (M) {
+    case 1: return launch_one<1, IT, NMAT, IN, OUT>(p, stream);
+    case 2: return launch_one<2, IT, NMAT, IN, OUT>(p, stream);
+    case 3: return launch_one<3, IT, NMAT, IN, OUT>(p, stream);
+    case 4: return launch_one<4, IT, NMAT, IN, OUT>(p, stream);
+    case 8: return launch_one<8, IT, NMAT, IN, OUT>(p, stream);
+    default: return hipErrorNotSupported;
+    }
+}
+
+// Activation rows per launch for reduction steps `it`: the largest of
+// 8, 4, 3, 2, 1 that is at most `left` and whose staging fits in LDS.
+int group_rows(int left, int it)
+{
+    for (int g : {8, 4, 3, 2, 1})
+        if (g <= left && g * it * 4096 <= kWaveLdsMax)
+            return g;
+    return 0;
+}
+
+// Splits the batch into launches of group_rows() activation rows each (rows
+// of a batch are independent, so the grouping does not change any result).
+template <int NMAT, int IN, int OUT>
+hipError_t launch_groups(int M, int it, WaveParams p, size_t in_elem, size_t out_elem, hipStream_t stream)
+{
+    for (int m0 = 0; m0 < M;) {
+        const int g = group_rows(M - m0, it);
+        if (g == 0)
+            return hipErrorNotSupported;
+        WaveParams q = p;
+        q.in0 = static_cast<const uint8_t *>(p.in0) + static_cast<size_t>(m0) * p.cols * in_elem;
+        if (p.in1)
+            q.in1 = p.in1 + static_cast<size_t>(m0) * p.cols;
+        q.out0 = static_cast<uint8_t *>(p.out0) + static_cast<size_t>(m0) * p.rows * out_elem;
+        if (p.out1)
+            q.out1 = static_cast<uint8_t *>(p.out1) + static_cast<size_t>(m0) * p.rows * out_elem;
+        hipError_t e = hipErrorNotSupported;
+        switch (it) {
+#define FFN_WAVE_CASE(IT_) \
+        case IT_: e = launch_m<IT_, NMAT, IN, OUT>(g, q, stream); break;
         FFN_WAVE_CASE(1)
         FFN_WAVE_CASE(2)
         FFN_WAVE_CASE(3)
@@ -65,10 +124,14 @@ hipError_t launch_it(int M, int it, const WaveParams &p, hipStream_t stream)
         FFN_WAVE_CASE(10)
         FFN_WAVE_CASE(11)
         FFN_WAVE_CASE(12)
-    default:
-        return hipErrorNotSupported;
-    }
 #undef FFN_WAVE_CASE
+        default: break;
+        }
+        if (e != hipSuccess)
+            return e;
+        m0 += g;
+    }
+    return hipSuccess;
 }
 
 WaveParams wave_params(const void *in0, const float *in1, const WeightArg &w0, const WeightArg &w1, void *out0,
@@ -107,13 +170,13 @@ hipError_t launch_wave_dual(int M, OutKind out, const void *x, const WeightArg &
                             void *out1, int rows, int cols, hipStream_t stream)
 {
     const int it = wave_iters(cols);
-    if (M < 1 || M > 2 || it < 1 || it > kWaveMaxIt)
+    if (M < 1 || M > 8 || it < 1 || it > kWaveMaxIt || group_rows(1, it) == 0)
         return hipErrorNotSupported;
     const WaveParams p = wave_params(x, nullptr, w0, w1, out0, out1, rows, cols);
     switch (out) {
-    case OUT_F32_PAIR: return launch_it<2, IN_BF16, OUT_F32_PAIR>(M, it, p, stream);
-    case OUT_H_SILU: return launch_it<2, IN_BF16, OUT_H_SILU>(M, it, p, stream);
-    case OUT_H_GELU: return launch_it<2, IN_BF16, OUT_H_GELU>(M, it, p, stream);
+    case OUT_F32_PAIR: return launch_groups<2, IN_BF16, OUT_F32_PAIR>(M, it, p, 2, 4, stream);
+    case OUT_H_SILU: return launch_groups<2, IN_BF16, OUT_H_SILU>(M, it, p, 2, 2, stream);
+    case OUT_H_GELU: return launch_groups<2, IN_BF16, OUT_H_GELU>(M, it, p, 2, 2, stream);
     default: return hipErrorNotSupported;
     }
 }
@@ -122,13 +185,13 @@ hipError_t launch_wave_down(int M, InKind in, const void *in0, const float *in1,
                             int rows, int cols, hipStream_t stream)
 {
     const int it = wave_iters(cols);
-    if (M < 1 || M > 2 || it < 1 || it > kWaveMaxIt)
+    if (M < 1 || M > 8 || it < 1 || it > kWaveMaxIt || group_rows(1, it) == 0)
         return hipErrorNotSupported;
     const WaveParams p = wave_params(in0, in1, w, w, out, nullptr, rows, cols);
     switch (in) {
-    case IN_BF16: return launch_it<1, IN_BF16, OUT_BF16>(M, it, p, stream);
-    case IN_GATEUP_SILU: return launch_it<1, IN_GATEUP_SILU, OUT_BF16>(M, it, p, stream);
-    case IN_GATEUP_GELU: return launch_it<1, IN_GATEUP_GELU, OUT_BF16>(M, it, p, stream);
+    case IN_BF16: return launch_groups<1, IN_BF16, OUT_BF16>(M, it, p, 2, 2, stream);
+    case IN_GATEUP_SILU: return launch_groups<1, IN_GATEUP_SILU, OUT_BF16>(M, it, p, 4, 2, stream);
+    case IN_GATEUP_GELU: return launch_groups<1, IN_GATEUP_GELU, OUT_BF16>(M, it, p, 4, 2, stream);
     default: return hipErrorNotSupported;
     }
 }
