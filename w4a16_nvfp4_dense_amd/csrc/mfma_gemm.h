@@ -144,15 +144,6 @@ __device__ __forceinline__ int opaque_lane(int x)
     return x;
 }
 
-// Workgroup barrier for LDS only: waits for this wave's LDS traffic and meets
-// the other waves, without the vector-memory drain of __syncthreads() (which
-// would also wait for the direct loads still in flight for later units).
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt untouched
-    __builtin_amdgcn_s_barrier();
-}
-
 // Eight codes (one dword) times one block scale, as eight bf16 (exact).
 __device__ __forceinline__ bf16x8_t dequant8(uint32_t d, float sc)
 {

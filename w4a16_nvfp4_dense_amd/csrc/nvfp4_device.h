@@ -75,6 +75,17 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier for LDS only: waits for this wave's LDS traffic and meets
+// the other waves, without the vector-memory drain of __syncthreads() (which
+// would also wait for global loads still in flight for later use).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------- activations
 // SiLU(g) = g / (1 + e^-g). GELU with the tanh approximation,
 // 0.5 g (1 + tanh(s (g + 0.044715 g^3))), s = sqrt(2/pi), is written in the

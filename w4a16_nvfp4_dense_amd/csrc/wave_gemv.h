@@ -9,13 +9,12 @@
 // wave per SIMD (its activations in registers) spends most of its time
 // issuing arithmetic, not streaming. Here a compute unit runs many waves
 // (up to 5 per SIMD), each with a small register footprint: a wave takes one
-// whole weight row at a time, issues all of that row's loads at once
-// (non-temporal, 16 bytes of codes per lane per 32-column chunk), and the
-// activations sit in LDS, staged once per workgroup. The next row's loads go
-// out as soon as a row's arithmetic is done. Measured on MI355X at the
-// 5120/17408 decode shapes: dual GEMV 17.1 us with 2 x 8 waves per compute
-// unit (19.6 us for a one-wave-per-SIMD ring), down GEMV 11.1 us with 16
-// waves per compute unit (13.8 us).
+// whole weight row at a time, issues all of that row's loads at once (16
+// bytes of codes per lane per 32-column chunk), and the activations sit in
+// LDS, staged once per workgroup. The next row's loads go out as soon as a
+// row's arithmetic is done. Measured on MI355X at the 5120/17408 decode
+// shapes, the dual GEMV beat a one-wave-per-SIMD ring 17.1 to 19.6 us with
+// 2 x 8 waves per compute unit, the down GEMV 11.1 to 13.8 us with 16.
 //
 // The arithmetic per chunk and the reduction are those of the other GEMV
 // kernels of the library (lane l owns chunks l, l + 64, ...; 16 FP4 -> bf16
@@ -45,190 +44,257 @@ struct WaveParams {
     int cpr;  // 32-column chunks per row
 };
 
+// Geometry of one weight row as seen by one lane: lane l owns chunks
+// l, l + 64, ..., l + 64 (IT - 1); only the last step can run past the row end
+// (64 (IT - 1) < cpr <= 64 IT), where the lane re-reads the row's last chunk
+// and its result is dropped.
+struct RowGeom {
+    int lane;
+    int clast;    // chunk the lane reads in the last step
+    bool oklast;  // whether that chunk is really the lane's
+    size_t row_codes, row_scales;
+};
+
+template <int IT>
+__device__ __forceinline__ RowGeom row_geom(int cpr)
+{
+    RowGeom rg;
+    rg.lane = threadIdx.x & 63;
+    rg.clast = min(rg.lane + 64 * (IT - 1), cpr - 1);
+    rg.oklast = rg.lane + 64 * (IT - 1) < cpr;
+    rg.row_codes = static_cast<size_t>(cpr) * 16;
+    rg.row_scales = static_cast<size_t>(cpr) * 2;
+    return rg;
+}
+
+// One row of NMAT weights in registers: 16 bytes of codes and 2 bytes of
+// scales per lane and step.
+template <int IT, int NMAT>
+struct WaveRow {
+    u32x4_t wc[NMAT][IT];
+    uint32_t ws[NMAT][IT];
+};
+
+// Issues all loads of row r; NT marks them non-temporal.
+template <bool NT, int IT, int NMAT>
+__device__ __forceinline__ void load_row(WaveRow<IT, NMAT> &w, const uint8_t *codes0, const uint8_t *scales0,
+                                         const uint8_t *codes1, const uint8_t *scales1, int r, const RowGeom &rg)
+{
+#pragma unroll
+    for (int t = 0; t < NMAT; ++t) {
+        const u32x4_t *cb =
+            reinterpret_cast<const u32x4_t *>((t == 0 ? codes0 : codes1) + static_cast<size_t>(r) * rg.row_codes);
+        const uint16_t *sb =
+            reinterpret_cast<const uint16_t *>((t == 0 ? scales0 : scales1) + static_cast<size_t>(r) * rg.row_scales);
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int c = (i == IT - 1) ? rg.clast : rg.lane + 64 * i;
+            if constexpr (NT) {
+                w.wc[t][i] = __builtin_nontemporal_load(cb + c);
+                w.ws[t][i] = __builtin_nontemporal_load(sb + c);
+            } else {
+                w.wc[t][i] = cb[c];
+                w.ws[t][i] = sb[c];
+            }
+        }
+    }
+}
+
+// Stages M activation rows of `cols` (= 32 cpr) columns into LDS as 16-byte
+// units ((m * IT + i) * 4 + q) * 64 + l: quarter q of the chunk lane l reads
+// in step i (chunk l + 64 i; zero past the row end), so every read is
+// conflict-free and its address is the lane's offset plus a constant. Uses
+// M * IT * 4 KB. The W waves of the workgroup load in batches of SU units per
+// thread; `issue()` runs right after the last batch's global loads (the
+// first weight row goes out there: waiting for the activations then does not
+// wait for the weights, as loads complete in order, and the weight registers
+// are not live while earlier batches are in flight). The caller synchronises
+// the workgroup before reading.
+template <int M, int IT, int IN, int W, class F>
+__device__ __forceinline__ void stage_act(u32x4_t *act, const void *in0, const float *in1, int cols, int cpr,
+                                          F &&issue)
+{
+    constexpr int total = M * IT * 64 * 4;
+    constexpr int nthr = 64 * W;
+    constexpr int need = (total + nthr - 1) / nthr;
+    constexpr int SU = (IN == IN_BF16) ? (need < 8 ? need : 8) : 2;
+    constexpr int nbatch = (total + SU * nthr - 1) / (SU * nthr);
+#pragma unroll
+    for (int bi = 0; bi < nbatch; ++bi) {
+        const int base = bi * SU * nthr;
+        u32x4_t v[SU];
+#pragma unroll
+        for (int k = 0; k < SU; ++k) {
+            // global piece u: row m, chunk c, quarter q (q fastest)
+            const int u = base + k * nthr + static_cast<int>(threadIdx.x);
+            const int m = min(u / (IT * 256), M - 1);
+            const int rem = u - m * IT * 256;
+            const int c = min(rem >> 2, cpr - 1);
+            const size_t off = static_cast<size_t>(m) * cols + static_cast<size_t>(c) * 32 + (rem & 3) * 8;
+            if constexpr (IN == IN_BF16) {
+                v[k] = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(in0) + off);
+            } else {
+                constexpr int A = (IN == IN_GATEUP_SILU) ? ACT_SILU : ACT_GELU_TANH;
+                const f32x4_t *gp = reinterpret_cast<const f32x4_t *>(static_cast<const float *>(in0) + off);
+                const f32x4_t *up = reinterpret_cast<const f32x4_t *>(in1 + off);
+                const f32x4_t g0 = gp[0], g1 = gp[1], u0 = up[0], u1 = up[1];
+                v[k][0] = pack_bf16x2(gate_act<A>(g0[0]) * u0[0], gate_act<A>(g0[1]) * u0[1]);
+                v[k][1] = pack_bf16x2(gate_act<A>(g0[2]) * u0[2], gate_act<A>(g0[3]) * u0[3]);
+                v[k][2] = pack_bf16x2(gate_act<A>(g1[0]) * u1[0], gate_act<A>(g1[1]) * u1[1]);
+                v[k][3] = pack_bf16x2(gate_act<A>(g1[2]) * u1[2], gate_act<A>(g1[3]) * u1[3]);
+            }
+        }
+        if (bi == nbatch - 1)
+            issue();
+#pragma unroll
+        for (int k = 0; k < SU; ++k) {
+            const int u = base + k * nthr + static_cast<int>(threadIdx.x);
+            if (u < total) {
+                const int m = u / (IT * 256);
+                const int rem = u - m * IT * 256;
+                const int c = rem >> 2;  // chunk l + 64 i
+                act[((m * IT + (c >> 6)) * 4 + (rem & 3)) * 64 + (c & 63)] = c < cpr ? v[k] : u32x4_t{0, 0, 0, 0};
+            }
+        }
+    }
+}
+
+// Per-lane partial sums of one row: acc[t][m] = sum over the lane's chunks of
+// (two 8-term dot2 chains of 16 columns each) times their E4M3 block scales.
+template <int M, int IT, int NMAT>
+__device__ __forceinline__ void row_dot(float (&acc)[NMAT][M], const WaveRow<IT, NMAT> &w, const u32x4_t *act,
+                                        const RowGeom &rg)
+{
+    // The activation reads are the same for every row; an opaque zero keeps
+    // them inside the row loop (hoisted, they would pin M * IT * 16 registers
+    // for the whole kernel).
+    int lz;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(lz));
+    const u32x4_t *ar = act + lz + rg.lane;
+#pragma unroll
+    for (int t = 0; t < NMAT; ++t)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            acc[t][m] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        // this chunk's weights of every matrix as bf16 pairs, and scales
+        bf16x2_t wp[NMAT][16];
+        float s0[NMAT], s1[NMAT];
+#pragma unroll
+        for (int t = 0; t < NMAT; ++t) {
+            const u32x4_t c = w.wc[t][i];
+            // past the row end: zero activations, and a zero scale so that a
+            // NaN scale of the re-read chunk cannot leak in
+            const uint32_t sw = (i < IT - 1 || rg.oklast) ? w.ws[t][i] : 0u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                wp[t][4 * q + 0] = fp4x2_to_bf16x2<0>(c[q]);
+                wp[t][4 * q + 1] = fp4x2_to_bf16x2<1>(c[q]);
+                wp[t][4 * q + 2] = fp4x2_to_bf16x2<2>(c[q]);
+                wp[t][4 * q + 3] = fp4x2_to_bf16x2<3>(c[q]);
+            }
+            s0[t] = e4m3_to_f32<0>(sw);
+            s1[t] = e4m3_to_f32<1>(sw);
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            u32x4_t a[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                a[q] = ar[((m * IT + i) * 4 + q) * 64];
+#pragma unroll
+            for (int t = 0; t < NMAT; ++t) {
+                float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    t0 = dot2_bf16(wp[t][b], as_bf16x2(a[0][b]), t0);
+                    t1 = dot2_bf16(wp[t][8 + b], as_bf16x2(a[2][b]), t1);
+                }
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    t0 = dot2_bf16(wp[t][4 + b], as_bf16x2(a[1][b]), t0);
+                    t1 = dot2_bf16(wp[t][12 + b], as_bf16x2(a[3][b]), t1);
+                }
+                acc[t][m] = __builtin_fmaf(t0, s0[t], acc[t][m]);
+                acc[t][m] = __builtin_fmaf(t1, s1[t], acc[t][m]);
+            }
+            // One activation row at a time: its accumulators pass through an
+            // empty asm that also orders memory, so its arithmetic is done
+            // before the next activation reads (otherwise all of them are
+            // issued first and pinned in registers).
+#pragma unroll
+            for (int t = 0; t < NMAT; ++t)
+                asm volatile("" : "+v"(acc[t][m])::"memory");
+        }
+    }
+}
+
+// Sums the lanes' partials of row r over the wave (fixed DPP tree) and lane
+// 63 writes the row's outputs for the M activation rows (outputs [M, rows]).
+template <int M, int NMAT, int OUT>
+__device__ __forceinline__ void row_store(float (&acc)[NMAT][M], int r, int rows, float s2_0, float s2_1, void *out0,
+                                          void *out1, int lane)
+{
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        float tot[NMAT];
+#pragma unroll
+        for (int t = 0; t < NMAT; ++t)
+            tot[t] = segment_sum<64>(acc[t][m]);
+        if (lane == 63) {
+            const size_t o = static_cast<size_t>(m) * rows + r;
+            if constexpr (OUT == OUT_F32_PAIR) {
+                static_cast<float *>(out0)[o] = s2_0 * tot[0];
+                static_cast<float *>(out1)[o] = s2_1 * tot[NMAT - 1];
+            } else if constexpr (OUT == OUT_BF16) {
+                static_cast<uint16_t *>(out0)[o] = to_bf16_bits(s2_0 * tot[0]);
+            } else {
+                constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
+                const float h = gate_act<A>(s2_0 * tot[0]) * (s2_1 * tot[NMAT - 1]);
+                static_cast<uint16_t *>(out0)[o] = to_bf16_bits(h);
+            }
+        }
+    }
+}
+
 // W waves per workgroup; each wave takes rows g, g + G, ... (G = all waves of
 // the grid), with g = wave * gridDim.x + blockIdx.x: when the rows do not
 // divide evenly, the waves that get one more row are the low waves of every
 // workgroup, one per SIMD, so every compute unit and SIMD gets the same
-// share.
+// share. Each wave issues its next row's loads as soon as a row's arithmetic
+// is done. Dynamic LDS: M * IT * 4 KB.
 //
-// LDS holds the activations as 16-byte units ((m * IT + i) * 4 + q) * 64 + l:
-// quarter q of the chunk lane l reads in step i (chunk l + 64 i; zero past
-// the row end), so every read is conflict-free and its address is the lane's
-// offset plus a constant. Dynamic LDS: M * IT * 4 KB.
+// Measured on MI355X at the decode shapes (each change alone, same run):
+// issuing the first weight row before the activation loads and meeting at an
+// LDS-only barrier takes the dual GEMV from 18.4 to 17.2 us; plain (cached)
+// weight loads take the down GEMV from 11.4 to 10.75 us, while they slow the
+// dual GEMV (19.2 us), which keeps non-temporal loads.
 template <int M, int IT, int NMAT, int IN, int OUT, int W>
 __global__ __launch_bounds__(64 * W) void wave_gemv_kernel(const WaveParams p)
 {
     extern __shared__ u32x4_t act[];
-    const int lane = threadIdx.x & 63;
+    constexpr bool kNt = NMAT == 2;
+    constexpr bool kWeightsFirst = NMAT == 2;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = gridDim.x * W;
     const int g = wave * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x);
-    const int cpr = p.cpr;
-    // Only the last step can run past the row end (64 (IT - 1) < cpr <= 64 IT).
-    const int clast = min(lane + 64 * (IT - 1), cpr - 1);
-    const bool oklast = lane + 64 * (IT - 1) < cpr;
-    const size_t row_codes = static_cast<size_t>(cpr) * 16;
-    const size_t row_scales = static_cast<size_t>(cpr) * 2;
-
-    u32x4_t wc[NMAT][IT];
-    uint32_t ws[NMAT][IT];
-    auto load_row = [&](int r) {
-#pragma unroll
-        for (int t = 0; t < NMAT; ++t) {
-            const u32x4_t *cb = reinterpret_cast<const u32x4_t *>((t == 0 ? p.codes0 : p.codes1) +
-                                                                  static_cast<size_t>(r) * row_codes);
-            const uint16_t *sb = reinterpret_cast<const uint16_t *>((t == 0 ? p.scales0 : p.scales1) +
-                                                                    static_cast<size_t>(r) * row_scales);
-#pragma unroll
-            for (int i = 0; i < IT; ++i) {
-                const int c = (i == IT - 1) ? clast : lane + 64 * i;
-                wc[t][i] = __builtin_nontemporal_load(cb + c);
-                ws[t][i] = __builtin_nontemporal_load(sb + c);
-            }
-        }
-    };
-
-    // Activations into LDS, in batches of SU 16-byte units per thread. The
-    // first row's weight loads go out right after the last batch's global
-    // loads: waiting for the activations then does not wait for the weights
-    // (loads complete in order), and the weight registers are not live while
-    // earlier batches are in flight.
-    {
-        constexpr int total = M * IT * 64 * 4;
-        constexpr int nthr = 64 * W;
-        constexpr int need = (total + nthr - 1) / nthr;
-        constexpr int SU = (IN == IN_BF16) ? (need < 8 ? need : 8) : 2;
-        constexpr int nbatch = (total + SU * nthr - 1) / (SU * nthr);
-#pragma unroll
-        for (int bi = 0; bi < nbatch; ++bi) {
-            const int base = bi * SU * nthr;
-            u32x4_t v[SU];
-#pragma unroll
-            for (int k = 0; k < SU; ++k) {
-                // global piece u: row m, chunk c, quarter q (q fastest)
-                const int u = base + k * nthr + static_cast<int>(threadIdx.x);
-                const int m = min(u / (IT * 256), M - 1);
-                const int rem = u - m * IT * 256;
-                const int c = min(rem >> 2, cpr - 1);
-                const size_t off = static_cast<size_t>(m) * p.cols + static_cast<size_t>(c) * 32 + (rem & 3) * 8;
-                if constexpr (IN == IN_BF16) {
-                    v[k] = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(p.in0) + off);
-                } else {
-                    constexpr int A = (IN == IN_GATEUP_SILU) ? ACT_SILU : ACT_GELU_TANH;
-                    const f32x4_t *gp = reinterpret_cast<const f32x4_t *>(static_cast<const float *>(p.in0) + off);
-                    const f32x4_t *up = reinterpret_cast<const f32x4_t *>(p.in1 + off);
-                    const f32x4_t g0 = gp[0], g1 = gp[1], u0 = up[0], u1 = up[1];
-                    v[k][0] = pack_bf16x2(gate_act<A>(g0[0]) * u0[0], gate_act<A>(g0[1]) * u0[1]);
-                    v[k][1] = pack_bf16x2(gate_act<A>(g0[2]) * u0[2], gate_act<A>(g0[3]) * u0[3]);
-                    v[k][2] = pack_bf16x2(gate_act<A>(g1[0]) * u1[0], gate_act<A>(g1[1]) * u1[1]);
-                    v[k][3] = pack_bf16x2(gate_act<A>(g1[2]) * u1[2], gate_act<A>(g1[3]) * u1[3]);
-                }
-            }
-            if (bi == nbatch - 1 && g < p.rows)
-                load_row(g);
-#pragma unroll
-            for (int k = 0; k < SU; ++k) {
-                const int u = base + k * nthr + static_cast<int>(threadIdx.x);
-                if (u < total) {
-                    const int m = u / (IT * 256);
-                    const int rem = u - m * IT * 256;
-                    const int c = rem >> 2;  // chunk l + 64 i
-                    act[((m * IT + (c >> 6)) * 4 + (rem & 3)) * 64 + (c & 63)] =
-                        c < cpr ? v[k] : u32x4_t{0, 0, 0, 0};
-                }
-            }
-        }
-        __syncthreads();
-    }
-
+    const RowGeom rg = row_geom<IT>(p.cpr);
+    WaveRow<IT, NMAT> w;
+    if (kWeightsFirst && g < p.rows)
+        load_row<kNt>(w, p.codes0, p.scales0, p.codes1, p.scales1, g, rg);
+    stage_act<M, IT, IN, W>(act, p.in0, p.in1, p.cols, p.cpr, [&] {
+        if (!kWeightsFirst && g < p.rows)
+            load_row<kNt>(w, p.codes0, p.scales0, p.codes1, p.scales1, g, rg);
+    });
+    lds_barrier();
     for (int r = g; r < p.rows; r += G) {
-        // The activation reads are the same for every row; an opaque zero
-        // keeps them inside the loop (hoisted, they would pin M * IT * 16
-        // registers for the whole kernel).
-        int lz;
-        asm volatile("s_mov_b32 %0, 0" : "=s"(lz));
-        const u32x4_t *ar = act + lz + lane;
         float acc[NMAT][M];
-#pragma unroll
-        for (int t = 0; t < NMAT; ++t)
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-                acc[t][m] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < IT; ++i) {
-            // this chunk's weights of every matrix as bf16 pairs, and scales
-            bf16x2_t wp[NMAT][16];
-            float s0[NMAT], s1[NMAT];
-#pragma unroll
-            for (int t = 0; t < NMAT; ++t) {
-                const u32x4_t w = wc[t][i];
-                // past the row end: zero activations, and a zero scale so that
-                // a NaN scale of the clamped duplicate chunk cannot leak in
-                const uint32_t sw = (i < IT - 1 || oklast) ? ws[t][i] : 0u;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    wp[t][4 * q + 0] = fp4x2_to_bf16x2<0>(w[q]);
-                    wp[t][4 * q + 1] = fp4x2_to_bf16x2<1>(w[q]);
-                    wp[t][4 * q + 2] = fp4x2_to_bf16x2<2>(w[q]);
-                    wp[t][4 * q + 3] = fp4x2_to_bf16x2<3>(w[q]);
-                }
-                s0[t] = e4m3_to_f32<0>(sw);
-                s1[t] = e4m3_to_f32<1>(sw);
-            }
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                u32x4_t a[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    a[q] = ar[((m * IT + i) * 4 + q) * 64];
-#pragma unroll
-                for (int t = 0; t < NMAT; ++t) {
-                    float t0 = 0.0f, t1 = 0.0f;
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        t0 = dot2_bf16(wp[t][b], as_bf16x2(a[0][b]), t0);
-                        t1 = dot2_bf16(wp[t][8 + b], as_bf16x2(a[2][b]), t1);
-                    }
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        t0 = dot2_bf16(wp[t][4 + b], as_bf16x2(a[1][b]), t0);
-                        t1 = dot2_bf16(wp[t][12 + b], as_bf16x2(a[3][b]), t1);
-                    }
-                    acc[t][m] = __builtin_fmaf(t0, s0[t], acc[t][m]);
-                    acc[t][m] = __builtin_fmaf(t1, s1[t], acc[t][m]);
-                }
-                // One activation row at a time: its accumulators pass through
-                // an empty asm that also orders memory, so its arithmetic is
-                // done before the next activation reads (otherwise all of them
-                // are issued first and pinned in registers).
-#pragma unroll
-                for (int t = 0; t < NMAT; ++t)
-                    asm volatile("" : "+v"(acc[t][m])::"memory");
-            }
-        }
+        row_dot<M, IT, NMAT>(acc, w, act, rg);
         // the next row's loads go out before this row's reduction and store
         if (r + G < p.rows)
-            load_row(r + G);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            float tot[NMAT];
-#pragma unroll
-            for (int t = 0; t < NMAT; ++t)
-                tot[t] = segment_sum<64>(acc[t][m]);
-            if (lane == 63) {
-                const size_t o = static_cast<size_t>(m) * p.rows + r;
-                if constexpr (OUT == OUT_F32_PAIR) {
-                    static_cast<float *>(p.out0)[o] = p.s2_0 * tot[0];
-                    static_cast<float *>(p.out1)[o] = p.s2_1 * tot[NMAT - 1];
-                } else if constexpr (OUT == OUT_BF16) {
-                    static_cast<uint16_t *>(p.out0)[o] = to_bf16_bits(p.s2_0 * tot[0]);
-                } else {
-                    constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
-                    const float h = gate_act<A>(p.s2_0 * tot[0]) * (p.s2_1 * tot[NMAT - 1]);
-                    static_cast<uint16_t *>(p.out0)[o] = to_bf16_bits(h);
-                }
-            }
-        }
+            load_row<kNt>(w, p.codes0, p.scales0, p.codes1, p.scales1, r + G, rg);
+        row_store<M, NMAT, OUT>(acc, r, p.rows, p.s2_0, p.s2_1, p.out0, p.out1, rg.lane);
     }
 }
 
