@@ -95,6 +95,9 @@ SMALL = [
     (7, 4096, 18432, fi.ACT_SILU, 19),      # down: 9 chunks per lane, launches of 4 + 3 rows
     (6, 12288, 1056, fi.ACT_SILU, 20),      # dual: 6 chunks per lane, launches of 4 + 2 rows
     (3, 24576, 1056, fi.ACT_GELU_TANH, 21), # dual: 12 chunks per lane, 8-wave workgroups
+    # activations staged in pieces of steps (M x steps x 4 KB over the LDS budget)
+    (4, 1056, 21504, fi.ACT_GELU_TANH, 27), # down: 11 steps in pieces of 6 + 5
+    (8, 2080, 12352, fi.ACT_SILU, 28),      # down: 386 chunks, 7 steps in pieces of 4 + 3
 ]
 
 

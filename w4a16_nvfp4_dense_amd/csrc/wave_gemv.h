@@ -75,11 +75,13 @@ struct WaveRow {
     uint32_t ws[NMAT][IT];
 };
 
-// Issues all loads of row r; NT marks them non-temporal.
-template <bool NT, int IT, int NMAT>
-__device__ __forceinline__ void load_row(WaveRow<IT, NMAT> &w, const uint8_t *codes0, const uint8_t *scales0,
+// Issues all loads of steps I0 .. I0 + IS - 1 of row r (a row has IT steps;
+// the whole row by default); NT marks them non-temporal.
+template <bool NT, int IT, int NMAT, int I0 = 0, int IS = IT>
+__device__ __forceinline__ void load_row(WaveRow<IS, NMAT> &w, const uint8_t *codes0, const uint8_t *scales0,
                                          const uint8_t *codes1, const uint8_t *scales1, int r, const RowGeom &rg)
 {
+    static_assert(I0 >= 0 && IS >= 1 && I0 + IS <= IT, "piece of the row");
 #pragma unroll
     for (int t = 0; t < NMAT; ++t) {
         const u32x4_t *cb =
@@ -87,33 +89,36 @@ __device__ __forceinline__ void load_row(WaveRow<IT, NMAT> &w, const uint8_t *co
         const uint16_t *sb =
             reinterpret_cast<const uint16_t *>((t == 0 ? scales0 : scales1) + static_cast<size_t>(r) * rg.row_scales);
 #pragma unroll
-        for (int i = 0; i < IT; ++i) {
+        for (int j = 0; j < IS; ++j) {
+            const int i = I0 + j;
             const int c = (i == IT - 1) ? rg.clast : rg.lane + 64 * i;
             if constexpr (NT) {
-                w.wc[t][i] = __builtin_nontemporal_load(cb + c);
-                w.ws[t][i] = __builtin_nontemporal_load(sb + c);
+                w.wc[t][j] = __builtin_nontemporal_load(cb + c);
+                w.ws[t][j] = __builtin_nontemporal_load(sb + c);
             } else {
-                w.wc[t][i] = cb[c];
-                w.ws[t][i] = sb[c];
+                w.wc[t][j] = cb[c];
+                w.ws[t][j] = sb[c];
             }
         }
     }
 }
 
-// Stages M activation rows of `cols` (= 32 cpr) columns into LDS as 16-byte
-// units ((m * IT + i) * 4 + q) * 64 + l: quarter q of the chunk lane l reads
-// in step i (chunk l + 64 i; zero past the row end), so every read is
+// Stages the columns of steps I0 .. I0 + IS - 1 of M activation rows of
+// `cols` (= 32 cpr) columns into LDS as 16-byte units
+// ((m * IS + j) * 4 + q) * 64 + l: quarter q of the chunk lane l reads in step
+// I0 + j (chunk l + 64 (I0 + j); zero past the row end), so every read is
 // conflict-free and its address is the lane's offset plus a constant. Uses
-// M * IT * 4 KB. The W waves of the workgroup load in batches of SU units per
+// M * IS * 4 KB. The W waves of the workgroup load in batches of SU units per
 // thread; `issue()` runs right after the last batch's global loads (the
 // first weight row goes out there: waiting for the activations then does not
 // wait for the weights, as loads complete in order, and the weight registers
 // are not live while earlier batches are in flight). The caller synchronises
 // the workgroup before reading.
-template <int M, int IT, int IN, int W, class F>
+template <int M, int IS, int IN, int W, int I0 = 0, class F>
 __device__ __forceinline__ void stage_act(u32x4_t *act, const void *in0, const float *in1, int cols, int cpr,
                                           F &&issue)
 {
+    constexpr int IT = IS;  // steps staged
     constexpr int total = M * IT * 64 * 4;
     constexpr int nthr = 64 * W;
     constexpr int need = (total + nthr - 1) / nthr;
@@ -129,7 +134,7 @@ __device__ __forceinline__ void stage_act(u32x4_t *act, const void *in0, const f
             const int u = base + k * nthr + static_cast<int>(threadIdx.x);
             const int m = min(u / (IT * 256), M - 1);
             const int rem = u - m * IT * 256;
-            const int c = min(rem >> 2, cpr - 1);
+            const int c = min(64 * I0 + (rem >> 2), cpr - 1);
             const size_t off = static_cast<size_t>(m) * cols + static_cast<size_t>(c) * 32 + (rem & 3) * 8;
             if constexpr (IN == IN_BF16) {
                 v[k] = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(in0) + off);
@@ -152,17 +157,20 @@ __device__ __forceinline__ void stage_act(u32x4_t *act, const void *in0, const f
             if (u < total) {
                 const int m = u / (IT * 256);
                 const int rem = u - m * IT * 256;
-                const int c = rem >> 2;  // chunk l + 64 i
-                act[((m * IT + (c >> 6)) * 4 + (rem & 3)) * 64 + (c & 63)] = c < cpr ? v[k] : u32x4_t{0, 0, 0, 0};
+                const int c = rem >> 2;  // chunk l + 64 (I0 + j), c = 64 j + l
+                act[((m * IT + (c >> 6)) * 4 + (rem & 3)) * 64 + (c & 63)] =
+                    64 * I0 + c < cpr ? v[k] : u32x4_t{0, 0, 0, 0};
             }
         }
     }
 }
 
 // Per-lane partial sums of one row: acc[t][m] = sum over the lane's chunks of
-// (two 8-term dot2 chains of 16 columns each) times their E4M3 block scales.
-template <int M, int IT, int NMAT>
-__device__ __forceinline__ void row_dot(float (&acc)[NMAT][M], const WaveRow<IT, NMAT> &w, const u32x4_t *act,
+// (two 8-term dot2 chains of 16 columns each) times their E4M3 block scales,
+// over steps I0 .. I0 + IS - 1 of the row's IT steps (activations staged for
+// those steps), starting from zero (INIT) or adding to acc.
+template <int M, int IT, int NMAT, int I0 = 0, int IS = IT, bool INIT = true>
+__device__ __forceinline__ void row_dot(float (&acc)[NMAT][M], const WaveRow<IS, NMAT> &w, const u32x4_t *act,
                                         const RowGeom &rg)
 {
     // The activation reads are the same for every row; an opaque zero keeps
@@ -171,22 +179,25 @@ __device__ __forceinline__ void row_dot(float (&acc)[NMAT][M], const WaveRow<IT,
     int lz;
     asm volatile("s_mov_b32 %0, 0" : "=s"(lz));
     const u32x4_t *ar = act + lz + rg.lane;
+    if constexpr (INIT) {
 #pragma unroll
-    for (int t = 0; t < NMAT; ++t)
+        for (int t = 0; t < NMAT; ++t)
 #pragma unroll
-        for (int m = 0; m < M; ++m)
-            acc[t][m] = 0.0f;
+            for (int m = 0; m < M; ++m)
+                acc[t][m] = 0.0f;
+    }
 #pragma unroll
-    for (int i = 0; i < IT; ++i) {
+    for (int j = 0; j < IS; ++j) {
+        const int i = I0 + j;  // step of the row
         // this chunk's weights of every matrix as bf16 pairs, and scales
         bf16x2_t wp[NMAT][16];
         float s0[NMAT], s1[NMAT];
 #pragma unroll
         for (int t = 0; t < NMAT; ++t) {
-            const u32x4_t c = w.wc[t][i];
+            const u32x4_t c = w.wc[t][j];
             // past the row end: zero activations, and a zero scale so that a
             // NaN scale of the re-read chunk cannot leak in
-            const uint32_t sw = (i < IT - 1 || rg.oklast) ? w.ws[t][i] : 0u;
+            const uint32_t sw = (i < IT - 1 || rg.oklast) ? w.ws[t][j] : 0u;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 wp[t][4 * q + 0] = fp4x2_to_bf16x2<0>(c[q]);
@@ -197,12 +208,23 @@ __device__ __forceinline__ void row_dot(float (&acc)[NMAT][M], const WaveRow<IT,
             s0[t] = e4m3_to_f32<0>(sw);
             s1[t] = e4m3_to_f32<1>(sw);
         }
+        // Activation row m + 1 is read from LDS while row m's products run
+        // (two rows of registers at most).
+        u32x4_t an[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            an[q] = ar[(j * 4 + q) * 64];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             u32x4_t a[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                a[q] = ar[((m * IT + i) * 4 + q) * 64];
+                a[q] = an[q];
+            if (m + 1 < M) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    an[q] = ar[(((m + 1) * IS + j) * 4 + q) * 64];
+            }
 #pragma unroll
             for (int t = 0; t < NMAT; ++t) {
                 float t0 = 0.0f, t1 = 0.0f;
@@ -221,8 +243,8 @@ __device__ __forceinline__ void row_dot(float (&acc)[NMAT][M], const WaveRow<IT,
             }
             // One activation row at a time: its accumulators pass through an
             // empty asm that also orders memory, so its arithmetic is done
-            // before the next activation reads (otherwise all of them are
-            // issued first and pinned in registers).
+            // before the activation reads of the row after next (otherwise
+            // all of them are issued first and pinned in registers).
 #pragma unroll
             for (int t = 0; t < NMAT; ++t)
                 asm volatile("" : "+v"(acc[t][m])::"memory");
@@ -258,6 +280,44 @@ __device__ __forceinline__ void row_store(float (&acc)[NMAT][M], int r, int rows
     }
 }
 
+// Rows a wave holds accumulators for when the activations are staged in
+// pieces (the launcher sizes the grid so that no wave has more).
+constexpr int kPieceMaxRows = 2;
+
+// One piece of the staged kernel (steps I0 .. I0 + IS - 1 of every row), then
+// the next: the workgroup stages the piece's activations (the first row's
+// weights for the piece go out behind them), and each wave adds the piece's
+// products of its rows g, g + G to their accumulators. A barrier before each
+// restaging keeps the previous piece in LDS until every wave is done with it.
+template <int M, int IT, int NMAT, int IN, int W, int P, int p>
+__device__ __forceinline__ void wave_pieces(const WaveParams &wp, u32x4_t *act, float (&acc)[kPieceMaxRows][NMAT][M],
+                                            int g, int G, const RowGeom &rg)
+{
+    constexpr int IP = (IT + P - 1) / P;
+    constexpr int I0 = p * IP;
+    constexpr int IS = (IT - I0 < IP) ? IT - I0 : IP;
+    constexpr bool kNt = NMAT == 2;
+    WaveRow<IS, NMAT> w;
+    if constexpr (p > 0)
+        lds_barrier();
+    stage_act<M, IS, IN, W, I0>(act, wp.in0, wp.in1, wp.cols, wp.cpr, [&] {
+        if (g < wp.rows)
+            load_row<kNt, IT, NMAT, I0, IS>(w, wp.codes0, wp.scales0, wp.codes1, wp.scales1, g, rg);
+    });
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < kPieceMaxRows; ++k) {
+        const int r = g + k * G;
+        if (r >= wp.rows)
+            break;
+        row_dot<M, IT, NMAT, I0, IS, p == 0>(acc[k], w, act, rg);
+        if (k + 1 < kPieceMaxRows && r + G < wp.rows)
+            load_row<kNt, IT, NMAT, I0, IS>(w, wp.codes0, wp.scales0, wp.codes1, wp.scales1, r + G, rg);
+    }
+    if constexpr (p + 1 < P)
+        wave_pieces<M, IT, NMAT, IN, W, P, p + 1>(wp, act, acc, g, G, rg);
+}
+
 // W waves per workgroup; each wave takes rows g, g + G, ... (G = all waves of
 // the grid), with g = wave * gridDim.x + blockIdx.x: when the rows do not
 // divide evenly, the waves that get one more row are the low waves of every
@@ -265,12 +325,21 @@ __device__ __forceinline__ void row_store(float (&acc)[NMAT][M], int r, int rows
 // share. Each wave issues its next row's loads as soon as a row's arithmetic
 // is done. Dynamic LDS: M * IT * 4 KB.
 //
+// When that exceeds the LDS budget (long rows and up to 8 activation rows:
+// the down GEMV of a verify batch), the activations are staged in P pieces of
+// steps instead (M * ceil(IT / P) * 4 KB), every weight row is still read once
+// for all M rows, and each wave keeps its rows' accumulators across pieces
+// (at most kPieceMaxRows rows per wave). A lane still visits its chunks in
+// increasing order, so the results are those of the one-piece kernel.
+//
 // Measured on MI355X at the decode shapes (each change alone, same run):
 // issuing the first weight row before the activation loads and meeting at an
 // LDS-only barrier takes the dual GEMV from 18.4 to 17.2 us; plain (cached)
 // weight loads take the down GEMV from 11.4 to 10.75 us, while they slow the
-// dual GEMV (19.2 us), which keeps non-temporal loads.
-template <int M, int IT, int NMAT, int IN, int OUT, int W>
+// dual GEMV (19.2 us), which keeps non-temporal loads; reading the next
+// activation row from LDS while the current one's products run takes the
+// dual GEMV from 19.3 to 18.6 us at M = 1 and from 50.5 to 48.8 us at M = 8.
+template <int M, int IT, int NMAT, int IN, int OUT, int W, int P = 1>
 __global__ __launch_bounds__(64 * W) void wave_gemv_kernel(const WaveParams p)
 {
     extern __shared__ u32x4_t act[];
@@ -280,12 +349,24 @@ __global__ __launch_bounds__(64 * W) void wave_gemv_kernel(const WaveParams p)
     const int G = gridDim.x * W;
     const int g = wave * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x);
     const RowGeom rg = row_geom<IT>(p.cpr);
+    if constexpr (P > 1) {
+        float acc[kPieceMaxRows][NMAT][M];
+        wave_pieces<M, IT, NMAT, IN, W, P, 0>(p, act, acc, g, G, rg);
+#pragma unroll
+        for (int k = 0; k < kPieceMaxRows; ++k) {
+            const int r = g + k * G;
+            if (r >= p.rows)
+                break;
+            row_store<M, NMAT, OUT>(acc[k], r, p.rows, p.s2_0, p.s2_1, p.out0, p.out1, rg.lane);
+        }
+        return;
+    }
     WaveRow<IT, NMAT> w;
     if (kWeightsFirst && g < p.rows)
-        load_row<kNt>(w, p.codes0, p.scales0, p.codes1, p.scales1, g, rg);
+        load_row<kNt, IT, NMAT>(w, p.codes0, p.scales0, p.codes1, p.scales1, g, rg);
     stage_act<M, IT, IN, W>(act, p.in0, p.in1, p.cols, p.cpr, [&] {
         if (!kWeightsFirst && g < p.rows)
-            load_row<kNt>(w, p.codes0, p.scales0, p.codes1, p.scales1, g, rg);
+            load_row<kNt, IT, NMAT>(w, p.codes0, p.scales0, p.codes1, p.scales1, g, rg);
     });
     lds_barrier();
     for (int r = g; r < p.rows; r += G) {
@@ -293,7 +374,7 @@ __global__ __launch_bounds__(64 * W) void wave_gemv_kernel(const WaveParams p)
         row_dot<M, IT, NMAT>(acc, w, act, rg);
         // the next row's loads go out before this row's reduction and store
         if (r + G < p.rows)
-            load_row<kNt>(w, p.codes0, p.scales0, p.codes1, p.scales1, r + G, rg);
+            load_row<kNt, IT, NMAT>(w, p.codes0, p.scales0, p.codes1, p.scales1, r + G, rg);
         row_store<M, NMAT, OUT>(acc, r, p.rows, p.s2_0, p.s2_1, p.out0, p.out1, rg.lane);
     }
 }

@@ -13,21 +13,36 @@ namespace {
 constexpr int kWaveMaxIt = 12;        // chunks per lane: reduction length up to 24576
 constexpr int kWaveLdsMax = 144 * 1024;  // of the 160 KB per compute unit
 
-// Activation rows one launch stages in LDS (M x IT x 4 KB).
+// Pieces the activations are staged in: the fewest whose steps
+// (M x ceil(IT / P) x 4 KB) fit the LDS budget.
 template <int M, int IT>
-constexpr bool wave_fits()
+constexpr int wave_pieces()
 {
-    return M * IT * 4096 <= kWaveLdsMax;
+    int pc = 1;
+    while (M * ((IT + pc - 1) / pc) * 4096 > kWaveLdsMax)
+        ++pc;
+    return pc;
+}
+
+// Steps staged at a time.
+template <int M, int IT>
+constexpr int wave_piece_steps()
+{
+    return (IT + wave_pieces<M, IT>() - 1) / wave_pieces<M, IT>();
 }
 
 // Waves per workgroup: 16 (at most 128 registers per lane) while the
 // weight registers of one row (5 per chunk and matrix), the converted chunk
 // (16 per matrix) and the accumulators fit in that with room to spare,
 // otherwise 8 (up to 256 registers).
+// (With the activations in pieces the weight registers hold one piece of a
+// row, and the accumulators of two rows.)
 template <int M, int IT, int NMAT>
 constexpr int wave_w_regs()
 {
-    return (NMAT * IT * 5 + NMAT * 16 + M * NMAT + 30 <= 120) ? 16 : 8;
+    constexpr int IS = wave_piece_steps<M, IT>();
+    constexpr int acc = (wave_pieces<M, IT>() > 1 ? kPieceMaxRows : 1) * M * NMAT;
+    return (NMAT * IS * 5 + NMAT * 16 + acc + 30 <= 120) ? 16 : 8;
 }
 
 // Measured on MI355X at the decode shapes: the dual GEMV runs best as 2 x 8
@@ -36,37 +51,39 @@ constexpr int wave_w_regs()
 template <int M, int IT, int NMAT>
 constexpr int wave_w()
 {
-    return (NMAT == 2 && 2 * M * IT * 4096 <= kWaveLdsMax) ? 8 : wave_w_regs<M, IT, NMAT>();
+    return (NMAT == 2 && wave_pieces<M, IT>() == 1 && 2 * M * IT * 4096 <= kWaveLdsMax) ? 8
+                                                                                       : wave_w_regs<M, IT, NMAT>();
 }
 
 template <int M, int IT, int NMAT>
 constexpr int wave_blocks_per_cu()
 {
-    return (wave_w<M, IT, NMAT>() == 8 && 2 * M * IT * 4096 <= kWaveLdsMax) ? 2 : 1;
+    return (wave_w<M, IT, NMAT>() == 8 && 2 * M * wave_piece_steps<M, IT>() * 4096 <= kWaveLdsMax) ? 2 : 1;
 }
 
 template <int M, int IT, int NMAT, int IN, int OUT>
 hipError_t launch_one(const WaveParams &p, hipStream_t stream)
 {
-    if constexpr (!wave_fits<M, IT>()) {
-        return hipErrorNotSupported;
-    } else {
-        constexpr int W = wave_w<M, IT, NMAT>();
-        auto kern = wave_gemv_kernel<M, IT, NMAT, IN, OUT, W>;
-        const int lds = M * IT * 4096;
-        if (lds > 64 * 1024) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-            if (e != hipSuccess)
-                return e;
-        }
-        const int want = device_cu_count() * wave_blocks_per_cu<M, IT, NMAT>();
-        const int blocks = std::max(1, std::min(want, (p.rows + W - 1) / W));
-        WaveParams q = p;
-        void *args[] = {&q};
-        return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(blocks), dim3(W * 64), args, lds,
-                               stream);
+    constexpr int W = wave_w<M, IT, NMAT>();
+    constexpr int P = wave_pieces<M, IT>();
+    auto kern = wave_gemv_kernel<M, IT, NMAT, IN, OUT, W, P>;
+    const int lds = M * wave_piece_steps<M, IT>() * 4096;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess)
+            return e;
     }
+    const int want = device_cu_count() * wave_blocks_per_cu<M, IT, NMAT>();
+    int blocks = std::max(1, std::min(want, (p.rows + W - 1) / W));
+    if constexpr (P > 1) {
+        // every wave holds at most kPieceMaxRows rows
+        const int rows_per_block = W * kPieceMaxRows;
+        blocks = std::max(blocks, (p.rows + rows_per_block - 1) / rows_per_block);
+    }
+    WaveParams q = p;
+    void *args[] = {&q};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(blocks), dim3(W * 64), args, lds, stream);
 }
 
 template <int IT, int NMAT, int IN, int OUT>
@@ -82,23 +99,24 @@ hipError_t launch_m(int M, const WaveParams &p, hipStream_t stream)
     }
 }
 
-// Activation rows per launch for reduction steps `it`: the largest of
-// 8, 4, 3, 2, 1 that is at most `left` and whose staging fits in LDS.
-int group_rows(int left, int it)
+// Activation rows per launch: the largest of 8, 4, 3, 2, 1 that is at most
+// `left` (staging that does not fit LDS at once goes in pieces).
+int group_rows(int left)
 {
     for (int g : {8, 4, 3, 2, 1})
-        if (g <= left && g * it * 4096 <= kWaveLdsMax)
+        if (g <= left)
             return g;
     return 0;
 }
 
 // Splits the batch into launches of group_rows() activation rows each (rows
-// of a batch are independent, so the grouping does not change any result).
+// of a batch are independent, so the grouping does not change any result;
+// batches of 1 to 4 and of 8 rows are one launch).
 template <int NMAT, int IN, int OUT>
 hipError_t launch_groups(int M, int it, WaveParams p, size_t in_elem, size_t out_elem, hipStream_t stream)
 {
     for (int m0 = 0; m0 < M;) {
-        const int g = group_rows(M - m0, it);
+        const int g = group_rows(M - m0);
         if (g == 0)
             return hipErrorNotSupported;
         WaveParams q = p;
@@ -170,7 +188,7 @@ hipError_t launch_wave_dual(int M, OutKind out, const void *x, const WeightArg &
                             void *out1, int rows, int cols, hipStream_t stream)
 {
     const int it = wave_iters(cols);
-    if (M < 1 || M > 8 || it < 1 || it > kWaveMaxIt || group_rows(1, it) == 0)
+    if (M < 1 || M > 8 || it < 1 || it > kWaveMaxIt)
         return hipErrorNotSupported;
     const WaveParams p = wave_params(x, nullptr, w0, w1, out0, out1, rows, cols);
     switch (out) {
@@ -185,7 +203,7 @@ hipError_t launch_wave_down(int M, InKind in, const void *in0, const float *in1,
                             int rows, int cols, hipStream_t stream)
 {
     const int it = wave_iters(cols);
-    if (M < 1 || M > 8 || it < 1 || it > kWaveMaxIt || group_rows(1, it) == 0)
+    if (M < 1 || M > 8 || it < 1 || it > kWaveMaxIt)
         return hipErrorNotSupported;
     const WaveParams p = wave_params(in0, in1, w, w, out, nullptr, rows, cols);
     switch (in) {
