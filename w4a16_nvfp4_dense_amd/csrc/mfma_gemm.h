@@ -425,16 +425,26 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaPa
 }
 
 // Finishes the tiles a stream-K launch left as pieces: every element sums its
-// pieces in k order (the slot order) and goes through the same epilogue.
-// Grid: (tiles, ceil(4 * MT * 16 * 64 / 256)), 256 threads.
+// pieces in k order (the slot order) and goes through the same epilogue. A
+// thread takes 4 consecutive positions of one fragment pair (16-byte loads)
+// and issues the loads of up to 16 pieces before adding any of them, so a tile
+// split many ways is not read one dependent load at a time.
+// Grid: (tiles, mfma_reduce_blocks<MT>()), 256 threads.
+template <int MT>
+constexpr int mfma_reduce_blocks()
+{
+    return (kMfmaWaves * MT * 16 * 64 / 4 + 255) / 256;
+}
+
 template <int MT, int NMAT, int OUT>
 __global__ __launch_bounds__(256) void mfma_reduce_kernel(const MfmaParams p, int G)
 {
     constexpr int ROWS_TILE = mfma_rows_per_tile<NMAT>();
     constexpr int SLOT = mfma_slot_floats<MT>();
     constexpr int PER_WAVE = MT * 16 * 64;  // positions of one fragment of one wave
+    constexpr int B = 16;                   // pieces loaded at once
     const int t = blockIdx.x;
-    const int e = blockIdx.y * 256 + threadIdx.x;
+    const int e = (blockIdx.y * 256 + threadIdx.x) * 4;
     if (e >= kMfmaWaves * PER_WAVE)
         return;
     const long long U = p.units;
@@ -444,19 +454,38 @@ __global__ __launch_bounds__(256) void mfma_reduce_kernel(const MfmaParams p, in
     if (g_lo == g_hi)
         return;  // one workgroup held the whole tile and stored it
     const int wave = e / PER_WAVE;
-    const int rem = e - wave * PER_WAVE;
+    const int rem = e - wave * PER_WAVE;  // 4 positions rem .. rem + 3: one q, 4 lanes
     const int q = rem >> 6;
-    const int lane = rem & 63;
-    float y0 = 0.0f, y1 = 0.0f;
-    for (int gg = g_lo; gg <= g_hi; ++gg) {
-        const int slot = 2 * gg + (t == sk_begin(gg, U, G) / KU ? 0 : 1);
-        const float *src = p.partials + static_cast<size_t>(slot) * SLOT + wave * (SLOT / kMfmaWaves) + rem;
-        const float x0 = src[0];
-        const float x1 = src[PER_WAVE];
-        y0 = gg == g_lo ? x0 : y0 + x0;
-        y1 = gg == g_lo ? x1 : y1 + x1;
+    const int lane0 = rem & 63;
+    f32x4_t y0 = {0.0f, 0.0f, 0.0f, 0.0f}, y1 = y0;
+    for (int g0 = g_lo; g0 <= g_hi; g0 += B) {
+        f32x4_t x0[B], x1[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const int gg = g0 + i;  // uniform over the workgroup (one tile)
+            if (gg > g_hi)
+                break;
+            const int slot = 2 * gg + (t == sk_begin(gg, U, G) / KU ? 0 : 1);
+            const float *src = p.partials + static_cast<size_t>(slot) * SLOT + wave * (SLOT / kMfmaWaves) + rem;
+            x0[i] = *reinterpret_cast<const f32x4_t *>(src);
+            x1[i] = *reinterpret_cast<const f32x4_t *>(src + PER_WAVE);
+        }
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            if (g0 + i > g_hi)
+                break;
+            if (g0 + i == g_lo) {
+                y0 = x0[i];
+                y1 = x1[i];
+            } else {
+                y0 = y0 + x0[i];
+                y1 = y1 + x1[i];
+            }
+        }
     }
-    emit_pair<NMAT, OUT, ROWS_TILE>(p, p.rows, p.M, t, wave, lane, q >> 4, q & 15, y0, y1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        emit_pair<NMAT, OUT, ROWS_TILE>(p, p.rows, p.M, t, wave, lane0 + c, q >> 4, q & 15, y0[c], y1[c]);
 }
 
 }  // namespace ffn

@@ -41,8 +41,7 @@ hipError_t launch_gemm_reduce(const MfmaParams &p, int G, hipStream_t stream)
     hipError_t e = launch_t<MT, NMAT, IN, OUT>(p, G, stream);
     if (e != hipSuccess || p.partials == nullptr)
         return e;
-    constexpr int per_tile = kMfmaWaves * MT * 16 * 64;
-    hipLaunchKernelGGL((mfma_reduce_kernel<MT, NMAT, OUT>), dim3(p.tiles, (per_tile + 255) / 256), dim3(256), 0,
+    hipLaunchKernelGGL((mfma_reduce_kernel<MT, NMAT, OUT>), dim3(p.tiles, mfma_reduce_blocks<MT>()), dim3(256), 0,
                        stream, p, G);
     return hipGetLastError();
 }
