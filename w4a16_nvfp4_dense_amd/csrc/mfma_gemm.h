@@ -94,6 +94,10 @@ constexpr int mfma_rows_per_tile()
 }
 
 // Floats of one partial slot: 4 waves x 2 x MT accumulator tiles x 16 x 64.
+// Within a wave's part, accumulator values q = 4 q4 .. 4 q4 + 3 of tile
+// (f, mt) of lane l are 16 contiguous bytes at float
+// (((f MT + mt) 4 + q4) 64 + l) 4, so a piece is written and read with
+// 16-byte accesses.
 template <int MT>
 constexpr int mfma_slot_floats()
 {
@@ -413,22 +417,25 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaPa
         }
         // A piece of a tile shared with other workgroups: to its slot, for
         // mfma_reduce_kernel.
-        float *mine = slot_ptr(g, t) + (opaque_lane(lane) - lane);
+        f32x4_t *mine = reinterpret_cast<f32x4_t *>(slot_ptr(g, t)) + opaque_lane(lane);
 #pragma unroll
         for (int f = 0; f < 2; ++f)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    mine[((f * MT + mt) * 16 + q) * 64 + lane] = acc[f][mt][q];
+                for (int q4 = 0; q4 < 4; ++q4)
+                    mine[((f * MT + mt) * 4 + q4) * 64] =
+                        f32x4_t{acc[f][mt][4 * q4], acc[f][mt][4 * q4 + 1], acc[f][mt][4 * q4 + 2],
+                                acc[f][mt][4 * q4 + 3]};
     }
 }
 
 // Finishes the tiles a stream-K launch left as pieces: every element sums its
 // pieces in k order (the slot order) and goes through the same epilogue. A
-// thread takes 4 consecutive positions of one fragment pair (16-byte loads)
-// and issues the loads of up to 16 pieces before adding any of them, so a tile
-// split many ways is not read one dependent load at a time.
+// thread takes accumulator values 4 q4 .. 4 q4 + 3 of one lane and tile of a
+// fragment pair (16-byte loads) and issues the loads of up to 16 pieces
+// before adding any of them, so a tile split many ways is not read one
+// dependent load at a time.
 // Grid: (tiles, mfma_reduce_blocks<MT>()), 256 threads.
 template <int MT>
 constexpr int mfma_reduce_blocks()
@@ -454,9 +461,10 @@ __global__ __launch_bounds__(256) void mfma_reduce_kernel(const MfmaParams p, in
     if (g_lo == g_hi)
         return;  // one workgroup held the whole tile and stored it
     const int wave = e / PER_WAVE;
-    const int rem = e - wave * PER_WAVE;  // 4 positions rem .. rem + 3: one q, 4 lanes
-    const int q = rem >> 6;
-    const int lane0 = rem & 63;
+    const int rem = e - wave * PER_WAVE;  // float offset of fragment 0's 4 values
+    const int lane = (rem >> 2) & 63;
+    const int mt = rem >> 10;             // (rem / 4) / 64 = mt * 4 + q4
+    const int q4 = (rem >> 8) & 3;
     f32x4_t y0 = {0.0f, 0.0f, 0.0f, 0.0f}, y1 = y0;
     for (int g0 = g_lo; g0 <= g_hi; g0 += B) {
         f32x4_t x0[B], x1[B];
@@ -485,7 +493,7 @@ __global__ __launch_bounds__(256) void mfma_reduce_kernel(const MfmaParams p, in
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-        emit_pair<NMAT, OUT, ROWS_TILE>(p, p.rows, p.M, t, wave, lane0 + c, q >> 4, q & 15, y0[c], y1[c]);
+        emit_pair<NMAT, OUT, ROWS_TILE>(p, p.rows, p.M, t, wave, lane, mt, 4 * q4 + c, y0[c], y1[c]);
 }
 
 }  // namespace ffn
