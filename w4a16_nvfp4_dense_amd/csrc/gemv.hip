@@ -109,9 +109,10 @@ __device__ __forceinline__ void chunk_dot(const u32x4_t w, uint32_t sc, const u3
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             a[q] = lds[(m * 4 + q) * pitch + cl];
-        float t0 = 0.0f, t1 = 0.0f;
+        float t0 = dot2_bf16_first(wp[0], as_bf16x2(a[0][0]));
+        float t1 = dot2_bf16_first(wp[8], as_bf16x2(a[2][0]));
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 1; b < 4; ++b) {
             t0 = dot2_bf16(wp[b], as_bf16x2(a[0][b]), t0);
             t1 = dot2_bf16(wp[8 + b], as_bf16x2(a[2][b]), t1);
         }

@@ -41,6 +41,17 @@ __device__ __forceinline__ float dot2_bf16(bf16x2_t a, bf16x2_t b, float c)
     return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
 }
 
+// The first link of a chain, 0 + a.x*b.x + a.y*b.y (the same operation as
+// dot2_bf16(a, b, 0.0f)). Written as the three-operand form with an inline
+// zero: the builtin selects the accumulating two-operand form, which needs a
+// register cleared to zero first (one extra move per chain).
+__device__ __forceinline__ float dot2_bf16_first(bf16x2_t a, bf16x2_t b)
+{
+    float d;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u)
 {
     return __builtin_bit_cast(bf16x2_t, u);

@@ -227,9 +227,10 @@ __device__ __forceinline__ void row_dot(float (&acc)[NMAT][M], const WaveRow<IS,
             }
 #pragma unroll
             for (int t = 0; t < NMAT; ++t) {
-                float t0 = 0.0f, t1 = 0.0f;
+                float t0 = dot2_bf16_first(wp[t][0], as_bf16x2(a[0][0]));
+                float t1 = dot2_bf16_first(wp[t][8], as_bf16x2(a[2][0]));
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
+                for (int b = 1; b < 4; ++b) {
                     t0 = dot2_bf16(wp[t][b], as_bf16x2(a[0][b]), t0);
                     t1 = dot2_bf16(wp[t][8 + b], as_bf16x2(a[2][b]), t1);
                 }
