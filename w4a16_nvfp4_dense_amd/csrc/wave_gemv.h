@@ -253,30 +253,106 @@ __device__ __forceinline__ void row_dot(float (&acc)[NMAT][M], const WaveRow<IS,
     }
 }
 
-// Sums the lanes' partials of row r over the wave (fixed DPP tree) and lane
-// 63 writes the row's outputs for the M activation rows (outputs [M, rows]).
+// The wave sums of P values per lane (P = 2, 4 or 8), transposed: at each of
+// the first log2 P levels of segment_sum<64>'s tree a lane keeps half of its
+// values and adds the partner's copies of them, so P values cost about 3 P
+// instructions instead of 8 P. Every sum combines the same lanes in the same
+// tree as segment_sum<64> (pairs, quads, mirrored halves of rows, rows, 32
+// lanes, 64 lanes; only the operand order of an addition can differ, and
+// addition commutes), so the totals are bit-identical to it. Which half a
+// lane keeps is chosen from parities of its lane bits that the mirror
+// partners of the later levels share. The total returned in a lane is that
+// of value wave_sum_index<P>(lane), in every row of the wave.
+template <int P>
+__device__ __forceinline__ int wave_sum_index(int lane)
+{
+    const int p = lane & 15;
+    const int c1 = (p ^ (p >> 2)) & 1;         // kept half at the pairs level
+    const int c2 = ((p >> 1) ^ (p >> 2)) & 1;  // ... at the quads level
+    const int c3 = ((p >> 2) ^ (p >> 3)) & 1;  // ... at the half-row level
+    if constexpr (P == 2)
+        return c1;
+    else if constexpr (P == 4)
+        return 2 * c1 + c2;
+    else
+        return 4 * c1 + 2 * c2 + c3;
+}
+
+// One level: partner lanes (DPP control CTRL) hold the same N values; the
+// lane keeps the upper half when c is set and adds the partner's copy.
+template <int N, int CTRL>
+__device__ __forceinline__ void wave_sum_split(float *v, bool c)
+{
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+        const float keep = c ? v[j + N / 2] : v[j];
+        const float send = c ? v[j] : v[j + N / 2];
+        v[j] = keep + dpp_move<CTRL>(send);
+    }
+}
+
+template <int P>
+__device__ __forceinline__ float wave_sums(float (&v)[P], int lane)
+{
+    static_assert(P == 2 || P == 4 || P == 8, "values per lane");
+    const int p = lane & 15;
+    wave_sum_split<P, 0xB1>(v, ((p ^ (p >> 2)) & 1) != 0);  // quad_perm [1,0,3,2]: pairs
+    if constexpr (P >= 4)
+        wave_sum_split<P / 2, 0x4E>(v, (((p >> 1) ^ (p >> 2)) & 1) != 0);  // quad_perm [2,3,0,1]: quads
+    else
+        v[0] += dpp_move<0x4E>(v[0]);
+    if constexpr (P >= 8)
+        wave_sum_split<2, 0x141>(v, (((p >> 2) ^ (p >> 3)) & 1) != 0);  // row_half_mirror: 8 lanes
+    else
+        v[0] += dpp_move<0x141>(v[0]);
+    float t = v[0];
+    t += dpp_move<0x140>(t);  // row_mirror: 16 lanes
+    t += __shfl_xor(t, 16);   // rows 0 + 1, rows 2 + 3
+    t += __shfl_xor(t, 32);   // all four rows
+    return t;
+}
+
+// Sums the lanes' partials of row r over the wave (the fixed tree of
+// segment_sum<64>) and writes the row's outputs for the M activation rows
+// (outputs [M, rows]): from lane 63 for one row, else from lanes 0 .. M - 1
+// (lane l holds activation row wave_sum_index(l)).
 template <int M, int NMAT, int OUT>
 __device__ __forceinline__ void row_store(float (&acc)[NMAT][M], int r, int rows, float s2_0, float s2_1, void *out0,
                                           void *out1, int lane)
 {
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        float tot[NMAT];
+    constexpr int P = M == 1 ? 1 : M == 2 ? 2 : M <= 4 ? 4 : 8;
+    static_assert(M <= 8, "activation rows");
+    float tot[NMAT];
+    int m = 0;
+    bool mine;
+    if constexpr (P == 1) {
 #pragma unroll
         for (int t = 0; t < NMAT; ++t)
-            tot[t] = segment_sum<64>(acc[t][m]);
-        if (lane == 63) {
-            const size_t o = static_cast<size_t>(m) * rows + r;
-            if constexpr (OUT == OUT_F32_PAIR) {
-                static_cast<float *>(out0)[o] = s2_0 * tot[0];
-                static_cast<float *>(out1)[o] = s2_1 * tot[NMAT - 1];
-            } else if constexpr (OUT == OUT_BF16) {
-                static_cast<uint16_t *>(out0)[o] = to_bf16_bits(s2_0 * tot[0]);
-            } else {
-                constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
-                const float h = gate_act<A>(s2_0 * tot[0]) * (s2_1 * tot[NMAT - 1]);
-                static_cast<uint16_t *>(out0)[o] = to_bf16_bits(h);
-            }
+            tot[t] = segment_sum<64>(acc[t][0]);
+        mine = lane == 63;
+    } else {
+#pragma unroll
+        for (int t = 0; t < NMAT; ++t) {
+            float v[P];
+#pragma unroll
+            for (int i = 0; i < P; ++i)
+                v[i] = i < M ? acc[t][i < M ? i : 0] : 0.0f;
+            tot[t] = wave_sums<P>(v, lane);
+        }
+        m = wave_sum_index<P>(lane);
+        mine = lane < P && m < M;
+    }
+    if (mine) {
+        const size_t o = static_cast<size_t>(m) * rows + r;
+        if constexpr (OUT == OUT_F32_PAIR) {
+            static_cast<float *>(out0)[o] = s2_0 * tot[0];
+            static_cast<float *>(out1)[o] = s2_1 * tot[NMAT - 1];
+        } else if constexpr (OUT == OUT_BF16) {
+            static_cast<uint16_t *>(out0)[o] = to_bf16_bits(s2_0 * tot[0]);
+        } else {
+            constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
+            const float h = gate_act<A>(s2_0 * tot[0]) * (s2_1 * tot[NMAT - 1]);
+            static_cast<uint16_t *>(out0)[o] = to_bf16_bits(h);
         }
     }
 }
