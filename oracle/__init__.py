@@ -27,7 +27,7 @@ def build(force: bool = True, src: str = _SRC, out: str = LIB_PATH) -> str:
     """Compile the oracle with gcc (-O2, no fast-math, OpenMP over outputs)."""
     if force or not os.path.exists(out):
         tmp = out + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-ffp-contract=off",
                src, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, out)
@@ -76,6 +76,12 @@ class Oracle:
         lib.oracle_ffn.argtypes = [_P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _F, _P, _P, _F, _P]
         lib.oracle_num_threads.restype = _I
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_e2m1_encode.restype = _I
+        lib.oracle_e2m1_encode.argtypes = [_F]
+        lib.oracle_e4m3_encode.restype = _I
+        lib.oracle_e4m3_encode.argtypes = [_F]
+        lib.oracle_quantize.restype = None
+        lib.oracle_quantize.argtypes = [_P, _I, _I, _P, _P, _P]
         self.lib = lib
         self.path = lib_path
 
@@ -170,6 +176,24 @@ class Oracle:
     def num_threads(self) -> int:
         return self.lib.oracle_num_threads()
 
+    def e2m1_encode(self, q: float) -> int:
+        return self.lib.oracle_e2m1_encode(float(q))
+
+    def e4m3_encode(self, s: float) -> int:
+        return self.lib.oracle_e4m3_encode(float(s))
+
+    def quantize(self, w_bits: np.ndarray):
+        """BF16 weight bits [rows, cols] -> (codes [rows, cols/2], scales
+        [rows, cols/16], scale2 as an fp32 value)."""
+        w = _c(w_bits, np.uint16)
+        rows, cols = w.shape
+        assert cols % 16 == 0
+        codes = np.empty((rows, cols // 2), dtype=np.uint8)
+        scales = np.empty((rows, cols // 16), dtype=np.uint8)
+        s2 = np.zeros(1, dtype=np.float32)
+        self.lib.oracle_quantize(_ptr(w), rows, cols, _ptr(codes), _ptr(scales), _ptr(s2))
+        return codes, scales, float(s2[0])
+
 
 _default: Optional[Oracle] = None
 
@@ -215,6 +239,18 @@ def ffn(case, rows=None) -> np.ndarray:
 
 def num_threads() -> int:
     return default().num_threads()
+
+
+def e2m1_encode(q: float) -> int:
+    return default().e2m1_encode(q)
+
+
+def e4m3_encode(s: float) -> int:
+    return default().e4m3_encode(s)
+
+
+def quantize(w_bits: np.ndarray):
+    return default().quantize(w_bits)
 
 
 def ulp_bf16(v: np.ndarray) -> np.ndarray:

@@ -25,6 +25,9 @@
  *    are bounded by 448, i.e. the OCP "E4M3FN" variant (no infinities).
  *  - The E2M1 and E4M3 bit layouts follow the OCP Microscaling Formats (MX)
  *    v1.0 specification.
+ *  - qwen35_dense.rs page, weight loader: a dense BF16 weight is turned into
+ *    NVFP4 on the GPU by a global-absmax pass followed by a quantise pass
+ *    (the quantiser below; its scale rule is a reading, the pages give none).
  *
  * Readings taken where the pages are silent (each is listed in the design
  * notes): the even column of a byte is its low nibble; GELU is the tanh form;
@@ -223,4 +226,110 @@ int oracle_num_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* ------------------------------------------------------------ quantiser
+ * BF16 -> NVFP4 (qwen35_dense.rs page, weight loader: a global absmax pass,
+ * then a pass writing packed E2M1 codes [rows, cols/2], per-16 E4M3 scales
+ * [rows, cols/16] and the per-tensor weight_scale_2). The pages give no scale
+ * rule; the reading taken is the plainest one that fills both formats:
+ *   scale2 = amax / (6 * 448)       (largest E2M1 value x largest E4M3 value),
+ *   block scale byte = E4M3(bmax / (6 * scale2)), nearest, ties to even, at most 448,
+ *   code = E2M1(w * (1 / (block scale * scale2))), nearest, ties to even, at most 6,
+ * with everything zero when amax = 0 and code 0 where block scale * scale2 is
+ * zero. These steps decide integers, so they are taken in fp32 with the same
+ * operations as the GPU: one correctly rounded division or multiplication
+ * each, no fused multiply-add. Inputs must be finite.
+ *
+ * The two encoders are brute-force nearest-value searches over the decoders
+ * above (no bit tricks), so they are correct by inspection. */
+
+/* The E2M1 code nearest to q (ties to the code with mantissa bit 0),
+ * saturating at 6; a zero result is code 0 whatever the sign of q. */
+int oracle_e2m1_encode(float q)
+{
+    const double a = fabs((double)q);
+    int best = 0;
+    double bd = INFINITY;
+    if (a >= 6.0)  /* saturation (for huge a every distance would round alike) */
+        return q < 0.0f ? 15 : 7;
+    for (int k = 0; k < 8; ++k) {
+        const double d = fabs(a - oracle_e2m1_value(k));
+        if (d < bd || (d == bd && (k & 1) == 0 && (best & 1) == 1)) {
+            best = k;
+            bd = d;
+        }
+    }
+    return (q < 0.0f && best != 0) ? (best | 8) : best;
+}
+
+/* The E4M3FN byte nearest to s >= 0 (ties to the byte with mantissa bit 0),
+ * saturating at 448 (byte 0x7E). */
+int oracle_e4m3_encode(float s)
+{
+    const double a = (double)s;
+    int best = 0;
+    double bd = INFINITY;
+    if (a >= 448.0)  /* saturation */
+        return 0x7E;
+    for (int b = 0; b < 127; ++b) {  /* 0x00 .. 0x7E: the non-negative finite values */
+        const double d = fabs(a - oracle_e4m3_value(b));
+        if (d < bd || (d == bd && (b & 1) == 0 && (best & 1) == 1)) {
+            best = b;
+            bd = d;
+        }
+    }
+    return best;
+}
+
+static float bf16_to_float(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+void oracle_quantize(const uint16_t *w_bits, int rows, int cols, uint8_t *codes, uint8_t *scales,
+                     float *scale2_out)
+{
+    const size_t n = (size_t)rows * (size_t)cols;
+    float amax = 0.0f;
+    for (size_t i = 0; i < n; ++i) {
+        const float v = fabsf(bf16_to_float(w_bits[i]));
+        if (v > amax)
+            amax = v;
+    }
+    memset(codes, 0, n / 2);
+    memset(scales, 0, n / 16);
+    if (amax == 0.0f) {
+        *scale2_out = 0.0f;
+        return;
+    }
+    const float scale2 = amax / 2688.0f;  /* 6 * 448 */
+    const float d = scale2 * 6.0f;
+    const int nb = cols / 16;
+    for (int r = 0; r < rows; ++r) {
+        for (int b = 0; b < nb; ++b) {
+            const uint16_t *blk = w_bits + (size_t)r * cols + (size_t)b * 16;
+            float bmax = 0.0f;
+            for (int j = 0; j < 16; ++j) {
+                const float v = fabsf(bf16_to_float(blk[j]));
+                if (v > bmax)
+                    bmax = v;
+            }
+            const float sv = bmax / d;
+            const int sb = oracle_e4m3_encode(sv);
+            const float denom = (float)oracle_e4m3_value(sb) * scale2;
+            const float inv = denom == 0.0f ? 0.0f : 1.0f / denom;
+            scales[(size_t)r * nb + b] = (uint8_t)sb;
+            for (int j = 0; j < 16; ++j) {
+                const int c = b * 16 + j;
+                const int code = denom == 0.0f ? 0 : oracle_e2m1_encode(bf16_to_float(blk[j]) * inv);
+                uint8_t *byte = codes + (size_t)r * (cols / 2) + c / 2;
+                *byte |= (uint8_t)((c % 2 == 0) ? code : (code << 4));
+            }
+        }
+    }
+    *scale2_out = scale2;
 }

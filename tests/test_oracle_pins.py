@@ -301,11 +301,122 @@ def pin_ffn_composition(orc):
         np.testing.assert_array_equal(orc.ffn(case, rows=np.array([1])), out[1:2])
 
 
+# ------------------------------------------------------------ quantiser
+
+
+def _bits_of(values):
+    """bf16 bit patterns of float values that are exact in bf16."""
+    f = np.asarray(values, dtype=np.float32)
+    b = f.view(np.uint32)
+    assert np.all((b & 0xFFFF) == 0), "value not exact in bf16"
+    return (b >> 16).astype(np.uint16)
+
+
+def pin_e2m1_encode_grid(orc):
+    """Every E2M1 value (from the OCP table fixture) encodes to its own code;
+    each midpoint goes to its even neighbour; beyond 6 saturates; a zero
+    result is code 0 whatever the sign."""
+    table = _read_table("e2m1_values.txt")
+    for code, val in table:
+        if int(code) == 8:
+            continue  # -0 encodes as +0
+        assert orc.e2m1_encode(val) == int(code), (code, val)
+    assert orc.e2m1_encode(-0.0) == 0 and orc.e2m1_encode(-0.2) == 0
+    mids = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6}
+    for m, k in mids.items():
+        assert orc.e2m1_encode(m) == k, (m, orc.e2m1_encode(m))
+        assert orc.e2m1_encode(-m) == (k | 8 if k else 0), (-m, orc.e2m1_encode(-m))
+        lo = float(np.nextafter(np.float32(m), np.float32(0)))
+        hi = float(np.nextafter(np.float32(m), np.float32(10)))
+        vals = sorted((abs(v), int(c)) for c, v in table if int(c) < 8)
+        below = max(c for v, c in vals if v < m)
+        above = min(c for v, c in vals if v > m)
+        assert orc.e2m1_encode(lo) == below and orc.e2m1_encode(hi) == above, m
+    for v in (6.0001, 7.0, 1e30):
+        assert orc.e2m1_encode(v) == 7 and orc.e2m1_encode(-v) == 15
+
+
+def pin_e4m3_encode_vs_torch(orc):
+    """Nearest-even E4M3 of values up to 448 agrees with torch's float8
+    conversion (an independent implementation): every finite byte's own
+    value, the midpoints between neighbours, and random values; above 448
+    the encoder saturates to 0x7E."""
+    rng = np.random.default_rng(17)
+    vals = torch.arange(0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    mids = ((vals[:-1].astype(np.float64) + vals[1:]) / 2).astype(np.float32)
+    rand = np.concatenate([rng.uniform(0, 448, 2000), 2.0 ** rng.uniform(-12, 8.8, 2000)]).astype(np.float32)
+    probe = np.concatenate([vals, mids, rand, np.float32([0.0, 2 ** -10, 2 ** -10 * 1.0001, 447.9, 448.0])])
+    probe = probe[probe <= 448.0]
+    ref = torch.from_numpy(probe).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([orc.e4m3_encode(float(v)) for v in probe])
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(probe[i]), hex(got[i]), hex(ref[i])) for i in bad[:5]]
+    for v in (448.5, 464.0, 480.0, 1e6):
+        assert orc.e4m3_encode(v) == 0x7E
+
+
+def pin_quantize_zero(orc):
+    codes, scales, s2 = orc.quantize(np.zeros((3, 64), dtype=np.uint16))
+    assert s2 == 0.0 and not codes.any() and not scales.any()
+
+
+def _exact_nvfp4_weight(rng, rows, cols, scale2_exp=-4):
+    """A weight whose every element is e2m1 x e4m3 x 2^scale2_exp with one
+    element of each block at +-6 times the block scale, and one block scale
+    448: the quantiser's rule must give back exactly these codes and scales
+    and scale2 = 2^scale2_exp."""
+    e2 = np.array([v for _, v in _read_table("e2m1_values.txt")])
+    nb = cols // 16
+    code_idx = rng.integers(0, 16, size=(rows, cols))
+    pos = rng.integers(0, 16, size=(rows, nb))
+    for r in range(rows):
+        for b in range(nb):
+            code_idx[r, b * 16 + pos[r, b]] = 7 if rng.random() < 0.5 else 15  # +-6
+    finite = np.arange(1, 0x7F)  # non-zero, non-negative finite scale bytes
+    sbytes = rng.choice(finite, size=(rows, nb))
+    sbytes[rng.integers(rows), rng.integers(nb)] = 0x7E
+    sval = torch.from_numpy(sbytes.astype(np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    w = e2[code_idx] * np.repeat(sval, 16, axis=1) * 2.0 ** scale2_exp
+    return _bits_of(w), w, sbytes.astype(np.uint8)
+
+
+def pin_quantize_exact_roundtrip(orc):
+    rng = np.random.default_rng(23)
+    bits, w, sbytes = _exact_nvfp4_weight(rng, 24, 256)
+    codes, scales, s2 = orc.quantize(bits)
+    assert s2 == 2.0 ** -4, s2
+    np.testing.assert_array_equal(scales, sbytes)
+    back = orc.dequant(fi.Nvfp4Weight(codes, scales, s2))
+    np.testing.assert_array_equal(back, w)
+
+
+def pin_quantize_error_bound(orc):
+    """Random weights: scale2 maps the largest magnitude to 6 * 448 (the block
+    holding it gets scale byte 0x7E), and every element is reproduced to
+    within one block unit (half the widest E2M1 step, 2) of the block scale."""
+    rng = np.random.default_rng(29)
+    rows, cols = 40, 512
+    f = (rng.standard_normal((rows, cols)) * np.exp(rng.uniform(-6, 3, size=(rows, 1)))).astype(np.float32)
+    bits = (f.view(np.uint32) >> 16).astype(np.uint16)  # truncated to bf16
+    wv = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    codes, scales, s2 = orc.quantize(bits)
+    amax = np.abs(wv).max()
+    assert s2 == float(np.float32(amax) / np.float32(2688.0))
+    r, c = np.unravel_index(np.argmax(np.abs(wv)), wv.shape)
+    assert scales[r, c // 16] == 0x7E
+    back = orc.dequant(fi.Nvfp4Weight(codes, scales, s2))
+    sv = torch.from_numpy(scales).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    unit = np.repeat(sv, 16, axis=1) * s2
+    assert np.all(np.abs(back - wv) <= unit * (1 + 1e-6) + 1e-300)
+    assert np.all(scales < 0x7F)
+
+
 PINS = [pin_e2m1_table, pin_e4m3_vs_torch, pin_e4m3_anchors_and_order, pin_byte_nibble_order,
         pin_scale_blocks, pin_dequant_independent, pin_activations, pin_gated_act,
         pin_one_hot_selects, pin_down_orientation, pin_ternary_exact_vs_numpy,
         pin_matches_numpy_matmul, pin_fraction_brute_force, pin_down_fraction_bound,
-        pin_ffn_composition]
+        pin_ffn_composition, pin_e2m1_encode_grid, pin_e4m3_encode_vs_torch, pin_quantize_zero,
+        pin_quantize_exact_roundtrip, pin_quantize_error_bound]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -379,6 +490,16 @@ MUTANTS = {
     "gate_up_swapped": ("h[i] = oracle_act(act, gate[i]) * up[i];", "h[i] = oracle_act(act, up[i]) * gate[i];"),
     "dropped_last_term": ("for (int c = 0; c < cols; ++c)\n            acc +=", "for (int c = 0; c < cols - 1; ++c)\n            acc +="),
     "row_index": ("codes[(size_t)r * (size_t)(cols / 2)", "codes[(size_t)(r / 2) * (size_t)(cols / 2)"),
+    "q_e2m1_ties_odd": ("if (d < bd || (d == bd && (k & 1) == 0 && (best & 1) == 1)) {\n            best = k;",
+                        "if (d < bd || (d == bd && (k & 1) == 1 && (best & 1) == 0)) {\n            best = k;"),
+    "q_e4m3_ties_odd": ("if (d < bd || (d == bd && (b & 1) == 0 && (best & 1) == 1)) {",
+                        "if (d < bd || (d == bd && (b & 1) == 1 && (best & 1) == 0)) {"),
+    "q_e2m1_sign": ("return (q < 0.0f && best != 0) ? (best | 8) : best;", "return best;"),
+    "q_scale_rule": ("amax / 2688.0f", "amax / 448.0f"),
+    "q_block_max": ("for (int j = 0; j < 16; ++j) {\n                const float v", "for (int j = 0; j < 15; ++j) {\n                const float v"),
+    "q_pack_nibble": ("(c % 2 == 0) ? code : (code << 4)", "(c % 2 == 0) ? (code << 4) : code"),
+    "q_e2m1_saturation": ("return q < 0.0f ? 15 : 7;", "return q < 0.0f ? 14 : 6;"),
+    "q_e4m3_range": ("for (int b = 0; b < 127; ++b) {", "for (int b = 0; b < 126; ++b) {"),
 }
 
 
