@@ -42,6 +42,10 @@ WORKLOADS = {
     "verify_silu_m8": (3, 8),
     "prefill_silu_m128": (4, 128),
 }
+# The BF16 -> NVFP4 quantiser (ffn_nvfp4_quantize) on one weight of the decode
+# gate/up shape; timed like the forward, reported on its own line.
+QUANT_WORKLOADS = {"quantize_17408x5120": (17408, 5120)}
+QUANT_METRIC = "µs per BF16->NVFP4 weight quantise + achieved HBM GB/s (% of peak)"
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 
 
@@ -101,12 +105,105 @@ def cpu_baseline(case, seconds):
                       f"{el:.1f} s"}
 
 
+def quant_bytes(rows, cols):
+    """Bytes the two passes must move: the bf16 weight read by the absmax pass
+    and again by the quantise pass, then the codes, scale bytes and scale2."""
+    n = rows * cols
+    return 2 * (2 * n) + n // 2 + n // 16 + 4
+
+
+def bench_quantize(args):
+    import torch
+    import ffn_inputs as fi
+    import w4a16_nvfp4_dense_amd as ffn
+
+    lib = ffn.load()
+    rows, cols = QUANT_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bits = fi.make_dense_bf16(rows, cols, 1)
+    # byte-identical copies rotated over, so the Infinity Cache cannot serve repeats
+    ws_in = [ffn.bf16_from_bits(bits, dev) for _ in range(args.copies)]
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    s2 = torch.empty(1, dtype=torch.float32, device=dev)
+    wsb = ffn.quantize_workspace_bytes(rows, cols)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    q = lib.ffn_nvfp4_quantize
+    ptrs = [w.data_ptr() for w in ws_in]
+    cp, sp, s2p, wp = codes.data_ptr(), scales.data_ptr(), s2.data_ptr(), ws.data_ptr()
+    nc = len(ptrs)
+
+    def step(i):
+        rc = q(ptrs[i % nc], rows, cols, cp, sp, s2p, wp, wsb, sh)
+        if rc:
+            raise ffn.FfnError(rc, "ffn_nvfp4_quantize")
+
+    outs = []
+    for i in range(nc):
+        step(i)
+        outs.append((codes.clone(), scales.clone(), s2.clone()))
+    torch.cuda.synchronize()
+    assert all(all(torch.equal(a, b) for a, b in zip(o, outs[0])) for o in outs), "input copies disagree"
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    steps = min(args.steps, 1000)
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / steps
+    us = ms_per_step * 1e3
+    nbytes = quant_bytes(rows, cols)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"[bench] {args.workload}: {us:.2f} us/quantise, {gbs:.1f} GB/s algorithmic "
+        f"({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f}); host wall {wall * 1e3 / steps * 1e3:.2f} us/step")
+    result = {
+        "metric": QUANT_METRIC, "value": round(gbs, 2), "unit": "GB/s", "us_per_quantise": round(us, 3),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: BF16 weight [{rows}, {cols}] (normal values, per-row factors "
+                               f"e^U[-4,2]) to NVFP4, inputs rotated over {nc} copies",
+                   "rows": rows, "cols": cols, "algorithmic_bytes_per_quantise": nbytes},
+        "roofline": {"kernel": "whole quantise (absmax pass + quantise pass)", "bound": "hbm",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "us_per_launch": round(us, 3),
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.default()
+        n = 0
+        tq = time.perf_counter()
+        while True:
+            orc.quantize(bits)
+            n += 1
+            el = time.perf_counter() - tq
+            if el >= args.cpu_seconds:
+                break
+        cus = el / n * 1e6
+        result["cpu_baseline"] = {"value": round(nbytes / (cus * 1e-6) / 1e9, 3), "unit": "GB/s",
+                                  "us_per_quantise": round(cus, 1), "cores": 1, "kind": "oracle",
+                                  "sample": f"{n} full quantises of the same weight (C oracle, one thread), "
+                                            f"{el:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="decode_silu_m1", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="decode_silu_m1", choices=sorted(WORKLOADS) + sorted(QUANT_WORKLOADS))
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated over")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -125,6 +222,9 @@ def main():
     import ffn_inputs as fi
     import w4a16_nvfp4_dense_amd as ffn
 
+    if args.workload in QUANT_WORKLOADS:
+        bench_quantize(args)
+        return
     lib = ffn.load()
     idx, M = WORKLOADS[args.workload]
     case = fi.make_config(idx, M=M) if idx in (3, 4) else fi.make_config(idx)

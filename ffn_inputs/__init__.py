@@ -188,6 +188,17 @@ def make_format_coverage(act: int = ACT_SILU, seed: int = 99, M: int = 1) -> Ffn
                    x_bits=x_bits, gate=gate, up=up, down=down)
 
 
+def make_dense_bf16(rows: int, cols: int, seed: int, spread: float = 4.0) -> np.ndarray:
+    """Seeded dense bf16 weight bits [rows, cols] (the quantiser's input): a
+    normal draw times a per-row factor e^u, u uniform on [-spread, spread / 2]
+    (rows of different magnitude, so block scales spread over the E4M3
+    range), rounded to bf16 (nearest, ties to even)."""
+    rng = np.random.default_rng(SEED_BASE + 7919 * seed + 11)
+    f = rng.standard_normal((rows, cols)).astype(np.float32)
+    f *= np.exp(rng.uniform(-spread, spread / 2, size=(rows, 1))).astype(np.float32)
+    return f32_to_bf16_bits(f)
+
+
 def weight_copies(w: Nvfp4Weight, n: int) -> List[Nvfp4Weight]:
     """``n`` byte-identical copies (used to defeat cache reuse in timing)."""
     return [Nvfp4Weight(w.codes.copy(), w.scales.copy(), w.scale2) for _ in range(n)]

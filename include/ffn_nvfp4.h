@@ -147,6 +147,34 @@ int ffn_nvfp4_down_gemv(const float *gate_in, const float *up_in, int M, int N, 
                         const ffn_nvfp4_weight *down, int act,
                         void *out, hipStream_t stream);
 
+/* BF16 -> NVFP4 weight quantiser: produces the codes, scales and scale2 the
+ * entry points above take (qwen35_dense.rs page, weight loader: a dense BF16
+ * weight is quantised on the GPU by a global-absmax pass, then a pass that
+ * writes the packed codes and per-16 scales). The pages give no scale rule;
+ * this one fills both formats:
+ *   scale2       = amax / (6 * 448)                      (amax = max |w|)
+ *   scale byte   = E4M3(bmax / (6 * scale2))   per 16 columns, bmax = the block's max |w|
+ *   code         = E2M1(w * (1 / (E4M3 value * scale2)))
+ * each rounded to the nearest representable value (ties to the even
+ * encoding), E4M3 at most 448 and E2M1 at most 6; a zero code where
+ * E4M3 value * scale2 is zero, and all zeros (scale2 = 0) when amax = 0. Each
+ * arithmetic step is one correctly rounded fp32 division or multiplication,
+ * so the result is reproducible bit for bit. w must be finite.
+ *   w          device, bf16 [rows, cols], 16-byte aligned
+ *   rows       1 .. 65536
+ *   cols       a positive multiple of 32, at most 65536
+ *   codes      device, uint8 [rows, cols/2], 8-byte aligned (written)
+ *   scales     device, uint8 [rows, cols/16] (written)
+ *   scale2     device, one fp32, 4-byte aligned (written; copy it to the
+ *              host for ffn_nvfp4_weight.scale2)
+ *   workspace  device, >= ffn_nvfp4_quantize_workspace_bytes(rows, cols)
+ *              bytes, 4-byte aligned; clobbered; calls that share it must not
+ *              overlap
+ * Two kernel launches on `stream`; asynchronous like every entry point. */
+size_t ffn_nvfp4_quantize_workspace_bytes(int rows, int cols);
+int ffn_nvfp4_quantize(const void *w, int rows, int cols, uint8_t *codes, uint8_t *scales, float *scale2,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static text for a status code. */
 const char *ffn_nvfp4_strerror(int status);
 

@@ -40,7 +40,8 @@ def test_exports_every_header_symbol():
     lib = ffn.load()
     names = ffn.header_functions()
     assert set(names) == {"ffn_nvfp4_forward", "ffn_nvfp4_dual_gemv", "ffn_nvfp4_down_gemv",
-                          "ffn_nvfp4_workspace_bytes", "ffn_nvfp4_strerror", "ffn_nvfp4_version"}
+                          "ffn_nvfp4_workspace_bytes", "ffn_nvfp4_strerror", "ffn_nvfp4_version",
+                          "ffn_nvfp4_quantize", "ffn_nvfp4_quantize_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -142,3 +143,35 @@ def test_empty_batch_is_a_noop():
     assert fwd(M=0, K=100) == ffn.ERR_SHAPE
     assert fwd(M=0, act=5) == ffn.ERR_ACT
     assert dual(M=0, g=W(codes=0)) == ffn.ERR_NULL
+
+
+# ------------------------------------------------------------ quantiser
+
+
+def quant(w=FAKE, rows=64, cols=256, codes=FAKE + 0x200000, scales=FAKE + 0x400000, s2=FAKE + 0x500000,
+          ws=FAKE + 0x600000, wsb=1 << 16):
+    return ffn.load().ffn_nvfp4_quantize(w, rows, cols, codes, scales, s2, ws, wsb, 0)
+
+
+def test_quantize_workspace_bytes():
+    assert ffn.quantize_workspace_bytes(17408, 5120) == 4096
+    assert ffn.quantize_workspace_bytes(1, 32) == 4096
+    for rows, cols in [(0, 256), (64, 0), (64, 48), (65537, 256), (64, 65568), (-1, 256)]:
+        assert ffn.quantize_workspace_bytes(rows, cols) == 0
+
+
+def test_quantize_validation():
+    assert quant(w=0) == ffn.ERR_NULL
+    assert quant(codes=0) == ffn.ERR_NULL
+    assert quant(scales=0) == ffn.ERR_NULL
+    assert quant(s2=0) == ffn.ERR_NULL
+    assert quant(ws=0) == ffn.ERR_NULL
+    assert quant(w=FAKE + 8) == ffn.ERR_ALIGN
+    assert quant(codes=FAKE + 0x200004) == ffn.ERR_ALIGN
+    assert quant(s2=FAKE + 0x500002) == ffn.ERR_ALIGN
+    assert quant(ws=FAKE + 0x600002) == ffn.ERR_ALIGN
+    assert quant(wsb=4095) == ffn.ERR_WORKSPACE
+    for rows, cols in [(0, 256), (64, 0), (64, 48), (65537, 256), (64, 65568)]:
+        assert quant(rows=rows, cols=cols) == ffn.ERR_SHAPE
+    # shape is checked before pointers
+    assert quant(rows=0, w=0) == ffn.ERR_SHAPE

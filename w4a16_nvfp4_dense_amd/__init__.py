@@ -11,6 +11,8 @@ The functions mirror the C entry points:
 * :func:`dual_gemv`  -- ``ffn_nvfp4_dual_gemv`` gate, up = W_g x, W_u x (fp32)
 * :func:`down_gemv`  -- ``ffn_nvfp4_down_gemv`` out = W_d bf16(act(gate) * up)
 * :func:`workspace_bytes` -- ``ffn_nvfp4_workspace_bytes``
+* :func:`quantize`   -- ``ffn_nvfp4_quantize``  bf16 weight -> NVFP4 codes, scales, scale2
+* :func:`quantize_workspace_bytes` -- ``ffn_nvfp4_quantize_workspace_bytes``
 """
 from __future__ import annotations
 
@@ -77,6 +79,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ffn_nvfp4_dual_gemv.argtypes = [_P, _I, _I, _I, _WP, _WP, _P, _P, _P]
     lib.ffn_nvfp4_down_gemv.restype = _I
     lib.ffn_nvfp4_down_gemv.argtypes = [_P, _P, _I, _I, _I, _WP, _I, _P, _P]
+    lib.ffn_nvfp4_quantize_workspace_bytes.restype = ctypes.c_size_t
+    lib.ffn_nvfp4_quantize_workspace_bytes.argtypes = [_I, _I]
+    lib.ffn_nvfp4_quantize.restype = _I
+    lib.ffn_nvfp4_quantize.argtypes = [_P, _I, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]
     _lib = lib
     return lib
 
@@ -213,6 +219,43 @@ def down_gemv(gate_in, up_in, down: DeviceWeight, act: int = ACT_SILU, out=None,
                                     out.data_ptr(), _stream_handle(stream))
     _check(rc, "ffn_nvfp4_down_gemv")
     return out
+
+
+def quantize_workspace_bytes(rows: int, cols: int) -> int:
+    return int(load().ffn_nvfp4_quantize_workspace_bytes(int(rows), int(cols)))
+
+
+def quantize(w, codes=None, scales=None, scale2=None, workspace=None, stream=None):
+    """NVFP4 of the bf16 weight w [rows, cols]: (codes uint8 [rows, cols/2],
+    scales uint8 [rows, cols/16], scale2 fp32 [1]), all on w's device."""
+    import torch
+    rows, cols = w.shape
+    _check_tensor(w, torch.bfloat16, (rows, cols), "w")
+    dev = w.device
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    if scale2 is None:
+        scale2 = torch.empty(1, dtype=torch.float32, device=dev)
+    _check_tensor(codes, torch.uint8, (rows, cols // 2), "codes")
+    _check_tensor(scales, torch.uint8, (rows, cols // 16), "scales")
+    _check_tensor(scale2, torch.float32, (1,), "scale2")
+    need = quantize_workspace_bytes(rows, cols)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    rc = load().ffn_nvfp4_quantize(w.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(),
+                                   scale2.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _check(rc, "ffn_nvfp4_quantize")
+    return codes, scales, scale2
+
+
+def quantize_weight(w, stream=None) -> DeviceWeight:
+    """:func:`quantize` as a DeviceWeight (waits for the result to read
+    scale2 back to the host)."""
+    codes, scales, scale2 = quantize(w, stream=stream)
+    return DeviceWeight(codes, scales, float(scale2.cpu()[0]))
 
 
 def bf16_from_bits(bits, device="cuda"):

@@ -8,6 +8,7 @@
 
 #include "kernels.h"
 #include "mfma_launch.h"
+#include "quantize.h"
 
 namespace {
 
@@ -288,6 +289,28 @@ int ffn_nvfp4_forward(const void *x, int M, int K, int N, const ffn_nvfp4_weight
     if (e != hipSuccess)
         return FFN_NVFP4_ERR_LAUNCH;
     return launch_status(run_down(M, ffn::IN_BF16, workspace, nullptr, warg(down), out, K, N, stream));
+}
+
+size_t ffn_nvfp4_quantize_workspace_bytes(int rows, int cols)
+{
+    if (rows <= 0 || rows > kMaxDim || !dim_ok(cols))
+        return 0;
+    return static_cast<size_t>(ffn::kQuantizeMaxPartials) * sizeof(uint32_t);
+}
+
+int ffn_nvfp4_quantize(const void *w, int rows, int cols, uint8_t *codes, uint8_t *scales, float *scale2,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (rows <= 0 || rows > kMaxDim || !dim_ok(cols))
+        return FFN_NVFP4_ERR_SHAPE;
+    if (!w || !codes || !scales || !scale2 || !workspace)
+        return FFN_NVFP4_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(codes, 8) || !aligned(scale2, 4) || !aligned(workspace, 4))
+        return FFN_NVFP4_ERR_ALIGN;
+    if (workspace_bytes < ffn_nvfp4_quantize_workspace_bytes(rows, cols))
+        return FFN_NVFP4_ERR_WORKSPACE;
+    return launch_status(ffn::launch_quantize(w, rows, cols, codes, scales, scale2, static_cast<uint32_t *>(workspace),
+                                              stream));
 }
 
 }  // extern "C"
