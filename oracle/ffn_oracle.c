@@ -236,6 +236,7 @@ int oracle_num_threads(void)
  *   scale2 = amax / (6 * 448)       (largest E2M1 value x largest E4M3 value),
  *   block scale byte = E4M3(bmax / (6 * scale2)), nearest, ties to even, at most 448,
  *   code = E2M1(w * (1 / (block scale * scale2))), nearest, ties to even, at most 6,
+ *          with the sign of w (negative values that round to zero give -0),
  * with everything zero when amax = 0 and code 0 where block scale * scale2 is
  * zero. These steps decide integers, so they are taken in fp32 with the same
  * operations as the GPU: one correctly rounded division or multiplication
@@ -245,14 +246,15 @@ int oracle_num_threads(void)
  * above (no bit tricks), so they are correct by inspection. */
 
 /* The E2M1 code nearest to q (ties to the code with mantissa bit 0),
- * saturating at 6; a zero result is code 0 whatever the sign of q. */
+ * saturating at 6; the sign bit is q's (so -0 and small negatives give code
+ * 8, negative zero). */
 int oracle_e2m1_encode(float q)
 {
     const double a = fabs((double)q);
     int best = 0;
     double bd = INFINITY;
     if (a >= 6.0)  /* saturation (for huge a every distance would round alike) */
-        return q < 0.0f ? 15 : 7;
+        return signbit(q) ? 15 : 7;
     for (int k = 0; k < 8; ++k) {
         const double d = fabs(a - oracle_e2m1_value(k));
         if (d < bd || (d == bd && (k & 1) == 0 && (best & 1) == 1)) {
@@ -260,7 +262,7 @@ int oracle_e2m1_encode(float q)
             bd = d;
         }
     }
-    return (q < 0.0f && best != 0) ? (best | 8) : best;
+    return signbit(q) ? (best | 8) : best;
 }
 
 /* The E4M3FN byte nearest to s >= 0 (ties to the byte with mantissa bit 0),

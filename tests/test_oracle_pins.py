@@ -313,19 +313,18 @@ def _bits_of(values):
 
 
 def pin_e2m1_encode_grid(orc):
-    """Every E2M1 value (from the OCP table fixture) encodes to its own code;
-    each midpoint goes to its even neighbour; beyond 6 saturates; a zero
-    result is code 0 whatever the sign."""
+    """Every E2M1 value (from the OCP table fixture, -0 included) encodes to
+    its own code; each midpoint goes to its even neighbour; beyond 6
+    saturates; the sign bit is the input's (small negatives give -0)."""
     table = _read_table("e2m1_values.txt")
     for code, val in table:
-        if int(code) == 8:
-            continue  # -0 encodes as +0
         assert orc.e2m1_encode(val) == int(code), (code, val)
-    assert orc.e2m1_encode(-0.0) == 0 and orc.e2m1_encode(-0.2) == 0
+    assert orc.e2m1_encode(0.0) == 0 and orc.e2m1_encode(0.2) == 0
+    assert orc.e2m1_encode(-0.0) == 8 and orc.e2m1_encode(-0.2) == 8
     mids = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6}
     for m, k in mids.items():
         assert orc.e2m1_encode(m) == k, (m, orc.e2m1_encode(m))
-        assert orc.e2m1_encode(-m) == (k | 8 if k else 0), (-m, orc.e2m1_encode(-m))
+        assert orc.e2m1_encode(-m) == k | 8, (-m, orc.e2m1_encode(-m))
         lo = float(np.nextafter(np.float32(m), np.float32(0)))
         hi = float(np.nextafter(np.float32(m), np.float32(10)))
         vals = sorted((abs(v), int(c)) for c, v in table if int(c) < 8)
@@ -494,11 +493,11 @@ MUTANTS = {
                         "if (d < bd || (d == bd && (k & 1) == 1 && (best & 1) == 0)) {\n            best = k;"),
     "q_e4m3_ties_odd": ("if (d < bd || (d == bd && (b & 1) == 0 && (best & 1) == 1)) {",
                         "if (d < bd || (d == bd && (b & 1) == 1 && (best & 1) == 0)) {"),
-    "q_e2m1_sign": ("return (q < 0.0f && best != 0) ? (best | 8) : best;", "return best;"),
+    "q_e2m1_sign": ("return signbit(q) ? (best | 8) : best;", "return best;"),
     "q_scale_rule": ("amax / 2688.0f", "amax / 448.0f"),
     "q_block_max": ("for (int j = 0; j < 16; ++j) {\n                const float v", "for (int j = 0; j < 15; ++j) {\n                const float v"),
     "q_pack_nibble": ("(c % 2 == 0) ? code : (code << 4)", "(c % 2 == 0) ? (code << 4) : code"),
-    "q_e2m1_saturation": ("return q < 0.0f ? 15 : 7;", "return q < 0.0f ? 14 : 6;"),
+    "q_e2m1_saturation": ("return signbit(q) ? 15 : 7;", "return signbit(q) ? 14 : 6;"),
     "q_e4m3_range": ("for (int b = 0; b < 127; ++b) {", "for (int b = 0; b < 126; ++b) {"),
 }
 
