@@ -156,7 +156,8 @@ int ffn_nvfp4_down_gemv(const float *gate_in, const float *up_in, int M, int N, 
  *   scale byte   = E4M3(bmax / (6 * scale2))   per 16 columns, bmax = the block's max |w|
  *   code         = E2M1(w * (1 / (E4M3 value * scale2)))
  * each rounded to the nearest representable value (ties to the even
- * encoding), E4M3 at most 448 and E2M1 at most 6; a zero code where
+ * encoding), E4M3 at most 448 and E2M1 at most 6, a code keeping the sign of
+ * its input (negatives that round to zero encode -0); a zero code where
  * E4M3 value * scale2 is zero, and all zeros (scale2 = 0) when amax = 0. Each
  * arithmetic step is one correctly rounded fp32 division or multiplication,
  * so the result is reproducible bit for bit. w must be finite.

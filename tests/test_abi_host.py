@@ -154,8 +154,8 @@ def quant(w=FAKE, rows=64, cols=256, codes=FAKE + 0x200000, scales=FAKE + 0x4000
 
 
 def test_quantize_workspace_bytes():
-    assert ffn.quantize_workspace_bytes(17408, 5120) == 4096
-    assert ffn.quantize_workspace_bytes(1, 32) == 4096
+    assert ffn.quantize_workspace_bytes(17408, 5120) == 8192
+    assert ffn.quantize_workspace_bytes(1, 32) == 8192
     for rows, cols in [(0, 256), (64, 0), (64, 48), (65537, 256), (64, 65568), (-1, 256)]:
         assert ffn.quantize_workspace_bytes(rows, cols) == 0
 
@@ -170,7 +170,7 @@ def test_quantize_validation():
     assert quant(codes=FAKE + 0x200004) == ffn.ERR_ALIGN
     assert quant(s2=FAKE + 0x500002) == ffn.ERR_ALIGN
     assert quant(ws=FAKE + 0x600002) == ffn.ERR_ALIGN
-    assert quant(wsb=4095) == ffn.ERR_WORKSPACE
+    assert quant(wsb=8191) == ffn.ERR_WORKSPACE
     for rows, cols in [(0, 256), (64, 0), (64, 48), (65537, 256), (64, 65568)]:
         assert quant(rows=rows, cols=cols) == ffn.ERR_SHAPE
     # shape is checked before pointers

@@ -7,8 +7,9 @@
 
 namespace ffn {
 
-// Workgroups of the absmax pass at most; its workspace is one uint32 each.
-constexpr int kQuantizeMaxPartials = 1024;
+// Workgroups of either pass at most; the absmax pass leaves one uint32 of
+// workspace per workgroup.
+constexpr int kQuantizeMaxPartials = 2048;
 
 // w: bf16 [rows, cols] (16-byte aligned, cols a multiple of 16); writes codes
 // [rows, cols/2] (8-byte aligned), scales [rows, cols/16] and *scale2 (device

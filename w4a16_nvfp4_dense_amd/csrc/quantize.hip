@@ -7,18 +7,23 @@
 // The pages give no scale rule. The one used fills both formats:
 //   scale2     = amax / (6 * 448)     (largest E2M1 value x largest E4M3 value)
 //   block byte = E4M3(bmax / (6 * scale2)), nearest, ties to even, at most 448
-//   code       = E2M1(w * (1 / (E4M3 value * scale2))), nearest, ties to even, at most 6
+//   code       = E2M1(w * (1 / (E4M3 value * scale2))), nearest, ties to even, at most 6,
+//                with the sign of w (negatives that round to zero give -0)
 // with everything zero when amax = 0, and code 0 where E4M3 value * scale2 is
 // zero. Each step is one correctly rounded fp32 division or multiplication (no
 // fused multiply-add), so the integers it decides are reproducible; the codes
 // of a block take one reciprocal and 16 multiplications. Inputs must be
-// finite.
+// finite. The two roundings are gfx950's conversions: v_cvt_pk_fp8_f32 (E4M3
+// nearest-even, the input clamped to 448 first) and v_cvt_scalef32_pk_fp4_f32
+// with unit scale (E2M1 nearest-even, saturating, sign kept); both were
+// checked to round exactly so on every E4M3 and E2M1 value, midpoint and
+// neighbour of a midpoint, and 400k random values.
 //
 // Two launches, both memory-bound streams over the weight:
-//   absmax_kernel:   per-workgroup maxima of |w| (taken on the bf16 bit
+//   quantize_absmax_kernel: per-workgroup maxima of |w| (taken on the bf16 bit
 //                    patterns: for finite values the magnitude order is the
 //                    unsigned order of the low 15 bits), written to the
-//                    workspace;
+//                    workspace, with the same traversal as the quantise pass;
 //   quantize_kernel: every workgroup reduces those maxima (a few KB from L2),
 //                    then each thread encodes one 16-element block at a time:
 //                    32 bytes in (two 16-byte loads), 8 code bytes and 1 scale
@@ -61,29 +66,10 @@ __device__ __forceinline__ uint32_t workgroup_max(uint32_t m, uint32_t *sh)
 }
 
 // E4M3FN byte nearest to s (finite, s >= 0), ties to the even mantissa,
-// saturating at 448 (0x7E). Normals round the fp32 mantissa to 3 bits; below
-// 2^-6 the value is a multiple of 2^-9 (s * 512 is exact, then rounded to an
-// integer, ties to even), and 8 * 2^-9 = 2^-6 is byte 0x08.
+// saturating at 448 (0x7E).
 __device__ __forceinline__ uint32_t e4m3_encode(float s)
 {
-    if (s >= 448.0f)
-        return 0x7E;
-    const uint32_t bits = __float_as_uint(s);
-    const int e = static_cast<int>((bits >> 23) & 0xFF) - 127;
-    if (e < -6)
-        return static_cast<uint32_t>(__builtin_rintf(s * 512.0f));
-    uint32_t m3 = (bits >> 20) & 7;
-    const uint32_t rem = bits & 0xFFFFF;
-    if (rem > 0x80000 || (rem == 0x80000 && (m3 & 1)))
-        ++m3;
-    uint32_t E = static_cast<uint32_t>(e + 7);
-    if (m3 == 8) {
-        m3 = 0;
-        ++E;
-    }
-    if (E > 15 || (E == 15 && m3 == 7))
-        return 0x7E;
-    return (E << 3) | m3;
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s, 448.0f), 0.0f, 0, false)) & 0xFF;
 }
 
 // Value of a non-negative E4M3FN byte (0x00 .. 0x7E).
@@ -94,33 +80,32 @@ __device__ __forceinline__ float e4m3_decode(uint32_t b)
                   : __uint_as_float(((E + 120) << 23) | (m << 20));
 }
 
-// E2M1 code nearest to q (finite), ties to the even code, saturating at 6;
-// a zero result is code 0 whatever the sign. The grid is 0, .5, 1, 1.5, 2,
-// 3, 4, 6, and each midpoint goes to its even neighbour.
-__device__ __forceinline__ uint32_t e2m1_encode(float q)
+// Four E2M1 codes of (a0, a1, a2, a3) * inv, nearest with ties to the even
+// code, saturating at 6, sign kept: code i in nibble i of the result.
+__device__ __forceinline__ uint32_t e2m1_encode4(float a0, float a1, float a2, float a3, float inv)
 {
-    const float a = fabsf(q);
-    const uint32_t k = a <= 0.25f ? 0
-                     : a < 0.75f  ? 1
-                     : a <= 1.25f ? 2
-                     : a < 1.75f  ? 3
-                     : a <= 2.5f  ? 4
-                     : a < 3.5f   ? 5
-                     : a <= 5.0f  ? 6
-                                  : 7;
-    return (q < 0.0f && k != 0) ? (k | 8) : k;
+    uint32_t p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a0 * inv, a1 * inv, 1.0f, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, a2 * inv, a3 * inv, 1.0f, 1);
+    return p & 0xFFFF;
 }
 
-__global__ __launch_bounds__(kThreads) void absmax_kernel(const u32x4_t *w, size_t n16, uint32_t *partial)
+}  // namespace
+
+__global__ __launch_bounds__(kThreads) void quantize_absmax_kernel(const u32x4_t *w, size_t nblocks,
+                                                                   uint32_t *partial)
 {
     __shared__ uint32_t sh[kThreads / 64];
     uint32_t m = 0;
-    for (size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; i < n16;
-         i += static_cast<size_t>(gridDim.x) * kThreads) {
-        const u32x4_t v = w[i];
+    // the quantise pass's traversal: one 16-element block (32 bytes) per thread and step
+    for (size_t b = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; b < nblocks;
+         b += static_cast<size_t>(gridDim.x) * kThreads) {
+        const u32x4_t v0 = w[2 * b];
+        const u32x4_t v1 = w[2 * b + 1];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            m = max(m, max(v[q] & 0x7FFFu, (v[q] >> 16) & 0x7FFFu));
+        for (int q = 0; q < 4; ++q) {
+            m = max(m, max(v0[q] & 0x7FFFu, (v0[q] >> 16) & 0x7FFFu));
+            m = max(m, max(v1[q] & 0x7FFFu, (v1[q] >> 16) & 0x7FFFu));
+        }
     }
     m = workgroup_max(m, sh);
     if (threadIdx.x == 0)
@@ -166,25 +151,28 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t *w, si
         uint2 packed = {0u, 0u};
         if (denom != 0.0f) {
             const float inv = 1.0f / denom;
+            float f[16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const uint32_t code = e2m1_encode(bf16_bits_to_float(bits[j]) * inv);
-                if (j < 8)
-                    packed.x |= code << (4 * j);
-                else
-                    packed.y |= code << (4 * (j - 8));
-            }
+            for (int j = 0; j < 16; ++j)
+                f[j] = bf16_bits_to_float(bits[j]);
+            packed.x = e2m1_encode4(f[0], f[1], f[2], f[3], inv) | (e2m1_encode4(f[4], f[5], f[6], f[7], inv) << 16);
+            packed.y = e2m1_encode4(f[8], f[9], f[10], f[11], inv) | (e2m1_encode4(f[12], f[13], f[14], f[15], inv) << 16);
         }
         codes[b] = packed;
         scales[b] = static_cast<uint8_t>(sb);
     }
 }
 
-int absmax_blocks(size_t n16)
+namespace {
+
+// Workgroups of either pass: a few per compute unit (each quantise workgroup
+// first re-reduces the absmax pass's per-workgroup maxima), at most
+// kQuantizeMaxPartials.
+int quantize_blocks(size_t nblocks)
 {
-    // about 8 loads of 16 bytes per thread, at most kQuantizeMaxPartials workgroups
-    const size_t want = (n16 + static_cast<size_t>(kThreads) * 8 - 1) / (static_cast<size_t>(kThreads) * 8);
-    return static_cast<int>(std::max<size_t>(1, std::min<size_t>(want, kQuantizeMaxPartials)));
+    const size_t want = (nblocks + kThreads - 1) / kThreads;
+    const size_t cap = std::min<size_t>(kQuantizeMaxPartials, static_cast<size_t>(device_cu_count()) * 8);
+    return static_cast<int>(std::max<size_t>(1, std::min(want, cap)));
 }
 
 }  // namespace
@@ -192,20 +180,15 @@ int absmax_blocks(size_t n16)
 hipError_t launch_quantize(const void *w, int rows, int cols, uint8_t *codes, uint8_t *scales, float *scale2,
                            uint32_t *partial, hipStream_t stream)
 {
-    const size_t n = static_cast<size_t>(rows) * static_cast<size_t>(cols);
-    const size_t n16 = n / 8;      // 16-byte pieces of 8 bf16
-    const size_t nblocks = n / 16;  // 16-element scale blocks
-    const int g1 = absmax_blocks(n16);
-    hipLaunchKernelGGL(absmax_kernel, dim3(g1), dim3(kThreads), 0, stream, static_cast<const u32x4_t *>(w), n16,
-                       partial);
+    const size_t nblocks = static_cast<size_t>(rows) * static_cast<size_t>(cols) / 16;  // 16-element blocks
+    const int g = quantize_blocks(nblocks);
+    hipLaunchKernelGGL(quantize_absmax_kernel, dim3(g), dim3(kThreads), 0, stream, static_cast<const u32x4_t *>(w),
+                       nblocks, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    // a few workgroups per compute unit: each first re-reduces the g1 maxima
-    const size_t want = (nblocks + kThreads - 1) / kThreads;
-    const int g2 = static_cast<int>(std::max<size_t>(1, std::min<size_t>(want, static_cast<size_t>(device_cu_count()) * 8)));
-    hipLaunchKernelGGL(quantize_kernel, dim3(g2), dim3(kThreads), 0, stream, static_cast<const u32x4_t *>(w), nblocks,
-                       partial, g1, reinterpret_cast<uint2 *>(codes), scales, scale2);
+    hipLaunchKernelGGL(quantize_kernel, dim3(g), dim3(kThreads), 0, stream, static_cast<const u32x4_t *>(w), nblocks,
+                       partial, g, reinterpret_cast<uint2 *>(codes), scales, scale2);
     return hipGetLastError();
 }
 
