@@ -41,7 +41,11 @@ WORKLOADS = {
     "verify_silu_m3": (3, 3),
     "verify_silu_m8": (3, 8),
     "prefill_silu_m128": (4, 128),
+    # small batches (9 <= M <= 16) on the prefill shapes: the small-batch arm
+    "smallbatch_silu_m9": (4, 9),
+    "smallbatch_silu_m16": (4, 16),
 }
+SMALL_BATCH_MAX_M = 16  # above this the forward runs the 128-row matrix-core arm
 # The BF16 -> NVFP4 quantiser (ffn_nvfp4_quantize) on one weight of the decode
 # gate/up shape; timed like the forward, reported on its own line.
 QUANT_WORKLOADS = {"quantize_17408x5120": (17408, 5120)}
@@ -295,7 +299,7 @@ def main():
     log(f"[bench] {args.workload}: {us:.2f} us/forward, {gbs:.1f} GB/s algorithmic "
         f"({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f}); host wall {wall * 1e3 / args.steps * 1e3:.2f} us/step")
 
-    if M > 8:
+    if M > SMALL_BATCH_MAX_M:
         # Matrix-core arm: bound by the bf16 MFMA rate; the whole forward's
         # flops (three [M, K] x [K, N]-sized products) over its time.
         flops = 2.0 * 3 * M * K * N
@@ -340,7 +344,7 @@ def main():
     torch.cuda.synchronize()
     dual_us = d0.elapsed_time(d1) / nk * 1e3
     dual_gbs = nbytes["dual_f32"] / (dual_us * 1e-6) / 1e9
-    log(f"[bench] dual GEMV: {dual_us:.2f} us/launch, {dual_gbs:.1f} GB/s")
+    log(f"[bench] dual {'GEMV' if M <= 8 else 'GEMM'}: {dual_us:.2f} us/launch, {dual_gbs:.1f} GB/s")
 
     traffic = measured_traffic(args.workload)
     if traffic is not None:
@@ -368,7 +372,9 @@ def main():
             "algorithmic_bytes_per_forward": nbytes["forward"],
         },
         "roofline": {
-            "kernel": "dual gate+up GEMV (ffn_nvfp4_dual_gemv entry point: wave_gemv_kernel, gate and up fp32 out)",
+            "kernel": ("dual gate+up GEMV (ffn_nvfp4_dual_gemv entry point: wave_gemv_kernel, gate and up fp32 out)"
+                       if M <= 8 else
+                       "dual gate+up GEMM (ffn_nvfp4_dual_gemv entry point: smallm_gemm_kernel, gate and up fp32 out)"),
             "bound": "hbm",
             "achieved": round(dual_gbs, 2),
             "peak": HBM_PEAK_GBS,

@@ -36,10 +36,11 @@
  *     any HIP kernel.
  *   - Results are deterministic: the same inputs on the same device give
  *     bit-identical outputs. Row m of a batched call is bit-identical to an
- *     M=1 call on that row for every M <= 8; for M > 8 a row's result does
- *     not depend on the other rows of the batch (but differs in rounding from
- *     the M <= 8 arm, and the forward's split of the reduction depends on the
- *     device's compute-unit count).
+ *     M=1 call on that row for every M <= 8. Within each matrix-core arm (see
+ *     the batch sizes below) a row's result does not depend on the other rows
+ *     of the batch; the arms differ from each other and from the M <= 8 arm
+ *     in rounding, and the 128-row arm's forward splits its reductions by the
+ *     device's compute-unit count.
  *   - The functions hold no global mutable state and may be called from
  *     several host threads (on distinct output buffers).
  */
@@ -58,7 +59,7 @@ extern "C" {
 #define FFN_NVFP4_OK 0
 #define FFN_NVFP4_ERR_NULL (-1)          /* a required pointer is NULL */
 #define FFN_NVFP4_ERR_ALIGN (-2)         /* codes / x / out / workspace not 16-byte aligned;
-                                            scales not 2-byte (M > 8: 4-byte) aligned */
+                                            scales not 2-byte (M > 8: 8-byte) aligned */
 #define FFN_NVFP4_ERR_SHAPE (-3)         /* K or N not a positive multiple of 32 (of 64 when
                                             M > 8), or larger than 65536 */
 #define FFN_NVFP4_ERR_BATCH (-4)         /* M outside the supported set (see below) */
@@ -88,19 +89,23 @@ typedef struct ffn_nvfp4_weight {
  *   1 <= M <= 8      the weight-streaming GEMV arm (each weight byte read once
  *                    for all M rows; dense_ffn.rs page, forward_k2 / forward_k3 /
  *                    forward_km);
- *   9 <= M <= 65536  the matrix-core arm (dense_ffn.rs page, forward_prefill:
+ *   9 <= M <= 65536  the matrix-core arms (dense_ffn.rs page, forward_prefill:
  *                    weights dequantised to bf16 feeding bf16 matrix products
- *                    with fp32 accumulation), in blocks of 128 token rows,
- *                    each block reading the weights once. It needs K and N in
- *                    multiples of 64 (else ERR_SHAPE) and scales 4-byte
- *                    aligned (else ERR_ALIGN).
+ *                    with fp32 accumulation). They need K and N in multiples
+ *                    of 64 (else ERR_SHAPE) and scales 8-byte aligned (else
+ *                    ERR_ALIGN).
+ *     9 <= M <= 64, K and N multiples of 128: the small-batch arm, one launch
+ *                    per projection, weights read once for all rows;
+ *     otherwise      the 128-row arm, in blocks of 128 token rows, each block
+ *                    reading the weights once.
  * Other M: ERR_BATCH. K and N: positive multiples of 32, at most 65536. */
 
 /* Bytes of device workspace ffn_nvfp4_forward needs for (M, K, N);
- * 0 if M = 0 or the shape is unsupported. For M <= 8 it holds h [M, N] bf16;
- * for M > 8, h for one block of up to 128 rows plus the fp32 slots in which
- * the matrix-core arm leaves the pieces of split reductions (about 64 MiB,
- * whatever M). Its contents need no initialisation. */
+ * 0 if M = 0 or the shape is unsupported. For M <= 8 and for the small-batch
+ * arm it holds h [M, N] bf16; for the 128-row arm, h for one block of up to
+ * 128 rows plus the fp32 slots in which that arm leaves the pieces of split
+ * reductions (about 64 MiB, whatever M). Its contents need no
+ * initialisation. */
 size_t ffn_nvfp4_workspace_bytes(int M, int K, int N);
 
 /* The whole FFN: out[M, K] (bf16) = W_d (act(W_g x) * (W_u x)) for
@@ -124,7 +129,8 @@ int ffn_nvfp4_forward(const void *x, int M, int K, int N,
 
 /* Dual GEMV (one pass over x for both projections; dense_ffn.rs page,
  * DenseFfnLayer::forward, w4a16_gemv_dual). For M > 8 it runs the
- * matrix-core arm with one workgroup per output tile (no workspace):
+ * small-batch arm when it applies, else the 128-row arm with one workgroup
+ * per output tile (no workspace either way):
  *   gate_out[m, n] = scale2_g * sum_k W_g[n, k] x[m, k]
  *   up_out[m, n]   = scale2_u * sum_k W_u[n, k] x[m, k]
  *   x          device, bf16 [M, K], 16-byte aligned
@@ -136,7 +142,7 @@ int ffn_nvfp4_dual_gemv(const void *x, int M, int K, int N,
 
 /* Down GEMV with the activation fused into its input load (dense_ffn.rs
  * page, DenseFfnLayer::forward, w4a16_gemv_silu_input / gelu_mul). For M > 8
- * it runs the matrix-core arm with one workgroup per output tile (no
+ * it runs the 128-row matrix-core arm with one workgroup per output tile (no
  * workspace, so it is much slower than the forward's down projection):
  *   out[m, j] = bf16(scale2_d * sum_n W_d[j, n] * bf16(act(gate[m, n]) * up[m, n]))
  *   gate_in, up_in   device, fp32 [M, N] (as written by the dual GEMV),

@@ -55,9 +55,15 @@ def test_version_strerror_workspace():
     assert ffn.workspace_bytes(8, 5120, 17408) == 8 * 17408 * 2
     assert ffn.workspace_bytes(0, 256, 512) == 0
     assert ffn.workspace_bytes(1, 250, 512) == 0
-    # matrix-core arm (M > 8): h for one block of 128 rows, counters, partial slots
-    ws9 = ffn.workspace_bytes(9, 256, 512)
-    assert ws9 > 9 * 512 * 2 and ws9 % 256 == 0
+    # small-batch arm (9 <= M <= 16, K <= 5120): h, and the down projection's
+    # partial sums when its reduction is split (N = 17408: 4 parts)
+    assert ffn.workspace_bytes(9, 256, 512) == 9 * 512 * 2
+    assert ffn.workspace_bytes(16, 5120, 17408) == 16 * 17408 * 2 + 4 * 16 * 5120 * 4
+    # 128-row matrix-core arm (M > 16, or K > 5120): h for one block of 128
+    # rows and the partial slots
+    ws17 = ffn.workspace_bytes(17, 256, 512)
+    assert ws17 > 17 * 512 * 2 and ws17 % 256 == 0
+    assert ffn.workspace_bytes(16, 5376, 512) > 16 * 512 * 2
     assert ffn.workspace_bytes(128, 5120, 17408) == ffn.workspace_bytes(4096, 5120, 17408)
     assert ffn.workspace_bytes(128, 5120, 17408) >= 128 * 17408 * 2
     assert ffn.workspace_bytes(9, 96, 512) == 0   # the arm needs K, N multiples of 64
@@ -92,10 +98,12 @@ def test_misaligned():
     assert dual(go=FAKE + 4) == ffn.ERR_ALIGN
     assert down(ui=FAKE + 0x200004) == ffn.ERR_ALIGN
     # scales need 2-byte alignment up to M = 8 (this one fails later, on M),
-    # 4-byte alignment on the matrix-core arm
+    # 8-byte alignment on the matrix-core arms
     assert fwd(g=W(scales=FAKE + 2), M=-1) == ffn.ERR_BATCH
     assert fwd(g=W(scales=FAKE + 2), M=9, wsb=1 << 30) == ffn.ERR_ALIGN
+    assert fwd(g=W(scales=FAKE + 4), M=9, wsb=1 << 30) == ffn.ERR_ALIGN
     assert dual(u=W(scales=FAKE + 6), M=64) == ffn.ERR_ALIGN
+    assert dual(u=W(scales=FAKE + 4), M=17) == ffn.ERR_ALIGN
     assert down(d=W(scales=FAKE + 2), M=128) == ffn.ERR_ALIGN
 
 

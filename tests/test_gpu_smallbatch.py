@@ -1,0 +1,114 @@
+"""GPU parity of the small-batch matrix-core arm (9 <= M <= 16 token rows,
+K and N multiples of 256, K at most 5120) against the CPU oracle, with the
+bounds of the other arms: |out - out_ref| <= 1e-2 rms(out_ref) + 1 bf16 ulp(out_ref); the dual
+entry's fp32 gate/up within 1e-4 rms(ref) + 1e-6 |ref|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import ffn_inputs as fi
+import oracle
+import w4a16_nvfp4_dense_amd as ffn
+from test_gpu_parity import assert_dual_close, assert_ffn_close, loaded
+
+pytestmark = pytest.mark.gpu
+
+# (M, K, N, act, seed). A round is 1024 reduction columns (16 waves x 64);
+# the shapes give one-round reductions with idle waves (K = 256, 768), a short
+# last round (K = 1280, N = 1280), the longest one-part reduction (K = 5120:
+# five rounds), down projections split in two parts with partial sums and the
+# in-order reduction (N = 6144, 8192), one to three row tiles per workgroup,
+# and 9 to 16 token rows.
+SMALL_BATCH = [
+    (9, 256, 512, fi.ACT_SILU, 51),
+    (12, 768, 1280, fi.ACT_GELU_TANH, 52),
+    (16, 1280, 2048, fi.ACT_SILU, 53),
+    (10, 4096, 512, fi.ACT_GELU_TANH, 54),
+    (16, 2048, 8192, fi.ACT_SILU, 55),
+    (13, 5120, 6144, fi.ACT_GELU_TANH, 56),
+    (11, 5120, 1024, fi.ACT_SILU, 57),
+]
+IDS = [f"m{m}_k{k}_n{n}_a{a}" for m, k, n, a, _ in SMALL_BATCH]
+
+
+def case_of(M, K, N, act, seed):
+    return fi.make_small(M, K, N, act=act, seed=seed)
+
+
+@pytest.mark.parametrize("M,K,N,act,seed", SMALL_BATCH, ids=IDS)
+def test_smallbatch_forward(M, K, N, act, seed):
+    case = case_of(M, K, N, act, seed)
+    L = loaded(case.name, lambda: case)
+    out = L.forward()
+    torch.cuda.synchronize()
+    assert_ffn_close(out, oracle.ffn(case), case.name)
+
+
+@pytest.mark.parametrize("M,K,N,act,seed", SMALL_BATCH, ids=IDS)
+def test_smallbatch_dual_entry(M, K, N, act, seed):
+    case = case_of(M, K, N, act, seed)
+    L = loaded(case.name, lambda: case)
+    g, u = ffn.dual_gemv(L.x, L.gate, L.up)
+    torch.cuda.synchronize()
+    g_ref, u_ref = oracle.dual(case)
+    assert_dual_close(g, g_ref, "gate")
+    assert_dual_close(u, u_ref, "up")
+
+
+def test_smallbatch_workspace():
+    """The small-batch arm keeps h = act(gate) * up and, when the down
+    projection's reduction is split, its fp32 partial sums."""
+    r256 = lambda b: (b + 255) // 256 * 256
+    assert ffn.workspace_bytes(9, 256, 512) == r256(9 * 512 * 2)
+    # N = 17408: 272 units of 64 columns in parts of at most 80: 4 parts
+    assert ffn.workspace_bytes(16, 5120, 17408) == r256(16 * 17408 * 2) + 4 * 16 * 5120 * 4
+    # M = 17, K above 5120, or K or N not a multiple of 256: the 128-row arm
+    # with its partial slots
+    assert ffn.workspace_bytes(17, 5120, 17408) > 32 << 20
+    assert ffn.workspace_bytes(16, 5376, 21504) > 32 << 20
+    assert ffn.workspace_bytes(16, 640, 1024) > 32 << 20
+
+
+def test_smallbatch_rows_independent_of_batch():
+    """Inside the arm a token row's result does not depend on the other rows
+    of the batch: its position in the token tile and M do not change the order
+    of any sum."""
+    case = fi.make_small(16, 2048, 6144, act=fi.ACT_GELU_TANH, seed=59)
+    L = loaded(case.name, lambda: case)
+    full = L.forward()
+    for lo, hi in ((0, 9), (7, 16), (2, 13), (3, 15)):
+        part = L.forward(L.x[lo:hi].contiguous())
+        assert torch.equal(part, full[lo:hi]), (lo, hi)
+    g, u = ffn.dual_gemv(L.x, L.gate, L.up)
+    g2, u2 = ffn.dual_gemv(L.x[4:14].contiguous(), L.gate, L.up)
+    assert torch.equal(g2, g[4:14]) and torch.equal(u2, u[4:14])
+
+
+def test_smallbatch_determinism():
+    case = fi.make_small(14, 2048, 8192, seed=60)
+    L = loaded(case.name, lambda: case)
+    first = L.forward().clone()
+    for _ in range(5):
+        assert torch.equal(L.forward(), first)
+
+
+SAMPLE = {9: [0, 4, 8], 16: [0, 3, 8, 15]}
+
+
+@pytest.mark.parametrize("M", [9, 16])
+def test_config_smallbatch(M):
+    """The prefill shapes (hidden 5120, intermediate 17408, SiLU) at 9 and 16
+    token rows, the launch configuration the bench times: the forward and the
+    dual entry against the oracle on sampled token rows."""
+    case = fi.make_config(4, M=M)
+    L = loaded(case.name, lambda: case)
+    out = L.forward()
+    g, u = ffn.dual_gemv(L.x, L.gate, L.up)
+    torch.cuda.synchronize()
+    rows = SAMPLE[M]
+    sub = case.with_x(case.x_bits[rows])
+    assert_ffn_close(out[rows], oracle.ffn(sub), case.name)
+    g_ref, u_ref = oracle.dual(sub)
+    assert_dual_close(g[rows], g_ref, "gate")
+    assert_dual_close(u[rows], u_ref, "up")

@@ -9,6 +9,7 @@
 #include "kernels.h"
 #include "mfma_launch.h"
 #include "quantize.h"
+#include "smallm_launch.h"
 
 namespace {
 
@@ -51,14 +52,15 @@ int check_prefill_shape(int M, int K, int N)
     return FFN_NVFP4_OK;
 }
 
-// ... and scales aligned to 4 bytes.
+// ... and scales aligned to 8 bytes (the small-batch arm loads a row's 8
+// scale bytes of a 128-column unit at once).
 int check_prefill_scales(int M, const ffn_nvfp4_weight *a, const ffn_nvfp4_weight *b = nullptr,
                          const ffn_nvfp4_weight *c = nullptr)
 {
     if (M <= kMaxGemvM)
         return FFN_NVFP4_OK;
     for (const ffn_nvfp4_weight *w : {a, b, c})
-        if (w && !aligned(w->scales, 4))
+        if (w && !aligned(w->scales, 8))
             return FFN_NVFP4_ERR_ALIGN;
     return FFN_NVFP4_OK;
 }
@@ -73,6 +75,18 @@ size_t round256(size_t b)
 struct PrefillLayout {
     size_t h, partials, total;
 };
+
+// Batches of 9 to 16 rows take the small-batch arm when it covers the shape;
+// its workspace is h and the down projection's partial sums.
+bool small_arm(int M, int K, int N)
+{
+    return M > kMaxGemvM && ffn::smallm_supported(M, K, N);
+}
+
+size_t small_partials_offset(int M, int N)
+{
+    return round256(static_cast<size_t>(M) * static_cast<size_t>(N) * 2);
+}
 
 PrefillLayout prefill_layout(int M, int N)
 {
@@ -119,6 +133,8 @@ hipError_t run_down(int M, ffn::InKind in, const void *in0, const float *in1, co
 hipError_t run_prefill_dual(int M, const void *x, const ffn::WeightArg &g, const ffn::WeightArg &u, float *gate_out,
                             float *up_out, int N, int K, hipStream_t stream)
 {
+    if (small_arm(M, K, N))
+        return ffn::launch_smallm_dual(M, ffn::OUT_F32_PAIR, x, g, u, gate_out, up_out, N, K, stream);
     for (int m0 = 0; m0 < M; m0 += ffn::kMfmaMaxM) {
         const int mb = M - m0 < ffn::kMfmaMaxM ? M - m0 : ffn::kMfmaMaxM;
         const size_t xo = static_cast<size_t>(m0) * K, oo = static_cast<size_t>(m0) * N;
@@ -148,6 +164,13 @@ hipError_t run_prefill_forward(int M, ffn::OutKind epi, const void *x, const ffn
                                const ffn::WeightArg &u, const ffn::WeightArg &d, void *workspace, void *out, int K,
                                int N, hipStream_t stream)
 {
+    if (small_arm(M, K, N)) {
+        float *partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + small_partials_offset(M, N));
+        hipError_t e = ffn::launch_smallm_dual(M, epi, x, g, u, workspace, nullptr, N, K, stream);
+        if (e != hipSuccess)
+            return e;
+        return ffn::launch_smallm_down(M, workspace, d, out, partials, K, N, stream);
+    }
     const PrefillLayout l = prefill_layout(M, N);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     ffn::MfmaScratch scratch{reinterpret_cast<float *>(ws + l.partials)};
@@ -181,7 +204,7 @@ const char *ffn_nvfp4_strerror(int status)
     case FFN_NVFP4_OK: return "ok";
     case FFN_NVFP4_ERR_NULL: return "a required pointer is NULL";
     case FFN_NVFP4_ERR_ALIGN:
-        return "pointer misaligned (codes/x/out/workspace need 16 bytes, scales 2, or 4 when M > 8)";
+        return "pointer misaligned (codes/x/out/workspace need 16 bytes, scales 2, or 8 when M > 8)";
     case FFN_NVFP4_ERR_SHAPE:
         return "K and N must be positive multiples of 32 (of 64 when M > 8), at most 65536";
     case FFN_NVFP4_ERR_BATCH: return "unsupported batch size M";
@@ -199,6 +222,8 @@ size_t ffn_nvfp4_workspace_bytes(int M, int K, int N)
         return 0;
     if (M == 0 || check_prefill_shape(M, K, N) != FFN_NVFP4_OK)
         return 0;
+    if (small_arm(M, K, N))
+        return small_partials_offset(M, N) + round256(ffn::smallm_partial_floats(M, K, N) * sizeof(float));
     if (M > kMaxGemvM)
         return prefill_layout(M, N).total;
     // h = act(gate) * up in bf16, [M, N]

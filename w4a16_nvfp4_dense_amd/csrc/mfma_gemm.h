@@ -52,9 +52,7 @@
 
 namespace ffn {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kMfmaWaves = 4;
 constexpr int kUnitCols = 64;  // reduction columns per unit
@@ -146,25 +144,6 @@ __device__ __forceinline__ int opaque_lane(int x)
 {
     asm volatile("" : "+v"(x));
     return x;
-}
-
-// Eight codes (one dword) times one block scale, as eight bf16 (exact).
-__device__ __forceinline__ bf16x8_t dequant8(uint32_t d, float sc)
-{
-    const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
-    const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
-    const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
-    const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
-    bf16x8_t w;
-    w[0] = static_cast<__bf16>(p0[0] * sc);
-    w[1] = static_cast<__bf16>(p0[1] * sc);
-    w[2] = static_cast<__bf16>(p1[0] * sc);
-    w[3] = static_cast<__bf16>(p1[1] * sc);
-    w[4] = static_cast<__bf16>(p2[0] * sc);
-    w[5] = static_cast<__bf16>(p2[1] * sc);
-    w[6] = static_cast<__bf16>(p3[0] * sc);
-    w[7] = static_cast<__bf16>(p3[1] * sc);
-    return w;
 }
 
 // Epilogue of one accumulator position. Accumulator (f, mt, v) of lane

@@ -16,6 +16,8 @@ namespace ffn {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Byte SEL of `word` holds two E2M1 codes; returns them as a bf16 pair with
 // element 0 = low nibble. The hardware conversion takes an fp32 scale of which
@@ -33,6 +35,25 @@ template <int SEL>
 __device__ __forceinline__ float e4m3_to_f32(uint32_t word)
 {
     return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(word), SEL);
+}
+
+// Eight codes (one dword) times one block scale, as eight bf16 (exact).
+__device__ __forceinline__ bf16x8_t dequant8(uint32_t d, float sc)
+{
+    const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+    const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+    const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+    const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+    bf16x8_t w;
+    w[0] = static_cast<__bf16>(p0[0] * sc);
+    w[1] = static_cast<__bf16>(p0[1] * sc);
+    w[2] = static_cast<__bf16>(p1[0] * sc);
+    w[3] = static_cast<__bf16>(p1[1] * sc);
+    w[4] = static_cast<__bf16>(p2[0] * sc);
+    w[5] = static_cast<__bf16>(p2[1] * sc);
+    w[6] = static_cast<__bf16>(p3[0] * sc);
+    w[7] = static_cast<__bf16>(p3[1] * sc);
+    return w;
 }
 
 // c + a.x*b.x + a.y*b.y with bf16 pairs and an fp32 accumulator.

@@ -1,0 +1,335 @@
+// smallm_gemm.h -- the small-batch matrix-core arm of the NVFP4 gated FFN
+// (9 <= M <= 16 token rows): the dual gate+up projection and the down
+// projection as skinny GEMMs on bf16 matrix cores, for the batch sizes between
+// the batched GEMV and the 128-row prefill tiles (dense_ffn.rs page, the
+// prefill GEMM dispatch by token count, whose small-M tiles exist because
+// padding a few tokens to a 64- or 128-row tile wastes most of it).
+//
+// Product. The weight rows are cut into tiles of 16 and the reduction into
+// units of 64 columns. For every tile the workgroup's 16 waves take 16
+// consecutive units at a time (a "round" of 1024 columns, wave q the q-th
+// unit) and compute D[m, r] = sum_c A[m, c] W[r, c] over them with
+// v_mfma_f32_16x16x32_bf16: activations as the A operand (rows = tokens), the
+// dequantised weights as the B operand (columns = weight rows). A lane's four
+// accumulators hold one weight row (lane % 16) and four tokens
+// (4 (lane / 16) + v). At the end of the tile the 16 waves add their
+// accumulators through LDS in wave order. At M <= 16 this MFMA shape reads each
+// weight once per 16 cycles, twice the rate of the 32x32x16 shape.
+//
+// Dequantisation. As in the prefill arm: FP4 pair -> fp32 pair (unit-scale
+// hardware conversion) times the E4M3 block scale, rounded to bf16, which is
+// exact (E2M1 x E4M3 has at most 6 significant bits), so the matrix core's fp32
+// accumulation is the only rounding of the product. scale2 multiplies in the
+// epilogue.
+//
+// Why this data movement. In the MFMA operand layout the 16 lanes of a quarter
+// wave hold 16 different rows, so a load straight into that layout touches 16
+// cache lines per quarter wave; measured, such loads (of the activations
+// above all) cost several times the whole weight stream. Here every global
+// load is coalesced (a quarter wave reads 256 or 64 contiguous bytes of one
+// to four rows) and the operand layout is made on chip:
+//   - activations: a wave's units are the same in every tile of the
+//     workgroup, so it loads its slice of the activations once (16 bytes per
+//     lane and load, four tokens per quarter wave) and moves it into operand
+//     layout with ds_bpermute; the slice stays in registers for all tiles;
+//   - weights: the workgroup streams each round's codes (16 rows x 512 bytes
+//     per projection) and scales (16 x 64 bytes) with direct global->LDS
+//     loads into a ring of kSmStages stages, kSmStages - 1 rounds ahead, and
+//     every wave reads its unit from LDS in operand layout.
+// K order inside a unit: MFMA step s (of 2) gives lane group g = lane / 16 the
+// columns 16 g + 8 s .. + 7, so a lane's codes of a unit are 8 contiguous
+// bytes and both steps use one scale.
+//
+// Work split. Workgroup w takes part w % P of the reduction (P consecutive
+// ranges of 256-column blocks; P > 1 only for the down projection, whose
+// reduction is long and whose tiles are few) and tiles [g T / G, (g + 1) T / G) with
+// g = w / P, T tiles and G = gridDim / P groups. With P = 1 the epilogue
+// writes finished outputs; with P > 1 it writes the part's fp32 sums and
+// smallm_reduce_kernel adds the parts in order. Nothing depends on the timing
+// of other workgroups, and a token row's result does not depend on the other
+// rows of the batch.
+#pragma once
+
+#include "kernels.h"
+#include "nvfp4_device.h"
+
+namespace ffn {
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kSmWaves = 16;                  // waves per workgroup
+constexpr int kSmRows = 16;                   // weight rows per tile
+constexpr int kSmUnit = 64;                   // reduction columns per wave and round
+constexpr int kSmRound = kSmWaves * kSmUnit;  // reduction columns per round
+constexpr int kSmMaxRounds = 5;               // rounds per tile and part (activations kept in registers)
+constexpr int kSmStages = 5;                  // LDS ring stages
+
+struct SmallParams {
+    const void *in0;  // bf16 [M, cols]
+    const uint8_t *codes0;
+    const uint8_t *scales0;
+    const uint8_t *codes1;
+    const uint8_t *scales1;
+    float s2_0;
+    float s2_1;
+    void *out0;
+    void *out1;
+    int M;       // token rows, 1 <= M <= 16
+    int rows;    // weight rows (output columns), a multiple of 16
+    int cols;    // reduction length, a multiple of 256
+    int parts;   // P
+    int groups;  // G: workgroups per part
+};
+
+// LDS of one ring stage: codes [NMAT][8 column blocks][16 rows][64 B], then
+// scales [NMAT][16 rows][64 B] (16-byte chunks and dwords swizzled by row).
+template <int NMAT>
+constexpr int sm_stage_bytes()
+{
+    return NMAT * kSmRows * (kSmRound / 2 + kSmRound / 16);
+}
+
+// LDS of the reduction area: [16 waves][NMAT] accumulator sets of 64 lanes x 16 B.
+template <int NMAT>
+constexpr int sm_red_bytes()
+{
+    return kSmWaves * NMAT * 1024;
+}
+
+// Ring, reduction area, and 256 bytes that the dummy scale loads write and
+// nothing reads.
+template <int NMAT>
+constexpr int sm_lds_bytes()
+{
+    return kSmStages * sm_stage_bytes<NMAT>() + sm_red_bytes<NMAT>() + 256;
+}
+
+template <int NMAT, int OUT, int NR>
+__global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallParams p)
+{
+    static_assert(NR >= 1 && NR <= kSmMaxRounds, "rounds");
+    constexpr int S = kSmStages;
+    constexpr int STAGE = sm_stage_bytes<NMAT>();
+    constexpr int CODES = NMAT * kSmRows * (kSmRound / 2);  // code bytes of a stage
+    static_assert(S >= 3 && 2 * (S - 2) < 64, "ring stages / vmcnt range");
+
+    extern __shared__ u32x4_t lds_raw[];
+    FFN_LDS uint8_t *lds = (FFN_LDS uint8_t *)lds_raw;
+    FFN_LDS f32x4_t *red = (FFN_LDS f32x4_t *)(lds + S * STAGE);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int q = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    const int cols = p.cols;
+    const int M = p.M;
+    const int T = p.rows / kSmRows;
+    const int P = p.parts;
+    const int part = blockIdx.x % P;
+    const int grp = blockIdx.x / P;
+    const int ta = grp * T / p.groups;
+    const int ntiles = (grp + 1) * T / p.groups - ta;
+    const int NU = cols / kSmUnit;
+    const int NB = NU / 4;                               // 256-column blocks (parts end on them)
+    const int ua = 4 * (part * NB / P);
+    const int nu = 4 * ((part + 1) * NB / P) - ua;       // units of this part
+    const int nrounds = (nu + kSmWaves - 1) / kSmWaves;  // <= NR
+    const int total = ntiles * nrounds;                  // rounds of this workgroup
+    const size_t row_codes = static_cast<size_t>(cols) / 2;
+    const size_t row_scales = static_cast<size_t>(cols) / 16;
+
+    // Loads of one round: codes (16 rows x 512 bytes per projection) and
+    // scales (16 x 64 bytes per projection), by every wave (NMAT = 2) or by
+    // waves 0-7 (NMAT = 1), each loading wave issuing exactly two.
+    //   codes: wave q takes column block b = q % 8 (64 bytes of each of the 16
+    //     rows) of projection q / 8; lane l loads row l / 4, 16-byte chunk
+    //     (l % 4) ^ (l / 16) of the block into LDS slot l, so a quarter wave
+    //     reads four whole 64-byte row pieces and the 8-byte operand reads
+    //     below (16 rows x 4 lanes) fall on all 64 banks once;
+    //   scales: wave q < 4 NMAT takes rows 4 (q % 4) .. + 3 of projection
+    //     q / 4; lane l loads row 4 (q % 4) + l / 16, dword (l % 16) ^ (q % 4)
+    //     of the row's 64 bytes into slot l (again conflict-free to read); the
+    //     other loading waves load a dummy dword (a valid one) into LDS that
+    //     is never read, so that every loading wave has the same number of
+    //     loads in flight.
+    // The per-lane row pointers are advanced a tile at a time, so a round
+    // costs the scalar unit (shared by the compute unit's 16 waves) only a few
+    // instructions. Addresses past the part (a short last round) are clamped
+    // inside the row and never used.
+    const bool loads = NMAT == 2 || q < 8;
+    const bool scale_wave = q < 4 * NMAT;
+    const int fc = NMAT == 2 ? (q >> 3) : 0;
+    const int fs = NMAT == 2 ? ((q >> 2) & 1) : 0;
+    const uint8_t *csrc = (fc == 0 ? p.codes0 : p.codes1) + static_cast<size_t>(ta * kSmRows + (lane >> 2)) * row_codes;
+    const uint8_t *ssrc =
+        (fs == 0 ? p.scales0 : p.scales1) + static_cast<size_t>(ta * kSmRows + 4 * (q & 3) + (lane >> 4)) * row_scales;
+    const uint32_t cchunk = 64 * (q & 7) + 16 * ((lane & 3) ^ (lane >> 4));
+    const uint32_t sdword = scale_wave ? 4 * ((lane & 15) ^ (q & 3)) : 0;
+    const uint32_t clast = static_cast<uint32_t>(row_codes) - 16;
+    const uint32_t slast = static_cast<uint32_t>(row_scales) - 4;
+    constexpr int DUMMY = S * STAGE + sm_red_bytes<NMAT>();
+    auto issue = [&](const uint8_t *cb, const uint8_t *sb, int i, int st) {
+        const uint32_t u0 = static_cast<uint32_t>(ua + kSmWaves * i);  // first unit of the round
+        FFN_LDS uint8_t *base = lds + st * STAGE;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(cb + min(u0 * (kSmUnit / 2) + cchunk, clast)),
+                                         reinterpret_cast<FFN_LDS void *>(base + q * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(sb + min(u0 * (kSmUnit / 16) + sdword, slast)),
+                                         reinterpret_cast<FFN_LDS void *>(scale_wave ? base + CODES + q * 256
+                                                                                     : lds + DUMMY),
+                                         4, 0, 0);
+    };
+    // Issue side of the ring: the next round to load (tile pointers, round
+    // index, stage). After the last round it loads the last round again into
+    // stages nothing reads (from L2), so that every wait below has the same
+    // number of rounds in flight.
+    const size_t tile_codes = kSmRows * row_codes;
+    const size_t tile_scales = kSmRows * row_scales;
+    int iss_i = 0, iss_st = 0, issued = 0;
+    auto issue_next = [&]() {
+        if (loads)
+            issue(csrc, ssrc, iss_i, iss_st);
+        if (++issued < total) {
+            if (++iss_i == nrounds) {
+                iss_i = 0;
+                csrc += tile_codes;
+                ssrc += tile_scales;
+            }
+        }
+        if (++iss_st == S)
+            iss_st = 0;
+    };
+
+    // The wave's activation slice, loaded coalesced (lane l: token l / 4,
+    // columns 16 (l % 4) + 8 s .. + 7 of the unit; a quarter wave reads four
+    // 128-byte token pieces) and moved to operand layout with ds_bpermute
+    // (lane (r, g) takes the piece of lane 4 r + g), for every round i (unit
+    // ua + 16 i + q) and step s.
+    u32x4_t xr[NR][2];
+    {
+        const uint16_t *X = static_cast<const uint16_t *>(p.in0);
+        const int tok = min(lane >> 2, M - 1);  // rows past the batch re-read the last one (never stored)
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int u = min(ua + kSmWaves * i + q, NU - 1);
+                xr[i][s] = *reinterpret_cast<const u32x4_t *>(X + static_cast<size_t>(tok) * cols + u * kSmUnit +
+                                                              16 * (lane & 3) + 8 * s);
+            }
+    }
+
+    // Ring prologue: rounds 0 .. S - 2.
+#pragma unroll
+    for (int k = 0; k < S - 1; ++k)
+        issue_next();
+
+    {
+        const int src = (4 * r + g) * 4;  // byte address of the source lane
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    xr[i][s][d] = static_cast<uint32_t>(
+                        __builtin_amdgcn_ds_bpermute(src, static_cast<int>(xr[i][s][d])));
+    }
+
+    f32x4_t acc[NMAT];
+#pragma unroll
+    for (int f = 0; f < NMAT; ++f)
+        acc[f] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const uint32_t scale_shift = 8 * g;  // both steps use scale byte g of the unit's 4
+    // this lane's operand bytes in a code block: row r, chunk 2 (q % 2) + g / 2
+    // (swizzled), 8-byte half g % 2; its scale dword: slot q ^ (r / 4)
+    const int code_off = (q >> 1) * 1024 + r * 64 + 16 * ((2 * (q & 1) + (g >> 1)) ^ (r >> 2)) + 8 * (g & 1);
+    const int scale_off = CODES + r * 64 + 4 * (q ^ (r >> 2));
+    int st = 0;  // ring stage of the round being multiplied
+    for (int tt = 0; tt < ntiles; ++tt) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            if (i >= nrounds)
+                break;
+            // round v has landed in every wave (S - 2 later rounds of this
+            // wave's loads still in flight); the stage of round v - 1 is free
+            if (loads)
+                wait_vmcnt<2 * (S - 2)>();
+            lds_barrier();
+            issue_next();
+            if (kSmWaves * i + q < nu) {
+                const FFN_LDS uint8_t *base = lds + st * STAGE;
+#pragma unroll
+                for (int f = 0; f < NMAT; ++f) {
+                    const u32x2_t c = *reinterpret_cast<const FFN_LDS u32x2_t *>(base + f * 8192 + code_off);
+                    const float sc = e4m3_to_f32<0>(
+                        *reinterpret_cast<const FFN_LDS uint32_t *>(base + f * 1024 + scale_off) >> scale_shift);
+                    const bf16x8_t b0 = dequant8(c[0], sc);
+                    const bf16x8_t b1 = dequant8(c[1], sc);
+                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[i][0]), b0, acc[f],
+                                                                    0, 0, 0);
+                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[i][1]), b1, acc[f],
+                                                                    0, 0, 0);
+                }
+            }
+            if (++st == S)
+                st = 0;
+        }
+
+        // Tile done: add the 16 waves' accumulators in wave order.
+#pragma unroll
+        for (int f = 0; f < NMAT; ++f) {
+            red[(q * NMAT + f) * 64 + lane] = acc[f];
+            acc[f] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        lds_barrier();
+        if (tid < 256) {
+            // output (token m, row rr) of the tile: accumulator v = m % 4 of lane 16 (m / 4) + rr
+            const int m = tid >> 4;
+            const int rr = tid & 15;
+            const int al = 16 * (m >> 2) + rr;
+            const int av = m & 3;
+            const FFN_LDS float *redf = reinterpret_cast<const FFN_LDS float *>(red);
+            float y[NMAT];
+#pragma unroll
+            for (int f = 0; f < NMAT; ++f) {
+                float a = redf[(f * 64 + al) * 4 + av];
+#pragma unroll
+                for (int w = 1; w < kSmWaves; ++w)
+                    a += redf[((w * NMAT + f) * 64 + al) * 4 + av];
+                y[f] = a;
+            }
+            if (m < M) {
+                const int row = (ta + tt) * kSmRows + rr;
+                const size_t o = static_cast<size_t>(m) * p.rows + row;
+                if constexpr (OUT == OUT_F32_PAIR) {
+                    static_cast<float *>(p.out0)[o] = y[0] * p.s2_0;
+                    static_cast<float *>(p.out1)[o] = y[NMAT - 1] * p.s2_1;
+                } else if constexpr (OUT == OUT_H_SILU || OUT == OUT_H_GELU) {
+                    constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
+                    static_cast<uint16_t *>(p.out0)[o] = to_bf16_bits(gate_act<A>(y[0] * p.s2_0) * (y[NMAT - 1] * p.s2_1));
+                } else if constexpr (OUT == OUT_BF16) {
+                    static_cast<uint16_t *>(p.out0)[o] = to_bf16_bits(y[0] * p.s2_0);
+                } else {
+                    static_cast<float *>(p.out0)[static_cast<size_t>(part) * M * p.rows + o] = y[0];
+                }
+            }
+        }
+    }
+}
+
+// out[m, j] = bf16(s2 * sum_p part[p, m, j]), the parts added in order.
+__global__ __launch_bounds__(256) void smallm_reduce_kernel(const float *part, int parts, size_t n, float s2,
+                                                            uint16_t *out)
+{
+    const size_t e = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (e >= n)
+        return;
+    float a = part[e];
+    for (int k = 1; k < parts; ++k)
+        a += part[static_cast<size_t>(k) * n + e];
+    out[e] = to_bf16_bits(a * s2);
+}
+
+}  // namespace ffn
