@@ -61,7 +61,8 @@ def test_smallbatch_workspace():
     projection's reduction is split, its fp32 partial sums."""
     r256 = lambda b: (b + 255) // 256 * 256
     assert ffn.workspace_bytes(9, 256, 512) == r256(9 * 512 * 2)
-    # N = 17408: 272 units of 64 columns in parts of at most 80: 4 parts
+    # N = 17408: 68 blocks of 256 columns in parts of at most 20: 4 parts,
+    # 64 groups of 5 tiles
     assert ffn.workspace_bytes(16, 5120, 17408) == r256(16 * 17408 * 2) + 4 * 16 * 5120 * 4
     # M = 17, K above 5120, or K or N not a multiple of 256: the 128-row arm
     # with its partial slots

@@ -13,7 +13,8 @@
 // dequantised weights as the B operand (columns = weight rows). A lane's four
 // accumulators hold one weight row (lane % 16) and four tokens
 // (4 (lane / 16) + v). At the end of the tile the 16 waves add their
-// accumulators through LDS in wave order. At M <= 16 this MFMA shape reads each
+// accumulators through LDS in a fixed order (waves 0-7 and 8-15 in wave
+// order, then the two halves). At M <= 16 this MFMA shape reads each
 // weight once per 16 cycles, twice the rate of the 32x32x16 shape.
 //
 // Dequantisation. As in the prefill arm: FP4 pair -> fp32 pair (unit-scale
@@ -45,9 +46,11 @@
 // reduction is long and whose tiles are few) and tiles [g T / G, (g + 1) T / G) with
 // g = w / P, T tiles and G = gridDim / P groups. With P = 1 the epilogue
 // writes finished outputs; with P > 1 it writes the part's fp32 sums and
-// smallm_reduce_kernel adds the parts in order. Nothing depends on the timing
-// of other workgroups, and a token row's result does not depend on the other
-// rows of the batch.
+// smallm_reduce_kernel adds the parts in order. (Adding them in the kernel,
+// by the last of a group's workgroups to finish, measured no faster: the
+// exchange between XCDs costs the same round trips as a second launch.) No
+// workgroup waits for another, the order of every sum is fixed, and a token
+// row's result does not depend on the other rows of the batch.
 #pragma once
 
 #include "kernels.h"
@@ -81,27 +84,29 @@ struct SmallParams {
     int groups;  // G: workgroups per part
 };
 
-// LDS of one ring stage: codes [NMAT][8 column blocks][16 rows][64 B], then
-// scales [NMAT][16 rows][64 B] (16-byte chunks and dwords swizzled by row).
+// LDS of one ring stage: codes [NMAT][2 row halves][4 column blocks][8 rows]
+// [128 B], then scales [NMAT][16 rows][64 B] (16-byte chunks and dwords
+// swizzled by row).
 template <int NMAT>
 constexpr int sm_stage_bytes()
 {
     return NMAT * kSmRows * (kSmRound / 2 + kSmRound / 16);
 }
 
-// LDS of the reduction area: [16 waves][NMAT] accumulator sets of 64 lanes x 16 B.
+// LDS of the reduction area: [16 waves][NMAT] accumulator sets of 64 lanes x
+// 16 B, then [NMAT][2][256] half sums.
 template <int NMAT>
 constexpr int sm_red_bytes()
 {
-    return kSmWaves * NMAT * 1024;
+    return kSmWaves * NMAT * 1024 + NMAT * 2 * 256 * 4;
 }
 
-// Ring, reduction area, and 256 bytes that the dummy scale loads write and
-// nothing reads.
+// Ring, reduction area (the waves' accumulators and the two half sums), and
+// 1280 bytes that the dummy loads write and nothing reads.
 template <int NMAT>
 constexpr int sm_lds_bytes()
 {
-    return kSmStages * sm_stage_bytes<NMAT>() + sm_red_bytes<NMAT>() + 256;
+    return kSmStages * sm_stage_bytes<NMAT>() + sm_red_bytes<NMAT>() + 1280;
 }
 
 template <int NMAT, int OUT, int NR>
@@ -140,43 +145,46 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
     const size_t row_scales = static_cast<size_t>(cols) / 16;
 
     // Loads of one round: codes (16 rows x 512 bytes per projection) and
-    // scales (16 x 64 bytes per projection), by every wave (NMAT = 2) or by
-    // waves 0-7 (NMAT = 1), each loading wave issuing exactly two.
-    //   codes: wave q takes column block b = q % 8 (64 bytes of each of the 16
-    //     rows) of projection q / 8; lane l loads row l / 4, 16-byte chunk
-    //     (l % 4) ^ (l / 16) of the block into LDS slot l, so a quarter wave
-    //     reads four whole 64-byte row pieces and the 8-byte operand reads
-    //     below (16 rows x 4 lanes) fall on all 64 banks once;
+    // scales (16 x 64 bytes per projection). Every wave issues exactly two
+    // (so the number of loads in flight is the same in every wave):
+    //   codes: wave q < 8 NMAT takes projection q / 8, rows 8 ((q / 4) % 2) ..
+    //     + 7 and column block q % 4 (128 bytes of each row); lane l loads
+    //     row 8 ((q / 4) % 2) + l / 8, 16-byte chunk (l % 8) ^ ((row / 2) % 8)
+    //     of the block into LDS slot l, so a quarter wave reads two whole
+    //     cache lines and the 8-byte operand reads below (16 rows x 4 lanes)
+    //     fall on all 64 banks once;
     //   scales: wave q < 4 NMAT takes rows 4 (q % 4) .. + 3 of projection
     //     q / 4; lane l loads row 4 (q % 4) + l / 16, dword (l % 16) ^ (q % 4)
-    //     of the row's 64 bytes into slot l (again conflict-free to read); the
-    //     other loading waves load a dummy dword (a valid one) into LDS that
-    //     is never read, so that every loading wave has the same number of
-    //     loads in flight.
+    //     of the row's 64 bytes into slot l (again conflict-free to read);
+    //   the other waves load dummies (valid addresses) into LDS that is never
+    //     read.
     // The per-lane row pointers are advanced a tile at a time, so a round
     // costs the scalar unit (shared by the compute unit's 16 waves) only a few
     // instructions. Addresses past the part (a short last round) are clamped
     // inside the row and never used.
-    const bool loads = NMAT == 2 || q < 8;
+    const bool code_wave = q < 8 * NMAT;
     const bool scale_wave = q < 4 * NMAT;
-    const int fc = NMAT == 2 ? (q >> 3) : 0;
+    const int qc = q & (8 * NMAT - 1);  // dummy code waves load what wave qc loads
+    const int fc = NMAT == 2 ? (qc >> 3) : 0;
     const int fs = NMAT == 2 ? ((q >> 2) & 1) : 0;
-    const uint8_t *csrc = (fc == 0 ? p.codes0 : p.codes1) + static_cast<size_t>(ta * kSmRows + (lane >> 2)) * row_codes;
+    const int crow = 8 * ((qc >> 2) & 1) + (lane >> 3);  // row of the tile this lane's code chunk is in
+    const uint8_t *csrc = (fc == 0 ? p.codes0 : p.codes1) + static_cast<size_t>(ta * kSmRows + crow) * row_codes;
     const uint8_t *ssrc =
         (fs == 0 ? p.scales0 : p.scales1) + static_cast<size_t>(ta * kSmRows + 4 * (q & 3) + (lane >> 4)) * row_scales;
-    const uint32_t cchunk = 64 * (q & 7) + 16 * ((lane & 3) ^ (lane >> 4));
+    const uint32_t cchunk = 128 * (qc & 3) + 16 * ((lane & 7) ^ ((crow >> 1) & 7));
     const uint32_t sdword = scale_wave ? 4 * ((lane & 15) ^ (q & 3)) : 0;
     const uint32_t clast = static_cast<uint32_t>(row_codes) - 16;
     const uint32_t slast = static_cast<uint32_t>(row_scales) - 4;
-    constexpr int DUMMY = S * STAGE + sm_red_bytes<NMAT>();
+    constexpr int DUMMY = S * STAGE + sm_red_bytes<NMAT>();  // 1 KB + 256 B never read
     auto issue = [&](const uint8_t *cb, const uint8_t *sb, int i, int st) {
         const uint32_t u0 = static_cast<uint32_t>(ua + kSmWaves * i);  // first unit of the round
         FFN_LDS uint8_t *base = lds + st * STAGE;
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(cb + min(u0 * (kSmUnit / 2) + cchunk, clast)),
-                                         reinterpret_cast<FFN_LDS void *>(base + q * 1024), 16, 0, 0);
+                                         reinterpret_cast<FFN_LDS void *>(code_wave ? base + q * 1024 : lds + DUMMY),
+                                         16, 0, 0);
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(sb + min(u0 * (kSmUnit / 16) + sdword, slast)),
                                          reinterpret_cast<FFN_LDS void *>(scale_wave ? base + CODES + q * 256
-                                                                                     : lds + DUMMY),
+                                                                                     : lds + DUMMY + 1024),
                                          4, 0, 0);
     };
     // Issue side of the ring: the next round to load (tile pointers, round
@@ -187,8 +195,7 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
     const size_t tile_scales = kSmRows * row_scales;
     int iss_i = 0, iss_st = 0, issued = 0;
     auto issue_next = [&]() {
-        if (loads)
-            issue(csrc, ssrc, iss_i, iss_st);
+        issue(csrc, ssrc, iss_i, iss_st);
         if (++issued < total) {
             if (++iss_i == nrounds) {
                 iss_i = 0;
@@ -205,6 +212,12 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
     // 128-byte token pieces) and moved to operand layout with ds_bpermute
     // (lane (r, g) takes the piece of lane 4 r + g), for every round i (unit
     // ua + 16 i + q) and step s.
+    // Ring prologue, round 0 first: the compiler waits for every load in
+    // flight before the ds_bpermute below (it cannot tell that the
+    // permutation reads no LDS that a direct load writes), so the later
+    // prologue rounds are issued after it; round 0 is needed first anyway.
+    issue_next();
+
     u32x4_t xr[NR][2];
     {
         const uint16_t *X = static_cast<const uint16_t *>(p.in0);
@@ -219,11 +232,6 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
             }
     }
 
-    // Ring prologue: rounds 0 .. S - 2.
-#pragma unroll
-    for (int k = 0; k < S - 1; ++k)
-        issue_next();
-
     {
         const int src = (4 * r + g) * 4;  // byte address of the source lane
 #pragma unroll
@@ -236,15 +244,22 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
                         __builtin_amdgcn_ds_bpermute(src, static_cast<int>(xr[i][s][d])));
     }
 
+#pragma unroll
+    for (int k = 1; k < S - 1; ++k)
+        issue_next();
+
     f32x4_t acc[NMAT];
 #pragma unroll
     for (int f = 0; f < NMAT; ++f)
         acc[f] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     const uint32_t scale_shift = 8 * g;  // both steps use scale byte g of the unit's 4
-    // this lane's operand bytes in a code block: row r, chunk 2 (q % 2) + g / 2
-    // (swizzled), 8-byte half g % 2; its scale dword: slot q ^ (r / 4)
-    const int code_off = (q >> 1) * 1024 + r * 64 + 16 * ((2 * (q & 1) + (g >> 1)) ^ (r >> 2)) + 8 * (g & 1);
+    // this lane's operand bytes: unit q is bytes 32 (q % 4) .. + 31 of column
+    // block q / 4; the lane's 8 bytes are chunk 2 (q % 4) + g / 2 (swizzled)
+    // and half g % 2 of row r, in the load of rows 8 (r / 8) .. + 7; its scale
+    // dword is slot q ^ (r / 4)
+    const int code_off = (4 * (r >> 3) + (q >> 2)) * 1024 + (r & 7) * 128 +
+                         16 * ((2 * (q & 3) + (g >> 1)) ^ ((r >> 1) & 7)) + 8 * (g & 1);
     const int scale_off = CODES + r * 64 + 4 * (q ^ (r >> 2));
     int st = 0;  // ring stage of the round being multiplied
     for (int tt = 0; tt < ntiles; ++tt) {
@@ -254,8 +269,7 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
                 break;
             // round v has landed in every wave (S - 2 later rounds of this
             // wave's loads still in flight); the stage of round v - 1 is free
-            if (loads)
-                wait_vmcnt<2 * (S - 2)>();
+            wait_vmcnt<2 * (S - 2)>();
             lds_barrier();
             issue_next();
             if (kSmWaves * i + q < nu) {
@@ -277,29 +291,38 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
                 st = 0;
         }
 
-        // Tile done: add the 16 waves' accumulators in wave order.
+        // Tile done: add the 16 waves' accumulators, waves 0-7 and 8-15 in
+        // order by separate threads, then the two halves.
 #pragma unroll
         for (int f = 0; f < NMAT; ++f) {
             red[(q * NMAT + f) * 64 + lane] = acc[f];
             acc[f] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         }
         lds_barrier();
+        const FFN_LDS float *redf = reinterpret_cast<const FFN_LDS float *>(red);
+        FFN_LDS float *half = reinterpret_cast<FFN_LDS float *>(red + kSmWaves * NMAT * 64);
+        if (tid < NMAT * 512) {
+            // job (f, h, o): output o = 16 m + rr (accumulator m % 4 of lane
+            // 16 (m / 4) + rr), waves 8 h .. 8 h + 7 of projection f
+            const int o = tid & 255;
+            const int h = (tid >> 8) & 1;
+            const int f = tid >> 9;
+            const int m = o >> 4;
+            const int at = (16 * (m >> 2) + (o & 15)) * 4 + (m & 3);
+            float a = redf[((8 * h) * NMAT + f) * 256 + at];
+#pragma unroll
+            for (int w = 1; w < 8; ++w)
+                a += redf[((8 * h + w) * NMAT + f) * 256 + at];
+            half[(f * 2 + h) * 256 + o] = a;
+        }
+        lds_barrier();
         if (tid < 256) {
-            // output (token m, row rr) of the tile: accumulator v = m % 4 of lane 16 (m / 4) + rr
             const int m = tid >> 4;
             const int rr = tid & 15;
-            const int al = 16 * (m >> 2) + rr;
-            const int av = m & 3;
-            const FFN_LDS float *redf = reinterpret_cast<const FFN_LDS float *>(red);
             float y[NMAT];
 #pragma unroll
-            for (int f = 0; f < NMAT; ++f) {
-                float a = redf[(f * 64 + al) * 4 + av];
-#pragma unroll
-                for (int w = 1; w < kSmWaves; ++w)
-                    a += redf[((w * NMAT + f) * 64 + al) * 4 + av];
-                y[f] = a;
-            }
+            for (int f = 0; f < NMAT; ++f)
+                y[f] = half[(f * 2) * 256 + tid] + half[(f * 2 + 1) * 256 + tid];
             if (m < M) {
                 const int row = (ta + tt) * kSmRows + rr;
                 const size_t o = static_cast<size_t>(m) * p.rows + row;
@@ -317,6 +340,7 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
             }
         }
     }
+
 }
 
 // out[m, j] = bf16(s2 * sum_p part[p, m, j]), the parts added in order.
