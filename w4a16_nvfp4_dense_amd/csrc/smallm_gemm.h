@@ -65,7 +65,7 @@ constexpr int kSmRows = 16;                   // weight rows per tile
 constexpr int kSmUnit = 64;                   // reduction columns per wave and round
 constexpr int kSmRound = kSmWaves * kSmUnit;  // reduction columns per round
 constexpr int kSmMaxRounds = 5;               // rounds per tile and part (activations kept in registers)
-constexpr int kSmStages = 5;                  // LDS ring stages
+constexpr int kSmStages = 3;                  // LDS ring stages (deeper measured slower: the arm is bound by its arithmetic, not by load latency)
 
 struct SmallParams {
     const void *in0;  // bf16 [M, cols]
