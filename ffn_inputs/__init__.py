@@ -188,6 +188,116 @@ def make_format_coverage(act: int = ACT_SILU, seed: int = 99, M: int = 1) -> Ffn
                    x_bits=x_bits, gate=gate, up=up, down=down)
 
 
+@dataclasses.dataclass
+class Fp8Weight:
+    """One block-scaled FP8 weight of logical shape [rows, cols] (the format
+    the qwen35_dense.rs page describes for native FP8 checkpoints):
+
+    * ``codes`` uint8 ``[rows, cols]``: one E4M3FN byte per element, row-major;
+    * ``block_scale`` float32 ``[ceil(rows/128), ceil(cols/128)]``: one fp32
+      multiplier per 128 x 128 block, row-major.
+    """
+
+    codes: np.ndarray        # uint8 [rows, cols]
+    block_scale: np.ndarray  # float32 [ceil(rows/128), ceil(cols/128)]
+
+    @property
+    def rows(self) -> int:
+        return int(self.codes.shape[0])
+
+    @property
+    def cols(self) -> int:
+        return int(self.codes.shape[1])
+
+    @property
+    def nbytes(self) -> int:
+        return int(self.codes.nbytes + self.block_scale.nbytes)
+
+
+@dataclasses.dataclass
+class Fp8FfnCase:
+    """Inputs of one gated FFN over FP8 weights (same shapes as FfnCase)."""
+
+    name: str
+    M: int
+    K: int
+    N: int
+    act: int
+    x_bits: np.ndarray  # uint16 [M, K], bf16 bit patterns
+    gate: Fp8Weight     # [N, K]
+    up: Fp8Weight       # [N, K]
+    down: Fp8Weight     # [K, N]
+
+    def with_x(self, x_bits: np.ndarray, name: Optional[str] = None) -> "Fp8FfnCase":
+        x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        return dataclasses.replace(self, x_bits=x_bits, M=int(x_bits.shape[0]),
+                                   name=name or self.name)
+
+    @property
+    def weight_bytes(self) -> int:
+        return self.gate.nbytes + self.up.nbytes + self.down.nbytes
+
+
+def _draw_fp8_weight(rng: np.random.Generator, rows: int, cols: int, mags: int) -> Fp8Weight:
+    """Codes: uniform over the finite E4M3FN bytes whose magnitude field
+    (low 7 bits) is below ``mags`` (a random sign, no NaN); block scales: fp32
+    uniform on [2**-10, 2**-9), so not powers of two."""
+    sign = rng.integers(0, 2, size=(rows, cols), dtype=np.uint8) << 7
+    mag = rng.integers(0, mags, size=(rows, cols), dtype=np.uint8)
+    codes = (sign | mag).astype(np.uint8)
+    grid = ((rows + 127) // 128, (cols + 127) // 128)
+    bs = (rng.uniform(1.0, 2.0, size=grid) * 2.0 ** -10).astype(np.float32)
+    return Fp8Weight(codes=codes, block_scale=bs)
+
+
+# Magnitude fields 0..0x77 span +-[0, 240]: every exponent, so every decode
+# path, appears, while values stay in the range block-scaled checkpoints use
+# (their per-block absmax maps to at most 448 = field 0x7E).
+FP8_RECIPE_MAGS = 0x78
+
+
+def make_fp8_ffn(name: str, M: int, K: int, N: int, act: int = ACT_SILU, sigma: float = 1.0,
+                 seed: int = 11, x_seed: Optional[int] = None, mags: int = FP8_RECIPE_MAGS) -> Fp8FfnCase:
+    """Draw one FP8 case: gate, up, down codes and block scales in that order,
+    then x (from ``x_seed`` when given). Any K, N >= 1 are allowed here; the
+    library states its own shape limits."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    gate = _draw_fp8_weight(rng, N, K, mags)
+    up = _draw_fp8_weight(rng, N, K, mags)
+    down = _draw_fp8_weight(rng, K, N, mags)
+    if x_seed is not None:
+        rng = np.random.Generator(np.random.PCG64(x_seed))
+    x_bits = _draw_x(rng, M, K, sigma)
+    return Fp8FfnCase(name=name, M=M, K=K, N=N, act=act, x_bits=x_bits, gate=gate, up=up, down=down)
+
+
+def make_fp8_config(M: int = 1, act: int = ACT_SILU) -> Fp8FfnCase:
+    """The decode workload of the dense layer with FP8 weights: K=5120,
+    N=17408 (the shape of the NVFP4 decode workload), ``M`` rows."""
+    return make_fp8_ffn(f"fp8_decode_{ACT_NAMES[act]}_m{M}", M, 5120, 17408, act, 1.0,
+                        SEED_BASE + 50, x_seed=SEED_BASE + 51 + 100 * M)
+
+
+def make_fp8_format_coverage(act: int = ACT_SILU, seed: int = 98, M: int = 1) -> Fp8FfnCase:
+    """Every finite E4M3FN byte (254 of them) appears in every weight, and the
+    block grids are ragged (K=384+64, N=256+32). Block scales as in the recipe."""
+    K, N = 448, 288
+    rng = np.random.Generator(np.random.PCG64(seed))
+    fin = finite_e4m3_bytes()
+
+    def weight(rows: int, cols: int) -> Fp8Weight:
+        codes = np.resize(rng.permutation(fin), rows * cols)
+        rng.shuffle(codes)
+        grid = ((rows + 127) // 128, (cols + 127) // 128)
+        bs = (rng.uniform(1.0, 2.0, size=grid) * 2.0 ** -10).astype(np.float32)
+        return Fp8Weight(codes=codes.reshape(rows, cols).astype(np.uint8), block_scale=bs)
+
+    gate, up, down = weight(N, K), weight(N, K), weight(K, N)
+    x_bits = _draw_x(rng, M, K, 1.0)
+    return Fp8FfnCase(name=f"fp8_format_coverage_{ACT_NAMES[act]}_m{M}", M=M, K=K, N=N, act=act,
+                      x_bits=x_bits, gate=gate, up=up, down=down)
+
+
 def make_dense_bf16(rows: int, cols: int, seed: int, spread: float = 4.0) -> np.ndarray:
     """Seeded dense bf16 weight bits [rows, cols] (the quantiser's input): a
     normal draw times a per-row factor e^u, u uniform on [-spread, spread / 2]

@@ -82,6 +82,14 @@ class Oracle:
         lib.oracle_e4m3_encode.argtypes = [_F]
         lib.oracle_quantize.restype = None
         lib.oracle_quantize.argtypes = [_P, _I, _I, _P, _P, _P]
+        lib.oracle_fp8_dequant.restype = None
+        lib.oracle_fp8_dequant.argtypes = [_P, _P, _I, _I, _P]
+        lib.oracle_fp8_linear_f64.restype = None
+        lib.oracle_fp8_linear_f64.argtypes = [_P, _I, _I, _I, _P, _P, _P]
+        lib.oracle_fp8_dual.restype = _I
+        lib.oracle_fp8_dual.argtypes = [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P]
+        lib.oracle_fp8_ffn.restype = _I
+        lib.oracle_fp8_ffn.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
         self.lib = lib
         self.path = lib_path
 
@@ -195,6 +203,56 @@ class Oracle:
         return codes, scales, float(s2[0])
 
 
+    # ------------------------------------------------------------ FP8
+    # An ffn_inputs.Fp8Weight: E4M3 bytes [rows, cols] and an fp32 block-scale
+    # grid [ceil(rows/128), ceil(cols/128)].
+
+    def fp8_dequant(self, w) -> np.ndarray:
+        codes = _c(w.codes, np.uint8)
+        bs = _c(w.block_scale, np.float32)
+        rows, cols = codes.shape
+        out = np.empty((rows, cols), dtype=np.float64)
+        self.lib.oracle_fp8_dequant(_ptr(codes), _ptr(bs), rows, cols, _ptr(out))
+        return out
+
+    def fp8_linear(self, a: np.ndarray, w) -> np.ndarray:
+        a = _c(a, np.float64)
+        codes = _c(w.codes, np.uint8)
+        bs = _c(w.block_scale, np.float32)
+        M, cols = a.shape
+        rows = codes.shape[0]
+        assert codes.shape[1] == cols
+        y = np.empty((M, rows), dtype=np.float64)
+        self.lib.oracle_fp8_linear_f64(_ptr(a), M, cols, rows, _ptr(codes), _ptr(bs), _ptr(y))
+        return y
+
+    def fp8_dual(self, case) -> Tuple[np.ndarray, np.ndarray]:
+        x = _c(case.x_bits, np.uint16)
+        g, u = case.gate, case.up
+        gate = np.empty((case.M, case.N), dtype=np.float64)
+        up = np.empty((case.M, case.N), dtype=np.float64)
+        gw, uw = _c(g.codes, np.uint8), _c(u.codes, np.uint8)
+        gb, ub = _c(g.block_scale, np.float32), _c(u.block_scale, np.float32)
+        rc = self.lib.oracle_fp8_dual(_ptr(x), case.M, case.K, case.N, _ptr(gw), _ptr(gb), _ptr(uw), _ptr(ub),
+                                      _ptr(gate), _ptr(up))
+        if rc != 0:
+            raise MemoryError("oracle_fp8_dual")
+        return gate, up
+
+    def fp8_ffn(self, case, rows: Optional[np.ndarray] = None) -> np.ndarray:
+        x = _c(case.x_bits if rows is None else case.x_bits[np.asarray(rows)], np.uint16)
+        M = x.shape[0]
+        g, u, d = case.gate, case.up, case.down
+        ws = [_c(t.codes, np.uint8) for t in (g, u, d)]
+        bs = [_c(t.block_scale, np.float32) for t in (g, u, d)]
+        out = np.empty((M, case.K), dtype=np.float64)
+        rc = self.lib.oracle_fp8_ffn(_ptr(x), M, case.K, case.N, int(case.act), _ptr(ws[0]), _ptr(bs[0]),
+                                     _ptr(ws[1]), _ptr(bs[1]), _ptr(ws[2]), _ptr(bs[2]), _ptr(out))
+        if rc != 0:
+            raise MemoryError("oracle_fp8_ffn")
+        return out
+
+
 _default: Optional[Oracle] = None
 
 
@@ -251,6 +309,22 @@ def e4m3_encode(s: float) -> int:
 
 def quantize(w_bits: np.ndarray):
     return default().quantize(w_bits)
+
+
+def fp8_dequant(w) -> np.ndarray:
+    return default().fp8_dequant(w)
+
+
+def fp8_linear(a: np.ndarray, w) -> np.ndarray:
+    return default().fp8_linear(a, w)
+
+
+def fp8_dual(case):
+    return default().fp8_dual(case)
+
+
+def fp8_ffn(case, rows=None) -> np.ndarray:
+    return default().fp8_ffn(case, rows)
 
 
 def ulp_bf16(v: np.ndarray) -> np.ndarray:

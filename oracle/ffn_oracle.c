@@ -28,6 +28,10 @@
  *  - qwen35_dense.rs page, weight loader: a dense BF16 weight is turned into
  *    NVFP4 on the GPU by a global-absmax pass followed by a quantise pass
  *    (the quantiser below; its scale rule is a reading, the pages give none).
+ *  - qwen35_dense.rs page, proj_is_fp8_any_scale doc comment: a native FP8
+ *    weight [N, K] is E4M3 bytes with an FP32 block-scale grid
+ *    [ceil(N/128), ceil(K/128)] that the kernels index as
+ *    block_scale[n/128, k/128] (the FP8 functions below).
  *
  * Readings taken where the pages are silent (each is listed in the design
  * notes): the even column of a byte is its low nibble; GELU is the tanh form;
@@ -334,4 +338,79 @@ void oracle_quantize(const uint16_t *w_bits, int rows, int cols, uint8_t *codes,
         }
     }
     *scale2_out = scale2;
+}
+
+/* ------------------------------------------------------------------ FP8
+ * An FP8 weight of logical shape [rows, cols]: E4M3FN bytes, row-major
+ * [rows, cols], and an fp32 block-scale grid [ceil(rows/128), ceil(cols/128)],
+ * row-major; element (r, c) = e4m3(w[r, c]) * block_scale[r/128, c/128]
+ * (qwen35_dense.rs page, proj_is_fp8_any_scale doc comment). There is no
+ * per-tensor multiplier. NaN bytes propagate. */
+static double fp8_weight_at(const double e4m3[256], const uint8_t *w, const float *bs,
+                            int cols, int r, int c)
+{
+    int bcols = (cols + 127) / 128;
+    return e4m3[w[(size_t)r * (size_t)cols + (size_t)c]] * (double)bs[(size_t)(r / 128) * (size_t)bcols + (size_t)(c / 128)];
+}
+
+void oracle_fp8_dequant(const uint8_t *w, const float *bs, int rows, int cols, double *w_out)
+{
+    double e2m1[16], e4m3[256];
+    build_tables(e2m1, e4m3);
+    for (int r = 0; r < rows; ++r)
+        for (int c = 0; c < cols; ++c)
+            w_out[(size_t)r * cols + c] = fp8_weight_at(e4m3, w, bs, cols, r, c);
+}
+
+/* y[m, r] = sum_c W[r, c] * a[m, c] over a [rows, cols] FP8 weight. */
+void oracle_fp8_linear_f64(const double *a, int M, int cols, int rows,
+                           const uint8_t *w, const float *bs, double *y)
+{
+    double e2m1[16], e4m3[256];
+    build_tables(e2m1, e4m3);
+    long total = (long)M * rows;
+#pragma omp parallel for schedule(static)
+    for (long idx = 0; idx < total; ++idx) {
+        int m = (int)(idx / rows);
+        int r = (int)(idx % rows);
+        double acc = 0.0;
+        for (int c = 0; c < cols; ++c)
+            acc += fp8_weight_at(e4m3, w, bs, cols, r, c) * a[(size_t)m * cols + c];
+        y[idx] = acc;
+    }
+}
+
+/* gate = W_g x, up = W_u x with FP8 W_g, W_u [N, K] and bf16 x [M, K]. */
+int oracle_fp8_dual(const uint16_t *x_bits, int M, int K, int N,
+                    const uint8_t *gw, const float *gbs, const uint8_t *uw, const float *ubs,
+                    double *gate, double *up)
+{
+    double *x = (double *)malloc(sizeof(double) * (size_t)M * (size_t)K);
+    if (!x)
+        return -1;
+    for (size_t i = 0; i < (size_t)M * (size_t)K; ++i)
+        x[i] = oracle_bf16_value(x_bits[i]);
+    oracle_fp8_linear_f64(x, M, K, N, gw, gbs, gate);
+    oracle_fp8_linear_f64(x, M, K, N, uw, ubs, up);
+    free(x);
+    return 0;
+}
+
+/* The whole gated FFN with FP8 weights (W_d of shape [K, N]), in double. */
+int oracle_fp8_ffn(const uint16_t *x_bits, int M, int K, int N, int act,
+                   const uint8_t *gw, const float *gbs, const uint8_t *uw, const float *ubs,
+                   const uint8_t *dw, const float *dbs, double *out)
+{
+    size_t mn = (size_t)M * (size_t)N;
+    double *gate = (double *)malloc(sizeof(double) * mn);
+    double *up = (double *)malloc(sizeof(double) * mn);
+    int rc = -1;
+    if (gate && up && oracle_fp8_dual(x_bits, M, K, N, gw, gbs, uw, ubs, gate, up) == 0) {
+        oracle_gated_act(act, gate, up, mn, gate); /* h overwrites gate */
+        oracle_fp8_linear_f64(gate, M, N, K, dw, dbs, out);
+        rc = 0;
+    }
+    free(gate);
+    free(up);
+    return rc;
 }

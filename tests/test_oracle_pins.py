@@ -410,12 +410,138 @@ def pin_quantize_error_bound(orc):
     assert np.all(scales < 0x7F)
 
 
+# ------------------------------------------------------------ FP8 weights
+
+
+def _torch_e4m3(codes):
+    """E4M3FN bytes decoded by torch's float8 type (a route independent of the
+    oracle's table)."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def _fp8_dense(w):
+    """Dense float64 [rows, cols]: torch-decoded codes times the block grid
+    expanded with numpy (block (i, j) covers rows 128i.., columns 128j..)."""
+    grid = np.repeat(np.repeat(w.block_scale.astype(np.float64), 128, axis=0), 128, axis=1)
+    return _torch_e4m3(w.codes) * grid[: w.rows, : w.cols]
+
+
+def _fp8_one_hot(rows, cols, pick, code=0x38):
+    """Row r holds `code` (0x38 = 1.0) at column pick[r]; block (i, j) has
+    the scale 2**(i - 2 * j), distinct for every block of the grid."""
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    codes[np.arange(rows), pick] = code
+    gr, gc = (rows + 127) // 128, (cols + 127) // 128
+    bs = np.array([[2.0 ** (i - 2 * j) for j in range(gc)] for i in range(gr)], dtype=np.float32)
+    return fi.Fp8Weight(codes, bs)
+
+
+def pin_fp8_block_indexing(orc):
+    """A one-hot FP8 weight with a distinct power-of-two scale per 128 x 128
+    block, ragged in both directions: gate[m, n] = x[m, pick[n]] * 2**(n//128 -
+    2 * (pick[n]//128)) exactly, and a [K, N] down weight picks from h the same
+    way."""
+    rng = np.random.default_rng(61)
+    M, K, N = 2, 400, 300
+    pick = rng.integers(0, K, size=N)
+    wg = _fp8_one_hot(N, K, pick)
+    wu = _fp8_one_hot(N, K, rng.integers(0, K, size=N), code=0xB8)  # -1.0
+    x_bits = fi.f32_to_bf16_bits(rng.normal(size=(M, K)).astype(np.float32))
+    x = fi.bf16_bits_to_f32(x_bits).astype(np.float64)
+    case = fi.Fp8FfnCase("fp8_onehot", M, K, N, fi.ACT_SILU, x_bits, wg, wu, _fp8_one_hot(K, N, np.zeros(K, int)))
+    gate, up = orc.fp8_dual(case)
+    n = np.arange(N)
+    np.testing.assert_array_equal(gate, x[:, pick] * 2.0 ** (n // 128 - 2 * (pick // 128)))
+    np.testing.assert_array_equal(up, -x[:, wu.codes.argmax(axis=1)] * 2.0 ** (n // 128 - 2 * (wu.codes.argmax(axis=1) // 128)))
+    pick_d = rng.integers(0, N, size=K)
+    h = rng.normal(size=(M, N))
+    out = orc.fp8_linear(h, _fp8_one_hot(K, N, pick_d))
+    j = np.arange(K)
+    np.testing.assert_array_equal(out, h[:, pick_d] * 2.0 ** (j // 128 - 2 * (pick_d // 128)))
+
+
+def pin_fp8_dequant_vs_torch(orc):
+    """Every finite E4M3FN byte, ragged grids: the oracle's dequantised weight
+    equals torch's float8 decode times the numpy-expanded block grid, bit for
+    bit (an E4M3 value times an fp32 value is exact in double)."""
+    case = fi.make_fp8_format_coverage()
+    for w in (case.gate, case.up, case.down):
+        assert len(np.unique(w.codes)) == 254
+        np.testing.assert_array_equal(orc.fp8_dequant(w), _fp8_dense(w))
+
+
+def pin_fp8_exact_vs_numpy(orc):
+    """Codes in {0, +-1, +-2} and power-of-two block scales: every partial sum
+    of bf16 inputs is exact in double, so the oracle equals numpy's float64
+    matmul bit for bit, including over a ragged last block."""
+    rng = np.random.default_rng(62)
+    M, K, N = 3, 320, 136
+    codes = rng.choice(np.array([0x00, 0x38, 0xB8, 0x40, 0xC0], dtype=np.uint8), size=(N, K))
+    bs = (2.0 ** rng.integers(-3, 4, size=((N + 127) // 128, (K + 127) // 128))).astype(np.float32)
+    w = fi.Fp8Weight(codes, bs)
+    x_bits = fi.f32_to_bf16_bits(rng.normal(size=(M, K)).astype(np.float32))
+    x = fi.bf16_bits_to_f32(x_bits).astype(np.float64)
+    np.testing.assert_array_equal(orc.fp8_linear(x, w), x @ _fp8_dense(w).T)
+
+
+def pin_fp8_fraction_bound(orc):
+    """Random finite codes and random fp32 block scales over two ragged block
+    columns and rows: the oracle's gate and up are within the standard bound
+    n*u*sum|w x| of the exact rational results."""
+    rng = np.random.default_rng(63)
+    M, K, N = 2, 160, 130
+    fin = fi.finite_e4m3_bytes()
+
+    def weight(rows, cols):
+        grid = ((rows + 127) // 128, (cols + 127) // 128)
+        return fi.Fp8Weight(rng.choice(fin, size=(rows, cols)).astype(np.uint8),
+                            rng.uniform(0.1, 3.0, size=grid).astype(np.float32))
+
+    wg, wu = weight(N, K), weight(N, K)
+    x_bits = _exact_x_bits(rng, (M, K))
+    case = fi.Fp8FfnCase("fp8_frac", M, K, N, fi.ACT_SILU, x_bits, wg, wu, weight(K, N))
+    gate, up = orc.fp8_dual(case)
+    xf = fi.bf16_bits_to_f32(x_bits).astype(np.float64)
+    u = 2.0 ** -53
+    for w, got in ((wg, gate), (wu, up)):
+        e4 = _torch_e4m3(w.codes)
+        for m in range(M):
+            for n in range(0, N, 3):
+                terms = [Fraction(float(e4[n, k])) * Fraction(float(w.block_scale[n // 128, k // 128]))
+                         * Fraction(float(xf[m, k])) for k in range(K)]
+                exact = sum(terms)
+                bound = K * u * float(sum(abs(t) for t in terms)) * 1.01
+                assert abs(float(Fraction(got[m, n]) - exact)) <= bound, (m, n)
+
+
+def pin_fp8_ffn_composition(orc):
+    """The whole FP8 FFN equals down(act(gate) * up) assembled from torch's
+    float8 decode, numpy matmul, scipy expit and torch's gelu, to double
+    rounding; a row subset gives the same rows."""
+    for act in (fi.ACT_SILU, fi.ACT_GELU_TANH):
+        case = fi.make_fp8_ffn("fp8_comp", 3, 192, 160, act=act, seed=64)
+        out = orc.fp8_ffn(case)
+        x = fi.bf16_bits_to_f32(case.x_bits).astype(np.float64)
+        g = x @ _fp8_dense(case.gate).T
+        u = x @ _fp8_dense(case.up).T
+        if act == fi.ACT_SILU:
+            h = g * scipy.special.expit(g) * u
+        else:
+            h = torch.nn.functional.gelu(torch.from_numpy(g), approximate="tanh").numpy() * u
+        ref = h @ _fp8_dense(case.down).T
+        scale = np.abs(h) @ np.abs(_fp8_dense(case.down)).T
+        assert np.all(np.abs(out - ref) <= 1e-10 * scale)
+        np.testing.assert_array_equal(orc.fp8_ffn(case, rows=np.array([2])), out[2:3])
+
+
 PINS = [pin_e2m1_table, pin_e4m3_vs_torch, pin_e4m3_anchors_and_order, pin_byte_nibble_order,
         pin_scale_blocks, pin_dequant_independent, pin_activations, pin_gated_act,
         pin_one_hot_selects, pin_down_orientation, pin_ternary_exact_vs_numpy,
         pin_matches_numpy_matmul, pin_fraction_brute_force, pin_down_fraction_bound,
         pin_ffn_composition, pin_e2m1_encode_grid, pin_e4m3_encode_vs_torch, pin_quantize_zero,
-        pin_quantize_exact_roundtrip, pin_quantize_error_bound]
+        pin_quantize_exact_roundtrip, pin_quantize_error_bound, pin_fp8_block_indexing,
+        pin_fp8_dequant_vs_torch, pin_fp8_exact_vs_numpy, pin_fp8_fraction_bound, pin_fp8_ffn_composition]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -455,6 +581,25 @@ def test_generator_deterministic_and_shapes():
     assert a.weight_bytes == 221184
 
 
+def test_fp8_generator_shapes_and_recipe():
+    """The FP8 draw: row-major codes, ceil-128 block grids, no NaN byte, the
+    recipe's magnitude fields only, scales in [2**-10, 2**-9), deterministic."""
+    a = fi.make_fp8_ffn("a", 2, 640, 1000, seed=5)
+    b = fi.make_fp8_ffn("b", 2, 640, 1000, seed=5)
+    for wa, wb, shape in ((a.gate, b.gate, (1000, 640)), (a.up, b.up, (1000, 640)), (a.down, b.down, (640, 1000))):
+        assert wa.codes.shape == shape and wa.codes.dtype == np.uint8
+        assert wa.block_scale.shape == ((shape[0] + 127) // 128, (shape[1] + 127) // 128)
+        assert wa.block_scale.dtype == np.float32
+        assert np.all((wa.codes & 0x7F) < fi.FP8_RECIPE_MAGS)
+        assert np.all((wa.block_scale >= 2.0 ** -10) & (wa.block_scale < 2.0 ** -9))
+        np.testing.assert_array_equal(wa.codes, wb.codes)
+        np.testing.assert_array_equal(wa.block_scale, wb.block_scale)
+    np.testing.assert_array_equal(a.x_bits, b.x_bits)
+    c = fi.make_fp8_config(M=1)
+    assert (c.K, c.N, c.M) == (5120, 17408, 1)
+    assert c.gate.block_scale.shape == (136, 40) and c.down.block_scale.shape == (40, 136)
+
+
 def test_format_coverage_case():
     c = fi.make_format_coverage()
     allsc = np.concatenate([c.gate.scales.ravel(), c.up.scales.ravel(), c.down.scales.ravel()])
@@ -487,7 +632,8 @@ MUTANTS = {
     "silu_sign": ("g / (1.0 + exp(-g))", "g / (1.0 + exp(g))"),
     "gelu_coeff": ("0.044715 * g * g * g", "0.044715 * g * g"),
     "gate_up_swapped": ("h[i] = oracle_act(act, gate[i]) * up[i];", "h[i] = oracle_act(act, up[i]) * gate[i];"),
-    "dropped_last_term": ("for (int c = 0; c < cols; ++c)\n            acc +=", "for (int c = 0; c < cols - 1; ++c)\n            acc +="),
+    "dropped_last_term": ("for (int c = 0; c < cols; ++c)\n            acc += weight_at",
+                          "for (int c = 0; c < cols - 1; ++c)\n            acc += weight_at"),
     "row_index": ("codes[(size_t)r * (size_t)(cols / 2)", "codes[(size_t)(r / 2) * (size_t)(cols / 2)"),
     "q_e2m1_ties_odd": ("if (d < bd || (d == bd && (k & 1) == 0 && (best & 1) == 1)) {\n            best = k;",
                         "if (d < bd || (d == bd && (k & 1) == 1 && (best & 1) == 0)) {\n            best = k;"),
@@ -499,6 +645,15 @@ MUTANTS = {
     "q_pack_nibble": ("(c % 2 == 0) ? code : (code << 4)", "(c % 2 == 0) ? (code << 4) : code"),
     "q_e2m1_saturation": ("return signbit(q) ? 15 : 7;", "return signbit(q) ? 14 : 6;"),
     "q_e4m3_range": ("for (int b = 0; b < 127; ++b) {", "for (int b = 0; b < 126; ++b) {"),
+    "fp8_block_cols": ("(size_t)(c / 128)]", "(size_t)(c / 64)]"),
+    "fp8_block_rows": ("(size_t)(r / 128) * (size_t)bcols", "(size_t)(r / 256) * (size_t)bcols"),
+    "fp8_grid_stride": ("int bcols = (cols + 127) / 128;", "int bcols = cols / 128;"),
+    "fp8_scale_dropped": ("c]] * (double)bs[", "c]] + 0.0 * (double)bs["),
+    "fp8_up_from_gate": ("oracle_fp8_linear_f64(x, M, K, N, uw, ubs, up);", "oracle_fp8_linear_f64(x, M, K, N, gw, gbs, up);"),
+    "fp8_down_from_up": ("oracle_fp8_linear_f64(gate, M, N, K, dw, dbs, out);",
+                         "oracle_fp8_linear_f64(gate, M, N, K, uw, ubs, out);"),
+    "fp8_dropped_last_term": ("for (int c = 0; c < cols; ++c)\n            acc += fp8_weight_at",
+                              "for (int c = 1; c < cols; ++c)\n            acc += fp8_weight_at"),
 }
 
 
