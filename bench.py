@@ -50,6 +50,11 @@ SMALL_BATCH_MAX_M = 16  # above this the forward runs the 128-row matrix-core ar
 # gate/up shape; timed like the forward, reported on its own line.
 QUANT_WORKLOADS = {"quantize_17408x5120": (17408, 5120)}
 QUANT_METRIC = "µs per BF16->NVFP4 weight quantise + achieved HBM GB/s (% of peak)"
+# The same FFN over block-scaled FP8 weights (ffn_fp8_forward, E4M3 codes and
+# fp32 128 x 128 block scales) on the decode shape; reported on its own line.
+FP8_WORKLOADS = {"fp8_decode_silu_m1": 1, "fp8_verify_silu_m2": 2, "fp8_verify_silu_m3": 3,
+                 "fp8_verify_silu_m8": 8}
+FP8_METRIC = "µs/FFN forward + achieved HBM GB/s (% of peak), block-scaled FP8 SwiGLU"
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 
 
@@ -107,6 +112,129 @@ def cpu_baseline(case, seconds):
             "cores": orc.num_threads(), "kind": "oracle",
             "sample": f"{n} full forwards of the same workload (fp64 C oracle, OpenMP over output rows), "
                       f"{el:.1f} s"}
+
+
+def fp8_algorithmic_bytes(M, K, N):
+    """As algorithmic_bytes for FP8 weights: one code byte per element and an
+    fp32 scale per 128 x 128 block."""
+    w1 = N * K + 4 * ((N + 127) // 128) * ((K + 127) // 128)
+    return {
+        "weights": 3 * w1,
+        "forward": 3 * w1 + 2 * M * K + 2 * M * N + 2 * M * N + 2 * M * K,
+        "dual_f32": 2 * w1 + 2 * M * K + 2 * M * N * 4,
+    }
+
+
+def fp8_cpu_baseline(case, seconds):
+    import oracle
+
+    orc = oracle.default()
+    b = fp8_algorithmic_bytes(case.M, case.K, case.N)["forward"]
+    orc.fp8_ffn(case)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.fp8_ffn(case)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    us = el / n * 1e6
+    return {"value": round(b / (us * 1e-6) / 1e9, 3), "unit": "GB/s", "us_per_forward": round(us, 1),
+            "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"{n} full FP8 forwards of the same workload (fp64 C oracle, OpenMP over output rows), "
+                      f"{el:.1f} s"}
+
+
+def bench_fp8(args):
+    import torch
+
+    import ffn_inputs as fi
+    import w4a16_nvfp4_dense_amd as ffn
+
+    lib = ffn.load()
+    M = FP8_WORKLOADS[args.workload]
+    case = fi.make_fp8_config(M=M)
+    K, N, act = case.K, case.N, case.act
+    nbytes = fp8_algorithmic_bytes(M, K, N)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    copies = [tuple(ffn.Fp8DeviceWeight.from_host(w, dev) for w in (case.gate, case.up, case.down))
+              for _ in range(args.copies)]
+    structs = [tuple(w.struct() for w in c) for c in copies]
+    refs = [tuple(ctypes.byref(s) for s in c) for c in structs]
+    x = ffn.bf16_from_bits(case.x_bits, dev)
+    out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    ws_bytes = ffn.fp8_workspace_bytes(M, K, N)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    gate_out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    up_out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    xp, op, wp, gp, upp = x.data_ptr(), out.data_ptr(), ws.data_ptr(), gate_out.data_ptr(), up_out.data_ptr()
+    nc = len(refs)
+
+    def step(i):
+        g, u, d = refs[i % nc]
+        rc = lib.ffn_fp8_forward(xp, M, K, N, g, u, d, act, wp, ws_bytes, op, sh)
+        if rc:
+            raise ffn.FfnError(rc, "ffn_fp8_forward")
+
+    def dual(i):
+        g, u, _ = refs[i % nc]
+        rc = lib.ffn_fp8_dual_gemv(xp, M, K, N, g, u, gp, upp, sh)
+        if rc:
+            raise ffn.FfnError(rc, "ffn_fp8_dual_gemv")
+
+    outs = []
+    for i in range(nc):
+        step(i)
+        outs.append(out.clone())
+    torch.cuda.synchronize()
+    assert all(torch.equal(o, outs[0]) for o in outs), "weight copies disagree"
+
+    def timed(fn, n):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    ms_total = timed(step, args.steps)
+    ms_per_step = ms_total / args.steps
+    us = ms_per_step * 1e3
+    gbs = nbytes["forward"] / (us * 1e-6) / 1e9
+    nk = min(args.steps, 1000)
+    dual_us = timed(dual, nk) / nk * 1e3
+    dual_gbs = nbytes["dual_f32"] / (dual_us * 1e-6) / 1e9
+    log(f"[bench] {args.workload}: {us:.2f} us/forward, {gbs:.1f} GB/s algorithmic "
+        f"({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f}); dual GEMV {dual_us:.2f} us, {dual_gbs:.1f} GB/s")
+    traffic = measured_traffic(args.workload)
+    result = {
+        "metric": FP8_METRIC, "value": round(gbs, 2), "unit": "GB/s", "us_per_forward": round(us, 3),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{case.name}: gated FFN forward, M={M}, hidden K={K}, intermediate N={N}, "
+                               f"act={fi.ACT_NAMES[act]}, block-scaled FP8 weights rotated over {nc} copies",
+                   "M": M, "K": K, "N": N, "act": fi.ACT_NAMES[act],
+                   "algorithmic_bytes_per_forward": nbytes["forward"]},
+        "roofline": {"kernel": "FP8 dual gate+up GEMV (ffn_fp8_dual_gemv entry point: fp8_gemv_kernel, gate and "
+                               "up fp32 out)",
+                     "bound": "hbm", "achieved": round(dual_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dual_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic["bytes"]),
+                     "us_per_launch": round(dual_us, 3), "algorithmic_bytes_per_launch": nbytes["dual_f32"]},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = fp8_cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
 
 
 def quant_bytes(rows, cols):
@@ -207,7 +335,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="decode_silu_m1", choices=sorted(WORKLOADS) + sorted(QUANT_WORKLOADS))
+    ap.add_argument("--workload", default="decode_silu_m1",
+                    choices=sorted(WORKLOADS) + sorted(QUANT_WORKLOADS) + sorted(FP8_WORKLOADS))
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated over")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -228,6 +357,9 @@ def main():
 
     if args.workload in QUANT_WORKLOADS:
         bench_quantize(args)
+        return
+    if args.workload in FP8_WORKLOADS:
+        bench_fp8(args)
         return
     lib = ffn.load()
     idx, M = WORKLOADS[args.workload]

@@ -347,6 +347,14 @@ def parity_bound(out_ref: np.ndarray, rms_ref: Optional[float] = None,
     return rel * rms_ref + ulp_bf16(out_ref)
 
 
+def fp8_h_rounding_bound(case) -> np.ndarray:
+    """h_rounding_bound for an FP8 case: 2^-8 * sum_n |W_d[j, n]| |h[m, n]|."""
+    g, u = default().fp8_dual(case)
+    h = default().gated_act(case.act, g, u)
+    wd = np.abs(default().fp8_dequant(case.down))
+    return (2.0 ** -8) * (np.abs(h) @ wd.T)
+
+
 def h_rounding_bound(case) -> np.ndarray:
     """First-order bound [M, K] of what rounding h = act(gate) * up to bf16
     (once, to nearest) can move out = W_d h: 2^-8 * sum_n |W_d[j, n]| |h[m, n]|

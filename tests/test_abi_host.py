@@ -42,7 +42,9 @@ def test_exports_every_header_symbol():
     assert set(names) == {"ffn_nvfp4_forward", "ffn_nvfp4_dual_gemv", "ffn_nvfp4_down_gemv",
                           "ffn_nvfp4_workspace_bytes", "ffn_nvfp4_strerror", "ffn_nvfp4_version",
                           "ffn_nvfp4_quantize", "ffn_nvfp4_quantize_workspace_bytes"}
-    for n in names:
+    fp8 = ffn.header_functions(ffn.FP8_HEADER_PATH)
+    assert set(fp8) == {"ffn_fp8_forward", "ffn_fp8_dual_gemv", "ffn_fp8_down_gemv", "ffn_fp8_workspace_bytes"}
+    for n in list(names) + list(fp8):
         assert hasattr(lib, n), n
 
 
@@ -183,3 +185,76 @@ def test_quantize_validation():
         assert quant(rows=rows, cols=cols) == ffn.ERR_SHAPE
     # shape is checked before pointers
     assert quant(rows=0, w=0) == ffn.ERR_SHAPE
+
+
+# ------------------------------------------------------------ FP8 entry points
+
+
+def F8(codes=FAKE, bs=FAKE + 0x10000):
+    return ffn.Fp8WeightStruct(codes, bs)
+
+
+def f8fwd(x=FAKE, M=1, K=256, N=512, g=None, u=None, d=None, act=0, ws=FAKE + 0x200000, wsb=1 << 20,
+          out=FAKE + 0x400000):
+    g, u, d = g or F8(), u or F8(), d or F8()
+    return ffn.load().ffn_fp8_forward(x, M, K, N, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), act,
+                                      ws, wsb, out, 0)
+
+
+def f8dual(x=FAKE, M=1, K=256, N=512, g=None, u=None, go=FAKE + 0x200000, uo=FAKE + 0x400000):
+    g, u = g or F8(), u or F8()
+    return ffn.load().ffn_fp8_dual_gemv(x, M, K, N, ctypes.byref(g), ctypes.byref(u), go, uo, 0)
+
+
+def f8down(gi=FAKE, ui=FAKE + 0x200000, M=1, N=512, K=256, d=None, act=0, out=FAKE + 0x400000):
+    d = d or F8()
+    return ffn.load().ffn_fp8_down_gemv(gi, ui, M, N, K, ctypes.byref(d), act, out, 0)
+
+
+def test_fp8_workspace_bytes():
+    assert ffn.fp8_workspace_bytes(1, 5120, 17408) == 17408 * 2
+    assert ffn.fp8_workspace_bytes(8, 5120, 17408) == 8 * 17408 * 2
+    assert ffn.fp8_workspace_bytes(3, 400, 336) == 2048  # 3 * 336 * 2 = 2016, rounded up to 256
+    assert ffn.fp8_workspace_bytes(0, 256, 512) == 0
+    assert ffn.fp8_workspace_bytes(9, 256, 512) == 0      # the FP8 path covers M <= 8
+    assert ffn.fp8_workspace_bytes(1, 264, 512) == 0      # K not a multiple of 16
+    assert ffn.fp8_workspace_bytes(1, 256, 24592) == 0    # N above 24576
+    assert ffn.fp8_workspace_bytes(1, 24576, 16) == 32 * 8
+
+
+@pytest.mark.parametrize("call", [f8fwd, f8dual, f8down])
+def test_fp8_validation(call):
+    kw = {"K": 256, "N": 512}
+    # NULL and misaligned weights
+    key = {"f8fwd": "g", "f8dual": "g", "f8down": "d"}[call.__name__]
+    assert call(**{key: F8(codes=0)}) == ffn.ERR_NULL
+    assert call(**{key: F8(bs=0)}) == ffn.ERR_NULL
+    assert call(**{key: F8(codes=FAKE + 8)}) == ffn.ERR_ALIGN
+    assert call(**{key: F8(bs=FAKE + 0x10002)}) == ffn.ERR_ALIGN
+    # shapes: multiples of 16 up to 24576
+    for K, N in ((0, 512), (256, 0), (264, 512), (256, 520), (24592, 512), (256, 24592), (-16, 512)):
+        assert call(K=K, N=N) == ffn.ERR_SHAPE, (K, N)
+    # batches: 0..8 only
+    for M in (-1, 9, 16, 128):
+        assert call(M=M, **kw) == ffn.ERR_BATCH, M
+    # the empty call validates weights and shape, then launches nothing
+    assert call(M=0, **kw) == ffn.OK
+    if call is f8fwd:
+        assert f8fwd(M=0, x=0, out=0, ws=0) == ffn.OK
+        assert f8fwd(x=0) == ffn.ERR_NULL
+        assert f8fwd(ws=0) == ffn.ERR_NULL
+        assert f8fwd(x=FAKE + 8) == ffn.ERR_ALIGN
+        assert f8fwd(ws=FAKE + 0x200008) == ffn.ERR_ALIGN
+        assert f8fwd(act=2) == ffn.ERR_ACT
+        assert f8fwd(wsb=512 * 2 - 1) == ffn.ERR_WORKSPACE
+        assert f8fwd(M=2, wsb=1024) == ffn.ERR_WORKSPACE
+    elif call is f8dual:
+        assert f8dual(M=0, x=0, go=0, uo=0) == ffn.OK
+        assert f8dual(go=0) == ffn.ERR_NULL
+        assert f8dual(uo=FAKE + 0x400004) == ffn.ERR_ALIGN
+    else:
+        assert f8down(M=0, gi=0, ui=0, out=0) == ffn.OK
+        assert f8down(ui=0) == ffn.ERR_NULL
+        assert f8down(out=FAKE + 0x400002) == ffn.ERR_ALIGN
+        assert f8down(act=-1) == ffn.ERR_ACT
+        assert f8down(M=0, act=7) == ffn.ERR_ACT

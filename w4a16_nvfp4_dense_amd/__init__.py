@@ -13,6 +13,13 @@ The functions mirror the C entry points:
 * :func:`workspace_bytes` -- ``ffn_nvfp4_workspace_bytes``
 * :func:`quantize`   -- ``ffn_nvfp4_quantize``  bf16 weight -> NVFP4 codes, scales, scale2
 * :func:`quantize_workspace_bytes` -- ``ffn_nvfp4_quantize_workspace_bytes``
+
+and, for block-scaled FP8 weights (``include/ffn_fp8.h``):
+
+* :func:`fp8_forward`    -- ``ffn_fp8_forward``
+* :func:`fp8_dual_gemv`  -- ``ffn_fp8_dual_gemv``
+* :func:`fp8_down_gemv`  -- ``ffn_fp8_down_gemv``
+* :func:`fp8_workspace_bytes` -- ``ffn_fp8_workspace_bytes``
 """
 from __future__ import annotations
 
@@ -24,6 +31,7 @@ from typing import Optional, Sequence
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "lib", "libffn_nvfp4.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "ffn_nvfp4.h")
+FP8_HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "ffn_fp8.h")
 
 ACT_SILU = 0
 ACT_GELU_TANH = 1
@@ -51,11 +59,18 @@ class WeightStruct(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("scale2", ctypes.c_float)]
 
 
+class Fp8WeightStruct(ctypes.Structure):
+    """ffn_fp8_weight: device codes, device fp32 block-scale grid."""
+
+    _fields_ = [("codes", ctypes.c_void_p), ("block_scale", ctypes.c_void_p)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _WP = ctypes.POINTER(WeightStruct)
+_FP = ctypes.POINTER(Fp8WeightStruct)
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -83,16 +98,24 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ffn_nvfp4_quantize_workspace_bytes.argtypes = [_I, _I]
     lib.ffn_nvfp4_quantize.restype = _I
     lib.ffn_nvfp4_quantize.argtypes = [_P, _I, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.ffn_fp8_workspace_bytes.restype = ctypes.c_size_t
+    lib.ffn_fp8_workspace_bytes.argtypes = [_I, _I, _I]
+    lib.ffn_fp8_forward.restype = _I
+    lib.ffn_fp8_forward.argtypes = [_P, _I, _I, _I, _FP, _FP, _FP, _I, _P, ctypes.c_size_t, _P, _P]
+    lib.ffn_fp8_dual_gemv.restype = _I
+    lib.ffn_fp8_dual_gemv.argtypes = [_P, _I, _I, _I, _FP, _FP, _P, _P, _P]
+    lib.ffn_fp8_down_gemv.restype = _I
+    lib.ffn_fp8_down_gemv.argtypes = [_P, _P, _I, _I, _I, _FP, _I, _P, _P]
     _lib = lib
     return lib
 
 
 def header_functions(path: str = HEADER_PATH) -> Sequence[str]:
-    """Names of the functions the public header declares."""
+    """Names of the functions a public header declares."""
     import re
     text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ffn_nvfp4_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ffn_(?:nvfp4|fp8)_[a-z_0-9]+)\s*\(", text)))
 
 
 def version() -> int:
@@ -269,3 +292,106 @@ def bf16_from_bits(bits, device="cuda"):
 def bf16_to_f64(t):
     """A bf16 torch tensor as a float64 numpy array (exact)."""
     return t.float().cpu().double().numpy()
+
+
+# ------------------------------------------------------------ FP8 weights
+
+
+@dataclasses.dataclass
+class Fp8DeviceWeight:
+    """A block-scaled FP8 weight resident on the GPU: codes uint8 [rows, cols]
+    (E4M3FN bytes) and block_scale float32 [ceil(rows/128), ceil(cols/128)]."""
+
+    codes: "object"
+    block_scale: "object"
+
+    @property
+    def rows(self) -> int:
+        return int(self.codes.shape[0])
+
+    @property
+    def cols(self) -> int:
+        return int(self.codes.shape[1])
+
+    def struct(self) -> Fp8WeightStruct:
+        return Fp8WeightStruct(self.codes.data_ptr(), self.block_scale.data_ptr())
+
+    @classmethod
+    def from_host(cls, w, device="cuda") -> "Fp8DeviceWeight":
+        """From an object with numpy ``codes`` and ``block_scale``."""
+        import torch
+        return cls(torch.from_numpy(w.codes).to(device), torch.from_numpy(w.block_scale).to(device))
+
+
+def _check_fp8_weight(w: Fp8DeviceWeight, rows: int, cols: int, name: str) -> None:
+    import torch
+    _check_tensor(w.codes, torch.uint8, (rows, cols), f"{name}.codes")
+    _check_tensor(w.block_scale, torch.float32, ((rows + 127) // 128, (cols + 127) // 128), f"{name}.block_scale")
+
+
+def fp8_workspace_bytes(M: int, K: int, N: int) -> int:
+    return int(load().ffn_fp8_workspace_bytes(int(M), int(K), int(N)))
+
+
+def fp8_forward(x, gate: Fp8DeviceWeight, up: Fp8DeviceWeight, down: Fp8DeviceWeight, act: int = ACT_SILU,
+                out=None, workspace=None, stream=None):
+    """out[M, K] (bf16) = W_d (act(W_g x) * (W_u x)) over FP8 weights."""
+    import torch
+    M, K = x.shape
+    N = gate.rows
+    _check_tensor(x, torch.bfloat16, (M, K), "x")
+    _check_fp8_weight(gate, N, K, "gate")
+    _check_fp8_weight(up, N, K, "up")
+    _check_fp8_weight(down, K, N, "down")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
+    _check_tensor(out, torch.bfloat16, (M, K), "out")
+    need = fp8_workspace_bytes(M, K, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    g, u, d = gate.struct(), up.struct(), down.struct()
+    rc = load().ffn_fp8_forward(x.data_ptr(), M, K, N, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                                int(act), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                out.data_ptr(), _stream_handle(stream))
+    _check(rc, "ffn_fp8_forward")
+    return out
+
+
+def fp8_dual_gemv(x, gate: Fp8DeviceWeight, up: Fp8DeviceWeight, gate_out=None, up_out=None, stream=None):
+    """(gate, up) fp32 [M, N] = (W_g x, W_u x) over FP8 weights."""
+    import torch
+    M, K = x.shape
+    N = gate.rows
+    _check_tensor(x, torch.bfloat16, (M, K), "x")
+    _check_fp8_weight(gate, N, K, "gate")
+    _check_fp8_weight(up, N, K, "up")
+    if gate_out is None:
+        gate_out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if up_out is None:
+        up_out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check_tensor(gate_out, torch.float32, (M, N), "gate_out")
+    _check_tensor(up_out, torch.float32, (M, N), "up_out")
+    g, u = gate.struct(), up.struct()
+    rc = load().ffn_fp8_dual_gemv(x.data_ptr(), M, K, N, ctypes.byref(g), ctypes.byref(u),
+                                  gate_out.data_ptr(), up_out.data_ptr(), _stream_handle(stream))
+    _check(rc, "ffn_fp8_dual_gemv")
+    return gate_out, up_out
+
+
+def fp8_down_gemv(gate_in, up_in, down: Fp8DeviceWeight, act: int = ACT_SILU, out=None, stream=None):
+    """out[M, K] (bf16) = W_d bf16(act(gate) * up) over an FP8 W_d, with the
+    activation fused into the down GEMV's input load."""
+    import torch
+    M, N = gate_in.shape
+    K = down.rows
+    _check_tensor(gate_in, torch.float32, (M, N), "gate_in")
+    _check_tensor(up_in, torch.float32, (M, N), "up_in")
+    _check_fp8_weight(down, K, N, "down")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=gate_in.device)
+    _check_tensor(out, torch.bfloat16, (M, K), "out")
+    d = down.struct()
+    rc = load().ffn_fp8_down_gemv(gate_in.data_ptr(), up_in.data_ptr(), M, N, K, ctypes.byref(d), int(act),
+                                  out.data_ptr(), _stream_handle(stream))
+    _check(rc, "ffn_fp8_down_gemv")
+    return out

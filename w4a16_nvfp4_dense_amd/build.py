@@ -20,7 +20,9 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libffn_nvfp4.so")
 
-SOURCES = ["gemv.hip", "wave_launch.hip", "mfma_launch.hip", "smallm_launch.hip", "quantize.hip", "abi.cpp"]
+# longest compiles first (they start first in the pool)
+SOURCES = ["fp8_down.hip", "fp8_dual.hip", "wave_launch.hip", "mfma_launch.hip", "smallm_launch.hip", "gemv.hip",
+           "quantize.hip", "abi.cpp", "abi_fp8.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

@@ -1,0 +1,394 @@
+// fp8_gemv.h -- many-wave GEMV over block-scaled FP8 weights for decode and
+// verify batches (1 <= M <= 8 activation rows): the dual gate+up GEMV with the
+// gated activation in its epilogue, and the down GEMV with bf16 h or with the
+// activation fused into its activation staging.
+//
+// Weight format (qwen35_dense.rs page, the doc comment on which FP8 scale
+// layouts the native path accepts): E4M3FN bytes, row-major [rows, cols], and
+// an fp32 block-scale grid [ceil(rows/128), ceil(cols/128)], row-major;
+// element (r, c) = e4m3(w[r, c]) * block_scale[r/128, c/128]. The pages run
+// these weights through a fused gate+up launch and an activation-fused down
+// launch (dense_ffn.rs page, DenseFfnLayer::forward, the FP8 dispatch).
+//
+// The structure is that of the NVFP4 many-wave GEMV (one whole weight row per
+// wave at a time, many waves per compute unit, activations staged once per
+// workgroup in LDS, the next row's loads issued as soon as a row's arithmetic
+// is done), with a 16-column chunk: lane l owns chunks l, l + 64, ... of a
+// row, 16 bytes of codes each. Per chunk a lane converts its 16 codes to
+// eight bf16 pairs (exact: E4M3 values have 4 significant bits and fit
+// bf16's range), runs one 8-term dot2 chain per activation row, and folds the
+// chain into its accumulator with the chunk's block scale (a chunk lies in
+// one 128-column block: 128 is a multiple of 16). The block scale is a 4-byte
+// load per lane and chunk from the grid row of the weight row's 128-row band
+// (the whole grid is 0.1% of the codes and stays in cache). The wave
+// reduction and the epilogues are those of the NVFP4 kernel (a fixed DPP
+// tree), with unit per-tensor scales.
+#pragma once
+
+#include "kernels.h"
+#include "nvfp4_device.h"
+#include "wave_gemv.h"
+
+namespace ffn {
+
+struct Fp8Params {
+    const void *in0;
+    const float *in1;
+    const uint8_t *codes0;
+    const float *bs0;
+    const uint8_t *codes1;
+    const float *bs1;
+    void *out0;
+    void *out1;
+    int rows;
+    int cols;
+    int cpr;    // 16-column chunks per row
+    int bcols;  // block-scale grid columns, ceil(cols / 128)
+};
+
+// Two E4M3FN codes (bytes 2 SEL and 2 SEL + 1 of `word`) as a bf16 pair,
+// element 0 from the lower byte. The conversion's scale operand only carries
+// a power-of-two exponent, so it is 1.0 and the block scale is applied to the
+// chunk's dot product instead. Exact.
+template <bool SEL>
+__device__ __forceinline__ bf16x2_t fp8x2_to_bf16x2(uint32_t word)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, SEL);
+}
+
+// One row of NMAT weights in registers: 16 code bytes and one block scale per
+// lane and step.
+template <int IT, int NMAT>
+struct Fp8Row {
+    u32x4_t wc[NMAT][IT];
+    float bs[NMAT][IT];
+};
+
+// Issues the loads of steps I0 .. I0 + IS - 1 of row r (the row has IT
+// steps); NT marks the code loads non-temporal. In the last step a lane past
+// the row end re-reads the row's last chunk (row_geom), whose result
+// fp8_row_dot drops.
+template <bool NT, int IT, int NMAT, int I0 = 0, int IS = IT>
+__device__ __forceinline__ void fp8_load_row(Fp8Row<IS, NMAT> &w, const Fp8Params &p, int r, const RowGeom &rg)
+{
+    static_assert(I0 >= 0 && IS >= 1 && I0 + IS <= IT, "piece of the row");
+#pragma unroll
+    for (int t = 0; t < NMAT; ++t) {
+        const u32x4_t *cb = reinterpret_cast<const u32x4_t *>((t == 0 ? p.codes0 : p.codes1) +
+                                                              static_cast<size_t>(r) * static_cast<size_t>(p.cols));
+        const float *sb = (t == 0 ? p.bs0 : p.bs1) + static_cast<size_t>(r >> 7) * static_cast<size_t>(p.bcols);
+#pragma unroll
+        for (int j = 0; j < IS; ++j) {
+            const int i = I0 + j;
+            const int c = (i == IT - 1) ? rg.clast : rg.lane + 64 * i;
+            if constexpr (NT)
+                w.wc[t][j] = __builtin_nontemporal_load(cb + c);
+            else
+                w.wc[t][j] = cb[c];
+            w.bs[t][j] = sb[c >> 3];  // 8 chunks per 128-column block
+        }
+    }
+}
+
+// Per-lane partial sums of one row over steps I0 .. I0 + IS - 1 (activations
+// staged for those steps, two 16-byte units per chunk): acc[t][m] += bs *
+// (8-term dot2 chain over the chunk), starting from zero (INIT) or adding.
+template <int M, int IT, int NMAT, int I0 = 0, int IS = IT, bool INIT = true>
+__device__ __forceinline__ void fp8_row_dot(float (&acc)[NMAT][M], const Fp8Row<IS, NMAT> &w, const u32x4_t *act,
+                                            const RowGeom &rg)
+{
+    // An opaque zero keeps the activation reads inside the row loop (see
+    // row_dot).
+    int lz;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(lz));
+    const u32x4_t *ar = act + lz + rg.lane;
+    if constexpr (INIT) {
+#pragma unroll
+        for (int t = 0; t < NMAT; ++t)
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                acc[t][m] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < IS; ++j) {
+        const int i = I0 + j;
+        // past the row end the re-read chunk's result is dropped by a select
+        // (its codes may hold NaN, which a zero factor would not remove)
+        const bool live = (i < IT - 1) || rg.oklast;
+        bf16x2_t wp[NMAT][8];
+#pragma unroll
+        for (int t = 0; t < NMAT; ++t) {
+            const u32x4_t c = w.wc[t][j];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                wp[t][2 * q + 0] = fp8x2_to_bf16x2<false>(c[q]);
+                wp[t][2 * q + 1] = fp8x2_to_bf16x2<true>(c[q]);
+            }
+        }
+        u32x4_t an[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            an[h] = ar[(j * 2 + h) * 64];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            u32x4_t a[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                a[h] = an[h];
+            if (m + 1 < M) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    an[h] = ar[(((m + 1) * IS + j) * 2 + h) * 64];
+            }
+#pragma unroll
+            for (int t = 0; t < NMAT; ++t) {
+                // columns 2b, 2b + 1 of the chunk: codes pair wp[b],
+                // activations unit b / 4, pair b % 4
+                float d = dot2_bf16_first(wp[t][0], as_bf16x2(a[0][0]));
+#pragma unroll
+                for (int b = 1; b < 8; ++b)
+                    d = dot2_bf16(wp[t][b], as_bf16x2(a[b >> 2][b & 3]), d);
+                const float nv = __builtin_fmaf(d, w.bs[t][j], acc[t][m]);
+                acc[t][m] = live ? nv : acc[t][m];
+            }
+#pragma unroll
+            for (int t = 0; t < NMAT; ++t)
+                asm volatile("" : "+v"(acc[t][m])::"memory");
+        }
+    }
+}
+
+// One piece of the staged kernel (steps I0 .. I0 + IS - 1 of every row), then
+// the next; as wave_pieces of the NVFP4 kernel.
+template <int M, int IT, int NMAT, int IN, int W, int P, int p>
+__device__ __forceinline__ void fp8_pieces(const Fp8Params &fp, u32x4_t *act, float (&acc)[kPieceMaxRows][NMAT][M],
+                                           int g, int G, const RowGeom &rg)
+{
+    constexpr int IP = (IT + P - 1) / P;
+    constexpr int I0 = p * IP;
+    constexpr int IS = (IT - I0 < IP) ? IT - I0 : IP;
+    constexpr bool kNt = NMAT == 2;
+    Fp8Row<IS, NMAT> w;
+    if constexpr (p > 0)
+        lds_barrier();
+    stage_act<M, IS, IN, W, I0, 2>(act, fp.in0, fp.in1, fp.cols, fp.cpr, [&] {
+        if (g < fp.rows)
+            fp8_load_row<kNt, IT, NMAT, I0, IS>(w, fp, g, rg);
+    });
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < kPieceMaxRows; ++k) {
+        const int r = g + k * G;
+        if (r >= fp.rows)
+            break;
+        fp8_row_dot<M, IT, NMAT, I0, IS, p == 0>(acc[k], w, act, rg);
+        if (k + 1 < kPieceMaxRows && r + G < fp.rows)
+            fp8_load_row<kNt, IT, NMAT, I0, IS>(w, fp, r + G, rg);
+    }
+    if constexpr (p + 1 < P)
+        fp8_pieces<M, IT, NMAT, IN, W, P, p + 1>(fp, act, acc, g, G, rg);
+}
+
+// W waves per workgroup; wave g = wave * gridDim.x + blockIdx.x takes rows
+// g, g + G, ... (G = all waves of the grid). Dynamic LDS: M * IT * 2 KB, or
+// M * ceil(IT / P) * 2 KB with the activations staged in P pieces (each wave
+// then holds at most kPieceMaxRows rows). The dual GEMV (NMAT = 2) issues its
+// first weight row before staging and streams codes non-temporally; the down
+// GEMV stages first (with the activation fused into the staging when its
+// input is gate and up) and uses cached loads, as the NVFP4 kernels do.
+template <int M, int IT, int NMAT, int IN, int OUT, int W, int P = 1>
+__global__ __launch_bounds__(64 * W) void fp8_gemv_kernel(const Fp8Params p)
+{
+    extern __shared__ u32x4_t act[];
+    constexpr bool kNt = NMAT == 2;
+    constexpr bool kWeightsFirst = NMAT == 2;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = gridDim.x * W;
+    const int g = wave * static_cast<int>(gridDim.x) + static_cast<int>(blockIdx.x);
+    const RowGeom rg = row_geom<IT>(p.cpr);
+    if constexpr (P > 1) {
+        float acc[kPieceMaxRows][NMAT][M];
+        fp8_pieces<M, IT, NMAT, IN, W, P, 0>(p, act, acc, g, G, rg);
+#pragma unroll
+        for (int k = 0; k < kPieceMaxRows; ++k) {
+            const int r = g + k * G;
+            if (r >= p.rows)
+                break;
+            row_store<M, NMAT, OUT>(acc[k], r, p.rows, 1.0f, 1.0f, p.out0, p.out1, rg.lane);
+        }
+        return;
+    }
+    Fp8Row<IT, NMAT> w;
+    if (kWeightsFirst && g < p.rows)
+        fp8_load_row<kNt, IT, NMAT>(w, p, g, rg);
+    stage_act<M, IT, IN, W, 0, 2>(act, p.in0, p.in1, p.cols, p.cpr, [&] {
+        if (!kWeightsFirst && g < p.rows)
+            fp8_load_row<kNt, IT, NMAT>(w, p, g, rg);
+    });
+    lds_barrier();
+    for (int r = g; r < p.rows; r += G) {
+        float acc[NMAT][M];
+        fp8_row_dot<M, IT, NMAT>(acc, w, act, rg);
+        if (r + G < p.rows)
+            fp8_load_row<kNt, IT, NMAT>(w, p, r + G, rg);
+        row_store<M, NMAT, OUT>(acc, r, p.rows, 1.0f, 1.0f, p.out0, p.out1, rg.lane);
+    }
+}
+
+// ------------------------------------------------------------------ launch
+// (host side; included by the FP8 launch sources)
+
+constexpr int kFp8MaxIt = 24;            // chunks per lane: reduction length up to 24576
+constexpr int kFp8LdsMax = 144 * 1024;   // of the 160 KB per compute unit
+
+// Pieces the steps of a row are processed in: the fewest whose activations
+// (M x ceil(IT / P) x 2 KB) fit the LDS budget and whose weight registers
+// (5 per step and matrix) stay within 160, so that long rows of the dual
+// GEMV do not spill.
+template <int M, int IT, int NMAT>
+constexpr int fp8_pieces_count()
+{
+    int pc = 1;
+    while (M * ((IT + pc - 1) / pc) * 2048 > kFp8LdsMax || NMAT * ((IT + pc - 1) / pc) * 5 > 160)
+        ++pc;
+    return pc;
+}
+
+template <int M, int IT, int NMAT>
+constexpr int fp8_piece_steps()
+{
+    return (IT + fp8_pieces_count<M, IT, NMAT>() - 1) / fp8_pieces_count<M, IT, NMAT>();
+}
+
+// Waves per workgroup: 16 (at most 128 registers per lane) while one row's
+// weight registers (5 per step and matrix), the converted chunk (8 per
+// matrix) and the accumulators fit with room to spare, otherwise 8.
+template <int M, int IT, int NMAT>
+constexpr int fp8_w_regs()
+{
+    constexpr int IS = fp8_piece_steps<M, IT, NMAT>();
+    constexpr int acc = (fp8_pieces_count<M, IT, NMAT>() > 1 ? kPieceMaxRows : 1) * M * NMAT;
+    return (NMAT * IS * 5 + NMAT * 8 + acc + 30 <= 120) ? 16 : 8;
+}
+
+// The dual GEMV as 2 x 8 waves per compute unit while two workgroups'
+// activations fit in LDS (as for NVFP4), else by registers.
+template <int M, int IT, int NMAT>
+constexpr int fp8_w()
+{
+    return (NMAT == 2 && fp8_pieces_count<M, IT, NMAT>() == 1 && 2 * M * IT * 2048 <= kFp8LdsMax)
+               ? 8
+               : fp8_w_regs<M, IT, NMAT>();
+}
+
+template <int M, int IT, int NMAT>
+constexpr int fp8_blocks_per_cu()
+{
+    return (fp8_w<M, IT, NMAT>() == 8 && 2 * M * fp8_piece_steps<M, IT, NMAT>() * 2048 <= kFp8LdsMax) ? 2 : 1;
+}
+
+template <int M, int IT, int NMAT, int IN, int OUT>
+hipError_t fp8_launch_one(const Fp8Params &p, hipStream_t stream)
+{
+    constexpr int W = fp8_w<M, IT, NMAT>();
+    constexpr int P = fp8_pieces_count<M, IT, NMAT>();
+    auto kern = fp8_gemv_kernel<M, IT, NMAT, IN, OUT, W, P>;
+    const int lds = M * fp8_piece_steps<M, IT, NMAT>() * 2048;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess)
+            return e;
+    }
+    const int want = device_cu_count() * fp8_blocks_per_cu<M, IT, NMAT>();
+    int blocks = want < (p.rows + W - 1) / W ? want : (p.rows + W - 1) / W;
+    if (blocks < 1)
+        blocks = 1;
+    if constexpr (P > 1) {
+        const int rows_per_block = W * kPieceMaxRows;
+        const int need = (p.rows + rows_per_block - 1) / rows_per_block;
+        if (blocks < need)
+            blocks = need;
+    }
+    Fp8Params q = p;
+    void *args[] = {&q};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(blocks), dim3(W * 64), args, lds, stream);
+}
+
+template <int IT, int NMAT, int IN, int OUT>
+hipError_t fp8_launch_m(int M, const Fp8Params &p, hipStream_t stream)
+{
+    switch (M) {
+    case 1: return fp8_launch_one<1, IT, NMAT, IN, OUT>(p, stream);
+    case 2: return fp8_launch_one<2, IT, NMAT, IN, OUT>(p, stream);
+    case 3: return fp8_launch_one<3, IT, NMAT, IN, OUT>(p, stream);
+    case 4: return fp8_launch_one<4, IT, NMAT, IN, OUT>(p, stream);
+    case 8: return fp8_launch_one<8, IT, NMAT, IN, OUT>(p, stream);
+    default: return hipErrorNotSupported;
+    }
+}
+
+// Activation rows per launch: the largest of 8, 4, 3, 2, 1 that is at most
+// `left`. Rows of a batch are independent, so the grouping changes no result.
+inline int fp8_group_rows(int left)
+{
+    for (int g : {8, 4, 3, 2, 1})
+        if (g <= left)
+            return g;
+    return 0;
+}
+
+template <int NMAT, int IN, int OUT>
+hipError_t fp8_launch_groups(int M, Fp8Params p, size_t in_elem, size_t out_elem, hipStream_t stream)
+{
+    const int it = (p.cpr + 63) / 64;
+    if (M < 1 || it < 1 || it > kFp8MaxIt)
+        return hipErrorNotSupported;
+    for (int m0 = 0; m0 < M;) {
+        const int g = fp8_group_rows(M - m0);
+        Fp8Params q = p;
+        q.in0 = static_cast<const uint8_t *>(p.in0) + static_cast<size_t>(m0) * p.cols * in_elem;
+        if (p.in1)
+            q.in1 = p.in1 + static_cast<size_t>(m0) * p.cols;
+        q.out0 = static_cast<uint8_t *>(p.out0) + static_cast<size_t>(m0) * p.rows * out_elem;
+        if (p.out1)
+            q.out1 = static_cast<uint8_t *>(p.out1) + static_cast<size_t>(m0) * p.rows * out_elem;
+        hipError_t e = hipErrorNotSupported;
+        switch (it) {
+#define FFN_FP8_CASE(IT_) \
+        case IT_: e = fp8_launch_m<IT_, NMAT, IN, OUT>(g, q, stream); break;
+        FFN_FP8_CASE(1)
+        FFN_FP8_CASE(2)
+        FFN_FP8_CASE(3)
+        FFN_FP8_CASE(4)
+        FFN_FP8_CASE(5)
+        FFN_FP8_CASE(6)
+        FFN_FP8_CASE(7)
+        FFN_FP8_CASE(8)
+        FFN_FP8_CASE(9)
+        FFN_FP8_CASE(10)
+        FFN_FP8_CASE(11)
+        FFN_FP8_CASE(12)
+        FFN_FP8_CASE(13)
+        FFN_FP8_CASE(14)
+        FFN_FP8_CASE(15)
+        FFN_FP8_CASE(16)
+        FFN_FP8_CASE(17)
+        FFN_FP8_CASE(18)
+        FFN_FP8_CASE(19)
+        FFN_FP8_CASE(20)
+        FFN_FP8_CASE(21)
+        FFN_FP8_CASE(22)
+        FFN_FP8_CASE(23)
+        FFN_FP8_CASE(24)
+#undef FFN_FP8_CASE
+        default: break;
+        }
+        if (e != hipSuccess)
+            return e;
+        m0 += g;
+    }
+    return hipSuccess;
+}
+
+}  // namespace ffn

@@ -59,3 +59,24 @@ int device_cu_count();
 int lanes_per_row(int cpr);
 
 }  // namespace ffn
+
+namespace ffn {
+
+// A block-scaled FP8 weight of shape [rows, cols]: E4M3FN codes [rows, cols]
+// and the fp32 block-scale grid [ceil(rows/128), ceil(cols/128)].
+struct Fp8WeightArg {
+    const uint8_t *codes;
+    const float *block_scale;
+};
+
+// Many-wave GEMV over FP8 weights, 1 <= M <= 8 (batches above 4 rows other
+// than 8 go in several launches); cols a multiple of 16, at most 24576.
+// The dual takes OUT_F32_PAIR, OUT_H_SILU or OUT_H_GELU; the down takes
+// IN_BF16, IN_GATEUP_SILU or IN_GATEUP_GELU and writes bf16. Returns
+// hipErrorNotSupported for anything else.
+hipError_t launch_fp8_dual(int M, OutKind out, const void *x, const Fp8WeightArg &w0, const Fp8WeightArg &w1,
+                           void *out0, void *out1, int rows, int cols, hipStream_t stream);
+hipError_t launch_fp8_down(int M, InKind in, const void *in0, const float *in1, const Fp8WeightArg &w, void *out,
+                           int rows, int cols, hipStream_t stream);
+
+}  // namespace ffn

@@ -104,22 +104,25 @@ __device__ __forceinline__ void load_row(WaveRow<IS, NMAT> &w, const uint8_t *co
 }
 
 // Stages the columns of steps I0 .. I0 + IS - 1 of M activation rows of
-// `cols` (= 32 cpr) columns into LDS as 16-byte units
-// ((m * IS + j) * 4 + q) * 64 + l: quarter q of the chunk lane l reads in step
+// `cols` (= 8 CQ cpr) columns into LDS as 16-byte units
+// ((m * IS + j) * CQ + q) * 64 + l: unit q of the chunk lane l reads in step
 // I0 + j (chunk l + 64 (I0 + j); zero past the row end), so every read is
-// conflict-free and its address is the lane's offset plus a constant. Uses
-// M * IS * 4 KB. The W waves of the workgroup load in batches of SU units per
+// conflict-free and its address is the lane's offset plus a constant. A chunk
+// is CQ = 4 units (32 columns: 16 bytes of FP4 codes) or CQ = 2 (16 columns:
+// 16 bytes of FP8 codes). Uses M * IS * CQ KB. The W waves of the workgroup load in batches of SU units per
 // thread; `issue()` runs right after the last batch's global loads (the
 // first weight row goes out there: waiting for the activations then does not
 // wait for the weights, as loads complete in order, and the weight registers
 // are not live while earlier batches are in flight). The caller synchronises
 // the workgroup before reading.
-template <int M, int IS, int IN, int W, int I0 = 0, class F>
+template <int M, int IS, int IN, int W, int I0 = 0, int CQ = 4, class F>
 __device__ __forceinline__ void stage_act(u32x4_t *act, const void *in0, const float *in1, int cols, int cpr,
                                           F &&issue)
 {
+    static_assert(CQ == 2 || CQ == 4, "16-byte units per chunk");
+    constexpr int kQs = CQ == 4 ? 2 : 1;  // log2 CQ
     constexpr int IT = IS;  // steps staged
-    constexpr int total = M * IT * 64 * 4;
+    constexpr int total = M * IT * 64 * CQ;
     constexpr int nthr = 64 * W;
     constexpr int need = (total + nthr - 1) / nthr;
     constexpr int SU = (IN == IN_BF16) ? (need < 8 ? need : 8) : 2;
@@ -132,10 +135,10 @@ __device__ __forceinline__ void stage_act(u32x4_t *act, const void *in0, const f
         for (int k = 0; k < SU; ++k) {
             // global piece u: row m, chunk c, quarter q (q fastest)
             const int u = base + k * nthr + static_cast<int>(threadIdx.x);
-            const int m = min(u / (IT * 256), M - 1);
-            const int rem = u - m * IT * 256;
-            const int c = min(64 * I0 + (rem >> 2), cpr - 1);
-            const size_t off = static_cast<size_t>(m) * cols + static_cast<size_t>(c) * 32 + (rem & 3) * 8;
+            const int m = min(u / (IT * 64 * CQ), M - 1);
+            const int rem = u - m * IT * 64 * CQ;
+            const int c = min(64 * I0 + (rem >> kQs), cpr - 1);
+            const size_t off = static_cast<size_t>(m) * cols + static_cast<size_t>(c) * (8 * CQ) + (rem & (CQ - 1)) * 8;
             if constexpr (IN == IN_BF16) {
                 v[k] = *reinterpret_cast<const u32x4_t *>(static_cast<const uint16_t *>(in0) + off);
             } else {
@@ -155,10 +158,10 @@ __device__ __forceinline__ void stage_act(u32x4_t *act, const void *in0, const f
         for (int k = 0; k < SU; ++k) {
             const int u = base + k * nthr + static_cast<int>(threadIdx.x);
             if (u < total) {
-                const int m = u / (IT * 256);
-                const int rem = u - m * IT * 256;
-                const int c = rem >> 2;  // chunk l + 64 (I0 + j), c = 64 j + l
-                act[((m * IT + (c >> 6)) * 4 + (rem & 3)) * 64 + (c & 63)] =
+                const int m = u / (IT * 64 * CQ);
+                const int rem = u - m * IT * 64 * CQ;
+                const int c = rem >> kQs;  // chunk l + 64 (I0 + j), c = 64 j + l
+                act[((m * IT + (c >> 6)) * CQ + (rem & (CQ - 1))) * 64 + (c & 63)] =
                     64 * I0 + c < cpr ? v[k] : u32x4_t{0, 0, 0, 0};
             }
         }
