@@ -18,11 +18,14 @@
 // eight bf16 pairs (exact: E4M3 values have 4 significant bits and fit
 // bf16's range), runs one 8-term dot2 chain per activation row, and folds the
 // chain into its accumulator with the chunk's block scale (a chunk lies in
-// one 128-column block: 128 is a multiple of 16). The block scale is a 4-byte
-// load per lane and chunk from the grid row of the weight row's 128-row band
-// (the whole grid is 0.1% of the codes and stays in cache). The wave
-// reduction and the epilogues are those of the NVFP4 kernel (a fixed DPP
-// tree), with unit per-tensor scales.
+// one 128-column block: 128 is a multiple of 16). In step i lane l's chunk
+// lies in block 8 i + l / 8 of its row's grid row, so the 8 lanes of a group
+// share one scale: lane l loads grid entries l, l + 64, ... once per row (one
+// register per 8 steps instead of one per step, which lets the long down
+// rows run 16 waves per compute unit), and each step fetches its scale from
+// lane 8 (i % 8) + l / 8 with ds_bpermute. The grid (0.1% of the codes) stays
+// in cache. The wave reduction and the epilogues are those of the NVFP4
+// kernel (a fixed DPP tree), with unit per-tensor scales.
 #pragma once
 
 #include "kernels.h"
@@ -56,22 +59,41 @@ __device__ __forceinline__ bf16x2_t fp8x2_to_bf16x2(uint32_t word)
     return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, SEL);
 }
 
-// One row of NMAT weights in registers: 16 code bytes and one block scale per
-// lane and step.
-template <int IT, int NMAT>
+// Scale registers of steps I0 .. I0 + IS - 1: step i's blocks 8 i .. 8 i + 7
+// sit in register i / 8 (entry 8 (i % 8) + l / 8 of grid blocks
+// 64 (i / 8) ..).
+template <int I0, int IS>
+constexpr int fp8_scale_reg0()
+{
+    return I0 / 8;
+}
+
+template <int I0, int IS>
+constexpr int fp8_scale_regs()
+{
+    return (I0 + IS - 1) / 8 - I0 / 8 + 1;
+}
+
+// One row of NMAT weights in registers: 16 code bytes per lane and step, and
+// NB block-scale registers (grid entries lane + 64 k).
+template <int IS, int NMAT, int NB>
 struct Fp8Row {
-    u32x4_t wc[NMAT][IT];
-    float bs[NMAT][IT];
+    u32x4_t wc[NMAT][IS];
+    float bs[NMAT][NB];
 };
 
 // Issues the loads of steps I0 .. I0 + IS - 1 of row r (the row has IT
 // steps); NT marks the code loads non-temporal. In the last step a lane past
 // the row end re-reads the row's last chunk (row_geom), whose result
-// fp8_row_dot drops.
+// fp8_row_dot drops. Scale entries past the grid row's end are clamped to its
+// last entry (no step reads them).
 template <bool NT, int IT, int NMAT, int I0 = 0, int IS = IT>
-__device__ __forceinline__ void fp8_load_row(Fp8Row<IS, NMAT> &w, const Fp8Params &p, int r, const RowGeom &rg)
+__device__ __forceinline__ void fp8_load_row(Fp8Row<IS, NMAT, fp8_scale_regs<I0, IS>()> &w, const Fp8Params &p, int r,
+                                             const RowGeom &rg)
 {
     static_assert(I0 >= 0 && IS >= 1 && I0 + IS <= IT, "piece of the row");
+    constexpr int K0 = fp8_scale_reg0<I0, IS>();
+    constexpr int NB = fp8_scale_regs<I0, IS>();
 #pragma unroll
     for (int t = 0; t < NMAT; ++t) {
         const u32x4_t *cb = reinterpret_cast<const u32x4_t *>((t == 0 ? p.codes0 : p.codes1) +
@@ -85,18 +107,32 @@ __device__ __forceinline__ void fp8_load_row(Fp8Row<IS, NMAT> &w, const Fp8Param
                 w.wc[t][j] = __builtin_nontemporal_load(cb + c);
             else
                 w.wc[t][j] = cb[c];
-            w.bs[t][j] = sb[c >> 3];  // 8 chunks per 128-column block
         }
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+            w.bs[t][k] = sb[min(rg.lane + 64 * (K0 + k), p.bcols - 1)];
     }
+}
+
+// The block scale of step i for this lane: grid block 8 i + lane / 8, held by
+// lane 8 (i % 8) + lane / 8 in register i / 8 - K0.
+template <int I0, int IS, int NB>
+__device__ __forceinline__ float fp8_step_scale(const float (&bs)[NB], int i, int lane)
+{
+    constexpr int K0 = fp8_scale_reg0<I0, IS>();
+    const int src = 8 * (i % 8) + (lane >> 3);
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_ds_bpermute(src * 4, __builtin_bit_cast(int, bs[i / 8 - K0])));
 }
 
 // Per-lane partial sums of one row over steps I0 .. I0 + IS - 1 (activations
 // staged for those steps, two 16-byte units per chunk): acc[t][m] += bs *
 // (8-term dot2 chain over the chunk), starting from zero (INIT) or adding.
 template <int M, int IT, int NMAT, int I0 = 0, int IS = IT, bool INIT = true>
-__device__ __forceinline__ void fp8_row_dot(float (&acc)[NMAT][M], const Fp8Row<IS, NMAT> &w, const u32x4_t *act,
-                                            const RowGeom &rg)
+__device__ __forceinline__ void fp8_row_dot(float (&acc)[NMAT][M], const Fp8Row<IS, NMAT, fp8_scale_regs<I0, IS>()> &w,
+                                            const u32x4_t *act, const RowGeom &rg)
 {
+    constexpr int NB = fp8_scale_regs<I0, IS>();
     // An opaque zero keeps the activation reads inside the row loop (see
     // row_dot).
     int lz;
@@ -116,8 +152,10 @@ __device__ __forceinline__ void fp8_row_dot(float (&acc)[NMAT][M], const Fp8Row<
         // (its codes may hold NaN, which a zero factor would not remove)
         const bool live = (i < IT - 1) || rg.oklast;
         bf16x2_t wp[NMAT][8];
+        float sc[NMAT];
 #pragma unroll
         for (int t = 0; t < NMAT; ++t) {
+            sc[t] = fp8_step_scale<I0, IS, NB>(w.bs[t], i, rg.lane);
             const u32x4_t c = w.wc[t][j];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -148,7 +186,7 @@ __device__ __forceinline__ void fp8_row_dot(float (&acc)[NMAT][M], const Fp8Row<
 #pragma unroll
                 for (int b = 1; b < 8; ++b)
                     d = dot2_bf16(wp[t][b], as_bf16x2(a[b >> 2][b & 3]), d);
-                const float nv = __builtin_fmaf(d, w.bs[t][j], acc[t][m]);
+                const float nv = __builtin_fmaf(d, sc[t], acc[t][m]);
                 acc[t][m] = live ? nv : acc[t][m];
             }
 #pragma unroll
@@ -168,7 +206,7 @@ __device__ __forceinline__ void fp8_pieces(const Fp8Params &fp, u32x4_t *act, fl
     constexpr int I0 = p * IP;
     constexpr int IS = (IT - I0 < IP) ? IT - I0 : IP;
     constexpr bool kNt = NMAT == 2;
-    Fp8Row<IS, NMAT> w;
+    Fp8Row<IS, NMAT, fp8_scale_regs<I0, IS>()> w;
     if constexpr (p > 0)
         lds_barrier();
     stage_act<M, IS, IN, W, I0, 2>(act, fp.in0, fp.in1, fp.cols, fp.cpr, [&] {
@@ -218,7 +256,7 @@ __global__ __launch_bounds__(64 * W) void fp8_gemv_kernel(const Fp8Params p)
         }
         return;
     }
-    Fp8Row<IT, NMAT> w;
+    Fp8Row<IT, NMAT, fp8_scale_regs<0, IT>()> w;
     if (kWeightsFirst && g < p.rows)
         fp8_load_row<kNt, IT, NMAT>(w, p, g, rg);
     stage_act<M, IT, IN, W, 0, 2>(act, p.in0, p.in1, p.cols, p.cpr, [&] {
@@ -242,14 +280,14 @@ constexpr int kFp8MaxIt = 24;            // chunks per lane: reduction length up
 constexpr int kFp8LdsMax = 144 * 1024;   // of the 160 KB per compute unit
 
 // Pieces the steps of a row are processed in: the fewest whose activations
-// (M x ceil(IT / P) x 2 KB) fit the LDS budget and whose weight registers
-// (5 per step and matrix) stay within 160, so that long rows of the dual
+// (M x ceil(IT / P) x 2 KB) fit the LDS budget and whose code registers
+// (4 per step and matrix) stay within 160, so that long rows of the dual
 // GEMV do not spill.
 template <int M, int IT, int NMAT>
 constexpr int fp8_pieces_count()
 {
     int pc = 1;
-    while (M * ((IT + pc - 1) / pc) * 2048 > kFp8LdsMax || NMAT * ((IT + pc - 1) / pc) * 5 > 160)
+    while (M * ((IT + pc - 1) / pc) * 2048 > kFp8LdsMax || NMAT * ((IT + pc - 1) / pc) * 4 > 160)
         ++pc;
     return pc;
 }
@@ -261,14 +299,15 @@ constexpr int fp8_piece_steps()
 }
 
 // Waves per workgroup: 16 (at most 128 registers per lane) while one row's
-// weight registers (5 per step and matrix), the converted chunk (8 per
-// matrix) and the accumulators fit with room to spare, otherwise 8.
+// weight registers (4 per step and matrix, plus the scale registers), the
+// converted chunk (8 per matrix) and the accumulators fit with room to
+// spare, otherwise 8.
 template <int M, int IT, int NMAT>
 constexpr int fp8_w_regs()
 {
     constexpr int IS = fp8_piece_steps<M, IT, NMAT>();
     constexpr int acc = (fp8_pieces_count<M, IT, NMAT>() > 1 ? kPieceMaxRows : 1) * M * NMAT;
-    return (NMAT * IS * 5 + NMAT * 8 + acc + 30 <= 120) ? 16 : 8;
+    return (NMAT * (IS * 4 + (IS + 7) / 8 + 1) + NMAT * 8 + acc + 30 <= 120) ? 16 : 8;
 }
 
 // The dual GEMV as 2 x 8 waves per compute unit while two workgroups'
