@@ -114,6 +114,18 @@ def cpu_baseline(case, seconds):
                       f"{el:.1f} s"}
 
 
+def calibration_copy(dev):
+    """A plain 64 MiB device-to-device copy (three times), the reference that
+    scales FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.empty(64 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def fp8_algorithmic_bytes(M, K, N):
     """As algorithmic_bytes for FP8 weights: one code byte per element and an
     fp32 scale per 128 x 128 block."""
@@ -192,6 +204,8 @@ def bench_fp8(args):
         outs.append(out.clone())
     torch.cuda.synchronize()
     assert all(torch.equal(o, outs[0]) for o in outs), "weight copies disagree"
+    if args.calibrate_copy:
+        calibration_copy(dev)
 
     def timed(fn, n):
         for i in range(args.warmup):
@@ -405,12 +419,7 @@ def main():
     assert all(torch.equal(o, outs[0]) for o in outs), "weight copies disagree"
 
     if args.calibrate_copy:
-        src = torch.empty(64 << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(dev)
 
     for i in range(args.warmup):
         step(i)
