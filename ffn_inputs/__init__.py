@@ -298,6 +298,27 @@ def make_fp8_format_coverage(act: int = ACT_SILU, seed: int = 98, M: int = 1) ->
                       x_bits=x_bits, gate=gate, up=up, down=down)
 
 
+@dataclasses.dataclass
+class MxWeight:
+    """An MXFP4 weight of logical shape [rows, cols] (the W4A4 arm's operand
+    layout): E2M1 codes [rows, cols/2] (element 2j in the low nibble of byte
+    j), one E8M0 exponent byte per 32 consecutive elements [rows, cols/32]
+    (value 2^(byte - 127)), and the per-tensor fp32 scale2 carried over from
+    the NVFP4 weight it was requantised from."""
+
+    codes: np.ndarray   # uint8 [rows, cols // 2]
+    e8m0: np.ndarray    # uint8 [rows, cols // 32]
+    scale2: float
+
+    @property
+    def rows(self) -> int:
+        return int(self.codes.shape[0])
+
+    @property
+    def cols(self) -> int:
+        return int(self.codes.shape[1]) * 2
+
+
 def make_dense_bf16(rows: int, cols: int, seed: int, spread: float = 4.0) -> np.ndarray:
     """Seeded dense bf16 weight bits [rows, cols] (the quantiser's input): a
     normal draw times a per-row factor e^u, u uniform on [-spread, spread / 2]

@@ -90,6 +90,23 @@ class Oracle:
         lib.oracle_fp8_dual.argtypes = [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P]
         lib.oracle_fp8_ffn.restype = _I
         lib.oracle_fp8_ffn.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
+        lib.oracle_mx_value.restype = ctypes.c_double
+        lib.oracle_mx_value.argtypes = [_I, _I]
+        lib.oracle_mx_block_exponent.restype = _I
+        lib.oracle_mx_block_exponent.argtypes = [ctypes.c_double]
+        lib.oracle_mx_quantize.restype = None
+        lib.oracle_mx_quantize.argtypes = [_P, _I, _I, _P, _P]
+        lib.oracle_mx_quantize_bf16.restype = _I
+        lib.oracle_mx_quantize_bf16.argtypes = [_P, _I, _I, _P, _P]
+        lib.oracle_mx_requant_nvfp4.restype = _I
+        lib.oracle_mx_requant_nvfp4.argtypes = [_P, _P, _I, _I, _P, _P]
+        lib.oracle_mx_linear_f64.restype = None
+        lib.oracle_mx_linear_f64.argtypes = [_P, _P, _I, _I, _P, _P, _I, _P]
+        lib.oracle_w4a4_dual.restype = _I
+        lib.oracle_w4a4_dual.argtypes = [_P, _I, _I, _I, _P, _P, ctypes.c_float, _P, _P, ctypes.c_float, _P, _P]
+        lib.oracle_w4a4_ffn.restype = _I
+        lib.oracle_w4a4_ffn.argtypes = [_P, _I, _I, _I, _I, _P, _P, ctypes.c_float, _P, _P, ctypes.c_float,
+                                        _P, _P, ctypes.c_float, _P]
         self.lib = lib
         self.path = lib_path
 
@@ -253,6 +270,79 @@ class Oracle:
         return out
 
 
+    # ------------------------------------------------------------ W4A4 (MXFP4)
+
+    def mx_value(self, code: int, e8m0: int) -> float:
+        return float(self.lib.oracle_mx_value(int(code), int(e8m0)))
+
+    def mx_block_exponent(self, amax: float) -> int:
+        return int(self.lib.oracle_mx_block_exponent(float(amax)))
+
+    def mx_quantize(self, v: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+        """float64 [rows, cols] -> (codes uint8 [rows, cols/2], e8m0 uint8 [rows, cols/32])."""
+        v = _c(v, np.float64)
+        rows, cols = v.shape
+        codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+        e8m0 = np.zeros((rows, cols // 32), dtype=np.uint8)
+        self.lib.oracle_mx_quantize(_ptr(v), rows, cols, _ptr(codes), _ptr(e8m0))
+        return codes, e8m0
+
+    def mx_quantize_bf16(self, x_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+        x = _c(x_bits, np.uint16)
+        M, K = x.shape
+        codes = np.zeros((M, K // 2), dtype=np.uint8)
+        e8m0 = np.zeros((M, K // 32), dtype=np.uint8)
+        if self.lib.oracle_mx_quantize_bf16(_ptr(x), M, K, _ptr(codes), _ptr(e8m0)) != 0:
+            raise MemoryError("oracle_mx_quantize_bf16")
+        return codes, e8m0
+
+    def mx_requant(self, w):
+        """An NVFP4 weight (ffn_inputs.Nvfp4Weight) requantised to MXFP4
+        (ffn_inputs.MxWeight, scale2 carried over)."""
+        import ffn_inputs
+        codes = _c(w.codes, np.uint8)
+        scales = _c(w.scales, np.uint8)
+        rows, cols = w.rows, w.cols
+        mc = np.zeros((rows, cols // 2), dtype=np.uint8)
+        me = np.zeros((rows, cols // 32), dtype=np.uint8)
+        if self.lib.oracle_mx_requant_nvfp4(_ptr(codes), _ptr(scales), rows, cols, _ptr(mc), _ptr(me)) != 0:
+            raise MemoryError("oracle_mx_requant_nvfp4")
+        return ffn_inputs.MxWeight(mc, me, float(w.scale2))
+
+    def mx_linear(self, a_codes, a_e8m0, w_codes, w_e8m0) -> np.ndarray:
+        ac, ae, wc, we = (_c(t, np.uint8) for t in (a_codes, a_e8m0, w_codes, w_e8m0))
+        M, cols = ac.shape[0], ac.shape[1] * 2
+        rows = wc.shape[0]
+        y = np.empty((M, rows), dtype=np.float64)
+        self.lib.oracle_mx_linear_f64(_ptr(ac), _ptr(ae), M, cols, _ptr(wc), _ptr(we), rows, _ptr(y))
+        return y
+
+    def w4a4_dual(self, case, gate_mx, up_mx) -> Tuple[np.ndarray, np.ndarray]:
+        x = _c(case.x_bits, np.uint16)
+        M = x.shape[0]
+        gate = np.empty((M, case.N), dtype=np.float64)
+        up = np.empty((M, case.N), dtype=np.float64)
+        gc, ge, uc, ue = (_c(t, np.uint8) for t in (gate_mx.codes, gate_mx.e8m0, up_mx.codes, up_mx.e8m0))
+        rc = self.lib.oracle_w4a4_dual(_ptr(x), M, case.K, case.N, _ptr(gc), _ptr(ge), float(gate_mx.scale2),
+                                       _ptr(uc), _ptr(ue), float(up_mx.scale2), _ptr(gate), _ptr(up))
+        if rc != 0:
+            raise MemoryError("oracle_w4a4_dual")
+        return gate, up
+
+    def w4a4_ffn(self, case, gate_mx, up_mx, rows: Optional[np.ndarray] = None) -> np.ndarray:
+        x = _c(case.x_bits if rows is None else case.x_bits[np.asarray(rows)], np.uint16)
+        M = x.shape[0]
+        gc, ge, uc, ue = (_c(t, np.uint8) for t in (gate_mx.codes, gate_mx.e8m0, up_mx.codes, up_mx.e8m0))
+        dc, ds = _c(case.down.codes, np.uint8), _c(case.down.scales, np.uint8)
+        out = np.empty((M, case.K), dtype=np.float64)
+        rc = self.lib.oracle_w4a4_ffn(_ptr(x), M, case.K, case.N, int(case.act), _ptr(gc), _ptr(ge),
+                                      float(gate_mx.scale2), _ptr(uc), _ptr(ue), float(up_mx.scale2), _ptr(dc),
+                                      _ptr(ds), float(case.down.scale2), _ptr(out))
+        if rc != 0:
+            raise MemoryError("oracle_w4a4_ffn")
+        return out
+
+
 _default: Optional[Oracle] = None
 
 
@@ -325,6 +415,22 @@ def fp8_dual(case):
 
 def fp8_ffn(case, rows=None) -> np.ndarray:
     return default().fp8_ffn(case, rows)
+
+
+def mx_quantize_bf16(x_bits):
+    return default().mx_quantize_bf16(x_bits)
+
+
+def mx_requant(w):
+    return default().mx_requant(w)
+
+
+def w4a4_dual(case, gate_mx, up_mx):
+    return default().w4a4_dual(case, gate_mx, up_mx)
+
+
+def w4a4_ffn(case, gate_mx, up_mx, rows=None) -> np.ndarray:
+    return default().w4a4_ffn(case, gate_mx, up_mx, rows)
 
 
 def ulp_bf16(v: np.ndarray) -> np.ndarray:

@@ -28,6 +28,12 @@
  *  - qwen35_dense.rs page, weight loader: a dense BF16 weight is turned into
  *    NVFP4 on the GPU by a global-absmax pass followed by a quantise pass
  *    (the quantiser below; its scale rule is a reading, the pages give none).
+ *  - dense_ffn.rs page, the W4A4 native-FP4 prefill (w4a4_gemm and
+ *    quantize_nvfp4 handles, and the NVFP4 W4A4 MMQ arm of forward_prefill):
+ *    NVFP4 weights against activations quantised to 4 bits on every call,
+ *    gate and up only, the down projection kept on the W4A16 path, scale2
+ *    applied to the products (the W4A4 functions below; the scale format is
+ *    a reading for gfx950, see there).
  *  - qwen35_dense.rs page, proj_is_fp8_any_scale doc comment: a native FP8
  *    weight [N, K] is E4M3 bytes with an FP32 block-scale grid
  *    [ceil(N/128), ceil(K/128)] that the kernels index as
@@ -408,6 +414,161 @@ int oracle_fp8_ffn(const uint16_t *x_bits, int M, int K, int N, int act,
     if (gate && up && oracle_fp8_dual(x_bits, M, K, N, gw, gbs, uw, ubs, gate, up) == 0) {
         oracle_gated_act(act, gate, up, mn, gate); /* h overwrites gate */
         oracle_fp8_linear_f64(gate, M, N, K, dw, dbs, out);
+        rc = 0;
+    }
+    free(gate);
+    free(up);
+    return rc;
+}
+
+/* ------------------------------------------------------------ W4A4 (MXFP4)
+ * The matrix instructions of gfx950 that multiply 4-bit operands take one
+ * power-of-two (E8M0) scale per 32 consecutive elements of a row, not an
+ * E4M3 scale per 16, so the reading taken for the W4A4 arm is that both
+ * operands are MXFP4 as the OCP MX v1.0 specification defines it:
+ *   - per row and 32-element block, the shared exponent is
+ *     se = floor(log2(amax)) - 2 (2 being the largest E2M1 exponent), clamped
+ *     to [-127, 127], stored as the E8M0 byte se + 127; a block of zeros
+ *     gets se = 0;
+ *   - each element is E2M1(v / 2^se), nearest with ties to even, saturating
+ *     at 6, keeping its sign (oracle_e2m1_encode); v / 2^se is taken in fp32,
+ *     as the hardware conversion takes it (exact for the inputs here);
+ *   - activations: v = the bf16 value, quantised on every call;
+ *   - weights: requantised once from NVFP4, v = e2m1(code) * e4m3(scale)
+ *     (exact); scale2 is not folded in: it multiplies the projection's sum;
+ *   - products of two MXFP4 values are exact; sums are taken in double.
+ * The down projection stays on the W4A16 path (oracle_down). Inputs and
+ * scales must be finite. */
+
+double oracle_mx_value(int code, int e8m0)
+{
+    return oracle_e2m1_value(code & 15) * ldexp(1.0, e8m0 - 127);
+}
+
+int oracle_mx_block_exponent(double amax)
+{
+    int e;
+    if (amax == 0.0)
+        return 0;
+    frexp(amax, &e);  /* amax = f 2^e with f in [0.5, 1): floor(log2(amax)) = e - 1 */
+    int se = (e - 1) - 2;
+    if (se < -127)
+        se = -127;
+    if (se > 127)
+        se = 127;
+    return se;
+}
+
+/* v [rows, cols] (cols a multiple of 32) -> codes [rows, cols/2] (element 2j
+ * in the low nibble of byte j) and E8M0 bytes [rows, cols/32]. */
+void oracle_mx_quantize(const double *v, int rows, int cols, uint8_t *codes, uint8_t *e8m0)
+{
+    const int nb = cols / 32;
+    for (int r = 0; r < rows; ++r) {
+        for (int b = 0; b < nb; ++b) {
+            const double *blk = v + (size_t)r * cols + (size_t)b * 32;
+            double amax = 0.0;
+            for (int j = 0; j < 32; ++j)
+                if (fabs(blk[j]) > amax)
+                    amax = fabs(blk[j]);
+            const int se = oracle_mx_block_exponent(amax);
+            e8m0[(size_t)r * nb + b] = (uint8_t)(se + 127);
+            for (int j = 0; j < 32; ++j) {
+                const float q = (float)(blk[j] / ldexp(1.0, se));
+                const int code = oracle_e2m1_encode(q);
+                const int c = b * 32 + j;
+                uint8_t *byte = &codes[(size_t)r * (cols / 2) + (size_t)(c / 2)];
+                if (c % 2 == 0)
+                    *byte = (uint8_t)code;
+                else
+                    *byte = (uint8_t)(*byte | (code << 4));
+            }
+        }
+    }
+}
+
+int oracle_mx_quantize_bf16(const uint16_t *x_bits, int M, int K, uint8_t *codes, uint8_t *e8m0)
+{
+    double *v = (double *)malloc(sizeof(double) * (size_t)M * (size_t)K);
+    if (!v)
+        return -1;
+    for (size_t i = 0; i < (size_t)M * (size_t)K; ++i)
+        v[i] = oracle_bf16_value(x_bits[i]);
+    oracle_mx_quantize(v, M, K, codes, e8m0);
+    free(v);
+    return 0;
+}
+
+/* NVFP4 [rows, cols] (codes, scales; scale2 left out) -> MXFP4. */
+int oracle_mx_requant_nvfp4(const uint8_t *codes, const uint8_t *scales, int rows, int cols, uint8_t *mx_codes,
+                            uint8_t *mx_e8m0)
+{
+    double *v = (double *)malloc(sizeof(double) * (size_t)rows * (size_t)cols);
+    if (!v)
+        return -1;
+    oracle_dequant(codes, scales, 1.0f, rows, cols, v);
+    oracle_mx_quantize(v, rows, cols, mx_codes, mx_e8m0);
+    free(v);
+    return 0;
+}
+
+/* y[m, r] = sum_c mx(a)[m, c] * mx(w)[r, c]. */
+void oracle_mx_linear_f64(const uint8_t *a_codes, const uint8_t *a_e8m0, int M, int cols, const uint8_t *w_codes,
+                          const uint8_t *w_e8m0, int rows, double *y)
+{
+    long total = (long)M * rows;
+#pragma omp parallel for schedule(static)
+    for (long idx = 0; idx < total; ++idx) {
+        const int m = (int)(idx / rows);
+        const int r = (int)(idx % rows);
+        double acc = 0.0;
+        for (int c = 0; c < cols; ++c) {
+            const uint8_t ab = a_codes[(size_t)m * (cols / 2) + (size_t)(c / 2)];
+            const uint8_t wb = w_codes[(size_t)r * (cols / 2) + (size_t)(c / 2)];
+            const int ac = (c % 2 == 0) ? (ab & 0x0F) : (ab >> 4);
+            const int wc = (c % 2 == 0) ? (wb & 0x0F) : (wb >> 4);
+            acc += oracle_mx_value(ac, a_e8m0[(size_t)m * (cols / 32) + (size_t)(c / 32)]) *
+                   oracle_mx_value(wc, w_e8m0[(size_t)r * (cols / 32) + (size_t)(c / 32)]);
+        }
+        y[idx] = acc;
+    }
+}
+
+/* gate = scale2_g * (mx(x) . mx(W_g)), up likewise, over MXFP4 weights. */
+int oracle_w4a4_dual(const uint16_t *x_bits, int M, int K, int N, const uint8_t *g_codes, const uint8_t *g_e8m0,
+                     float g_scale2, const uint8_t *u_codes, const uint8_t *u_e8m0, float u_scale2, double *gate,
+                     double *up)
+{
+    uint8_t *xc = (uint8_t *)malloc((size_t)M * (size_t)(K / 2));
+    uint8_t *xs = (uint8_t *)malloc((size_t)M * (size_t)(K / 32));
+    int rc = -1;
+    if (xc && xs && oracle_mx_quantize_bf16(x_bits, M, K, xc, xs) == 0) {
+        oracle_mx_linear_f64(xc, xs, M, K, g_codes, g_e8m0, N, gate);
+        oracle_mx_linear_f64(xc, xs, M, K, u_codes, u_e8m0, N, up);
+        for (size_t i = 0; i < (size_t)M * (size_t)N; ++i) {
+            gate[i] *= (double)g_scale2;
+            up[i] *= (double)u_scale2;
+        }
+        rc = 0;
+    }
+    free(xc);
+    free(xs);
+    return rc;
+}
+
+/* The hybrid FFN: W4A4 gate and up, h = act(gate) * up, W4A16 down (NVFP4). */
+int oracle_w4a4_ffn(const uint16_t *x_bits, int M, int K, int N, int act, const uint8_t *g_codes,
+                    const uint8_t *g_e8m0, float g_scale2, const uint8_t *u_codes, const uint8_t *u_e8m0,
+                    float u_scale2, const uint8_t *d_codes, const uint8_t *d_scales, float d_scale2, double *out)
+{
+    size_t mn = (size_t)M * (size_t)N;
+    double *gate = (double *)malloc(sizeof(double) * mn);
+    double *up = (double *)malloc(sizeof(double) * mn);
+    int rc = -1;
+    if (gate && up &&
+        oracle_w4a4_dual(x_bits, M, K, N, g_codes, g_e8m0, g_scale2, u_codes, u_e8m0, u_scale2, gate, up) == 0) {
+        oracle_gated_act(act, gate, up, mn, gate);
+        oracle_down(gate, M, N, K, d_codes, d_scales, d_scale2, out);
         rc = 0;
     }
     free(gate);

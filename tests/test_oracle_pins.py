@@ -535,13 +535,168 @@ def pin_fp8_ffn_composition(orc):
         np.testing.assert_array_equal(orc.fp8_ffn(case, rows=np.array([2])), out[2:3])
 
 
+# ------------------------------------------------------------ W4A4 (MXFP4)
+
+_E2M1 = None
+
+
+def _e2m1_table():
+    global _E2M1
+    if _E2M1 is None:
+        _E2M1 = np.array([v for _, v in _read_table("e2m1_values.txt")])
+    return _E2M1
+
+
+def _mx_decode(codes, e8m0):
+    """MXFP4 -> float64 with the OCP E2M1 value table fixture and numpy
+    (element 2j is the low nibble of byte j; 2^(byte - 127) per 32)."""
+    t = _e2m1_table()
+    vals = np.stack([t[codes & 15], t[codes >> 4]], axis=-1).reshape(codes.shape[0], -1)
+    return vals * np.repeat(np.ldexp(1.0, e8m0.astype(np.int64) - 127), 32, axis=1)
+
+
+def pin_mx_exponent_rule(orc):
+    """The shared exponent is floor(log2(amax)) - 2 (math.frexp here), clamped
+    to [-127, 127]; anchors: amax 1 -> -2, 4 -> 0, 6 -> 0, 7.99 -> 0, 3.99 -> -1,
+    0.75 -> -3, 0 -> 0."""
+    for amax, want in ((1.0, -2), (4.0, 0), (6.0, 0), (7.99, 0), (3.99, -1), (0.75, -3), (0.0, 0),
+                       (2.0 ** -130, -127), (2.0 ** 200, 127)):
+        assert orc.mx_block_exponent(amax) == want, (amax, orc.mx_block_exponent(amax), want)
+    rng = np.random.default_rng(71)
+    for amax in np.exp(rng.uniform(-60, 60, size=200)):
+        m, e = math.frexp(amax)
+        assert orc.mx_block_exponent(amax) == max(-127, min(127, e - 1 - 2))
+
+
+def pin_mx_quantize_nearest(orc):
+    """Every element decodes to a nearest point of the E2M1 grid times the
+    block's scale, ties to the even code, saturating at 6, sign kept; brute
+    force over the fixture table in numpy."""
+    rng = np.random.default_rng(72)
+    v = rng.normal(size=(6, 256)) * np.exp(rng.uniform(-8, 8, size=(6, 1)))
+    v[0, :32] = 0.0
+    v[1, 5] = -1e-30
+    codes, e8m0 = orc.mx_quantize(v)
+    t = _e2m1_table()
+    for r in range(v.shape[0]):
+        for b in range(v.shape[1] // 32):
+            blk = v[r, 32 * b:32 * b + 32]
+            amax = np.abs(blk).max()
+            se = 0 if amax == 0 else max(-127, min(127, math.frexp(amax)[1] - 3))
+            assert e8m0[r, b] == se + 127
+            for j in range(32):
+                c = 32 * b + j
+                byte = codes[r, c // 2]
+                code = byte & 15 if c % 2 == 0 else byte >> 4
+                q = float(np.float32(blk[j] / 2.0 ** se))
+                a = abs(q)
+                if a >= 6:
+                    assert code & 7 == 7
+                else:
+                    d = np.abs(t[:8] - a)
+                    best = np.flatnonzero(d == d.min())
+                    assert (code & 7) in best, (r, c, q, code)
+                    if len(best) == 2:
+                        assert (code & 7) % 2 == 0
+                assert (code >> 3) == (1 if math.copysign(1.0, q) < 0 else 0)
+
+
+def pin_mx_grid_roundtrip(orc):
+    """Blocks built as E2M1 values x 2^s with a largest magnitude of 4 or 6
+    come back exactly: codes, and E8M0 = s + 127."""
+    rng = np.random.default_rng(73)
+    rows, cols = 4, 128
+    codes = rng.integers(0, 16, size=(rows, cols)).astype(np.uint8)
+    codes[:, ::32] = rng.choice([6, 7, 14, 15], size=(rows, cols // 32))  # +-4 or +-6 in every block
+    s = rng.integers(-20, 20, size=(rows, cols // 32))
+    v = _e2m1_table()[codes] * np.repeat(np.ldexp(1.0, s), 32, axis=1)
+    mc, me = orc.mx_quantize(v)
+    np.testing.assert_array_equal(me, (s + 127).astype(np.uint8))
+    np.testing.assert_array_equal(_mx_decode(mc, me), v)
+
+
+def _aligned_nvfp4(rng, rows, cols):
+    """An NVFP4 weight whose two E4M3 scales in each 32-block are one power of
+    two and whose block maximum is 4 or 6: exactly MXFP4-representable."""
+    codes = rng.integers(0, 16, size=(rows, cols)).astype(np.uint8)
+    codes[:, ::32] = rng.choice([6, 7, 14, 15], size=(rows, cols // 32))
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    e = rng.integers(-6, 3, size=(rows, cols // 32))
+    sc = np.repeat(((e + 7) << 3).astype(np.uint8), 2, axis=1)  # E4M3 2^e, same for both halves
+    return fi.Nvfp4Weight(packed, sc, 0.75)
+
+
+def pin_mx_requant(orc):
+    """Requantising an exactly representable NVFP4 weight keeps every value;
+    on general weights every requantised value is the nearest-grid MXFP4 of
+    the NVFP4 value (checked through the quantiser pinned above, on the
+    independently dequantised weight)."""
+    rng = np.random.default_rng(74)
+    w = _aligned_nvfp4(rng, 8, 256)
+    mx = orc.mx_requant(w)
+    assert mx.scale2 == 0.75
+    np.testing.assert_array_equal(_mx_decode(mx.codes, mx.e8m0), _independent_dequant(fi.Nvfp4Weight(w.codes, w.scales, 1.0)))
+    g = fi.make_small(1, 256, 96, seed=75).gate
+    mx = orc.mx_requant(g)
+    c2, e2 = orc.mx_quantize(_independent_dequant(fi.Nvfp4Weight(g.codes, g.scales, 1.0)))
+    np.testing.assert_array_equal(mx.codes, c2)
+    np.testing.assert_array_equal(mx.e8m0, e2)
+
+
+def pin_w4a4_reduces_to_w4a16(orc):
+    """Activations exactly on each block's MXFP4 grid and exactly
+    representable weights: the W4A4 gate/up equal the W4A16 oracle's bit for
+    bit (both sum the same exact products in the same order)."""
+    rng = np.random.default_rng(76)
+    M, K, N = 3, 256, 64
+    wg, wu = _aligned_nvfp4(rng, N, K), _aligned_nvfp4(rng, N, K)
+    xc = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    xc[:, ::32] = 7
+    xs = rng.integers(-4, 4, size=(M, K // 32))
+    xv = _e2m1_table()[xc] * np.repeat(np.ldexp(1.0, xs), 32, axis=1)
+    x_bits = fi.f32_to_bf16_bits(xv.astype(np.float32))
+    assert np.array_equal(fi.bf16_bits_to_f32(x_bits).astype(np.float64), xv)
+    case = fi.FfnCase("w4a4_exact", M, K, N, fi.ACT_SILU, x_bits, wg, wu, _aligned_nvfp4(rng, K, N))
+    g4, u4 = orc.w4a4_dual(case, orc.mx_requant(wg), orc.mx_requant(wu))
+    g, u = orc.dual(case)
+    np.testing.assert_array_equal(g4, g)
+    np.testing.assert_array_equal(u4, u)
+
+
+def pin_w4a4_matches_numpy(orc):
+    """General activations and weights: W4A4 gate/up equal scale2 times numpy's
+    float64 matmul of the independently decoded MXFP4 operands, to double
+    rounding; the whole hybrid FFN equals the W4A16 down GEMV (oracle.down,
+    pinned above) of act(gate) * up from scipy/torch."""
+    for act in (fi.ACT_SILU, fi.ACT_GELU_TANH):
+        case = fi.make_small(2, 192, 160, act=act, seed=77, scale2=0.375)
+        gm, um = orc.mx_requant(case.gate), orc.mx_requant(case.up)
+        g4, u4 = orc.w4a4_dual(case, gm, um)
+        xc, xe = orc.mx_quantize_bf16(case.x_bits)
+        xa = _mx_decode(xc, xe)
+        for mx, got in ((gm, g4), (um, u4)):
+            wd = _mx_decode(mx.codes, mx.e8m0)
+            ref = 0.375 * (xa @ wd.T)
+            assert np.all(np.abs(got - ref) <= 1e-12 * (np.abs(xa) @ np.abs(wd).T) + 1e-300)
+        if act == fi.ACT_SILU:
+            h = g4 * scipy.special.expit(g4) * u4
+        else:
+            h = torch.nn.functional.gelu(torch.from_numpy(g4), approximate="tanh").numpy() * u4
+        ref = h @ _independent_dequant(case.down).T
+        out = orc.w4a4_ffn(case, gm, um)
+        assert np.all(np.abs(out - ref) <= 1e-10 * (np.abs(h) @ np.abs(_independent_dequant(case.down)).T))
+        np.testing.assert_array_equal(orc.w4a4_ffn(case, gm, um, rows=np.array([1])), out[1:2])
+
+
 PINS = [pin_e2m1_table, pin_e4m3_vs_torch, pin_e4m3_anchors_and_order, pin_byte_nibble_order,
         pin_scale_blocks, pin_dequant_independent, pin_activations, pin_gated_act,
         pin_one_hot_selects, pin_down_orientation, pin_ternary_exact_vs_numpy,
         pin_matches_numpy_matmul, pin_fraction_brute_force, pin_down_fraction_bound,
         pin_ffn_composition, pin_e2m1_encode_grid, pin_e4m3_encode_vs_torch, pin_quantize_zero,
         pin_quantize_exact_roundtrip, pin_quantize_error_bound, pin_fp8_block_indexing,
-        pin_fp8_dequant_vs_torch, pin_fp8_exact_vs_numpy, pin_fp8_fraction_bound, pin_fp8_ffn_composition]
+        pin_fp8_dequant_vs_torch, pin_fp8_exact_vs_numpy, pin_fp8_fraction_bound, pin_fp8_ffn_composition,
+        pin_mx_exponent_rule, pin_mx_quantize_nearest, pin_mx_grid_roundtrip, pin_mx_requant,
+        pin_w4a4_reduces_to_w4a16, pin_w4a4_matches_numpy]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -645,6 +800,16 @@ MUTANTS = {
     "q_pack_nibble": ("(c % 2 == 0) ? code : (code << 4)", "(c % 2 == 0) ? (code << 4) : code"),
     "q_e2m1_saturation": ("return signbit(q) ? 15 : 7;", "return signbit(q) ? 14 : 6;"),
     "q_e4m3_range": ("for (int b = 0; b < 127; ++b) {", "for (int b = 0; b < 126; ++b) {"),
+    "mx_exp_offset": ("int se = (e - 1) - 2;", "int se = (e - 1) - 1;"),
+    "mx_exp_round": ("int se = (e - 1) - 2;", "int se = e - 2;"),
+    "mx_zero_scale": ("            const int se = oracle_mx_block_exponent(amax);\n            e8m0[(size_t)r * nb + b] = (uint8_t)(se + 127);",
+                      "            const int se = oracle_mx_block_exponent(amax);\n            e8m0[(size_t)r * nb + b] = (uint8_t)(se + 126);"),
+    "mx_requant_scale_dropped": ("    oracle_dequant(codes, scales, 1.0f, rows, cols, v);\n    oracle_mx_quantize(v, rows, cols, mx_codes",
+                                 "    oracle_dequant(codes, scales, 1.0f, rows, cols, v);\n    for (size_t i = 0; i < (size_t)rows * cols; ++i) v[i] = v[i] > 0 ? 1.0 : (v[i] < 0 ? -1.0 : 0.0);\n    oracle_mx_quantize(v, rows, cols, mx_codes"),
+    "mx_act_nibbles": ("const int ac = (c % 2 == 0) ? (ab & 0x0F) : (ab >> 4);", "const int ac = (c % 2 == 0) ? (ab >> 4) : (ab & 0x0F);"),
+    "w4a4_scale2_dropped": ("            gate[i] *= (double)g_scale2;", "            gate[i] *= 1.0;"),
+    "w4a4_down_scale2": ("u_scale2, gate, up) == 0) {\n        oracle_gated_act(act, gate, up, mn, gate);\n        oracle_down(gate, M, N, K, d_codes, d_scales, d_scale2, out);",
+                         "u_scale2, gate, up) == 0) {\n        oracle_gated_act(act, gate, up, mn, gate);\n        oracle_down(gate, M, N, K, d_codes, d_scales, 1.0f, out);"),
     "fp8_block_cols": ("(size_t)(c / 128)]", "(size_t)(c / 64)]"),
     "fp8_block_rows": ("(size_t)(r / 128) * (size_t)bcols", "(size_t)(r / 256) * (size_t)bcols"),
     "fp8_grid_stride": ("int bcols = (cols + 127) / 128;", "int bcols = cols / 128;"),
