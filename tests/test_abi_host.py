@@ -44,7 +44,10 @@ def test_exports_every_header_symbol():
                           "ffn_nvfp4_quantize", "ffn_nvfp4_quantize_workspace_bytes"}
     fp8 = ffn.header_functions(ffn.FP8_HEADER_PATH)
     assert set(fp8) == {"ffn_fp8_forward", "ffn_fp8_dual_gemv", "ffn_fp8_down_gemv", "ffn_fp8_workspace_bytes"}
-    for n in list(names) + list(fp8):
+    w4 = ffn.header_functions(ffn.W4A4_HEADER_PATH)
+    assert set(w4) == {"ffn_w4a4_prepare_weight", "ffn_w4a4_workspace_bytes", "ffn_w4a4_dual_gemm",
+                       "ffn_w4a4_forward"}
+    for n in list(names) + list(fp8) + list(w4):
         assert hasattr(lib, n), n
 
 
@@ -258,3 +261,72 @@ def test_fp8_validation(call):
         assert f8down(out=FAKE + 0x400002) == ffn.ERR_ALIGN
         assert f8down(act=-1) == ffn.ERR_ACT
         assert f8down(M=0, act=7) == ffn.ERR_ACT
+
+
+# ------------------------------------------------------------ W4A4 entry points
+
+
+def MX(codes=FAKE, scales=FAKE + 0x10000, scale2=1.0):
+    return ffn.MxWeightStruct(codes, scales, scale2)
+
+
+def w4fwd(x=FAKE, M=1, K=256, N=64, g=None, u=None, d=None, act=0, ws=FAKE + 0x200000, wsb=1 << 24,
+          out=FAKE + 0x400000):
+    g, u, d = g or MX(), u or MX(), d or W()
+    return ffn.load().ffn_w4a4_forward(x, M, K, N, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), act,
+                                       ws, wsb, out, 0)
+
+
+def w4dual(x=FAKE, M=1, K=256, N=64, g=None, u=None, go=FAKE + 0x200000, uo=FAKE + 0x400000,
+           ws=FAKE + 0x600000, wsb=1 << 24):
+    g, u = g or MX(), u or MX()
+    return ffn.load().ffn_w4a4_dual_gemm(x, M, K, N, ctypes.byref(g), ctypes.byref(u), go, uo, ws, wsb, 0)
+
+
+def test_w4a4_workspace_bytes():
+    r = lambda b: (b + 255) // 256 * 256
+    partials = ffn.w4a4_workspace_bytes(1, 256, 64) - r(128) - r(8) - r(128)
+    assert partials > 0 and partials % 256 == 0
+    assert ffn.w4a4_workspace_bytes(128, 5120, 17408) == r(128 * 2560) + r(128 * 160) + r(128 * 17408 * 2) + partials
+    assert ffn.w4a4_workspace_bytes(0, 256, 64) == 0
+    assert ffn.w4a4_workspace_bytes(1, 128, 64) == 0     # K must be a multiple of 256
+    assert ffn.w4a4_workspace_bytes(1, 256, 96) == 0     # N must be a multiple of 64
+    assert ffn.w4a4_workspace_bytes(65537, 256, 64) == 0
+
+
+@pytest.mark.parametrize("call", [w4fwd, w4dual])
+def test_w4a4_validation(call):
+    assert call(g=MX(codes=0)) == ffn.ERR_NULL
+    assert call(u=MX(scales=0)) == ffn.ERR_NULL
+    assert call(g=MX(codes=FAKE + 8)) == ffn.ERR_ALIGN
+    assert call(g=MX(scales=FAKE + 0x10004)) == ffn.ERR_ALIGN
+    assert call(g=MX(scale2=float("inf"))) == ffn.ERR_SCALE2
+    for K, N in ((128, 64), (256, 96), (0, 64), (256, 0), (65792, 64)):
+        assert call(K=K, N=N) == ffn.ERR_SHAPE, (K, N)
+    assert call(M=-1) == ffn.ERR_BATCH
+    assert call(M=65537) == ffn.ERR_BATCH
+    assert call(M=0, x=0) == ffn.OK
+    assert call(x=0) == ffn.ERR_NULL
+    assert call(x=FAKE + 8) == ffn.ERR_ALIGN
+    assert call(wsb=100) == ffn.ERR_WORKSPACE
+    if call is w4fwd:
+        assert w4fwd(act=3) == ffn.ERR_ACT
+        assert w4fwd(d=W(scales=FAKE + 0x10002)) == ffn.ERR_ALIGN
+        assert w4fwd(d=W(codes=0)) == ffn.ERR_NULL
+        assert w4fwd(d=W(scale2=float("nan"))) == ffn.ERR_SCALE2
+    else:
+        assert w4dual(go=0) == ffn.ERR_NULL
+        assert w4dual(ws=0) == ffn.ERR_NULL
+
+
+def test_w4a4_prepare_validation():
+    lib = ffn.load()
+    w = W()
+    call = lambda rows=64, cols=256, mc=FAKE + 0x200000, ms=FAKE + 0x300000, wt=w: \
+        lib.ffn_w4a4_prepare_weight(ctypes.byref(wt), rows, cols, mc, ms, 0)
+    assert call(mc=0) == ffn.ERR_NULL
+    assert call(wt=W(codes=0)) == ffn.ERR_NULL
+    assert call(cols=48) == ffn.ERR_SHAPE
+    assert call(rows=0) == ffn.ERR_SHAPE
+    assert call(mc=FAKE + 0x200008) == ffn.ERR_ALIGN
+    assert call(wt=W(scales=FAKE + 0x10001)) == ffn.ERR_ALIGN

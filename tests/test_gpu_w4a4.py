@@ -1,0 +1,133 @@
+"""GPU parity of the W4A4 prefill arm against the W4A4 oracle (needs an MI355X).
+
+The integer steps are compared bit for bit: the NVFP4 -> MXFP4 weight
+requantisation and the per-call MXFP4 quantisation of the activations (read
+back from the workspace, where the entry points document it). The dual GEMM's
+fp32 outputs are held to 1e-4 * rms(ref) + 1e-6 * |ref| (products of MXFP4
+values are exact in fp32; only the accumulation order differs), the hybrid
+FFN to the FFN output bound. Against the lossless W4A16 oracle the arm is only
+expected to correlate (cosine), as the pages describe it as lossy.
+"""
+import numpy as np
+import pytest
+import torch
+
+import ffn_inputs as fi
+import oracle
+import w4a16_nvfp4_dense_amd as ffn
+
+pytestmark = pytest.mark.gpu
+
+
+def _r256(b):
+    return (b + 255) // 256 * 256
+
+
+class Loaded:
+    def __init__(self, case):
+        self.case = case
+        self.gate = ffn.DeviceWeight.from_host(case.gate)
+        self.up = ffn.DeviceWeight.from_host(case.up)
+        self.down = ffn.DeviceWeight.from_host(case.down)
+        self.gmx = ffn.w4a4_prepare_weight(self.gate)
+        self.umx = ffn.w4a4_prepare_weight(self.up)
+        self.x = ffn.bf16_from_bits(case.x_bits)
+        # the oracle's requantised weights (checked equal to the GPU's below)
+        self.ogmx = oracle.mx_requant(case.gate)
+        self.oumx = oracle.mx_requant(case.up)
+
+
+def assert_dual_close(got, ref, what):
+    got = got.double().cpu().numpy()
+    rms = np.sqrt(np.mean(ref ** 2))
+    bound = 1e-4 * rms + 1e-6 * np.abs(ref)
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), f"{what}: max err/rms {np.max(err) / rms:.3e}"
+
+
+def assert_ffn_close(out_gpu, out_ref, what):
+    got = ffn.bf16_to_f64(out_gpu)
+    bound = oracle.parity_bound(out_ref)
+    err = np.abs(got - out_ref)
+    bad = ~(err <= bound)
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside bound, max err/rms " \
+                          f"{np.max(err) / np.sqrt(np.mean(out_ref ** 2)):.3e}"
+
+
+def assert_requant_exact(L):
+    np.testing.assert_array_equal(L.gmx.codes.cpu().numpy(), L.ogmx.codes)
+    np.testing.assert_array_equal(L.gmx.scales.cpu().numpy(), L.ogmx.e8m0)
+    np.testing.assert_array_equal(L.umx.codes.cpu().numpy(), L.oumx.codes)
+    np.testing.assert_array_equal(L.umx.scales.cpu().numpy(), L.oumx.e8m0)
+
+
+SHAPES = [
+    # (M, K, N, act, seed)
+    (1, 256, 64, fi.ACT_SILU, 1),
+    (17, 512, 128, fi.ACT_GELU_TANH, 2),    # tokens not a multiple of 32
+    (45, 1024, 320, fi.ACT_SILU, 3),
+    (128, 2048, 1024, fi.ACT_SILU, 4),
+    (200, 768, 448, fi.ACT_GELU_TANH, 5),   # two token groups, two down blocks
+]
+
+
+@pytest.mark.parametrize("M,K,N,act,seed", SHAPES, ids=[f"m{m}_k{k}_n{n}_a{a}" for m, k, n, a, _ in SHAPES])
+def test_w4a4_parity(M, K, N, act, seed):
+    print(f"\nw4a4 case M={M} K={K} N={N} act={act}", flush=True)
+    case = fi.make_small(M, K, N, act=act, seed=seed)
+    case.x_bits[0, :64] = 0  # a block of zeros (shared exponent 0)
+    L = Loaded(case)
+    assert_requant_exact(L)
+    ws = torch.zeros(ffn.w4a4_workspace_bytes(M, K, N), dtype=torch.uint8, device="cuda")
+    g, u = ffn.w4a4_dual_gemm(L.x, L.gmx, L.umx, workspace=ws)
+    torch.cuda.synchronize()
+    # the activations' MXFP4 form, as the workspace documents it
+    xc, xe = oracle.mx_quantize_bf16(case.x_bits)
+    wsn = ws.cpu().numpy()
+    np.testing.assert_array_equal(wsn[:M * K // 2].reshape(M, K // 2), xc)
+    off = _r256(M * K // 2)
+    np.testing.assert_array_equal(wsn[off:off + M * K // 32].reshape(M, K // 32), xe)
+    gr, ur = oracle.w4a4_dual(case, L.ogmx, L.oumx)
+    assert_dual_close(g, gr, "gate")
+    assert_dual_close(u, ur, "up")
+    out = ffn.w4a4_forward(L.x, L.gmx, L.umx, L.down, act)
+    assert_ffn_close(out, oracle.w4a4_ffn(case, L.ogmx, L.oumx), case.name)
+    # repeatable
+    assert torch.equal(ffn.w4a4_forward(L.x, L.gmx, L.umx, L.down, act), out)
+
+
+def test_w4a4_format_coverage():
+    """Every E2M1 code and every finite E4M3 scale in the NVFP4 weights: the
+    requantisation bit for bit, the dual at the fp32 bound."""
+    case = fi.make_format_coverage(M=40)
+    L = Loaded(case)
+    assert_requant_exact(L)
+    g, u = ffn.w4a4_dual_gemm(L.x, L.gmx, L.umx)
+    gr, ur = oracle.w4a4_dual(case, L.ogmx, L.oumx)
+    assert_dual_close(g, gr, "gate")
+    assert_dual_close(u, ur, "up")
+
+
+def test_w4a4_prefill_config_sampled():
+    """The prefill shape (M = 128, K = 5120, N = 17408): requantisation bit
+    for bit on both weights, and the dual GEMM and the hybrid forward on
+    sampled token rows against the oracle (the arm's rows are independent:
+    quantisation is per token row). Against the lossless W4A16 oracle, the
+    sampled rows correlate (cosine > 0.95)."""
+    case = fi.make_config(4, M=128)
+    L = Loaded(case)
+    assert_requant_exact(L)
+    g, u = ffn.w4a4_dual_gemm(L.x, L.gmx, L.umx)
+    out = ffn.w4a4_forward(L.x, L.gmx, L.umx, L.down, case.act)
+    rows = np.array([0, 37, 127])
+    sub = case.with_x(case.x_bits[rows])
+    gr, ur = oracle.w4a4_dual(sub, L.ogmx, L.oumx)
+    assert_dual_close(g[rows], gr, "gate")
+    assert_dual_close(u[rows], ur, "up")
+    ref = oracle.w4a4_ffn(sub, L.ogmx, L.oumx)
+    assert_ffn_close(out[rows], ref, "w4a4 forward")
+    lossless = oracle.ffn(sub)
+    got = ffn.bf16_to_f64(out[rows])
+    cos = float(np.sum(got * lossless) / np.linalg.norm(got) / np.linalg.norm(lossless))
+    print(f"\nw4a4 vs w4a16 cosine on sampled rows: {cos:.5f}", flush=True)
+    assert cos > 0.95

@@ -20,6 +20,13 @@ and, for block-scaled FP8 weights (``include/ffn_fp8.h``):
 * :func:`fp8_dual_gemv`  -- ``ffn_fp8_dual_gemv``
 * :func:`fp8_down_gemv`  -- ``ffn_fp8_down_gemv``
 * :func:`fp8_workspace_bytes` -- ``ffn_fp8_workspace_bytes``
+
+and the W4A4 prefill arm over MXFP4 operands (``include/ffn_w4a4.h``):
+
+* :func:`w4a4_prepare_weight` -- ``ffn_w4a4_prepare_weight`` NVFP4 -> MXFP4 (once)
+* :func:`w4a4_dual_gemm`  -- ``ffn_w4a4_dual_gemm``
+* :func:`w4a4_forward`    -- ``ffn_w4a4_forward``
+* :func:`w4a4_workspace_bytes` -- ``ffn_w4a4_workspace_bytes``
 """
 from __future__ import annotations
 
@@ -32,6 +39,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "lib", "libffn_nvfp4.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "ffn_nvfp4.h")
 FP8_HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "ffn_fp8.h")
+W4A4_HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "ffn_w4a4.h")
 
 ACT_SILU = 0
 ACT_GELU_TANH = 1
@@ -65,12 +73,19 @@ class Fp8WeightStruct(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("block_scale", ctypes.c_void_p)]
 
 
+class MxWeightStruct(ctypes.Structure):
+    """ffn_mxfp4_weight: device codes, device E8M0 bytes, host fp32 scale2."""
+
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("scale2", ctypes.c_float)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _WP = ctypes.POINTER(WeightStruct)
 _FP = ctypes.POINTER(Fp8WeightStruct)
+_MP = ctypes.POINTER(MxWeightStruct)
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -106,6 +121,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ffn_fp8_dual_gemv.argtypes = [_P, _I, _I, _I, _FP, _FP, _P, _P, _P]
     lib.ffn_fp8_down_gemv.restype = _I
     lib.ffn_fp8_down_gemv.argtypes = [_P, _P, _I, _I, _I, _FP, _I, _P, _P]
+    lib.ffn_w4a4_prepare_weight.restype = _I
+    lib.ffn_w4a4_prepare_weight.argtypes = [_WP, _I, _I, _P, _P, _P]
+    lib.ffn_w4a4_workspace_bytes.restype = ctypes.c_size_t
+    lib.ffn_w4a4_workspace_bytes.argtypes = [_I, _I, _I]
+    lib.ffn_w4a4_dual_gemm.restype = _I
+    lib.ffn_w4a4_dual_gemm.argtypes = [_P, _I, _I, _I, _MP, _MP, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.ffn_w4a4_forward.restype = _I
+    lib.ffn_w4a4_forward.argtypes = [_P, _I, _I, _I, _MP, _MP, _WP, _I, _P, ctypes.c_size_t, _P, _P]
     _lib = lib
     return lib
 
@@ -115,7 +138,7 @@ def header_functions(path: str = HEADER_PATH) -> Sequence[str]:
     import re
     text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ffn_(?:nvfp4|fp8)_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ffn_(?:nvfp4|fp8|w4a4)_[a-z_0-9]+)\s*\(", text)))
 
 
 def version() -> int:
@@ -394,4 +417,89 @@ def fp8_down_gemv(gate_in, up_in, down: Fp8DeviceWeight, act: int = ACT_SILU, ou
     rc = load().ffn_fp8_down_gemv(gate_in.data_ptr(), up_in.data_ptr(), M, N, K, ctypes.byref(d), int(act),
                                   out.data_ptr(), _stream_handle(stream))
     _check(rc, "ffn_fp8_down_gemv")
+    return out
+
+
+# ------------------------------------------------------------ W4A4 (MXFP4)
+
+
+@dataclasses.dataclass
+class MxDeviceWeight:
+    """An MXFP4 weight on the GPU: codes uint8 [rows, cols/2], E8M0 scales
+    uint8 [rows, cols/32], and the host fp32 scale2."""
+
+    codes: "object"
+    scales: "object"
+    scale2: float
+
+    @property
+    def rows(self) -> int:
+        return int(self.codes.shape[0])
+
+    @property
+    def cols(self) -> int:
+        return int(self.codes.shape[1]) * 2
+
+    def struct(self) -> MxWeightStruct:
+        return MxWeightStruct(self.codes.data_ptr(), self.scales.data_ptr(), float(self.scale2))
+
+
+def w4a4_prepare_weight(w: DeviceWeight, stream=None) -> MxDeviceWeight:
+    """Requantise an NVFP4 weight to MXFP4 on the GPU (asynchronous)."""
+    import torch
+    rows, cols = w.rows, w.cols
+    dev = w.codes.device
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    st = w.struct()
+    rc = load().ffn_w4a4_prepare_weight(ctypes.byref(st), rows, cols, codes.data_ptr(), scales.data_ptr(),
+                                        _stream_handle(stream))
+    _check(rc, "ffn_w4a4_prepare_weight")
+    return MxDeviceWeight(codes, scales, float(w.scale2))
+
+
+def w4a4_workspace_bytes(M: int, K: int, N: int) -> int:
+    return int(load().ffn_w4a4_workspace_bytes(int(M), int(K), int(N)))
+
+
+def w4a4_dual_gemm(x, gate: MxDeviceWeight, up: MxDeviceWeight, gate_out=None, up_out=None, workspace=None,
+                   stream=None):
+    """(gate, up) fp32 [M, N] over MXFP4 activations and weights."""
+    import torch
+    M, K = x.shape
+    N = gate.rows
+    _check_tensor(x, torch.bfloat16, (M, K), "x")
+    if gate_out is None:
+        gate_out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if up_out is None:
+        up_out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check_tensor(gate_out, torch.float32, (M, N), "gate_out")
+    _check_tensor(up_out, torch.float32, (M, N), "up_out")
+    if workspace is None:
+        workspace = torch.empty(max(w4a4_workspace_bytes(M, K, N), 1), dtype=torch.uint8, device=x.device)
+    g, u = gate.struct(), up.struct()
+    rc = load().ffn_w4a4_dual_gemm(x.data_ptr(), M, K, N, ctypes.byref(g), ctypes.byref(u), gate_out.data_ptr(),
+                                   up_out.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _check(rc, "ffn_w4a4_dual_gemm")
+    return gate_out, up_out
+
+
+def w4a4_forward(x, gate: MxDeviceWeight, up: MxDeviceWeight, down: DeviceWeight, act: int = ACT_SILU, out=None,
+                 workspace=None, stream=None):
+    """out[M, K] (bf16): W4A4 gate and up, then the NVFP4 down projection."""
+    import torch
+    M, K = x.shape
+    N = gate.rows
+    _check_tensor(x, torch.bfloat16, (M, K), "x")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
+    _check_tensor(out, torch.bfloat16, (M, K), "out")
+    if workspace is None:
+        workspace = torch.empty(max(w4a4_workspace_bytes(M, K, N), 1), dtype=torch.uint8, device=x.device)
+    g, u, d = gate.struct(), up.struct(), down.struct()
+    rc = load().ffn_w4a4_forward(x.data_ptr(), M, K, N, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), int(act),
+                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(), out.data_ptr(),
+                                 _stream_handle(stream))
+    _check(rc, "ffn_w4a4_forward")
     return out

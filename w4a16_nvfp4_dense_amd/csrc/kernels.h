@@ -80,3 +80,27 @@ hipError_t launch_fp8_down(int M, InKind in, const void *in0, const float *in1, 
                            int rows, int cols, hipStream_t stream);
 
 }  // namespace ffn
+
+namespace ffn {
+
+// An MXFP4 weight of shape [rows, cols]: E2M1 codes [rows, cols/2], E8M0
+// exponent bytes [rows, cols/32], and the per-tensor fp32 scale2.
+struct MxWeightArg {
+    const uint8_t *codes;
+    const uint8_t *e8m0;
+    float scale2;
+};
+
+// bf16 [rows, cols] -> MXFP4 codes and E8M0 bytes (cols a multiple of 32).
+hipError_t launch_mx_quant_bf16(const void *x, int rows, int cols, uint8_t *codes, uint8_t *e8m0,
+                                hipStream_t stream);
+// NVFP4 codes and scales [rows, cols] -> MXFP4 (scale2 is not folded in).
+hipError_t launch_mx_requant(const uint8_t *codes, const uint8_t *scales, int rows, int cols, uint8_t *mx_codes,
+                             uint8_t *mx_e8m0, hipStream_t stream);
+// W4A4 dual GEMM over MXFP4 activations [M, K] and weights [N, K]: OUT_F32_PAIR
+// (out0 = fp32 gate, out1 = fp32 up) or OUT_H_SILU / OUT_H_GELU (out0 = bf16 h).
+// N a multiple of 32, K a multiple of 256.
+hipError_t launch_w4a4_dual(int M, OutKind out, const uint8_t *xc, const uint8_t *xe, const MxWeightArg &g,
+                            const MxWeightArg &u, void *out0, float *out1, int N, int K, hipStream_t stream);
+
+}  // namespace ffn
