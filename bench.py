@@ -55,6 +55,11 @@ QUANT_METRIC = "µs per BF16->NVFP4 weight quantise + achieved HBM GB/s (% of pe
 FP8_WORKLOADS = {"fp8_decode_silu_m1": 1, "fp8_verify_silu_m2": 2, "fp8_verify_silu_m3": 3,
                  "fp8_verify_silu_m8": 8}
 FP8_METRIC = "µs/FFN forward + achieved HBM GB/s (% of peak), block-scaled FP8 SwiGLU"
+# The W4A4 prefill arm (ffn_w4a4_forward: MXFP4 gate/up on FP4 matrix cores,
+# NVFP4 down on the bf16 arm) on the prefill shape; its own line.
+W4A4_WORKLOADS = {"w4a4_prefill_silu_m128": 128}
+W4A4_METRIC = "µs/FFN forward + achieved TFLOP/s, W4A4 (MXFP4 gate/up) prefill SwiGLU"
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 
 
@@ -251,6 +256,119 @@ def bench_fp8(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_w4a4(args):
+    import numpy as np
+    import torch
+
+    import ffn_inputs as fi
+    import w4a16_nvfp4_dense_amd as ffn
+
+    lib = ffn.load()
+    M = W4A4_WORKLOADS[args.workload]
+    case = fi.make_config(4, M=M)
+    K, N, act = case.K, case.N, case.act
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    copies = []
+    for _ in range(args.copies):
+        g, u, d = (ffn.DeviceWeight.from_host(w, dev) for w in (case.gate, case.up, case.down))
+        copies.append((ffn.w4a4_prepare_weight(g), ffn.w4a4_prepare_weight(u), d))
+    torch.cuda.synchronize()
+    structs = [(g.struct(), u.struct(), d.struct()) for g, u, d in copies]
+    refs = [tuple(ctypes.byref(x) for x in st) for st in structs]
+    x = ffn.bf16_from_bits(case.x_bits, dev)
+    out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    ws_bytes = ffn.w4a4_workspace_bytes(M, K, N)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    gate_out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    up_out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    nc = len(refs)
+
+    def step(i):
+        g, u, d = refs[i % nc]
+        rc = lib.ffn_w4a4_forward(x.data_ptr(), M, K, N, g, u, d, act, ws.data_ptr(), ws_bytes, out.data_ptr(), sh)
+        if rc:
+            raise ffn.FfnError(rc, "ffn_w4a4_forward")
+
+    def dual(i):
+        g, u, _ = refs[i % nc]
+        rc = lib.ffn_w4a4_dual_gemm(x.data_ptr(), M, K, N, g, u, gate_out.data_ptr(), up_out.data_ptr(),
+                                    ws.data_ptr(), ws_bytes, sh)
+        if rc:
+            raise ffn.FfnError(rc, "ffn_w4a4_dual_gemm")
+
+    outs = []
+    for i in range(nc):
+        step(i)
+        outs.append(out.clone())
+    torch.cuda.synchronize()
+    assert all(torch.equal(o, outs[0]) for o in outs), "weight copies disagree"
+
+    def timed(fn, n):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    steps = min(args.steps, 500)
+    ms_per_step = timed(step, steps) / steps
+    us = ms_per_step * 1e3
+    flops = 2.0 * 3 * M * K * N
+    tflops = flops / (us * 1e-6) / 1e12
+    dual_us = timed(dual, steps) / steps * 1e3
+    dual_flops = 2.0 * 2 * M * K * N
+    dual_tflops = dual_flops / (dual_us * 1e-6) / 1e12
+    log(f"[bench] {args.workload}: {us:.2f} us/forward, {tflops:.1f} TFLOP/s; W4A4 dual GEMM (with the activation "
+        f"quantisation) {dual_us:.2f} us, {dual_tflops:.1f} TFLOP/s ({100 * dual_tflops / MFMA_FP4_PEAK_TFLOPS:.1f}% "
+        f"of the FP4 peak)")
+    result = {
+        "metric": W4A4_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "us_per_forward": round(us, 3),
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp4 (gate/up), bf16 (down)",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: gated FFN forward, M={M}, hidden K={K}, intermediate N={N}, "
+                               f"act={fi.ACT_NAMES[act]}, MXFP4 gate/up requantised from NVFP4, NVFP4 down, "
+                               f"rotated over {nc} copies",
+                   "M": M, "K": K, "N": N, "act": fi.ACT_NAMES[act], "flops_per_forward": flops},
+        "roofline": {"kernel": "W4A4 dual GEMM entry (ffn_w4a4_dual_gemm: mx_quant_bf16_kernel + w4a4_dual_kernel, "
+                               "fp32 gate and up out)",
+                     "bound": "mfma", "achieved": round(dual_tflops, 2), "peak": MFMA_FP4_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(dual_tflops / MFMA_FP4_PEAK_TFLOPS, 4), "traffic": None,
+                     "us_per_launch": round(dual_us, 3), "flops_per_launch": dual_flops},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.default()
+        gm, um = orc.mx_requant(case.gate), orc.mx_requant(case.up)
+        rows = np.array([0])
+        sub = case.with_x(case.x_bits[rows])
+        orc.w4a4_ffn(sub, gm, um)
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            orc.w4a4_ffn(sub, gm, um)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        row_flops = 2.0 * 3 * K * N
+        result["cpu_baseline"] = {"value": round(n * row_flops / el / 1e12, 6), "unit": "TFLOP/s",
+                                  "us_per_token_row": round(el / n * 1e6, 1), "cores": orc.num_threads(),
+                                  "kind": "oracle",
+                                  "sample": f"{n} single-token-row W4A4 forwards of the same weights (fp64 C oracle, "
+                                            f"OpenMP over outputs), {el:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def quant_bytes(rows, cols):
     """Bytes the two passes must move: the bf16 weight read by the absmax pass
     and again by the quantise pass, then the codes, scale bytes and scale2."""
@@ -350,7 +468,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode_silu_m1",
-                    choices=sorted(WORKLOADS) + sorted(QUANT_WORKLOADS) + sorted(FP8_WORKLOADS))
+                    choices=sorted(WORKLOADS) + sorted(QUANT_WORKLOADS) + sorted(FP8_WORKLOADS)
+                    + sorted(W4A4_WORKLOADS))
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated over")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -374,6 +493,9 @@ def main():
         return
     if args.workload in FP8_WORKLOADS:
         bench_fp8(args)
+        return
+    if args.workload in W4A4_WORKLOADS:
+        bench_w4a4(args)
         return
     lib = ffn.load()
     idx, M = WORKLOADS[args.workload]

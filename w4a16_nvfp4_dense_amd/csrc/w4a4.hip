@@ -154,25 +154,24 @@ struct W4a4Params {
     int M, N, K;
 };
 
-// One 256-column piece (4 steps of 64) of a lane's operand row: 4 x 16 code
-// bytes and the 8 E8M0 bytes of blocks 8 q .. 8 q + 7, shifted down by one
-// byte in the upper lane half so that step t's scale is byte 2 (t % 2) of
-// word t / 2 in every lane.
-struct W4Piece {
-    u32x4_t c[4];
-    uint32_t s[2];
-};
 
-__device__ __forceinline__ void w4_load(W4Piece &p, const uint8_t *codes_row, const uint8_t *e8m0_row, int q,
-                                        int half)
+// LDS stage of one 256-column piece: A codes (128 token rows x 128 B), B codes
+// (32 gate rows, then 32 up rows, x 128 B), A scales (128 rows x 8 B), B
+// scales (64 rows x 8 B). In a row's 128 code bytes the 16-byte chunk c sits
+// at slot c ^ ((row / 2) % 8), so that the 16 lanes of a ds_read_b128 phase
+// (16 consecutive rows, one chunk) hit 16 distinct 16-byte bank groups.
+constexpr int kW4Stages = 3;
+constexpr int kW4ACodes = 0;
+constexpr int kW4BCodes = 128 * 128;
+constexpr int kW4AScales = kW4BCodes + 64 * 128;
+constexpr int kW4BScales = kW4AScales + 128 * 8;
+constexpr int kW4Stage = kW4BScales + 64 * 8;                 // 26112 B
+constexpr int kW4Dummy = kW4Stages * kW4Stage;                 // 256 B never read
+constexpr int kW4LdsBytes = kW4Dummy + 256;                    // 78592 B: two workgroups per CU
+
+__device__ __forceinline__ int w4_slot(int row, int chunk)
 {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-        p.c[t] = *reinterpret_cast<const u32x4_t *>(codes_row + (4 * q + t) * 32 + 16 * half);
-    const u32x2_w4_t s = *reinterpret_cast<const u32x2_w4_t *>(e8m0_row + 8 * q);
-    const uint64_t s64 = (static_cast<uint64_t>(s[1]) << 32 | s[0]) >> (8 * half);
-    p.s[0] = static_cast<uint32_t>(s64);
-    p.s[1] = static_cast<uint32_t>(s64 >> 32);
+    return chunk ^ ((row >> 1) & 7);
 }
 
 __device__ __forceinline__ i32x8_t w4_operand(const u32x4_t &c)
@@ -181,63 +180,138 @@ __device__ __forceinline__ i32x8_t w4_operand(const u32x4_t &c)
                    0, 0, 0, 0};
 }
 
-// Step t of a piece for both projections (format 4 = E2M1 for both operands;
-// the byte select of each scale register is 2 (t % 2)).
-template <int T>
-__device__ __forceinline__ void w4_step(w4_f32x16_t &cg, w4_f32x16_t &cu, const W4Piece &a, const W4Piece &g,
-                                        const W4Piece &u)
+// The 8 E8M0 bytes of a row's piece, shifted down by one byte in the upper
+// lane half: step t's scale is then byte 2 (t % 2) of word t / 2.
+__device__ __forceinline__ void w4_scales(uint32_t (&s)[2], const FFN_LDS uint8_t *row8, int half)
 {
-    constexpr int OPSEL = 2 * (T % 2);
-    const i32x8_t A = w4_operand(a.c[T]);
-    cg = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, w4_operand(g.c[T]), cg, 4, 4, OPSEL,
-                                                         static_cast<int>(a.s[T / 2]), OPSEL,
-                                                         static_cast<int>(g.s[T / 2]));
-    cu = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, w4_operand(u.c[T]), cu, 4, 4, OPSEL,
-                                                         static_cast<int>(a.s[T / 2]), OPSEL,
-                                                         static_cast<int>(u.s[T / 2]));
+    const u32x2_w4_t v = *reinterpret_cast<const FFN_LDS u32x2_w4_t *>(row8);
+    const uint64_t s64 = (static_cast<uint64_t>(v[1]) << 32 | v[0]) >> (8 * half);
+    s[0] = static_cast<uint32_t>(s64);
+    s[1] = static_cast<uint32_t>(s64 >> 32);
 }
 
 // Dual GEMM: workgroup (x, y) takes weight rows 32 x .. 32 x + 31 of both
-// projections and tokens 128 y .. 128 y + 127, one wave per 32 tokens. A lane
-// loads its own operand rows straight from global memory (16 contiguous code
-// bytes per step), one 256-column piece ahead of the products. Tokens past M
-// re-read row M - 1 and are not stored.
+// projections and tokens 128 y .. 128 y + 127, wave w the token tile
+// 32 w .. 32 w + 31 for the whole reduction. Per 256-column piece the
+// workgroup stages the activation codes and scales and both projections'
+// codes and scales into a 3-stage LDS ring with direct global-to-LDS loads
+// (every load instruction reads 8 rows x 128 contiguous bytes; every wave
+// issues the same 8 loads per stage, one of them into a dummy area), one
+// piece ahead of the products; each wave then reads its operands in the
+// MFMA layout (ds_read_b128) and runs 8 products. Tokens past M re-read row
+// M - 1 and are not stored.
 template <int OUT>
 __global__ __launch_bounds__(kW4Threads) void w4a4_dual_kernel(const W4a4Params p)
 {
+    extern __shared__ u32x4_t lds_raw[];
+    FFN_LDS uint8_t *lds = (FFN_LDS uint8_t *)lds_raw;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.y * kW4TokensPerGroup + wave * kW4TokensPerWave;
-    if (t0 >= p.M)
-        return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tg0 = blockIdx.y * kW4TokensPerGroup;
     const int n0 = blockIdx.x * kW4RowsPerTile;
     const int half = lane >> 5;
-    const int tok = min(t0 + (lane & 31), p.M - 1);
-    const int n = n0 + (lane & 31);
     const size_t kc = static_cast<size_t>(p.K) / 2, ke = static_cast<size_t>(p.K) / 32;
-    const uint8_t *xr = p.xc + tok * kc, *xs = p.xe + tok * ke;
-    const uint8_t *gr = p.gc + n * kc, *gs = p.ge + n * ke;
-    const uint8_t *ur = p.uc + n * kc, *us = p.ue + n * ke;
     const int pieces = p.K / 256;
-    w4_f32x16_t cg = {}, cu = {};
-    W4Piece a, g, u;
-    w4_load(a, xr, xs, 0, half);
-    w4_load(g, gr, gs, 0, half);
-    w4_load(u, ur, us, 0, half);
-    for (int q = 0; q < pieces; ++q) {
-        W4Piece an, gn, un;
-        const int qn = q + 1 < pieces ? q + 1 : q;  // the last piece re-reads itself (unused)
-        w4_load(an, xr, xs, qn, half);
-        w4_load(gn, gr, gs, qn, half);
-        w4_load(un, ur, us, qn, half);
-        w4_step<0>(cg, cu, a, g, u);
-        w4_step<1>(cg, cu, a, g, u);
-        w4_step<2>(cg, cu, a, g, u);
-        w4_step<3>(cg, cu, a, g, u);
-        a = an;
-        g = gn;
-        u = un;
+
+    // Load sources of this lane (piece 0; piece q adds 128 q code bytes, 8 q
+    // scale bytes). A codes: loads j = 0..3 cover rows 32 w + 8 j + lane / 8.
+    const uint8_t *asrc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int R = 32 * wave + 8 * j + (lane >> 3);
+        const int tok = min(tg0 + R, p.M - 1);
+        asrc[j] = p.xc + tok * kc + 16 * w4_slot(R, lane & 7);
     }
+    // B codes: loads j = 0, 1 cover rows 16 w + 8 j + lane / 8 (gate rows
+    // 0..31, up rows 32..63).
+    const uint8_t *bsrc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int Rb = 16 * wave + 8 * j + (lane >> 3);
+        const uint8_t *base = Rb < 32 ? p.gc : p.uc;
+        bsrc[j] = base + (n0 + (Rb & 31)) * kc + 16 * w4_slot(Rb, lane & 7);
+    }
+    // Scales: one dword per lane, rows 32 w + lane / 2 (A), and for waves 0
+    // and 1 the gate or up rows (B; waves 2 and 3 load a dummy).
+    const int atok = min(tg0 + 32 * wave + (lane >> 1), p.M - 1);
+    const uint8_t *assrc = p.xe + atok * ke + 4 * (lane & 1);
+    const uint8_t *bsbase = wave == 1 ? p.ue : p.ge;
+    const uint8_t *bssrc = bsbase + (n0 + (lane >> 1)) * ke + 4 * (lane & 1);
+    const bool bscale_wave = wave < 2;
+
+    auto issue = [&](int q, int st) {
+        FFN_LDS uint8_t *base = lds + st * kW4Stage;
+        const size_t co = static_cast<size_t>(q) * 128, so = static_cast<size_t>(q) * 8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(asrc[j] + co),
+                                             reinterpret_cast<FFN_LDS void *>(base + kW4ACodes +
+                                                                              (32 * wave + 8 * j) * 128),
+                                             16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(bsrc[j] + co),
+                                             reinterpret_cast<FFN_LDS void *>(base + kW4BCodes +
+                                                                              (16 * wave + 8 * j) * 128),
+                                             16, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(assrc + so),
+                                         reinterpret_cast<FFN_LDS void *>(base + kW4AScales + 32 * wave * 8), 4, 0,
+                                         0);
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void *>(bssrc + so),
+            reinterpret_cast<FFN_LDS void *>(bscale_wave ? base + kW4BScales + 32 * wave * 8 : lds + kW4Dummy), 4,
+            0, 0);
+    };
+
+    // prologue: pieces 0 .. S - 2 (a piece past the end loads the last one
+    // again, so every wait below has the same number of loads in flight)
+#pragma unroll
+    for (int k = 0; k < kW4Stages - 1; ++k)
+        issue(min(k, pieces - 1), k);
+
+    w4_f32x16_t cg = {}, cu = {};
+    const int ar = 32 * wave + (lane & 31);  // this lane's A row in a stage
+    const int br = lane & 31;                // its B row (gate; up is 32 rows on)
+    for (int q = 0; q < pieces; ++q) {
+        const int st = q % kW4Stages;
+        wait_vmcnt<8 * (kW4Stages - 2)>();
+        lds_barrier();
+        issue(min(q + kW4Stages - 1, pieces - 1), (q + kW4Stages - 1) % kW4Stages);
+        const FFN_LDS uint8_t *base = lds + st * kW4Stage;
+        uint32_t sa[2], sg[2], su[2];
+        w4_scales(sa, base + kW4AScales + ar * 8, half);
+        w4_scales(sg, base + kW4BScales + br * 8, half);
+        w4_scales(su, base + kW4BScales + (32 + br) * 8, half);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int c = 2 * t + half;
+            const u32x4_t a = *reinterpret_cast<const FFN_LDS u32x4_t *>(base + kW4ACodes + ar * 128 +
+                                                                          16 * w4_slot(ar, c));
+            const u32x4_t g = *reinterpret_cast<const FFN_LDS u32x4_t *>(base + kW4BCodes + br * 128 +
+                                                                          16 * w4_slot(br, c));
+            const u32x4_t u = *reinterpret_cast<const FFN_LDS u32x4_t *>(base + kW4BCodes + (32 + br) * 128 +
+                                                                          16 * w4_slot(32 + br, c));
+            const i32x8_t A = w4_operand(a);
+            if (t % 2 == 0) {
+                cg = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, w4_operand(g), cg, 4, 4, 0,
+                                                                     static_cast<int>(sa[t / 2]), 0,
+                                                                     static_cast<int>(sg[t / 2]));
+                cu = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, w4_operand(u), cu, 4, 4, 0,
+                                                                     static_cast<int>(sa[t / 2]), 0,
+                                                                     static_cast<int>(su[t / 2]));
+            } else {
+                cg = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, w4_operand(g), cg, 4, 4, 2,
+                                                                     static_cast<int>(sa[t / 2]), 2,
+                                                                     static_cast<int>(sg[t / 2]));
+                cu = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, w4_operand(u), cu, 4, 4, 2,
+                                                                     static_cast<int>(sa[t / 2]), 2,
+                                                                     static_cast<int>(su[t / 2]));
+            }
+        }
+    }
+    wait_vmcnt<0>();  // the trailing re-loads land before the workgroup ends
+    const int n = n0 + (lane & 31);
+    const int t0 = tg0 + 32 * wave;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         const int row = t0 + 8 * (v / 4) + 4 * half + (v % 4);
@@ -252,6 +326,19 @@ __global__ __launch_bounds__(kW4Threads) void w4a4_dual_kernel(const W4a4Params 
             }
         }
     }
+}
+
+template <int OUT>
+hipError_t launch_dual_t(const W4a4Params &p, dim3 grid, hipStream_t stream)
+{
+    auto kern = w4a4_dual_kernel<OUT>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kW4LdsBytes);
+    if (e != hipSuccess)
+        return e;
+    W4a4Params q = p;
+    void *args[] = {&q};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), grid, dim3(kW4Threads), args, kW4LdsBytes, stream);
 }
 
 }  // namespace
@@ -288,18 +375,11 @@ hipError_t launch_w4a4_dual(int M, OutKind out, const uint8_t *xc, const uint8_t
     W4a4Params p{xc, xe, g.codes, g.e8m0, u.codes, u.e8m0, g.scale2, u.scale2, out0, out1, M, N, K};
     const dim3 grid(N / kW4RowsPerTile, (M + kW4TokensPerGroup - 1) / kW4TokensPerGroup);
     switch (out) {
-    case OUT_F32_PAIR:
-        hipLaunchKernelGGL(w4a4_dual_kernel<OUT_F32_PAIR>, grid, dim3(kW4Threads), 0, stream, p);
-        break;
-    case OUT_H_SILU:
-        hipLaunchKernelGGL(w4a4_dual_kernel<OUT_H_SILU>, grid, dim3(kW4Threads), 0, stream, p);
-        break;
-    case OUT_H_GELU:
-        hipLaunchKernelGGL(w4a4_dual_kernel<OUT_H_GELU>, grid, dim3(kW4Threads), 0, stream, p);
-        break;
+    case OUT_F32_PAIR: return launch_dual_t<OUT_F32_PAIR>(p, grid, stream);
+    case OUT_H_SILU: return launch_dual_t<OUT_H_SILU>(p, grid, stream);
+    case OUT_H_GELU: return launch_dual_t<OUT_H_GELU>(p, grid, stream);
     default: return hipErrorNotSupported;
     }
-    return hipGetLastError();
 }
 
 }  // namespace ffn
