@@ -227,6 +227,10 @@ __device__ __forceinline__ void fp8_pieces(const Fp8Params &fp, u32x4_t *act, fl
         fp8_pieces<M, IT, NMAT, IN, W, P, p + 1>(fp, act, acc, g, G, rg);
 }
 
+// The down GEMV issues its first weight row only once its activations have
+// arrived (stage_act's LATE order): at the decode shape the 17 KB rows of the
+// whole grid would otherwise queue ahead of them (17.8 vs 18.7 us).
+//
 // W waves per workgroup; wave g = wave * gridDim.x + blockIdx.x takes rows
 // g, g + G, ... (G = all waves of the grid). Dynamic LDS: M * IT * 2 KB, or
 // M * ceil(IT / P) * 2 KB with the activations staged in P pieces (each wave
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(64 * W) void fp8_gemv_kernel(const Fp8Params p)
     Fp8Row<IT, NMAT, fp8_scale_regs<0, IT>()> w;
     if (kWeightsFirst && g < p.rows)
         fp8_load_row<kNt, IT, NMAT>(w, p, g, rg);
-    stage_act<M, IT, IN, W, 0, 2>(act, p.in0, p.in1, p.cols, p.cpr, [&] {
+    stage_act<M, IT, IN, W, 0, 2, !kWeightsFirst>(act, p.in0, p.in1, p.cols, p.cpr, [&] {
         if (!kWeightsFirst && g < p.rows)
             fp8_load_row<kNt, IT, NMAT>(w, p, g, rg);
     });
