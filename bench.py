@@ -305,6 +305,8 @@ def bench_w4a4(args):
         outs.append(out.clone())
     torch.cuda.synchronize()
     assert all(torch.equal(o, outs[0]) for o in outs), "weight copies disagree"
+    if args.calibrate_copy:
+        calibration_copy(dev)
 
     def timed(fn, n):
         for i in range(args.warmup):
@@ -327,6 +329,7 @@ def bench_w4a4(args):
     dual_us = timed(dual, steps) / steps * 1e3
     dual_flops = 2.0 * 2 * M * K * N
     dual_tflops = dual_flops / (dual_us * 1e-6) / 1e12
+    traffic = measured_traffic(args.workload)
     log(f"[bench] {args.workload}: {us:.2f} us/forward, {tflops:.1f} TFLOP/s; W4A4 dual GEMM (with the activation "
         f"quantisation) {dual_us:.2f} us, {dual_tflops:.1f} TFLOP/s ({100 * dual_tflops / MFMA_FP4_PEAK_TFLOPS:.1f}% "
         f"of the FP4 peak)")
@@ -342,7 +345,8 @@ def bench_w4a4(args):
         "roofline": {"kernel": "W4A4 dual GEMM entry (ffn_w4a4_dual_gemm: mx_quant_bf16_kernel + w4a4_dual_kernel, "
                                "fp32 gate and up out)",
                      "bound": "mfma", "achieved": round(dual_tflops, 2), "peak": MFMA_FP4_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(dual_tflops / MFMA_FP4_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(dual_tflops / MFMA_FP4_PEAK_TFLOPS, 4),
+                     "traffic": None if traffic is None else round(traffic["bytes"]),
                      "us_per_launch": round(dual_us, 3), "flops_per_launch": dual_flops},
     }
     if not args.no_cpu_baseline:
