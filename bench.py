@@ -483,7 +483,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
 

@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) when no GPU is visible, so a plain
-    # `pytest` run on a CPU-only machine stays green; `-m gpu` on the GPU machine
+    # `pytest` run on a CPU-only machine stays green; `-m gpu` on a machine with an MI355X
     # runs them for real.
     try:
         import torch
