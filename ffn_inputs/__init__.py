@@ -188,6 +188,50 @@ def make_format_coverage(act: int = ACT_SILU, seed: int = 99, M: int = 1) -> Ffn
                    x_bits=x_bits, gate=gate, up=up, down=down)
 
 
+def make_format_coverage_onesign(act: int = ACT_SILU, seed: int = 97, M: int = 1) -> FfnCase:
+    """Format coverage without cancellation: W_d holds every E2M1 code and
+    every finite E4M3 scale byte (negative, subnormal and 448 included), yet
+    every nonzero product in an output's sum has that output's sign, so the
+    one bf16 rounding of h cannot be amplified by cancellation. Shape K=512,
+    N=256.
+
+    Built from byte structure only: the sign is bit 3 of an E2M1 code and
+    bit 7 of an E4M3 byte, and E4M3 magnitudes increase with the low 7 bits.
+    x >= 0; row n of W_g and of W_u share one sign s_n (each code's sign bit
+    is set so that code sign times scale sign is s_n), so gate and up have
+    the same sign and h = act(gate) * up >= 0 (SiLU and GELU-tanh keep the
+    sign of their input); their scales are +-2^-2 .. +-1. Row j of W_d has
+    one sign t_j the same way, and its 16 scale bytes are consecutive in the
+    magnitude-sorted list of all scale bytes, so rows 32 b .. 32 b + 31 hold
+    scales within a few binades of each other ("bands" of like magnitude,
+    rows of band b smaller than those of band b + 1)."""
+    K, N = 512, 256
+    rng = np.random.Generator(np.random.PCG64(seed))
+    fin = finite_e4m3_bytes()
+
+    def onesign(rows: int, cols: int, scales: np.ndarray, signs: np.ndarray, s2: float) -> Nvfp4Weight:
+        mags = rng.integers(0, 8, size=(rows, cols), dtype=np.uint8)
+        # element (r, c): its block's scale sign bit, flipped when the row is negative
+        neg = ((scales >> 7).astype(np.uint8)[:, np.arange(cols) // 16] ^ (signs[:, None] < 0)).astype(np.uint8)
+        nib = mags | (neg << 3)
+        codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+        return Nvfp4Weight(codes=codes, scales=scales.astype(np.uint8), scale2=s2)
+
+    sn = rng.choice(np.array([-1, 1], dtype=np.int8), size=N)
+    small = lambda rows, cols: (rng.choice(np.array([0x28, 0x30, 0x38], dtype=np.uint8), size=(rows, cols // 16))
+                                | (rng.integers(0, 2, size=(rows, cols // 16), dtype=np.uint8) << 7))
+    gate = onesign(N, K, small(N, K), sn, 0.02)
+    up = onesign(N, K, small(N, K), sn, 0.03)
+    nsc = K * N // 16
+    sc = np.resize(rng.permutation(fin), nsc)
+    sc = sc[np.argsort(sc & 0x7F, kind="stable")].reshape(K, N // 16)
+    tj = rng.choice(np.array([-1, 1], dtype=np.int8), size=K)
+    down = onesign(K, N, sc, tj, 0.3)
+    x = np.abs(rng.standard_normal(size=(M, K), dtype=np.float32))
+    return FfnCase(name=f"format_coverage_onesign_{ACT_NAMES[act]}_m{M}", M=M, K=K, N=N, act=act,
+                   x_bits=f32_to_bf16_bits(x), gate=gate, up=up, down=down)
+
+
 @dataclasses.dataclass
 class Fp8Weight:
     """One block-scaled FP8 weight of logical shape [rows, cols] (the format

@@ -60,6 +60,17 @@ def assert_ffn_close(out_gpu, out_ref, what, extra=None):
                              f"max err/rms {np.max(err) / np.sqrt(np.mean(out_ref ** 2)):.3e}")
 
 
+def assert_banded_close(out_gpu, out_ref, what, band=32):
+    """The FFN output bound applied to each band of `band` consecutive output
+    columns as if it were the whole output (rms over the band), so columns
+    of small magnitude are checked at their own scale rather than at the
+    scale of the largest ones."""
+    got = ffn.bf16_to_f64(out_gpu) if torch.is_tensor(out_gpu) else out_gpu
+    for b0 in range(0, out_ref.shape[1], band):
+        sl = slice(b0, b0 + band)
+        assert_ffn_close(got[:, sl], out_ref[:, sl], f"{what} columns {b0}..{b0 + band - 1}")
+
+
 def assert_dual_close(got, ref, what):
     got = got.double().cpu().numpy()
     rms = np.sqrt(np.mean(ref ** 2))
@@ -91,9 +102,9 @@ SMALL = [
     (1, 4096, 96, fi.ACT_SILU, 15),         # fewer rows than compute units
     (2, 2048, 20000, fi.ACT_SILU, 16),      # 79 rows per CU; 625-chunk down rows from LDS
     (1, 12288, 4096, fi.ACT_GELU_TANH, 17), # 6 chunks per lane
-    (5, 1056, 12288, fi.ACT_GELU_TANH, 18), # down: 6 chunks per lane, launches of 4 + 1 rows
-    (7, 4096, 18432, fi.ACT_SILU, 19),      # down: 9 chunks per lane, launches of 4 + 3 rows
-    (6, 12288, 1056, fi.ACT_SILU, 20),      # dual: 6 chunks per lane, launches of 4 + 2 rows
+    (5, 1056, 12288, fi.ACT_GELU_TANH, 18), # down: 6 chunks per lane, 5 rows in one launch
+    (7, 4096, 18432, fi.ACT_SILU, 19),      # down: 9 chunks per lane, 7 rows staged in two pieces
+    (6, 12288, 1056, fi.ACT_SILU, 20),      # dual: 6 chunks per lane, 6 rows in one launch
     (3, 24576, 1056, fi.ACT_GELU_TANH, 21), # dual: 12 chunks per lane, 8-wave workgroups
     # activations staged in pieces of steps (M x steps x 4 KB over the LDS budget)
     (4, 1056, 21504, fi.ACT_GELU_TANH, 27), # down: 11 steps in pieces of 6 + 5
@@ -146,6 +157,33 @@ def test_format_coverage(act, M):
     assert_dual_close(g, g_ref, "gate")
     assert_dual_close(u, u_ref, "up")
     assert_ffn_close(out, oracle.ffn(case), case.name, extra=oracle.h_rounding_bound(case))
+
+
+@pytest.mark.parametrize("act", [fi.ACT_SILU, fi.ACT_GELU_TANH])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_format_coverage_onesign(act, M):
+    """All 16 E2M1 codes and all 254 finite E4M3 scales in W_d, with every
+    product of an output's sum of one sign (so nothing cancels): the forward
+    and the down entry at the plain output bound, over the whole output and
+    over each band of like-magnitude outputs (the subnormal-scale rows
+    included), with no allowance for the rounding of h."""
+    case = fi.make_format_coverage_onesign(act=act, M=M)
+    L = loaded(case.name, lambda: case)
+    out = L.forward()
+    g, u = ffn.dual_gemv(L.x, L.gate, L.up)
+    torch.cuda.synchronize()
+    g_ref, u_ref = oracle.dual(case)
+    assert_dual_close(g, g_ref, "gate")
+    assert_dual_close(u, u_ref, "up")
+    ref = oracle.ffn(case)
+    assert_ffn_close(out, ref, case.name)
+    assert_banded_close(out, ref, case.name)
+    g32, u32 = g_ref.astype(np.float32), u_ref.astype(np.float32)
+    d = ffn.down_gemv(torch.from_numpy(g32).to(DEV), torch.from_numpy(u32).to(DEV), L.down, act)
+    torch.cuda.synchronize()
+    d_ref = oracle.down(oracle.gated_act(act, g32.astype(np.float64), u32.astype(np.float64)), case.down)
+    assert_ffn_close(d, d_ref, "down entry")
+    assert_banded_close(d, d_ref, "down entry")
 
 
 def test_determinism_and_entry_composition():
@@ -256,3 +294,42 @@ def test_config_verify(M):
     assert_ffn_close(out, oracle.ffn(case), case.name)
     for m in range(M):
         assert torch.equal(L.forward(L.x[m:m + 1].contiguous())[0], out[m])
+
+
+# (config, M): the down entry at the decode and verify shapes, where a lane
+# takes 9 (N = 17408) or 11 (N = 21504) chunks and an 8-row batch stages its
+# activations in three pieces.
+DOWN_FULL = [(1, 1), (2, 1), (3, 2), (3, 3), (3, 8)]
+
+
+@pytest.mark.parametrize("idx,M", DOWN_FULL, ids=[f"config{i}_m{m}" for i, m in DOWN_FULL])
+def test_config_down_entry(idx, M):
+    """The activation-fused down entry at full size, every element: from the
+    oracle's gate and up rounded to fp32, against the oracle's down
+    projection of act(gate) * up from those same inputs. Then, on the GPU's
+    own gate and up, the down entry equals the forward bit for bit."""
+    case = fi.make_config(idx, M=M) if idx == 3 else fi.make_config(idx)
+    L = loaded(case.name, lambda: case)
+    g_ref, u_ref = oracle.dual(case)
+    g32, u32 = g_ref.astype(np.float32), u_ref.astype(np.float32)
+    out = ffn.down_gemv(torch.from_numpy(g32).to(DEV), torch.from_numpy(u32).to(DEV), L.down, case.act)
+    torch.cuda.synchronize()
+    h = oracle.gated_act(case.act, g32.astype(np.float64), u32.astype(np.float64))
+    assert_ffn_close(out, oracle.down(h, case.down), f"{case.name} down entry")
+    g, u = ffn.dual_gemv(L.x, L.gate, L.up)
+    assert torch.equal(ffn.down_gemv(g, u, L.down, case.act), L.forward()), "forward != dual + down"
+
+
+@pytest.mark.parametrize("M", [5, 6, 7])
+def test_verify_batch_one_launch(M):
+    """Verify batches of 5 to 7 rows at the decode shape (one launch per
+    projection): every element against the oracle, every row bit-identical
+    to the M = 1 call on it."""
+    case = fi.make_ffn(f"verify_silu_m{M}", M, 5120, 17408, fi.ACT_SILU, 1.0, 2.0 ** -4, fi.SEED_BASE + 1,
+                       x_seed=fi.SEED_BASE + 3 + 100 * M)
+    L = loaded(case.name, lambda: case)
+    out = L.forward()
+    torch.cuda.synchronize()
+    assert_ffn_close(out, oracle.ffn(case), case.name)
+    for m in range(M):
+        assert torch.equal(L.forward(L.x[m:m + 1].contiguous())[0], out[m]), m

@@ -192,10 +192,28 @@ def _stream_handle(stream) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _check_tensor(t, dtype, shape, name):
+def _record(stream, *tensors) -> None:
+    """Tensors allocated inside a binding belong to the current stream's
+    pool; when the call was enqueued on another stream, mark them as used
+    there so the caching allocator cannot hand their memory out again before
+    that stream's kernels are done."""
+    import torch
+    if stream is None:
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    if int(s.cuda_stream) == int(torch.cuda.current_stream().cuda_stream):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(s)
+
+
+def _check_tensor(t, dtype, shape, name, device=None):
     import torch
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
@@ -209,6 +227,18 @@ def _check(status: int, what: str) -> None:
         raise FfnError(status, what)
 
 
+def _check_nvfp4_weight(w: "DeviceWeight", rows: int, cols: int, name: str, device) -> None:
+    """An NVFP4 weight of logical shape [rows, cols]: contiguous uint8 codes
+    [rows, cols/2] and scales [rows, cols/16] on the device of the call (the C
+    ABI sees only pointers, so a mismatched weight would be read out of
+    bounds)."""
+    import torch
+    if cols % 16:
+        raise ValueError(f"{name}: {cols} columns is not a multiple of 16")
+    _check_tensor(w.codes, torch.uint8, (rows, cols // 2), f"{name}.codes", device)
+    _check_tensor(w.scales, torch.uint8, (rows, cols // 16), f"{name}.scales", device)
+
+
 def forward(x, gate: DeviceWeight, up: DeviceWeight, down: DeviceWeight, act: int = ACT_SILU,
             out=None, workspace=None, stream=None):
     """out[M, K] (bf16) = W_d (act(W_g x) * (W_u x)) for x bf16 [M, K]."""
@@ -216,17 +246,23 @@ def forward(x, gate: DeviceWeight, up: DeviceWeight, down: DeviceWeight, act: in
     M, K = x.shape
     N = gate.rows
     _check_tensor(x, torch.bfloat16, (M, K), "x")
-    if out is None:
+    _check_nvfp4_weight(gate, N, K, "gate", x.device)
+    _check_nvfp4_weight(up, N, K, "up", x.device)
+    _check_nvfp4_weight(down, K, N, "down", x.device)
+    new_out = out is None
+    if new_out:
         out = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
-    _check_tensor(out, torch.bfloat16, (M, K), "out")
+    _check_tensor(out, torch.bfloat16, (M, K), "out", x.device)
     need = workspace_bytes(M, K, N)
-    if workspace is None:
+    new_ws = workspace is None
+    if new_ws:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     g, u, d = gate.struct(), up.struct(), down.struct()
     rc = load().ffn_nvfp4_forward(x.data_ptr(), M, K, N, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
                                   int(act), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                   out.data_ptr(), _stream_handle(stream))
     _check(rc, "ffn_nvfp4_forward")
+    _record(stream, out if new_out else None, workspace if new_ws else None)
     return out
 
 
@@ -236,16 +272,20 @@ def dual_gemv(x, gate: DeviceWeight, up: DeviceWeight, gate_out=None, up_out=Non
     M, K = x.shape
     N = gate.rows
     _check_tensor(x, torch.bfloat16, (M, K), "x")
-    if gate_out is None:
+    _check_nvfp4_weight(gate, N, K, "gate", x.device)
+    _check_nvfp4_weight(up, N, K, "up", x.device)
+    new_g, new_u = gate_out is None, up_out is None
+    if new_g:
         gate_out = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    if up_out is None:
+    if new_u:
         up_out = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    _check_tensor(gate_out, torch.float32, (M, N), "gate_out")
-    _check_tensor(up_out, torch.float32, (M, N), "up_out")
+    _check_tensor(gate_out, torch.float32, (M, N), "gate_out", x.device)
+    _check_tensor(up_out, torch.float32, (M, N), "up_out", x.device)
     g, u = gate.struct(), up.struct()
     rc = load().ffn_nvfp4_dual_gemv(x.data_ptr(), M, K, N, ctypes.byref(g), ctypes.byref(u),
                                     gate_out.data_ptr(), up_out.data_ptr(), _stream_handle(stream))
     _check(rc, "ffn_nvfp4_dual_gemv")
+    _record(stream, gate_out if new_g else None, up_out if new_u else None)
     return gate_out, up_out
 
 
@@ -256,14 +296,17 @@ def down_gemv(gate_in, up_in, down: DeviceWeight, act: int = ACT_SILU, out=None,
     M, N = gate_in.shape
     K = down.rows
     _check_tensor(gate_in, torch.float32, (M, N), "gate_in")
-    _check_tensor(up_in, torch.float32, (M, N), "up_in")
-    if out is None:
+    _check_tensor(up_in, torch.float32, (M, N), "up_in", gate_in.device)
+    _check_nvfp4_weight(down, K, N, "down", gate_in.device)
+    new_out = out is None
+    if new_out:
         out = torch.empty((M, K), dtype=torch.bfloat16, device=gate_in.device)
-    _check_tensor(out, torch.bfloat16, (M, K), "out")
+    _check_tensor(out, torch.bfloat16, (M, K), "out", gate_in.device)
     d = down.struct()
     rc = load().ffn_nvfp4_down_gemv(gate_in.data_ptr(), up_in.data_ptr(), M, N, K, ctypes.byref(d), int(act),
                                     out.data_ptr(), _stream_handle(stream))
     _check(rc, "ffn_nvfp4_down_gemv")
+    _record(stream, out if new_out else None)
     return out
 
 
@@ -278,22 +321,28 @@ def quantize(w, codes=None, scales=None, scale2=None, workspace=None, stream=Non
     rows, cols = w.shape
     _check_tensor(w, torch.bfloat16, (rows, cols), "w")
     dev = w.device
+    fresh = []
     if codes is None:
         codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        fresh.append(codes)
     if scales is None:
         scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+        fresh.append(scales)
     if scale2 is None:
         scale2 = torch.empty(1, dtype=torch.float32, device=dev)
-    _check_tensor(codes, torch.uint8, (rows, cols // 2), "codes")
-    _check_tensor(scales, torch.uint8, (rows, cols // 16), "scales")
-    _check_tensor(scale2, torch.float32, (1,), "scale2")
+        fresh.append(scale2)
+    _check_tensor(codes, torch.uint8, (rows, cols // 2), "codes", dev)
+    _check_tensor(scales, torch.uint8, (rows, cols // 16), "scales", dev)
+    _check_tensor(scale2, torch.float32, (1,), "scale2", dev)
     need = quantize_workspace_bytes(rows, cols)
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+        fresh.append(workspace)
     rc = load().ffn_nvfp4_quantize(w.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(),
                                    scale2.data_ptr(), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream_handle(stream))
     _check(rc, "ffn_nvfp4_quantize")
+    _record(stream, *fresh)
     return codes, scales, scale2
 
 
@@ -346,10 +395,11 @@ class Fp8DeviceWeight:
         return cls(torch.from_numpy(w.codes).to(device), torch.from_numpy(w.block_scale).to(device))
 
 
-def _check_fp8_weight(w: Fp8DeviceWeight, rows: int, cols: int, name: str) -> None:
+def _check_fp8_weight(w: Fp8DeviceWeight, rows: int, cols: int, name: str, device=None) -> None:
     import torch
-    _check_tensor(w.codes, torch.uint8, (rows, cols), f"{name}.codes")
-    _check_tensor(w.block_scale, torch.float32, ((rows + 127) // 128, (cols + 127) // 128), f"{name}.block_scale")
+    _check_tensor(w.codes, torch.uint8, (rows, cols), f"{name}.codes", device)
+    _check_tensor(w.block_scale, torch.float32, ((rows + 127) // 128, (cols + 127) // 128), f"{name}.block_scale",
+                  device)
 
 
 def fp8_workspace_bytes(M: int, K: int, N: int) -> int:
@@ -363,20 +413,23 @@ def fp8_forward(x, gate: Fp8DeviceWeight, up: Fp8DeviceWeight, down: Fp8DeviceWe
     M, K = x.shape
     N = gate.rows
     _check_tensor(x, torch.bfloat16, (M, K), "x")
-    _check_fp8_weight(gate, N, K, "gate")
-    _check_fp8_weight(up, N, K, "up")
-    _check_fp8_weight(down, K, N, "down")
-    if out is None:
+    _check_fp8_weight(gate, N, K, "gate", x.device)
+    _check_fp8_weight(up, N, K, "up", x.device)
+    _check_fp8_weight(down, K, N, "down", x.device)
+    new_out = out is None
+    if new_out:
         out = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
-    _check_tensor(out, torch.bfloat16, (M, K), "out")
+    _check_tensor(out, torch.bfloat16, (M, K), "out", x.device)
     need = fp8_workspace_bytes(M, K, N)
-    if workspace is None:
+    new_ws = workspace is None
+    if new_ws:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     g, u, d = gate.struct(), up.struct(), down.struct()
     rc = load().ffn_fp8_forward(x.data_ptr(), M, K, N, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
                                 int(act), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                 out.data_ptr(), _stream_handle(stream))
     _check(rc, "ffn_fp8_forward")
+    _record(stream, out if new_out else None, workspace if new_ws else None)
     return out
 
 
@@ -386,18 +439,20 @@ def fp8_dual_gemv(x, gate: Fp8DeviceWeight, up: Fp8DeviceWeight, gate_out=None, 
     M, K = x.shape
     N = gate.rows
     _check_tensor(x, torch.bfloat16, (M, K), "x")
-    _check_fp8_weight(gate, N, K, "gate")
-    _check_fp8_weight(up, N, K, "up")
-    if gate_out is None:
+    _check_fp8_weight(gate, N, K, "gate", x.device)
+    _check_fp8_weight(up, N, K, "up", x.device)
+    new_g, new_u = gate_out is None, up_out is None
+    if new_g:
         gate_out = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    if up_out is None:
+    if new_u:
         up_out = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    _check_tensor(gate_out, torch.float32, (M, N), "gate_out")
-    _check_tensor(up_out, torch.float32, (M, N), "up_out")
+    _check_tensor(gate_out, torch.float32, (M, N), "gate_out", x.device)
+    _check_tensor(up_out, torch.float32, (M, N), "up_out", x.device)
     g, u = gate.struct(), up.struct()
     rc = load().ffn_fp8_dual_gemv(x.data_ptr(), M, K, N, ctypes.byref(g), ctypes.byref(u),
                                   gate_out.data_ptr(), up_out.data_ptr(), _stream_handle(stream))
     _check(rc, "ffn_fp8_dual_gemv")
+    _record(stream, gate_out if new_g else None, up_out if new_u else None)
     return gate_out, up_out
 
 
@@ -408,15 +463,17 @@ def fp8_down_gemv(gate_in, up_in, down: Fp8DeviceWeight, act: int = ACT_SILU, ou
     M, N = gate_in.shape
     K = down.rows
     _check_tensor(gate_in, torch.float32, (M, N), "gate_in")
-    _check_tensor(up_in, torch.float32, (M, N), "up_in")
-    _check_fp8_weight(down, K, N, "down")
-    if out is None:
+    _check_tensor(up_in, torch.float32, (M, N), "up_in", gate_in.device)
+    _check_fp8_weight(down, K, N, "down", gate_in.device)
+    new_out = out is None
+    if new_out:
         out = torch.empty((M, K), dtype=torch.bfloat16, device=gate_in.device)
-    _check_tensor(out, torch.bfloat16, (M, K), "out")
+    _check_tensor(out, torch.bfloat16, (M, K), "out", gate_in.device)
     d = down.struct()
     rc = load().ffn_fp8_down_gemv(gate_in.data_ptr(), up_in.data_ptr(), M, N, K, ctypes.byref(d), int(act),
                                   out.data_ptr(), _stream_handle(stream))
     _check(rc, "ffn_fp8_down_gemv")
+    _record(stream, out if new_out else None)
     return out
 
 
@@ -444,17 +501,29 @@ class MxDeviceWeight:
         return MxWeightStruct(self.codes.data_ptr(), self.scales.data_ptr(), float(self.scale2))
 
 
+def _check_mx_weight(w: MxDeviceWeight, rows: int, cols: int, name: str, device) -> None:
+    """An MXFP4 weight of logical shape [rows, cols]: contiguous uint8 codes
+    [rows, cols/2] and E8M0 bytes [rows, cols/32] on the device of the call."""
+    import torch
+    if cols % 32:
+        raise ValueError(f"{name}: {cols} columns is not a multiple of 32")
+    _check_tensor(w.codes, torch.uint8, (rows, cols // 2), f"{name}.codes", device)
+    _check_tensor(w.scales, torch.uint8, (rows, cols // 32), f"{name}.scales", device)
+
+
 def w4a4_prepare_weight(w: DeviceWeight, stream=None) -> MxDeviceWeight:
     """Requantise an NVFP4 weight to MXFP4 on the GPU (asynchronous)."""
     import torch
     rows, cols = w.rows, w.cols
     dev = w.codes.device
+    _check_nvfp4_weight(w, rows, cols, "w", dev)
     codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
     scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
     st = w.struct()
     rc = load().ffn_w4a4_prepare_weight(ctypes.byref(st), rows, cols, codes.data_ptr(), scales.data_ptr(),
                                         _stream_handle(stream))
     _check(rc, "ffn_w4a4_prepare_weight")
+    _record(stream, codes, scales)
     return MxDeviceWeight(codes, scales, float(w.scale2))
 
 
@@ -469,19 +538,26 @@ def w4a4_dual_gemm(x, gate: MxDeviceWeight, up: MxDeviceWeight, gate_out=None, u
     M, K = x.shape
     N = gate.rows
     _check_tensor(x, torch.bfloat16, (M, K), "x")
+    _check_mx_weight(gate, N, K, "gate", x.device)
+    _check_mx_weight(up, N, K, "up", x.device)
+    fresh = []
     if gate_out is None:
         gate_out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+        fresh.append(gate_out)
     if up_out is None:
         up_out = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    _check_tensor(gate_out, torch.float32, (M, N), "gate_out")
-    _check_tensor(up_out, torch.float32, (M, N), "up_out")
+        fresh.append(up_out)
+    _check_tensor(gate_out, torch.float32, (M, N), "gate_out", x.device)
+    _check_tensor(up_out, torch.float32, (M, N), "up_out", x.device)
     if workspace is None:
         workspace = torch.empty(max(w4a4_workspace_bytes(M, K, N), 1), dtype=torch.uint8, device=x.device)
+        fresh.append(workspace)
     g, u = gate.struct(), up.struct()
     rc = load().ffn_w4a4_dual_gemm(x.data_ptr(), M, K, N, ctypes.byref(g), ctypes.byref(u), gate_out.data_ptr(),
                                    up_out.data_ptr(), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream_handle(stream))
     _check(rc, "ffn_w4a4_dual_gemm")
+    _record(stream, *fresh)
     return gate_out, up_out
 
 
@@ -492,14 +568,21 @@ def w4a4_forward(x, gate: MxDeviceWeight, up: MxDeviceWeight, down: DeviceWeight
     M, K = x.shape
     N = gate.rows
     _check_tensor(x, torch.bfloat16, (M, K), "x")
+    _check_mx_weight(gate, N, K, "gate", x.device)
+    _check_mx_weight(up, N, K, "up", x.device)
+    _check_nvfp4_weight(down, K, N, "down", x.device)
+    fresh = []
     if out is None:
         out = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
-    _check_tensor(out, torch.bfloat16, (M, K), "out")
+        fresh.append(out)
+    _check_tensor(out, torch.bfloat16, (M, K), "out", x.device)
     if workspace is None:
         workspace = torch.empty(max(w4a4_workspace_bytes(M, K, N), 1), dtype=torch.uint8, device=x.device)
+        fresh.append(workspace)
     g, u, d = gate.struct(), up.struct(), down.struct()
     rc = load().ffn_w4a4_forward(x.data_ptr(), M, K, N, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), int(act),
                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), out.data_ptr(),
                                  _stream_handle(stream))
     _check(rc, "ffn_w4a4_forward")
+    _record(stream, *fresh)
     return out

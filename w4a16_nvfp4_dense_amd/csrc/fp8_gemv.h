@@ -366,72 +366,84 @@ hipError_t fp8_launch_m(int M, const Fp8Params &p, hipStream_t stream)
     case 2: return fp8_launch_one<2, IT, NMAT, IN, OUT>(p, stream);
     case 3: return fp8_launch_one<3, IT, NMAT, IN, OUT>(p, stream);
     case 4: return fp8_launch_one<4, IT, NMAT, IN, OUT>(p, stream);
+    case 5: return fp8_launch_one<5, IT, NMAT, IN, OUT>(p, stream);
+    case 6: return fp8_launch_one<6, IT, NMAT, IN, OUT>(p, stream);
+    case 7: return fp8_launch_one<7, IT, NMAT, IN, OUT>(p, stream);
     case 8: return fp8_launch_one<8, IT, NMAT, IN, OUT>(p, stream);
     default: return hipErrorNotSupported;
     }
 }
 
-// Activation rows per launch: the largest of 8, 4, 3, 2, 1 that is at most
-// `left`. Rows of a batch are independent, so the grouping changes no result.
-inline int fp8_group_rows(int left)
-{
-    for (int g : {8, 4, 3, 2, 1})
-        if (g <= left)
-            return g;
-    return 0;
-}
-
+// One launch for the whole batch (1 <= M <= 8): every weight byte is read
+// once for all M activation rows.
 template <int NMAT, int IN, int OUT>
-hipError_t fp8_launch_groups(int M, Fp8Params p, size_t in_elem, size_t out_elem, hipStream_t stream)
+hipError_t fp8_launch_batch(int M, const Fp8Params &p, hipStream_t stream)
 {
     const int it = (p.cpr + 63) / 64;
-    if (M < 1 || it < 1 || it > kFp8MaxIt)
+    if (M < 1 || M > 8 || it < 1 || it > kFp8MaxIt)
         return hipErrorNotSupported;
-    for (int m0 = 0; m0 < M;) {
-        const int g = fp8_group_rows(M - m0);
-        Fp8Params q = p;
-        q.in0 = static_cast<const uint8_t *>(p.in0) + static_cast<size_t>(m0) * p.cols * in_elem;
-        if (p.in1)
-            q.in1 = p.in1 + static_cast<size_t>(m0) * p.cols;
-        q.out0 = static_cast<uint8_t *>(p.out0) + static_cast<size_t>(m0) * p.rows * out_elem;
-        if (p.out1)
-            q.out1 = static_cast<uint8_t *>(p.out1) + static_cast<size_t>(m0) * p.rows * out_elem;
-        hipError_t e = hipErrorNotSupported;
-        switch (it) {
+    switch (it) {
 #define FFN_FP8_CASE(IT_) \
-        case IT_: e = fp8_launch_m<IT_, NMAT, IN, OUT>(g, q, stream); break;
-        FFN_FP8_CASE(1)
-        FFN_FP8_CASE(2)
-        FFN_FP8_CASE(3)
-        FFN_FP8_CASE(4)
-        FFN_FP8_CASE(5)
-        FFN_FP8_CASE(6)
-        FFN_FP8_CASE(7)
-        FFN_FP8_CASE(8)
-        FFN_FP8_CASE(9)
-        FFN_FP8_CASE(10)
-        FFN_FP8_CASE(11)
-        FFN_FP8_CASE(12)
-        FFN_FP8_CASE(13)
-        FFN_FP8_CASE(14)
-        FFN_FP8_CASE(15)
-        FFN_FP8_CASE(16)
-        FFN_FP8_CASE(17)
-        FFN_FP8_CASE(18)
-        FFN_FP8_CASE(19)
-        FFN_FP8_CASE(20)
-        FFN_FP8_CASE(21)
-        FFN_FP8_CASE(22)
-        FFN_FP8_CASE(23)
-        FFN_FP8_CASE(24)
+    case IT_: return fp8_launch_m<IT_, NMAT, IN, OUT>(M, p, stream);
+    FFN_FP8_CASE(1)
+    FFN_FP8_CASE(2)
+    FFN_FP8_CASE(3)
+    FFN_FP8_CASE(4)
+    FFN_FP8_CASE(5)
+    FFN_FP8_CASE(6)
+    FFN_FP8_CASE(7)
+    FFN_FP8_CASE(8)
+    FFN_FP8_CASE(9)
+    FFN_FP8_CASE(10)
+    FFN_FP8_CASE(11)
+    FFN_FP8_CASE(12)
+    FFN_FP8_CASE(13)
+    FFN_FP8_CASE(14)
+    FFN_FP8_CASE(15)
+    FFN_FP8_CASE(16)
+    FFN_FP8_CASE(17)
+    FFN_FP8_CASE(18)
+    FFN_FP8_CASE(19)
+    FFN_FP8_CASE(20)
+    FFN_FP8_CASE(21)
+    FFN_FP8_CASE(22)
+    FFN_FP8_CASE(23)
+    FFN_FP8_CASE(24)
 #undef FFN_FP8_CASE
-        default: break;
-        }
-        if (e != hipSuccess)
-            return e;
-        m0 += g;
+    default: return hipErrorNotSupported;
     }
-    return hipSuccess;
 }
+
+// Parameters of a launch over one weight (down) or two (dual).
+inline Fp8Params fp8_params(const void *in0, const float *in1, const Fp8WeightArg &w0, const Fp8WeightArg &w1,
+                            void *out0, void *out1, int rows, int cols)
+{
+    Fp8Params p{};
+    p.in0 = in0;
+    p.in1 = in1;
+    p.codes0 = w0.codes;
+    p.bs0 = w0.block_scale;
+    p.codes1 = w1.codes;
+    p.bs1 = w1.block_scale;
+    p.out0 = out0;
+    p.out1 = out1;
+    p.rows = rows;
+    p.cols = cols;
+    p.cpr = cols / 16;
+    p.bcols = (cols + 127) / 128;
+    return p;
+}
+
+// The instantiations are spread over translation units that compile in
+// parallel: fp8_dual.hip (fp32 gate and up), fp8_dual_silu.hip and
+// fp8_dual_gelu.hip (h in the epilogue), fp8_down.hip (h in bf16),
+// fp8_down_silu.hip and fp8_down_gelu.hip (the activation fused into the
+// staging).
+hipError_t fp8_dual_pair(int M, const Fp8Params &p, hipStream_t stream);
+hipError_t fp8_dual_h_silu(int M, const Fp8Params &p, hipStream_t stream);
+hipError_t fp8_dual_h_gelu(int M, const Fp8Params &p, hipStream_t stream);
+hipError_t fp8_down_h(int M, const Fp8Params &p, hipStream_t stream);
+hipError_t fp8_down_act_silu(int M, const Fp8Params &p, hipStream_t stream);
+hipError_t fp8_down_act_gelu(int M, const Fp8Params &p, hipStream_t stream);
 
 }  // namespace ffn

@@ -44,7 +44,7 @@ namespace ffn {
 
 // Many-wave GEMV (1 <= M <= 8; rows of 33 to 768 chunks): one whole row per
 // wave at a time, many waves per compute unit, activations staged in LDS
-// (in several launches of up to 8 activation rows when they do not fit).
+// (in pieces of the reduction when they do not fit); one launch per batch.
 // Returns hipErrorNotSupported for shapes it does not cover.
 hipError_t launch_wave_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1,
                             void *out0, void *out1, int rows, int cols, hipStream_t stream);
@@ -69,8 +69,8 @@ struct Fp8WeightArg {
     const float *block_scale;
 };
 
-// Many-wave GEMV over FP8 weights, 1 <= M <= 8 (batches above 4 rows other
-// than 8 go in several launches); cols a multiple of 16, at most 24576.
+// Many-wave GEMV over FP8 weights, 1 <= M <= 8 (one launch per batch);
+// cols a multiple of 16, at most 24576.
 // The dual takes OUT_F32_PAIR, OUT_H_SILU or OUT_H_GELU; the down takes
 // IN_BF16, IN_GATEUP_SILU or IN_GATEUP_GELU and writes bf16. Returns
 // hipErrorNotSupported for anything else.

@@ -1,6 +1,7 @@
 // wave_gemv.h -- many-wave NVFP4 GEMV for decode and verify batches
-// (1 <= M <= 8 activation rows, launched in groups whose activations fit in
-// LDS): the dual gate+up GEMV and the down GEMV (dense_ffn.rs page,
+// (1 <= M <= 8 activation rows in one launch, so every weight byte is read
+// once for the whole batch; activations staged in LDS, in pieces of the
+// reduction when they do not fit): the dual gate+up GEMV and the down GEMV (dense_ffn.rs page,
 // DenseFfnLayer::forward, forward_k2 / forward_k3 / forward_km) for rows of
 // 33 chunks (1056 columns) or more.
 //

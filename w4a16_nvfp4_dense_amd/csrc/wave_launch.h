@@ -1,5 +1,8 @@
-// wave_launch.hip -- host-side launch of the many-wave GEMV (1 <= M <= 8) and
-// its instantiations.
+// wave_launch.h -- host-side launch templates of the many-wave GEMV
+// (1 <= M <= 8), shared by the dual (wave_dual.hip) and down (wave_down.hip)
+// translation units, which compile in parallel.
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -8,7 +11,7 @@
 
 namespace ffn {
 
-namespace {
+namespace wave {
 
 constexpr int kWaveMaxIt = 12;        // chunks per lane: reduction length up to 24576
 constexpr int kWaveLdsMax = 144 * 1024;  // of the 160 KB per compute unit
@@ -94,65 +97,40 @@ hipError_t launch_m(int M, const WaveParams &p, hipStream_t stream)
     case 2: return launch_one<2, IT, NMAT, IN, OUT>(p, stream);
     case 3: return launch_one<3, IT, NMAT, IN, OUT>(p, stream);
     case 4: return launch_one<4, IT, NMAT, IN, OUT>(p, stream);
+    case 5: return launch_one<5, IT, NMAT, IN, OUT>(p, stream);
+    case 6: return launch_one<6, IT, NMAT, IN, OUT>(p, stream);
+    case 7: return launch_one<7, IT, NMAT, IN, OUT>(p, stream);
     case 8: return launch_one<8, IT, NMAT, IN, OUT>(p, stream);
     default: return hipErrorNotSupported;
     }
 }
 
-// Activation rows per launch: the largest of 8, 4, 3, 2, 1 that is at most
-// `left` (staging that does not fit LDS at once goes in pieces).
-int group_rows(int left)
-{
-    for (int g : {8, 4, 3, 2, 1})
-        if (g <= left)
-            return g;
-    return 0;
-}
-
-// Splits the batch into launches of group_rows() activation rows each (rows
-// of a batch are independent, so the grouping does not change any result;
-// batches of 1 to 4 and of 8 rows are one launch).
+// One launch for the whole batch (1 <= M <= 8): every weight byte is read
+// once for all M activation rows.
 template <int NMAT, int IN, int OUT>
-hipError_t launch_groups(int M, int it, WaveParams p, size_t in_elem, size_t out_elem, hipStream_t stream)
+hipError_t launch_batch(int M, int it, const WaveParams &p, hipStream_t stream)
 {
-    for (int m0 = 0; m0 < M;) {
-        const int g = group_rows(M - m0);
-        if (g == 0)
-            return hipErrorNotSupported;
-        WaveParams q = p;
-        q.in0 = static_cast<const uint8_t *>(p.in0) + static_cast<size_t>(m0) * p.cols * in_elem;
-        if (p.in1)
-            q.in1 = p.in1 + static_cast<size_t>(m0) * p.cols;
-        q.out0 = static_cast<uint8_t *>(p.out0) + static_cast<size_t>(m0) * p.rows * out_elem;
-        if (p.out1)
-            q.out1 = static_cast<uint8_t *>(p.out1) + static_cast<size_t>(m0) * p.rows * out_elem;
-        hipError_t e = hipErrorNotSupported;
-        switch (it) {
+    switch (it) {
 #define FFN_WAVE_CASE(IT_) \
-        case IT_: e = launch_m<IT_, NMAT, IN, OUT>(g, q, stream); break;
-        FFN_WAVE_CASE(1)
-        FFN_WAVE_CASE(2)
-        FFN_WAVE_CASE(3)
-        FFN_WAVE_CASE(4)
-        FFN_WAVE_CASE(5)
-        FFN_WAVE_CASE(6)
-        FFN_WAVE_CASE(7)
-        FFN_WAVE_CASE(8)
-        FFN_WAVE_CASE(9)
-        FFN_WAVE_CASE(10)
-        FFN_WAVE_CASE(11)
-        FFN_WAVE_CASE(12)
+    case IT_: return launch_m<IT_, NMAT, IN, OUT>(M, p, stream);
+    FFN_WAVE_CASE(1)
+    FFN_WAVE_CASE(2)
+    FFN_WAVE_CASE(3)
+    FFN_WAVE_CASE(4)
+    FFN_WAVE_CASE(5)
+    FFN_WAVE_CASE(6)
+    FFN_WAVE_CASE(7)
+    FFN_WAVE_CASE(8)
+    FFN_WAVE_CASE(9)
+    FFN_WAVE_CASE(10)
+    FFN_WAVE_CASE(11)
+    FFN_WAVE_CASE(12)
 #undef FFN_WAVE_CASE
-        default: break;
-        }
-        if (e != hipSuccess)
-            return e;
-        m0 += g;
+    default: return hipErrorNotSupported;
     }
-    return hipSuccess;
 }
 
-WaveParams wave_params(const void *in0, const float *in1, const WeightArg &w0, const WeightArg &w1, void *out0,
+inline WaveParams wave_params(const void *in0, const float *in1, const WeightArg &w0, const WeightArg &w1, void *out0,
                        void *out1, int rows, int cols)
 {
     WaveParams p{};
@@ -174,7 +152,7 @@ WaveParams wave_params(const void *in0, const float *in1, const WeightArg &w0, c
 
 // Chunks per lane when a whole wave takes one row (the canonical lane count
 // for this reduction length is 64), else 0.
-int wave_iters(int cols)
+inline int wave_iters(int cols)
 {
     const int cpr = cols / 32;
     if (lanes_per_row(cpr) != 64)
@@ -182,36 +160,6 @@ int wave_iters(int cols)
     return (cpr + 63) / 64;
 }
 
-}  // namespace
-
-hipError_t launch_wave_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1, void *out0,
-                            void *out1, int rows, int cols, hipStream_t stream)
-{
-    const int it = wave_iters(cols);
-    if (M < 1 || M > 8 || it < 1 || it > kWaveMaxIt)
-        return hipErrorNotSupported;
-    const WaveParams p = wave_params(x, nullptr, w0, w1, out0, out1, rows, cols);
-    switch (out) {
-    case OUT_F32_PAIR: return launch_groups<2, IN_BF16, OUT_F32_PAIR>(M, it, p, 2, 4, stream);
-    case OUT_H_SILU: return launch_groups<2, IN_BF16, OUT_H_SILU>(M, it, p, 2, 2, stream);
-    case OUT_H_GELU: return launch_groups<2, IN_BF16, OUT_H_GELU>(M, it, p, 2, 2, stream);
-    default: return hipErrorNotSupported;
-    }
-}
-
-hipError_t launch_wave_down(int M, InKind in, const void *in0, const float *in1, const WeightArg &w, void *out,
-                            int rows, int cols, hipStream_t stream)
-{
-    const int it = wave_iters(cols);
-    if (M < 1 || M > 8 || it < 1 || it > kWaveMaxIt)
-        return hipErrorNotSupported;
-    const WaveParams p = wave_params(in0, in1, w, w, out, nullptr, rows, cols);
-    switch (in) {
-    case IN_BF16: return launch_groups<1, IN_BF16, OUT_BF16>(M, it, p, 2, 2, stream);
-    case IN_GATEUP_SILU: return launch_groups<1, IN_GATEUP_SILU, OUT_BF16>(M, it, p, 4, 2, stream);
-    case IN_GATEUP_GELU: return launch_groups<1, IN_GATEUP_GELU, OUT_BF16>(M, it, p, 4, 2, stream);
-    default: return hipErrorNotSupported;
-    }
-}
+}  // namespace wave
 
 }  // namespace ffn
