@@ -42,7 +42,9 @@
  *     in rounding, and the 128-row arm's forward splits its reductions by the
  *     device's compute-unit count.
  *   - The functions hold no global mutable state and may be called from
- *     several host threads (on distinct output buffers).
+ *     several host threads (on distinct output buffers), except
+ *     ffn_nvfp4_forward_noalloc, whose per-device scratch array is shared by
+ *     all of its calls on that device.
  */
 #ifndef FFN_NVFP4_H
 #define FFN_NVFP4_H
@@ -126,6 +128,26 @@ int ffn_nvfp4_forward(const void *x, int M, int K, int N,
                       const ffn_nvfp4_weight *down, int act,
                       void *workspace, size_t workspace_bytes,
                       void *out, hipStream_t stream);
+
+/* ffn_nvfp4_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, serving loops,
+ * harnesses that forbid hipMalloc). It computes exactly what
+ * ffn_nvfp4_forward computes, bit for bit, with the workspace taken from a
+ * static device array of the library: 4 MiB per device, held by every device
+ * that runs this entry point until the process ends. The call allocates and
+ * frees nothing.
+ *   - Shapes whose ffn_nvfp4_workspace_bytes(M, K, N) exceeds 4 MiB return
+ *     FFN_NVFP4_ERR_WORKSPACE and launch nothing. M <= 8 always fits
+ *     (M * N * 2 bytes); the 128-row matrix-core arm never does.
+ *   - `stream` must belong to the current device (else FFN_NVFP4_ERR_LAUNCH).
+ *   - Every call on one device shares that device's array: calls that
+ *     overlap on one device (other streams, other host threads) race and
+ *     must be ordered by the caller. The contents need no initialisation.
+ * The other arguments, and every error code, are those of ffn_nvfp4_forward. */
+int ffn_nvfp4_forward_noalloc(const void *x, int M, int K, int N,
+                              const ffn_nvfp4_weight *gate, const ffn_nvfp4_weight *up,
+                              const ffn_nvfp4_weight *down, int act,
+                              void *out, hipStream_t stream);
 
 /* Dual GEMV (one pass over x for both projections; dense_ffn.rs page,
  * DenseFfnLayer::forward, w4a16_gemv_dual). For M > 8 it runs the

@@ -8,6 +8,8 @@ is missing or a call fails, an exception is raised.
 The functions mirror the C entry points:
 
 * :func:`forward`    -- ``ffn_nvfp4_forward``   out = W_d (act(W_g x) * (W_u x))
+* :func:`forward_noalloc` -- ``ffn_nvfp4_forward_noalloc`` the same with the
+  library's static scratch instead of a workspace (allocates nothing)
 * :func:`dual_gemv`  -- ``ffn_nvfp4_dual_gemv`` gate, up = W_g x, W_u x (fp32)
 * :func:`down_gemv`  -- ``ffn_nvfp4_down_gemv`` out = W_d bf16(act(gate) * up)
 * :func:`workspace_bytes` -- ``ffn_nvfp4_workspace_bytes``
@@ -105,6 +107,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ffn_nvfp4_workspace_bytes.argtypes = [_I, _I, _I]
     lib.ffn_nvfp4_forward.restype = _I
     lib.ffn_nvfp4_forward.argtypes = [_P, _I, _I, _I, _WP, _WP, _WP, _I, _P, ctypes.c_size_t, _P, _P]
+    lib.ffn_nvfp4_forward_noalloc.restype = _I
+    lib.ffn_nvfp4_forward_noalloc.argtypes = [_P, _I, _I, _I, _WP, _WP, _WP, _I, _P, _P]
     lib.ffn_nvfp4_dual_gemv.restype = _I
     lib.ffn_nvfp4_dual_gemv.argtypes = [_P, _I, _I, _I, _WP, _WP, _P, _P, _P]
     lib.ffn_nvfp4_down_gemv.restype = _I
@@ -263,6 +267,26 @@ def forward(x, gate: DeviceWeight, up: DeviceWeight, down: DeviceWeight, act: in
                                   out.data_ptr(), _stream_handle(stream))
     _check(rc, "ffn_nvfp4_forward")
     _record(stream, out if new_out else None, workspace if new_ws else None)
+    return out
+
+
+def forward_noalloc(x, gate: DeviceWeight, up: DeviceWeight, down: DeviceWeight, out, act: int = ACT_SILU,
+                    stream=None):
+    """:func:`forward` through ``ffn_nvfp4_forward_noalloc``: the caller
+    passes ``out`` (bf16 [M, K]); no device memory is allocated, by the
+    library or here."""
+    import torch
+    M, K = x.shape
+    N = gate.rows
+    _check_tensor(x, torch.bfloat16, (M, K), "x")
+    _check_nvfp4_weight(gate, N, K, "gate", x.device)
+    _check_nvfp4_weight(up, N, K, "up", x.device)
+    _check_nvfp4_weight(down, K, N, "down", x.device)
+    _check_tensor(out, torch.bfloat16, (M, K), "out", x.device)
+    g, u, d = gate.struct(), up.struct(), down.struct()
+    rc = load().ffn_nvfp4_forward_noalloc(x.data_ptr(), M, K, N, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                                          int(act), out.data_ptr(), _stream_handle(stream))
+    _check(rc, "ffn_nvfp4_forward_noalloc")
     return out
 
 
