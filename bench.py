@@ -39,6 +39,9 @@ WORKLOADS = {
     "decode_gelu_m1": (2, 1),
     "verify_silu_m2": (3, 2),
     "verify_silu_m3": (3, 3),
+    "verify_silu_m5": (3, 5),
+    "verify_silu_m6": (3, 6),
+    "verify_silu_m7": (3, 7),
     "verify_silu_m8": (3, 8),
     "prefill_silu_m128": (4, 128),
     # small batches (9 <= M <= 16) on the prefill shapes: the small-batch arm
@@ -65,6 +68,43 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def lead_spin(n_launch_calls):
+    """Starts a timed region with the GPU busy: a bounded spin kernel
+    (torch.cuda._sleep, on the current stream) runs while the host enqueues
+    the region's start event and launches, so the region holds the launches
+    back to back and not the host's latency to issue the first one after the
+    synchronisation. About 15 us per enqueued call plus 50 us, at most 20 ms
+    (cycles counted at ~2 GHz); the spin itself is outside the region."""
+    import torch
+    us = min(20000.0, 50.0 + 15.0 * n_launch_calls)
+    torch.cuda._sleep(int(us * 2000))
+
+
+def timed_ms(fn, n, stream, warmup=0):
+    """Milliseconds for fn(0) .. fn(n - 1), enqueued back to back on `stream`
+    (the current stream), between HIP events on that stream, after `warmup`
+    untimed calls and a synchronisation."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    lead_spin(n)
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def roofline_bound(flops, nbytes, peak_tflops, peak_gbs=8000.0):
+    """'mfma' when the arithmetic intensity is at or above the ridge point of
+    the matrix peak over HBM bandwidth, else 'hbm'."""
+    return "mfma" if flops / nbytes >= peak_tflops * 1e12 / (peak_gbs * 1e9) else "hbm"
 
 
 def algorithmic_bytes(M, K, N):
@@ -213,17 +253,7 @@ def bench_fp8(args):
         calibration_copy(dev)
 
     def timed(fn, n):
-        for i in range(args.warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1)
+        return timed_ms(fn, n, stream, args.warmup)
 
     ms_total = timed(step, args.steps)
     ms_per_step = ms_total / args.steps
@@ -309,17 +339,7 @@ def bench_w4a4(args):
         calibration_copy(dev)
 
     def timed(fn, n):
-        for i in range(args.warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1)
+        return timed_ms(fn, n, stream, args.warmup)
 
     steps = min(args.steps, 500)
     ms_per_step = timed(step, steps) / steps
@@ -329,6 +349,11 @@ def bench_w4a4(args):
     dual_us = timed(dual, steps) / steps * 1e3
     dual_flops = 2.0 * 2 * M * K * N
     dual_tflops = dual_flops / (dual_us * 1e-6) / 1e12
+    # the dual entry's bytes: both MXFP4 weights (codes + E8M0 per 32), x in
+    # bf16, fp32 gate and up out
+    dual_bytes = 2 * N * K // 2 + 2 * N * K // 32 + 2 * M * K + 8 * M * N
+    dual_gbs = dual_bytes / (dual_us * 1e-6) / 1e9
+    bound = roofline_bound(dual_flops, dual_bytes, MFMA_FP4_PEAK_TFLOPS)
     traffic = measured_traffic(args.workload)
     log(f"[bench] {args.workload}: {us:.2f} us/forward, {tflops:.1f} TFLOP/s; W4A4 dual GEMM (with the activation "
         f"quantisation) {dual_us:.2f} us, {dual_tflops:.1f} TFLOP/s ({100 * dual_tflops / MFMA_FP4_PEAK_TFLOPS:.1f}% "
@@ -344,10 +369,18 @@ def bench_w4a4(args):
                    "M": M, "K": K, "N": N, "act": fi.ACT_NAMES[act], "flops_per_forward": flops},
         "roofline": {"kernel": "W4A4 dual GEMM entry (ffn_w4a4_dual_gemm: mx_quant_bf16_kernel + w4a4_dual_kernel, "
                                "fp32 gate and up out)",
-                     "bound": "mfma", "achieved": round(dual_tflops, 2), "peak": MFMA_FP4_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(dual_tflops / MFMA_FP4_PEAK_TFLOPS, 4),
+                     "bound": bound,
+                     "achieved": round(dual_gbs if bound == "hbm" else dual_tflops, 2),
+                     "peak": HBM_PEAK_GBS if bound == "hbm" else MFMA_FP4_PEAK_TFLOPS,
+                     "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+                     "frac": round(dual_gbs / HBM_PEAK_GBS if bound == "hbm" else dual_tflops / MFMA_FP4_PEAK_TFLOPS,
+                                   4),
                      "traffic": None if traffic is None else round(traffic["bytes"]),
-                     "us_per_launch": round(dual_us, 3), "flops_per_launch": dual_flops},
+                     "us_per_launch": round(dual_us, 3), "flops_per_launch": dual_flops,
+                     "algorithmic_bytes_per_launch": dual_bytes,
+                     "intensity_flop_per_byte": round(dual_flops / dual_bytes, 1),
+                     "tflops": round(dual_tflops, 2),
+                     "frac_of_fp4_peak": round(dual_tflops / MFMA_FP4_PEAK_TFLOPS, 4)},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -415,20 +448,10 @@ def bench_quantize(args):
         outs.append((codes.clone(), scales.clone(), s2.clone()))
     torch.cuda.synchronize()
     assert all(all(torch.equal(a, b) for a, b in zip(o, outs[0])) for o in outs), "input copies disagree"
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
     steps = min(args.steps, 1000)
     t0 = time.perf_counter()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step = timed_ms(step, steps, stream, args.warmup) / steps
     wall = time.perf_counter() - t0
-    ms_per_step = ev0.elapsed_time(ev1) / steps
     us = ms_per_step * 1e3
     nbytes = quant_bytes(rows, cols)
     gbs = nbytes / (us * 1e-6) / 1e9
@@ -501,6 +524,42 @@ def main():
     if args.workload in W4A4_WORKLOADS:
         bench_w4a4(args)
         return
+    bench_nvfp4(args)
+
+
+def single_thread_oracle_us(trials=5):
+    """Median over `trials` runs of one full forward of the oracle on one
+    thread, for the tiny, decode SwiGLU and decode GELU-tanh configs."""
+    import statistics
+    import ffn_inputs as fi
+    import oracle
+
+    orc = oracle.default()
+    threads = orc.num_threads()
+    orc.set_num_threads(1)
+    out = {}
+    try:
+        for idx in (0, 1, 2):
+            case = fi.make_config(idx)
+            ts = []
+            for _ in range(trials):
+                t0 = time.perf_counter()
+                orc.ffn(case)
+                ts.append((time.perf_counter() - t0) * 1e6)
+            out[case.name] = round(statistics.median(ts), 1)
+    finally:
+        orc.set_num_threads(threads)
+    return out
+
+
+def bench_nvfp4(args):
+    import statistics
+
+    import torch
+
+    import ffn_inputs as fi
+    import w4a16_nvfp4_dense_amd as ffn
+
     lib = ffn.load()
     idx, M = WORKLOADS[args.workload]
     case = fi.make_config(idx, M=M) if idx in (3, 4) else fi.make_config(idx)
@@ -530,11 +589,17 @@ def main():
     act = case.act
     nc = len(refs)
 
-    def step(i):
+    def step(i, handle=None):
         g, u, d = refs[i % nc]
-        rc = fwd(xp, M, K, N, g, u, d, act, wp, ws_bytes, op, sh)
+        rc = fwd(xp, M, K, N, g, u, d, act, wp, ws_bytes, op, sh if handle is None else handle)
         if rc:
             raise ffn.FfnError(rc, "ffn_nvfp4_forward")
+
+    def dual_step(i):
+        g, u, _ = refs[i % nc]
+        rc = dual(xp, M, K, N, g, u, gp, upp, sh)
+        if rc:
+            raise ffn.FfnError(rc, "ffn_nvfp4_dual_gemv")
 
     # copies are byte-identical, so every copy must give the same output
     outs = []
@@ -547,76 +612,20 @@ def main():
     if args.calibrate_copy:
         calibration_copy(dev)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    # The timed region: W warmup forwards, then exactly K forwards.
     t0 = time.perf_counter()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms_total = timed_ms(step, args.steps, stream, args.warmup)
     wall = time.perf_counter() - t0
-    ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
     us = ms_per_step * 1e3
     gbs = nbytes["forward"] / (us * 1e-6) / 1e9
     log(f"[bench] {args.workload}: {us:.2f} us/forward, {gbs:.1f} GB/s algorithmic "
-        f"({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f}); host wall {wall * 1e3 / args.steps * 1e3:.2f} us/step")
+        f"({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f}); host wall {wall * 1e6 / args.steps:.2f} us/step")
+    # Context: five more trials of 200 forwards each, median.
+    trials = [timed_ms(step, 200, stream) / 200 * 1e3 for _ in range(5)]
+    us_med5 = statistics.median(trials)
+    log(f"[bench] 5 trials of 200 forwards: median {us_med5:.2f} us (" + ", ".join(f"{t:.2f}" for t in trials) + ")")
 
-    if M > SMALL_BATCH_MAX_M:
-        # Matrix-core arm: bound by the bf16 MFMA rate; the whole forward's
-        # flops (three [M, K] x [K, N]-sized products) over its time.
-        flops = 2.0 * 3 * M * K * N
-        tflops = flops / (us * 1e-6) / 1e12
-        log(f"[bench] {args.workload}: {tflops:.1f} TFLOP/s ({100 * tflops / MFMA_BF16_PEAK_TFLOPS:.1f}% of "
-            f"{MFMA_BF16_PEAK_TFLOPS:.0f})")
-        result = {
-            "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "us_per_forward": round(us, 3),
-            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": f"{case.name}: gated FFN forward, M={M}, hidden K={K}, intermediate N={N}, "
-                                   f"act={fi.ACT_NAMES[act]}, NVFP4 weights rotated over {nc} copies",
-                       "M": M, "K": K, "N": N, "act": fi.ACT_NAMES[act],
-                       "algorithmic_bytes_per_forward": nbytes["forward"]},
-            "roofline": {"kernel": "whole forward (dual GEMM + down GEMM on bf16 matrix cores)", "bound": "mfma",
-                         "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                         "flops_per_forward": flops},
-        }
-        if not args.no_cpu_baseline:
-            result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
-        print(json.dumps(result), flush=True)
-        return
-
-    # Dominant kernel: the dual GEMV, timed with events on its stream around a
-    # batch of back-to-back launches (rotating the weight copies); the average
-    # includes the short gaps between dependent launches.
-    nk = min(args.steps, 1000)
-    for i in range(args.warmup):
-        g, u, _ = refs[i % nc]
-        dual(xp, M, K, N, g, u, gp, upp, sh)
-    d0 = torch.cuda.Event(enable_timing=True)
-    d1 = torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for i in range(nk):
-        g, u, _ = refs[i % nc]
-        rc = dual(xp, M, K, N, g, u, gp, upp, sh)
-        if rc:
-            raise ffn.FfnError(rc, "ffn_nvfp4_dual_gemv")
-    d1.record(stream)
-    torch.cuda.synchronize()
-    dual_us = d0.elapsed_time(d1) / nk * 1e3
-    dual_gbs = nbytes["dual_f32"] / (dual_us * 1e-6) / 1e9
-    log(f"[bench] dual {'GEMV' if M <= 8 else 'GEMM'}: {dual_us:.2f} us/launch, {dual_gbs:.1f} GB/s")
-
-    traffic = measured_traffic(args.workload)
-    if traffic is not None:
-        log(f"[bench] measured HBM traffic of the dual GEMV: {traffic['bytes'] / 1e6:.2f} MB per launch "
-            f"({traffic['bytes'] / nbytes['dual_f32']:.4f} x algorithmic)")
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -638,22 +647,108 @@ def main():
             "M": M, "K": K, "N": N, "act": fi.ACT_NAMES[act],
             "algorithmic_bytes_per_forward": nbytes["forward"],
         },
-        "roofline": {
-            "kernel": ("dual gate+up GEMV (ffn_nvfp4_dual_gemv entry point: wave_gemv_kernel, gate and up fp32 out)"
-                       if M <= 8 else
-                       "dual gate+up GEMM (ffn_nvfp4_dual_gemv entry point: smallm_gemm_kernel, gate and up fp32 out)"),
-            "bound": "hbm",
-            "achieved": round(dual_gbs, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(dual_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None if traffic is None else round(traffic["bytes"]),
-            "us_per_launch": round(dual_us, 3),
-            "algorithmic_bytes_per_launch": nbytes["dual_f32"],
-        },
+        "us_per_forward_median5": round(us_med5, 3),
+        "us_per_forward_trials": [round(t, 3) for t in trials],
     }
+
+    if M > SMALL_BATCH_MAX_M:
+        # Matrix-core arm: bound by the bf16 MFMA rate; the whole forward's
+        # flops (three [M, K] x [K, N]-sized products) over its time.
+        flops = 2.0 * 3 * M * K * N
+        tflops = flops / (us * 1e-6) / 1e12
+        log(f"[bench] {args.workload}: {tflops:.1f} TFLOP/s ({100 * tflops / MFMA_BF16_PEAK_TFLOPS:.1f}% of "
+            f"{MFMA_BF16_PEAK_TFLOPS:.0f})")
+        result["roofline"] = {
+            "kernel": "whole forward (dual GEMM + down GEMM on bf16 matrix cores)",
+            "bound": roofline_bound(flops, nbytes["forward"], MFMA_BF16_PEAK_TFLOPS),
+            "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None, "flops_per_forward": flops,
+            "intensity_flop_per_byte": round(flops / nbytes["forward"], 1)}
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        print(json.dumps(result), flush=True)
+        return
+
+    # Dominant kernel: the dual GEMV (GEMM for the small-batch arm), timed
+    # with events on its stream around a batch of back-to-back launches
+    # (rotating the weight copies).
+    nk = min(args.steps, 1000)
+    dual_us = timed_ms(dual_step, nk, stream, args.warmup) / nk * 1e3
+    dual_gbs = nbytes["dual_f32"] / (dual_us * 1e-6) / 1e9
+    log(f"[bench] dual {'GEMV' if M <= 8 else 'GEMM'}: {dual_us:.2f} us/launch, {dual_gbs:.1f} GB/s")
+    traffic = measured_traffic(args.workload)
+    if traffic is not None:
+        log(f"[bench] measured HBM traffic of the dual GEMV: {traffic['bytes'] / 1e6:.2f} MB per launch "
+            f"({traffic['bytes'] / nbytes['dual_f32']:.4f} x algorithmic)")
+    result["roofline"] = {
+        "kernel": ("dual gate+up GEMV (ffn_nvfp4_dual_gemv entry point: wave_gemv_kernel, gate and up fp32 out)"
+                   if M <= 8 else
+                   "dual gate+up GEMM (ffn_nvfp4_dual_gemv entry point: smallm_gemm_kernel, gate and up fp32 out)"),
+        "bound": "hbm",
+        "achieved": round(dual_gbs, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(dual_gbs / HBM_PEAK_GBS, 4),
+        "traffic": None if traffic is None else round(traffic["bytes"]),
+        "us_per_launch": round(dual_us, 3),
+        "algorithmic_bytes_per_launch": nbytes["dual_f32"],
+    }
+
+    # Streaming-read ceiling (context, not `value`): a trivial kernel with the
+    # GEMVs' load width reading the same weight bytes, as one launch over all
+    # three weights and as two launches (W_g + W_u, then W_d), rotating copies.
+    one = [ffn.DiagRead([g.codes, g.scales, u.codes, u.scales, d.codes, d.scales]) for g, u, d in copies]
+    two = [(ffn.DiagRead([g.codes, g.scales, u.codes, u.scales]), ffn.DiagRead([d.codes, d.scales]))
+           for g, u, d in copies]
+    r1 = timed_ms(lambda i: one[i % nc].launch(stream), 200, stream, 20) / 200 * 1e3
+
+    def two_step(i):
+        a, b = two[i % nc]
+        a.launch(stream)
+        b.launch(stream)
+
+    r2 = timed_ms(two_step, 200, stream, 20) / 200 * 1e3
+    rd = timed_ms(lambda i: two[i % nc][0].launch(stream), 200, stream, 20) / 200 * 1e3
+    wbytes = one[0].bytes
+    log(f"[bench] read ceiling of the {wbytes / 1e6:.1f} MB of weights: one launch {r1:.2f} us "
+        f"({wbytes / r1 / 1e3:.1f} GB/s), two launches {r2:.2f} us; the dual GEMV's bytes alone {rd:.2f} us")
+    result["read_ceiling"] = {
+        "weight_bytes": wbytes,
+        "one_launch_us": round(r1, 3), "one_launch_GBs": round(wbytes / r1 / 1e3, 1),
+        "two_launch_us": round(r2, 3), "dual_bytes_us": round(rd, 3),
+        "forward_frac_of_one_launch": round(r1 / us, 4),
+        "forward_frac_of_two_launch": round(r2 / us, 4),
+        "dual_frac_of_its_read": round(rd / dual_us, 4),
+    }
+
+    if M <= 8:
+        # The same forwards replayed from a HIP graph (one capture of one
+        # forward per weight copy), checked against the eager output.
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for i in range(nc):
+                step(i, side.cuda_stream)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream().cuda_stream
+            for i in range(nc):
+                step(i, cap)
+        torch.cuda.synchronize()
+        out.zero_()
+        reps = max(1, 200 // nc)
+        g_ms = timed_ms(lambda i: graph.replay(), reps, stream, 5)
+        graph_us = g_ms / (reps * nc) * 1e3
+        assert torch.equal(out, outs[0]), "graph replay disagrees with the eager forward"
+        log(f"[bench] HIP graph replay: {graph_us:.2f} us/forward")
+        result["graph_us_per_forward"] = round(graph_us, 3)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        if args.workload == "decode_silu_m1":
+            result["cpu_baseline"]["single_thread_us_median5"] = single_thread_oracle_us()
     print(json.dumps(result), flush=True)
 
 

@@ -76,6 +76,8 @@ class Oracle:
         lib.oracle_ffn.argtypes = [_P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _F, _P, _P, _F, _P]
         lib.oracle_num_threads.restype = _I
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_set_num_threads.restype = None
+        lib.oracle_set_num_threads.argtypes = [_I]
         lib.oracle_e2m1_encode.restype = _I
         lib.oracle_e2m1_encode.argtypes = [_F]
         lib.oracle_e4m3_encode.restype = _I
@@ -200,6 +202,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return self.lib.oracle_num_threads()
+
+    def set_num_threads(self, n: int) -> None:
+        """Threads of later calls (results do not depend on it)."""
+        self.lib.oracle_set_num_threads(int(n))
 
     def e2m1_encode(self, q: float) -> int:
         return self.lib.oracle_e2m1_encode(float(q))

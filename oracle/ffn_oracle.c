@@ -238,6 +238,18 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads for later parallel regions (n >= 1); a no-op without OpenMP. The
+ * sums are per output element, so results do not depend on n. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------ quantiser
  * BF16 -> NVFP4 (qwen35_dense.rs page, weight loader: a global absmax pass,
  * then a pass writing packed E2M1 codes [rows, cols/2], per-16 E4M3 scales

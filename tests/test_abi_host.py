@@ -39,16 +39,50 @@ def down(gi=FAKE, ui=FAKE + 0x200000, M=1, N=512, K=256, d=None, act=0, out=FAKE
 def test_exports_every_header_symbol():
     lib = ffn.load()
     names = ffn.header_functions()
-    assert set(names) == {"ffn_nvfp4_forward", "ffn_nvfp4_dual_gemv", "ffn_nvfp4_down_gemv",
-                          "ffn_nvfp4_workspace_bytes", "ffn_nvfp4_strerror", "ffn_nvfp4_version",
-                          "ffn_nvfp4_quantize", "ffn_nvfp4_quantize_workspace_bytes"}
+    assert set(names) == {"ffn_nvfp4_forward", "ffn_nvfp4_forward_noalloc", "ffn_nvfp4_dual_gemv",
+                          "ffn_nvfp4_down_gemv", "ffn_nvfp4_workspace_bytes", "ffn_nvfp4_strerror",
+                          "ffn_nvfp4_version", "ffn_nvfp4_quantize", "ffn_nvfp4_quantize_workspace_bytes"}
     fp8 = ffn.header_functions(ffn.FP8_HEADER_PATH)
     assert set(fp8) == {"ffn_fp8_forward", "ffn_fp8_dual_gemv", "ffn_fp8_down_gemv", "ffn_fp8_workspace_bytes"}
     w4 = ffn.header_functions(ffn.W4A4_HEADER_PATH)
     assert set(w4) == {"ffn_w4a4_prepare_weight", "ffn_w4a4_workspace_bytes", "ffn_w4a4_dual_gemm",
                        "ffn_w4a4_forward"}
-    for n in list(names) + list(fp8) + list(w4):
+    diag = ffn.header_functions(ffn.DIAG_HEADER_PATH)
+    assert set(diag) == {"ffn_diag_read"}
+    for n in list(names) + list(fp8) + list(w4) + list(diag):
         assert hasattr(lib, n), n
+
+
+def test_noalloc_rejects_oversized_workspace_before_any_launch():
+    """Shapes whose workspace exceeds the 4 MiB static scratch are refused
+    before anything touches a device (the 128-row arm, and M <= 8 never)."""
+    lib = ffn.load()
+    w = W()
+    assert ffn.workspace_bytes(128, 5120, 17408) > 4 << 20
+    rc = lib.ffn_nvfp4_forward_noalloc(FAKE, 128, 5120, 17408, ctypes.byref(w), ctypes.byref(w), ctypes.byref(w),
+                                       0, FAKE + 0x400000, 0)
+    assert rc == ffn.ERR_WORKSPACE
+    assert ffn.workspace_bytes(8, 65536, 65536) <= 4 << 20
+
+
+def test_diag_read_validation():
+    lib = ffn.load()
+    P = ctypes.c_void_p
+    S = ctypes.c_size_t
+
+    def call(ptrs, sizes, n=None, sink=FAKE):
+        n = len(ptrs) if n is None else n
+        return lib.ffn_diag_read((P * max(1, len(ptrs)))(*ptrs), (S * max(1, len(sizes)))(*sizes), n, sink, 0)
+
+    assert call([FAKE], [16], n=0) == ffn.ERR_SHAPE
+    assert call([FAKE] * 9, [16] * 9) == ffn.ERR_SHAPE
+    assert call([FAKE], [24]) == ffn.ERR_SHAPE
+    assert call([FAKE + 8], [16]) == ffn.ERR_ALIGN
+    assert call([FAKE], [16], sink=FAKE + 2) == ffn.ERR_ALIGN
+    assert call([FAKE], [16], sink=0) == ffn.ERR_NULL
+    assert call([0], [16]) == ffn.ERR_NULL
+    assert lib.ffn_diag_read(None, None, 1, FAKE, 0) == ffn.ERR_NULL
+    assert call([0, 0], [0, 0]) == ffn.OK  # nothing to read: no launch
 
 
 def test_version_strerror_workspace():

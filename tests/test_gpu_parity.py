@@ -325,8 +325,7 @@ def test_verify_batch_one_launch(M):
     """Verify batches of 5 to 7 rows at the decode shape (one launch per
     projection): every element against the oracle, every row bit-identical
     to the M = 1 call on it."""
-    case = fi.make_ffn(f"verify_silu_m{M}", M, 5120, 17408, fi.ACT_SILU, 1.0, 2.0 ** -4, fi.SEED_BASE + 1,
-                       x_seed=fi.SEED_BASE + 3 + 100 * M)
+    case = fi.make_config(3, M=M)
     L = loaded(case.name, lambda: case)
     out = L.forward()
     torch.cuda.synchronize()

@@ -23,6 +23,11 @@ and, for block-scaled FP8 weights (``include/ffn_fp8.h``):
 * :func:`fp8_down_gemv`  -- ``ffn_fp8_down_gemv``
 * :func:`fp8_workspace_bytes` -- ``ffn_fp8_workspace_bytes``
 
+the streaming-read ceiling the decode GEMVs are measured against
+(``include/ffn_diag.h``):
+
+* :func:`diag_read` -- ``ffn_diag_read`` one launch reading device buffers once
+
 and the W4A4 prefill arm over MXFP4 operands (``include/ffn_w4a4.h``):
 
 * :func:`w4a4_prepare_weight` -- ``ffn_w4a4_prepare_weight`` NVFP4 -> MXFP4 (once)
@@ -42,6 +47,7 @@ LIB_PATH = os.path.join(PKG_DIR, "lib", "libffn_nvfp4.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "ffn_nvfp4.h")
 FP8_HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "ffn_fp8.h")
 W4A4_HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "ffn_w4a4.h")
+DIAG_HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "ffn_diag.h")
 
 ACT_SILU = 0
 ACT_GELU_TANH = 1
@@ -131,6 +137,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ffn_w4a4_workspace_bytes.argtypes = [_I, _I, _I]
     lib.ffn_w4a4_dual_gemm.restype = _I
     lib.ffn_w4a4_dual_gemm.argtypes = [_P, _I, _I, _I, _MP, _MP, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.ffn_diag_read.restype = _I
+    lib.ffn_diag_read.argtypes = [ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_size_t), _I, _P, _P]
     lib.ffn_w4a4_forward.restype = _I
     lib.ffn_w4a4_forward.argtypes = [_P, _I, _I, _I, _MP, _MP, _WP, _I, _P, ctypes.c_size_t, _P, _P]
     _lib = lib
@@ -142,7 +150,7 @@ def header_functions(path: str = HEADER_PATH) -> Sequence[str]:
     import re
     text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ffn_(?:nvfp4|fp8|w4a4)_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ffn_(?:nvfp4|fp8|w4a4|diag)_[a-z_0-9]+)\s*\(", text)))
 
 
 def version() -> int:
@@ -610,3 +618,35 @@ def w4a4_forward(x, gate: MxDeviceWeight, up: MxDeviceWeight, down: DeviceWeight
     _check(rc, "ffn_w4a4_forward")
     _record(stream, *fresh)
     return out
+
+
+# ------------------------------------------------------------ measurement aid
+
+
+class DiagRead:
+    """Prepared arguments of ``ffn_diag_read`` over a list of device tensors
+    (contiguous, sizes multiples of 16 bytes): ``launch(stream)`` enqueues one
+    read of all of them."""
+
+    def __init__(self, tensors):
+        import torch
+        if not 1 <= len(tensors) <= 8:
+            raise ValueError("1 to 8 buffers")
+        for t in tensors:
+            if t.device.type != "cuda" or not t.is_contiguous():
+                raise ValueError("buffers must be contiguous GPU tensors")
+        self._keep = list(tensors)
+        self.n = len(tensors)
+        self.bytes = sum(t.numel() * t.element_size() for t in tensors)
+        self._ptrs = (_P * self.n)(*[t.data_ptr() for t in tensors])
+        self._sizes = (ctypes.c_size_t * self.n)(*[t.numel() * t.element_size() for t in tensors])
+        self._sink = torch.zeros(1, dtype=torch.int32, device=tensors[0].device)
+
+    def launch(self, stream=None) -> None:
+        rc = load().ffn_diag_read(self._ptrs, self._sizes, self.n, self._sink.data_ptr(), _stream_handle(stream))
+        _check(rc, "ffn_diag_read")
+
+
+def diag_read(tensors, stream=None) -> None:
+    """One streaming read of every byte of ``tensors`` (see ``ffn_diag.h``)."""
+    DiagRead(tensors).launch(stream)

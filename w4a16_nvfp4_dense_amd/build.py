@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(LIB_DIR, "libffn_nvfp4.so")
 # longest compiles first (they start first in the pool)
 SOURCES = ["wave_dual.hip", "fp8_dual.hip", "fp8_dual_silu.hip", "fp8_dual_gelu.hip", "wave_down.hip",
            "fp8_down_silu.hip", "fp8_down_gelu.hip", "fp8_down.hip", "mfma_launch.hip", "smallm_launch.hip",
-           "gemv.hip", "quantize.hip", "w4a4.hip", "noalloc.hip", "abi.cpp", "abi_fp8.cpp", "abi_w4a4.cpp"]
+           "gemv.hip", "quantize.hip", "w4a4.hip", "noalloc.hip", "stream_read.hip", "abi.cpp", "abi_fp8.cpp", "abi_w4a4.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

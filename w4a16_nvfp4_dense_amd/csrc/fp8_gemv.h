@@ -338,8 +338,8 @@ hipError_t fp8_launch_one(const Fp8Params &p, hipStream_t stream)
     auto kern = fp8_gemv_kernel<M, IT, NMAT, IN, OUT, W, P>;
     const int lds = M * fp8_piece_steps<M, IT, NMAT>() * 2048;
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        static std::atomic<uint64_t> lds_done{0};
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds, lds_done);
         if (e != hipSuccess)
             return e;
     }

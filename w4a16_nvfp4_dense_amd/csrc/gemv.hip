@@ -225,9 +225,9 @@ hipError_t launch_one(const GemvParams &p, size_t lds_bytes, hipStream_t stream)
     const int blocks = (p.rows + rows_per_block - 1) / rows_per_block;
     auto kern = gemv_kernel<M, LPR, NMAT, IN, OUT>;
     if (lds_bytes > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(lds_bytes));
+        // the staged size depends on the shape: allow the whole LDS once
+        static std::atomic<uint64_t> lds_done{0};
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), 160 * 1024, lds_done);
         if (e != hipSuccess)
             return e;
     }

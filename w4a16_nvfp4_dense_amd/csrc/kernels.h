@@ -5,7 +5,28 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace ffn {
+
+// Lets `kern` use up to `lds` bytes of dynamic LDS on the current device.
+// hipFuncSetAttribute is a host call; `done` (one per kernel, a static of its
+// launcher) records the devices it was made on, so it runs once per kernel
+// and device instead of on every launch (and never while a caller captures
+// the launches into a graph, once they have run eagerly).
+inline hipError_t allow_lds(const void *kern, int lds, std::atomic<uint64_t> &done)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        dev = -1;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0)
+        return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess && bit != 0)
+        done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 struct WeightArg {
     const uint8_t *codes;   // [rows, cols/2]

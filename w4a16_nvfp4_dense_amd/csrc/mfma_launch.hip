@@ -26,8 +26,8 @@ hipError_t launch_t(MfmaParams p, int G, hipStream_t stream)
     constexpr int S = stages<MT>();
     auto kern = mfma_gemm_kernel<MT, NMAT, IN, OUT, S>;
     const int lds = S * mfma_stage_bytes<MT>();
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    static std::atomic<uint64_t> lds_done{0};
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds, lds_done);
     if (e != hipSuccess)
         return e;
     void *args[] = {&p};

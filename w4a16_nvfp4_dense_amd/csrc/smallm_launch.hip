@@ -53,7 +53,8 @@ hipError_t launch_t(const SmallParams &p, int rounds, hipStream_t stream)
     default: return hipErrorNotSupported;
     }
     constexpr int lds = sm_lds_bytes<NMAT>();
-    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    static std::atomic<uint64_t> lds_done[5];  // per rounds instantiation
+    hipError_t e = allow_lds(kern, lds, lds_done[rounds - 1]);
     if (e != hipSuccess)
         return e;
     void *args[] = {const_cast<SmallParams *>(&p)};

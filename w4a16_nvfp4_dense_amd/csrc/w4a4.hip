@@ -332,8 +332,8 @@ template <int OUT>
 hipError_t launch_dual_t(const W4a4Params &p, dim3 grid, hipStream_t stream)
 {
     auto kern = w4a4_dual_kernel<OUT>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kW4LdsBytes);
+    static std::atomic<uint64_t> lds_done{0};
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), kW4LdsBytes, lds_done);
     if (e != hipSuccess)
         return e;
     W4a4Params q = p;

@@ -72,8 +72,8 @@ hipError_t launch_one(const WaveParams &p, hipStream_t stream)
     auto kern = wave_gemv_kernel<M, IT, NMAT, IN, OUT, W, P>;
     const int lds = M * wave_piece_steps<M, IT>() * 4096;
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        static std::atomic<uint64_t> lds_done{0};
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds, lds_done);
         if (e != hipSuccess)
             return e;
     }
