@@ -44,11 +44,16 @@ WORKLOADS = {
     "verify_silu_m7": (3, 7),
     "verify_silu_m8": (3, 8),
     "prefill_silu_m128": (4, 128),
-    # small batches (9 <= M <= 16) on the prefill shapes: the small-batch arm
+    # small batches (9 <= M <= 32) on the prefill shapes: the small-batch arm
     "smallbatch_silu_m9": (4, 9),
     "smallbatch_silu_m16": (4, 16),
+    "smallbatch_silu_m17": (4, 17),
+    "smallbatch_silu_m32": (4, 32),
+    # 33 <= M <= 64: the 128-row matrix-core arm (one or two token tiles)
+    "smallbatch_silu_m48": (4, 48),
+    "smallbatch_silu_m64": (4, 64),
 }
-SMALL_BATCH_MAX_M = 16  # above this the forward runs the 128-row matrix-core arm
+SMALL_BATCH_MAX_M = 32  # above this the forward runs the 128-row matrix-core arm
 # The BF16 -> NVFP4 quantiser (ffn_nvfp4_quantize) on one weight of the decode
 # gate/up shape; timed like the forward, reported on its own line.
 QUANT_WORKLOADS = {"quantize_17408x5120": (17408, 5120)}
@@ -651,18 +656,26 @@ def bench_nvfp4(args):
         "us_per_forward_trials": [round(t, 3) for t in trials],
     }
 
-    if M > SMALL_BATCH_MAX_M:
-        # Matrix-core arm: bound by the bf16 MFMA rate; the whole forward's
-        # flops (three [M, K] x [K, N]-sized products) over its time.
+    if M > 16:
+        # Matrix-core arms beyond one token group: the roofline is the whole
+        # forward (its kernels are not all reachable through the dual entry),
+        # against HBM or the bf16 MFMA peak, whichever its arithmetic
+        # intensity (three [M, K] x [K, N]-sized products over the forward's
+        # bytes) makes the bound.
         flops = 2.0 * 3 * M * K * N
         tflops = flops / (us * 1e-6) / 1e12
+        bound = roofline_bound(flops, nbytes["forward"], MFMA_BF16_PEAK_TFLOPS)
+        arm = "small-batch GEMMs" if M <= SMALL_BATCH_MAX_M else "128-row GEMMs"
         log(f"[bench] {args.workload}: {tflops:.1f} TFLOP/s ({100 * tflops / MFMA_BF16_PEAK_TFLOPS:.1f}% of "
-            f"{MFMA_BF16_PEAK_TFLOPS:.0f})")
+            f"{MFMA_BF16_PEAK_TFLOPS:.0f}); bound by {bound}")
         result["roofline"] = {
-            "kernel": "whole forward (dual GEMM + down GEMM on bf16 matrix cores)",
-            "bound": roofline_bound(flops, nbytes["forward"], MFMA_BF16_PEAK_TFLOPS),
-            "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None, "flops_per_forward": flops,
+            "kernel": f"whole forward ({arm}: dual GEMM + down GEMM on bf16 matrix cores)",
+            "bound": bound,
+            "achieved": round(gbs if bound == "hbm" else tflops, 2),
+            "peak": HBM_PEAK_GBS if bound == "hbm" else MFMA_BF16_PEAK_TFLOPS,
+            "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+            "frac": round(gbs / HBM_PEAK_GBS if bound == "hbm" else tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None, "flops_per_forward": flops, "tflops": round(tflops, 2),
             "intensity_flop_per_byte": round(flops / nbytes["forward"], 1)}
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

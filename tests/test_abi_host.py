@@ -94,15 +94,22 @@ def test_version_strerror_workspace():
     assert ffn.workspace_bytes(8, 5120, 17408) == 8 * 17408 * 2
     assert ffn.workspace_bytes(0, 256, 512) == 0
     assert ffn.workspace_bytes(1, 250, 512) == 0
-    # small-batch arm (9 <= M <= 16, K <= 5120): h, and the down projection's
-    # partial sums when its reduction is split (N = 17408: 4 parts)
+    # small-batch arm (9 <= M <= 32, K and N multiples of 256): h, the down
+    # projection's partial sums when its reduction is split (N = 17408: 4
+    # parts), and the dual projection's when its reduction is split (two
+    # token groups at K = 5120: 2 parts)
+    r256 = lambda b: (b + 255) // 256 * 256
     assert ffn.workspace_bytes(9, 256, 512) == 9 * 512 * 2
     assert ffn.workspace_bytes(16, 5120, 17408) == 16 * 17408 * 2 + 4 * 16 * 5120 * 4
-    # 128-row matrix-core arm (M > 16, or K > 5120): h for one block of 128
-    # rows and the partial slots
-    ws17 = ffn.workspace_bytes(17, 256, 512)
-    assert ws17 > 17 * 512 * 2 and ws17 % 256 == 0
-    assert ffn.workspace_bytes(16, 5376, 512) > 16 * 512 * 2
+    assert ffn.workspace_bytes(17, 5120, 17408) == (r256(17 * 17408 * 2) + 4 * 17 * 5120 * 4
+                                                    + 2 * 2 * 17 * 17408 * 4)
+    assert ffn.workspace_bytes(32, 4096, 8192) == r256(32 * 8192 * 2) + 2 * 32 * 4096 * 4
+    assert ffn.workspace_bytes(16, 5376, 512) == r256(16 * 512 * 2) + 2 * 2 * 16 * 512 * 4
+    # 128-row matrix-core arm (M > 32, or K or N not a multiple of 256): h for
+    # one block of 128 rows and the partial slots
+    ws33 = ffn.workspace_bytes(33, 256, 512)
+    assert ws33 > 33 * 512 * 2 and ws33 % 256 == 0
+    assert ffn.workspace_bytes(16, 640, 1024) > 32 << 20
     assert ffn.workspace_bytes(128, 5120, 17408) == ffn.workspace_bytes(4096, 5120, 17408)
     assert ffn.workspace_bytes(128, 5120, 17408) >= 128 * 17408 * 2
     assert ffn.workspace_bytes(9, 96, 512) == 0   # the arm needs K, N multiples of 64

@@ -1,5 +1,5 @@
-"""GPU parity of the small-batch matrix-core arm (9 <= M <= 16 token rows,
-K and N multiples of 256, K at most 5120) against the CPU oracle, with the
+"""GPU parity of the small-batch matrix-core arm (9 <= M <= 32 token rows,
+K and N multiples of 256) against the CPU oracle, with the
 bounds of the other arms: |out - out_ref| <= 1e-2 rms(out_ref) + 1 bf16 ulp(out_ref); the dual
 entry's fp32 gate/up within 1e-4 rms(ref) + 1e-6 |ref|.
 """
@@ -28,6 +28,18 @@ SMALL_BATCH = [
     (16, 2048, 8192, fi.ACT_SILU, 55),
     (13, 5120, 6144, fi.ACT_GELU_TANH, 56),
     (11, 5120, 1024, fi.ACT_SILU, 57),
+    # two token groups (17 <= M <= 32): the second group from one row to
+    # full, the dual projection in one part (K <= 4096) and in two (K = 5120,
+    # with the paired reduction and the activation epilogue), down
+    # projections in one and several parts
+    (17, 256, 512, fi.ACT_SILU, 61),
+    (24, 1280, 2048, fi.ACT_GELU_TANH, 62),
+    (32, 4096, 1024, fi.ACT_SILU, 63),
+    (20, 5120, 2048, fi.ACT_GELU_TANH, 64),
+    (31, 2048, 8192, fi.ACT_SILU, 65),
+    (32, 5120, 6144, fi.ACT_GELU_TANH, 66),
+    # one token group with the dual projection split (K above 5120)
+    (12, 5376, 1024, fi.ACT_SILU, 67),
 ]
 IDS = [f"m{m}_k{k}_n{n}_a{a}" for m, k, n, a, _ in SMALL_BATCH]
 
@@ -64,17 +76,20 @@ def test_smallbatch_workspace():
     # N = 17408: 68 blocks of 256 columns in parts of at most 20: 4 parts,
     # 64 groups of 5 tiles
     assert ffn.workspace_bytes(16, 5120, 17408) == r256(16 * 17408 * 2) + 4 * 16 * 5120 * 4
-    # M = 17, K above 5120, or K or N not a multiple of 256: the 128-row arm
-    # with its partial slots
-    assert ffn.workspace_bytes(17, 5120, 17408) > 32 << 20
-    assert ffn.workspace_bytes(16, 5376, 21504) > 32 << 20
+    # two token groups: the dual projection's reduction in 2 parts (K = 5120),
+    # the down projection's in 4
+    assert ffn.workspace_bytes(17, 5120, 17408) == (r256(17 * 17408 * 2) + 4 * 17 * 5120 * 4
+                                                    + 2 * 2 * 17 * 17408 * 4)
+    # M = 33, or K or N not a multiple of 256: the 128-row arm with its
+    # partial slots
+    assert ffn.workspace_bytes(33, 5120, 17408) > 32 << 20
     assert ffn.workspace_bytes(16, 640, 1024) > 32 << 20
 
 
 def test_smallbatch_rows_independent_of_batch():
     """Inside the arm a token row's result does not depend on the other rows
-    of the batch: its position in the token tile and M do not change the order
-    of any sum."""
+    of a batch with the same token-group count: its position in the token
+    tile and M do not change the order of any sum."""
     case = fi.make_small(16, 2048, 6144, act=fi.ACT_GELU_TANH, seed=59)
     L = loaded(case.name, lambda: case)
     full = L.forward()
@@ -94,11 +109,23 @@ def test_smallbatch_determinism():
         assert torch.equal(L.forward(), first)
 
 
-@pytest.mark.parametrize("M", [9, 16])
+def test_smallbatch_two_groups_rows_independent():
+    """The same for two token groups (17 to 32 rows), with the dual
+    projection split in parts (K = 5120)."""
+    case = fi.make_small(32, 5120, 2048, act=fi.ACT_SILU, seed=68)
+    L = loaded(case.name, lambda: case)
+    full = L.forward()
+    for lo, hi in ((0, 17), (15, 32), (3, 29), (8, 32)):
+        part = L.forward(L.x[lo:hi].contiguous())
+        assert torch.equal(part, full[lo:hi]), (lo, hi)
+
+
+@pytest.mark.parametrize("M", [9, 16, 17, 32, 48, 64])
 def test_config_smallbatch(M):
-    """The prefill shapes (hidden 5120, intermediate 17408, SiLU) at 9 and 16
-    token rows, the launch configuration the bench times: the forward and the
-    dual entry against the oracle on every token row."""
+    """The prefill shapes (hidden 5120, intermediate 17408, SiLU) at 9 to 64
+    token rows (above 32 the 128-row arm, with one or two token tiles), the
+    launch configuration the bench times: the forward and the dual entry
+    against the oracle on every token row."""
     case = fi.make_config(4, M=M)
     L = loaded(case.name, lambda: case)
     out = L.forward()

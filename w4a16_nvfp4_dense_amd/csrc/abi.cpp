@@ -76,16 +76,25 @@ struct PrefillLayout {
     size_t h, partials, total;
 };
 
-// Batches of 9 to 16 rows take the small-batch arm when it covers the shape;
-// its workspace is h and the down projection's partial sums.
+// Batches of 9 to 32 rows take the small-batch arm when it covers the shape;
+// its workspace is h, the down projection's partial sums and, when the dual
+// projection's reduction is split in parts, its partial sums.
 bool small_arm(int M, int K, int N)
 {
     return M > kMaxGemvM && ffn::smallm_supported(M, K, N);
 }
 
-size_t small_partials_offset(int M, int N)
+struct SmallLayout {
+    size_t down_partials, dual_partials, total;
+};
+
+SmallLayout small_layout(int M, int K, int N)
 {
-    return round256(static_cast<size_t>(M) * static_cast<size_t>(N) * 2);
+    SmallLayout l{};
+    l.down_partials = round256(static_cast<size_t>(M) * static_cast<size_t>(N) * 2);
+    l.dual_partials = l.down_partials + round256(ffn::smallm_partial_floats(M, K, N) * sizeof(float));
+    l.total = l.dual_partials + round256(ffn::smallm_dual_partial_floats(M, K, N) * sizeof(float));
+    return l;
 }
 
 PrefillLayout prefill_layout(int M, int N)
@@ -133,8 +142,10 @@ hipError_t run_down(int M, ffn::InKind in, const void *in0, const float *in1, co
 hipError_t run_prefill_dual(int M, const void *x, const ffn::WeightArg &g, const ffn::WeightArg &u, float *gate_out,
                             float *up_out, int N, int K, hipStream_t stream)
 {
-    if (small_arm(M, K, N))
-        return ffn::launch_smallm_dual(M, ffn::OUT_F32_PAIR, x, g, u, gate_out, up_out, N, K, stream);
+    // The dual entry has no workspace: the small-batch arm only when its
+    // reduction is not split.
+    if (small_arm(M, K, N) && !ffn::smallm_dual_split(M, K, N))
+        return ffn::launch_smallm_dual(M, ffn::OUT_F32_PAIR, x, g, u, gate_out, up_out, nullptr, N, K, stream);
     for (int m0 = 0; m0 < M; m0 += ffn::kMfmaMaxM) {
         const int mb = M - m0 < ffn::kMfmaMaxM ? M - m0 : ffn::kMfmaMaxM;
         const size_t xo = static_cast<size_t>(m0) * K, oo = static_cast<size_t>(m0) * N;
@@ -165,11 +176,14 @@ hipError_t run_prefill_forward(int M, ffn::OutKind epi, const void *x, const ffn
                                int N, hipStream_t stream)
 {
     if (small_arm(M, K, N)) {
-        float *partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + small_partials_offset(M, N));
-        hipError_t e = ffn::launch_smallm_dual(M, epi, x, g, u, workspace, nullptr, N, K, stream);
+        const SmallLayout l = small_layout(M, K, N);
+        uint8_t *ws = static_cast<uint8_t *>(workspace);
+        hipError_t e = ffn::launch_smallm_dual(M, epi, x, g, u, workspace, nullptr,
+                                               reinterpret_cast<float *>(ws + l.dual_partials), N, K, stream);
         if (e != hipSuccess)
             return e;
-        return ffn::launch_smallm_down(M, workspace, d, out, partials, K, N, stream);
+        return ffn::launch_smallm_down(M, workspace, d, out, reinterpret_cast<float *>(ws + l.down_partials), K, N,
+                                       stream);
     }
     const PrefillLayout l = prefill_layout(M, N);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -223,7 +237,7 @@ size_t ffn_nvfp4_workspace_bytes(int M, int K, int N)
     if (M == 0 || check_prefill_shape(M, K, N) != FFN_NVFP4_OK)
         return 0;
     if (small_arm(M, K, N))
-        return small_partials_offset(M, N) + round256(ffn::smallm_partial_floats(M, K, N) * sizeof(float));
+        return small_layout(M, K, N).total;
     if (M > kMaxGemvM)
         return prefill_layout(M, N).total;
     // h = act(gate) * up in bf16, [M, N]

@@ -48,6 +48,7 @@ enum OutKind : int {
     OUT_H_SILU = 2,    // two projections: out0 = bf16(SiLU(s2_0 y0) * s2_1 y1) [M, rows]
     OUT_H_GELU = 3,    // same with GELU-tanh
     OUT_PART_F32 = 4,  // one projection, a piece of a split reduction: out0 = y0 (fp32, unscaled)
+    OUT_PART_PAIR = 5, // two projections, pieces of split reductions: out0 = y0, out1 = y1 (fp32, unscaled)
 };
 
 // Streaming GEMV over NVFP4 weights for 1 <= M <= 8 activation rows:

@@ -1,5 +1,5 @@
 // smallm_gemm.h -- the small-batch matrix-core arm of the NVFP4 gated FFN
-// (9 <= M <= 16 token rows): the dual gate+up projection and the down
+// (9 <= M <= 32 token rows): the dual gate+up projection and the down
 // projection as skinny GEMMs on bf16 matrix cores, for the batch sizes between
 // the batched GEMV and the 128-row prefill tiles (dense_ffn.rs page, the
 // prefill GEMM dispatch by token count, whose small-M tiles exist because
@@ -15,7 +15,10 @@
 // (4 (lane / 16) + v). At the end of the tile the 16 waves add their
 // accumulators through LDS in a fixed order (waves 0-7 and 8-15 in wave
 // order, then the two halves). At M <= 16 this MFMA shape reads each
-// weight once per 16 cycles, twice the rate of the 32x32x16 shape.
+// weight once per 16 cycles, twice the rate of the 32x32x16 shape. Batches
+// of 17 to 32 rows run two token groups of 16 (TG = 2): each dequantised
+// weight fragment feeds the products of both, so a weight is still read and
+// dequantised once.
 //
 // Dequantisation. As in the prefill arm: FP4 pair -> fp32 pair (unit-scale
 // hardware conversion) times the E4M3 block scale, rounded to bf16, which is
@@ -42,15 +45,19 @@
 // bytes and both steps use one scale.
 //
 // Work split. Workgroup w takes part w % P of the reduction (P consecutive
-// ranges of 256-column blocks; P > 1 only for the down projection, whose
-// reduction is long and whose tiles are few) and tiles [g T / G, (g + 1) T / G) with
-// g = w / P, T tiles and G = gridDim / P groups. With P = 1 the epilogue
-// writes finished outputs; with P > 1 it writes the part's fp32 sums and
-// smallm_reduce_kernel adds the parts in order. (Adding them in the kernel,
+// ranges of 256-column blocks, each at most as many rounds as a wave's
+// activations fit in registers: 5 rounds, 4 for the dual GEMM with two token
+// groups) and
+// tiles [g T / G, (g + 1) T / G) with g = w / P, T tiles and G = gridDim / P
+// groups. With P = 1 the epilogue writes finished outputs; with P > 1 it
+// writes the part's fp32 sums and smallm_reduce_kernel (down) or
+// smallm_reduce_pair_kernel (dual, with the activation epilogue) adds the
+// parts in order. (Adding them in the kernel,
 // by the last of a group's workgroups to finish, measured no faster: the
 // exchange between XCDs costs the same round trips as a second launch.) No
 // workgroup waits for another, the order of every sum is fixed, and a token
-// row's result does not depend on the other rows of the batch.
+// row's result does not depend on the other rows of the batch within one
+// token-group count (the count sets the parts, hence the order of the sums).
 #pragma once
 
 #include "kernels.h"
@@ -65,7 +72,9 @@ constexpr int kSmRows = 16;                   // weight rows per tile
 constexpr int kSmUnit = 64;                   // reduction columns per wave and round
 constexpr int kSmRound = kSmWaves * kSmUnit;  // reduction columns per round
 constexpr int kSmMaxRounds = 5;               // rounds per tile and part (activations kept in registers)
-constexpr int kSmStages = 3;                  // LDS ring stages (deeper measured slower: the arm is bound by its arithmetic, not by load latency)
+constexpr int kSmStages = 3;
+constexpr int kSmMaxGroups = 2;               // token groups of 16 (M <= 32)
+constexpr int kSmMaxRoundsTwoGroups = 4;      // rounds per tile and part of the dual GEMM with two token groups                  // LDS ring stages (deeper measured slower: the arm is bound by its arithmetic, not by load latency)
 
 struct SmallParams {
     const void *in0;  // bf16 [M, cols]
@@ -77,7 +86,7 @@ struct SmallParams {
     float s2_1;
     void *out0;
     void *out1;
-    int M;       // token rows, 1 <= M <= 16
+    int M;       // token rows, 1 <= M <= 16 TG
     int rows;    // weight rows (output columns), a multiple of 16
     int cols;    // reduction length, a multiple of 256
     int parts;   // P
@@ -109,10 +118,11 @@ constexpr int sm_lds_bytes()
     return kSmStages * sm_stage_bytes<NMAT>() + sm_red_bytes<NMAT>() + 1280;
 }
 
-template <int NMAT, int OUT, int NR>
+template <int NMAT, int OUT, int NR, int TG>
 __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallParams p)
 {
     static_assert(NR >= 1 && NR <= kSmMaxRounds, "rounds");
+    static_assert(TG >= 1 && TG <= kSmMaxGroups, "token groups");
     constexpr int S = kSmStages;
     constexpr int STAGE = sm_stage_bytes<NMAT>();
     constexpr int CODES = NMAT * kSmRows * (kSmRound / 2);  // code bytes of a stage
@@ -218,18 +228,22 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
     // prologue rounds are issued after it; round 0 is needed first anyway.
     issue_next();
 
-    u32x4_t xr[NR][2];
+    // Token group t holds tokens 16 t .. 16 t + 15.
+    u32x4_t xr[NR][TG][2];
     {
         const uint16_t *X = static_cast<const uint16_t *>(p.in0);
-        const int tok = min(lane >> 2, M - 1);  // rows past the batch re-read the last one (never stored)
 #pragma unroll
-        for (int i = 0; i < NR; ++i)
+        for (int t = 0; t < TG; ++t) {
+            const int tok = min(16 * t + (lane >> 2), M - 1);  // rows past the batch re-read the last one (never stored)
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int u = min(ua + kSmWaves * i + q, NU - 1);
-                xr[i][s] = *reinterpret_cast<const u32x4_t *>(X + static_cast<size_t>(tok) * cols + u * kSmUnit +
-                                                              16 * (lane & 3) + 8 * s);
-            }
+            for (int i = 0; i < NR; ++i)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int u = min(ua + kSmWaves * i + q, NU - 1);
+                    xr[i][t][s] = *reinterpret_cast<const u32x4_t *>(X + static_cast<size_t>(tok) * cols +
+                                                                     u * kSmUnit + 16 * (lane & 3) + 8 * s);
+                }
+        }
     }
 
     {
@@ -237,21 +251,25 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
 #pragma unroll
         for (int i = 0; i < NR; ++i)
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+            for (int t = 0; t < TG; ++t)
 #pragma unroll
-                for (int d = 0; d < 4; ++d)
-                    xr[i][s][d] = static_cast<uint32_t>(
-                        __builtin_amdgcn_ds_bpermute(src, static_cast<int>(xr[i][s][d])));
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        xr[i][t][s][d] = static_cast<uint32_t>(
+                            __builtin_amdgcn_ds_bpermute(src, static_cast<int>(xr[i][t][s][d])));
     }
 
 #pragma unroll
     for (int k = 1; k < S - 1; ++k)
         issue_next();
 
-    f32x4_t acc[NMAT];
+    f32x4_t acc[NMAT][TG];
 #pragma unroll
     for (int f = 0; f < NMAT; ++f)
-        acc[f] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t = 0; t < TG; ++t)
+            acc[f][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     const uint32_t scale_shift = 8 * g;  // both steps use scale byte g of the unit's 4
     // this lane's operand bytes: unit q is bytes 32 (q % 4) .. + 31 of column
@@ -281,61 +299,74 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
                         *reinterpret_cast<const FFN_LDS uint32_t *>(base + f * 1024 + scale_off) >> scale_shift);
                     const bf16x8_t b0 = dequant8(c[0], sc);
                     const bf16x8_t b1 = dequant8(c[1], sc);
-                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[i][0]), b0, acc[f],
-                                                                    0, 0, 0);
-                    acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[i][1]), b1, acc[f],
-                                                                    0, 0, 0);
+                    // one dequantised fragment, every token group
+#pragma unroll
+                    for (int t = 0; t < TG; ++t) {
+                        acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[i][t][0]),
+                                                                           b0, acc[f][t], 0, 0, 0);
+                        acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xr[i][t][1]),
+                                                                           b1, acc[f][t], 0, 0, 0);
+                    }
                 }
             }
             if (++st == S)
                 st = 0;
         }
 
-        // Tile done: add the 16 waves' accumulators, waves 0-7 and 8-15 in
-        // order by separate threads, then the two halves.
+        // Tile done: for each token group, add the 16 waves' accumulators,
+        // waves 0-7 and 8-15 in order by separate threads, then the two
+        // halves (the reduction area is reused group after group).
 #pragma unroll
-        for (int f = 0; f < NMAT; ++f) {
-            red[(q * NMAT + f) * 64 + lane] = acc[f];
-            acc[f] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-        lds_barrier();
-        const FFN_LDS float *redf = reinterpret_cast<const FFN_LDS float *>(red);
-        FFN_LDS float *half = reinterpret_cast<FFN_LDS float *>(red + kSmWaves * NMAT * 64);
-        if (tid < NMAT * 512) {
-            // job (f, h, o): output o = 16 m + rr (accumulator m % 4 of lane
-            // 16 (m / 4) + rr), waves 8 h .. 8 h + 7 of projection f
-            const int o = tid & 255;
-            const int h = (tid >> 8) & 1;
-            const int f = tid >> 9;
-            const int m = o >> 4;
-            const int at = (16 * (m >> 2) + (o & 15)) * 4 + (m & 3);
-            float a = redf[((8 * h) * NMAT + f) * 256 + at];
+        for (int t = 0; t < TG; ++t) {
 #pragma unroll
-            for (int w = 1; w < 8; ++w)
-                a += redf[((8 * h + w) * NMAT + f) * 256 + at];
-            half[(f * 2 + h) * 256 + o] = a;
-        }
-        lds_barrier();
-        if (tid < 256) {
-            const int m = tid >> 4;
-            const int rr = tid & 15;
-            float y[NMAT];
+            for (int f = 0; f < NMAT; ++f) {
+                red[(q * NMAT + f) * 64 + lane] = acc[f][t];
+                acc[f][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+            lds_barrier();
+            const FFN_LDS float *redf = reinterpret_cast<const FFN_LDS float *>(red);
+            FFN_LDS float *half = reinterpret_cast<FFN_LDS float *>(red + kSmWaves * NMAT * 64);
+            if (tid < NMAT * 512) {
+                // job (f, h, o): output o = 16 m + rr (accumulator m % 4 of lane
+                // 16 (m / 4) + rr), waves 8 h .. 8 h + 7 of projection f
+                const int o = tid & 255;
+                const int h = (tid >> 8) & 1;
+                const int f = tid >> 9;
+                const int m = o >> 4;
+                const int at = (16 * (m >> 2) + (o & 15)) * 4 + (m & 3);
+                float a = redf[((8 * h) * NMAT + f) * 256 + at];
 #pragma unroll
-            for (int f = 0; f < NMAT; ++f)
-                y[f] = half[(f * 2) * 256 + tid] + half[(f * 2 + 1) * 256 + tid];
-            if (m < M) {
-                const int row = (ta + tt) * kSmRows + rr;
-                const size_t o = static_cast<size_t>(m) * p.rows + row;
-                if constexpr (OUT == OUT_F32_PAIR) {
-                    static_cast<float *>(p.out0)[o] = y[0] * p.s2_0;
-                    static_cast<float *>(p.out1)[o] = y[NMAT - 1] * p.s2_1;
-                } else if constexpr (OUT == OUT_H_SILU || OUT == OUT_H_GELU) {
-                    constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
-                    static_cast<uint16_t *>(p.out0)[o] = to_bf16_bits(gate_act<A>(y[0] * p.s2_0) * (y[NMAT - 1] * p.s2_1));
-                } else if constexpr (OUT == OUT_BF16) {
-                    static_cast<uint16_t *>(p.out0)[o] = to_bf16_bits(y[0] * p.s2_0);
-                } else {
-                    static_cast<float *>(p.out0)[static_cast<size_t>(part) * M * p.rows + o] = y[0];
+                for (int w = 1; w < 8; ++w)
+                    a += redf[((8 * h + w) * NMAT + f) * 256 + at];
+                half[(f * 2 + h) * 256 + o] = a;
+            }
+            lds_barrier();
+            if (tid < 256) {
+                const int m = 16 * t + (tid >> 4);
+                const int rr = tid & 15;
+                float y[NMAT];
+#pragma unroll
+                for (int f = 0; f < NMAT; ++f)
+                    y[f] = half[(f * 2) * 256 + tid] + half[(f * 2 + 1) * 256 + tid];
+                if (m < M) {
+                    const int row = (ta + tt) * kSmRows + rr;
+                    const size_t o = static_cast<size_t>(m) * p.rows + row;
+                    if constexpr (OUT == OUT_F32_PAIR) {
+                        static_cast<float *>(p.out0)[o] = y[0] * p.s2_0;
+                        static_cast<float *>(p.out1)[o] = y[NMAT - 1] * p.s2_1;
+                    } else if constexpr (OUT == OUT_H_SILU || OUT == OUT_H_GELU) {
+                        constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
+                        static_cast<uint16_t *>(p.out0)[o] =
+                            to_bf16_bits(gate_act<A>(y[0] * p.s2_0) * (y[NMAT - 1] * p.s2_1));
+                    } else if constexpr (OUT == OUT_BF16) {
+                        static_cast<uint16_t *>(p.out0)[o] = to_bf16_bits(y[0] * p.s2_0);
+                    } else if constexpr (OUT == OUT_PART_PAIR) {
+                        const size_t po = static_cast<size_t>(part) * M * p.rows + o;
+                        static_cast<float *>(p.out0)[po] = y[0];
+                        static_cast<float *>(p.out1)[po] = y[NMAT - 1];
+                    } else {
+                        static_cast<float *>(p.out0)[static_cast<size_t>(part) * M * p.rows + o] = y[0];
+                    }
                 }
             }
         }
@@ -343,17 +374,65 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
 
 }
 
-// out[m, j] = bf16(s2 * sum_p part[p, m, j]), the parts added in order.
+// The parts' sums of four consecutive elements e .. e + 3 (e a multiple of
+// 4, n too): every load of a batch of up to 8 parts is issued before the
+// first addition, and the parts are added in order (part 0 first).
+__device__ __forceinline__ f32x4_t sum_parts4(const float *part, int parts, size_t n, size_t e)
+{
+    constexpr int B = 8;
+    f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < parts; k0 += B) {
+        f32x4_t v[B];
+#pragma unroll
+        for (int k = 0; k < B; ++k)
+            if (k0 + k < parts)
+                v[k] = *reinterpret_cast<const f32x4_t *>(part + static_cast<size_t>(k0 + k) * n + e);
+#pragma unroll
+        for (int k = 0; k < B; ++k)
+            if (k0 + k < parts)
+                a = (k0 + k == 0) ? v[k] : a + v[k];
+    }
+    return a;
+}
+
+// out[m, j] = bf16(s2 * sum_p part[p, m, j]), the parts added in order; four
+// elements per thread (n is a multiple of 4).
 __global__ __launch_bounds__(256) void smallm_reduce_kernel(const float *part, int parts, size_t n, float s2,
                                                             uint16_t *out)
 {
-    const size_t e = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    const size_t e = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
     if (e >= n)
         return;
-    float a = part[e];
-    for (int k = 1; k < parts; ++k)
-        a += part[static_cast<size_t>(k) * n + e];
-    out[e] = to_bf16_bits(a * s2);
+    const f32x4_t a = sum_parts4(part, parts, n, e);
+    *reinterpret_cast<u32x2_t *>(out + e) = u32x2_t{pack_bf16x2(a[0] * s2, a[1] * s2), pack_bf16x2(a[2] * s2, a[3] * s2)};
+}
+
+// The dual projection split in parts: g = sum_p gpart[p, m, n], u likewise
+// (parts added in order), then the same epilogue as an unsplit tile: the fp32
+// pair s2_g g, s2_u u, or h = bf16(act(s2_g g) * (s2_u u)). Four elements per
+// thread (n is a multiple of 4).
+template <int OUT>
+__global__ __launch_bounds__(256) void smallm_reduce_pair_kernel(const float *gpart, const float *upart, int parts,
+                                                                 size_t n, float s2_g, float s2_u, void *out0,
+                                                                 float *out1)
+{
+    const size_t e = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (e >= n)
+        return;
+    const f32x4_t g = sum_parts4(gpart, parts, n, e);
+    const f32x4_t u = sum_parts4(upart, parts, n, e);
+    if constexpr (OUT == OUT_F32_PAIR) {
+        *reinterpret_cast<f32x4_t *>(static_cast<float *>(out0) + e) = g * s2_g;
+        *reinterpret_cast<f32x4_t *>(out1 + e) = u * s2_u;
+    } else {
+        constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
+        float h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            h[i] = gate_act<A>(g[i] * s2_g) * (u[i] * s2_u);
+        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(out0) + e) =
+            u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+    }
 }
 
 }  // namespace ffn

@@ -11,19 +11,34 @@ namespace ffn {
 
 namespace {
 
-// Split of one GEMM: P parts of the reduction (each at most kSmMaxRounds
-// rounds, so a wave's activations fit in registers) and G row-tile groups,
-// about one workgroup per compute unit in all.
+// Token groups of 16 for M rows.
+int token_groups(int M)
+{
+    return (M + 15) / 16;
+}
+
+// Rounds a wave may take per tile and part: its activations (8 registers per
+// round and token group) and accumulators must fit the 128 registers a lane
+// has with 16 waves per compute unit (compiled, the two-group dual GEMM needs
+// 122 at 4 rounds and spills at 5; the two-group down GEMM fits 5).
+int max_rounds(int tg, int nmat)
+{
+    return (tg == 1 || nmat == 1) ? kSmMaxRounds : kSmMaxRoundsTwoGroups;
+}
+
+// Split of one GEMM: P parts of the reduction (each at most max_rounds(tg)
+// rounds) and G row-tile groups, about one workgroup per compute unit in all.
 struct SmallPlan {
-    int parts, groups, rounds;
+    int parts, groups, rounds, tg;
 };
 
-SmallPlan plan(int rows, int cols)
+SmallPlan plan(int rows, int cols, int M, int nmat)
 {
     const int nb = cols / 256;  // 256-column blocks (4 units)
     const int tiles = rows / kSmRows;
-    constexpr int max_blocks = kSmWaves * kSmMaxRounds / 4;  // per part
     SmallPlan s{};
+    s.tg = token_groups(M);
+    const int max_blocks = kSmWaves * max_rounds(s.tg, nmat) / 4;  // per part
     s.parts = std::max(1, (nb + max_blocks - 1) / max_blocks);
     const int max_units = 4 * ((nb + s.parts - 1) / s.parts);
     s.rounds = (max_units + kSmWaves - 1) / kSmWaves;
@@ -40,25 +55,40 @@ bool shape_ok(int rows, int cols)
     return rows > 0 && rows % kSmRows == 0 && cols > 0 && cols % 256 == 0;
 }
 
-template <int NMAT, int OUT>
-hipError_t launch_t(const SmallParams &p, int rounds, hipStream_t stream)
+template <int NMAT, int OUT, int TG>
+hipError_t launch_tg(const SmallParams &p, int rounds, hipStream_t stream)
 {
     const void *kern = nullptr;
     switch (rounds) {
-    case 1: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 1>); break;
-    case 2: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 2>); break;
-    case 3: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 3>); break;
-    case 4: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 4>); break;
-    case 5: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 5>); break;
+    case 1: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 1, TG>); break;
+    case 2: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 2, TG>); break;
+    case 3: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 3, TG>); break;
+    case 4: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 4, TG>); break;
+    case 5:
+        if constexpr (TG == 1 || NMAT == 1) {
+            kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 5, TG>);
+            break;
+        }
+        return hipErrorNotSupported;
     default: return hipErrorNotSupported;
     }
     constexpr int lds = sm_lds_bytes<NMAT>();
-    static std::atomic<uint64_t> lds_done[5];  // per rounds instantiation
+    static std::atomic<uint64_t> lds_done[kSmMaxRounds];  // per rounds instantiation
     hipError_t e = allow_lds(kern, lds, lds_done[rounds - 1]);
     if (e != hipSuccess)
         return e;
     void *args[] = {const_cast<SmallParams *>(&p)};
     return hipLaunchKernel(kern, dim3(p.parts * p.groups), dim3(kSmWaves * 64), args, lds, stream);
+}
+
+template <int NMAT, int OUT>
+hipError_t launch_t(const SmallParams &p, const SmallPlan &s, hipStream_t stream)
+{
+    switch (s.tg) {
+    case 1: return launch_tg<NMAT, OUT, 1>(p, s.rounds, stream);
+    case 2: return launch_tg<NMAT, OUT, 2>(p, s.rounds, stream);
+    default: return hipErrorNotSupported;
+    }
 }
 
 SmallParams params(int M, const void *in0, const WeightArg &w0, const WeightArg &w1, void *out0, void *out1,
@@ -86,29 +116,69 @@ SmallParams params(int M, const void *in0, const WeightArg &w0, const WeightArg 
 
 bool smallm_supported(int M, int K, int N)
 {
-    // the dual GEMM keeps its whole reduction in one part
-    return M >= 1 && M <= kSmallMaxM && shape_ok(N, K) && shape_ok(K, N) && plan(N, K).parts == 1;
+    return M >= 1 && M <= kSmallMaxM && shape_ok(N, K) && shape_ok(K, N);
+}
+
+bool smallm_dual_split(int M, int K, int N)
+{
+    return plan(N, K, M, 2).parts > 1;
 }
 
 size_t smallm_partial_floats(int M, int K, int N)
 {
-    const SmallPlan s = plan(K, N);
+    const SmallPlan s = plan(K, N, M, 1);
     return s.parts > 1 ? static_cast<size_t>(s.parts) * M * K : 0;
 }
 
+size_t smallm_dual_partial_floats(int M, int K, int N)
+{
+    const SmallPlan s = plan(N, K, M, 2);
+    return s.parts > 1 ? static_cast<size_t>(2) * s.parts * M * N : 0;
+}
+
 hipError_t launch_smallm_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1,
-                              void *out0, void *out1, int N, int K, hipStream_t stream)
+                              void *out0, void *out1, float *partials, int N, int K, hipStream_t stream)
 {
     if (!smallm_supported(M, K, N))
         return hipErrorNotSupported;
-    const SmallPlan s = plan(N, K);
-    const SmallParams p = params(M, x, w0, w1, out0, out1, N, K, s);
+    const SmallPlan s = plan(N, K, M, 2);
+    if (s.parts == 1) {
+        const SmallParams p = params(M, x, w0, w1, out0, out1, N, K, s);
+        switch (out) {
+        case OUT_F32_PAIR: return launch_t<2, OUT_F32_PAIR>(p, s, stream);
+        case OUT_H_SILU: return launch_t<2, OUT_H_SILU>(p, s, stream);
+        case OUT_H_GELU: return launch_t<2, OUT_H_GELU>(p, s, stream);
+        default: return hipErrorNotSupported;
+        }
+    }
+    // The reduction in parts: both projections' partial sums, then one pass
+    // that adds them in order and runs the epilogue.
+    if (partials == nullptr)
+        return hipErrorNotSupported;
+    const size_t n = static_cast<size_t>(M) * N;
+    float *gpart = partials;
+    float *upart = partials + static_cast<size_t>(s.parts) * n;
+    const SmallParams p = params(M, x, w0, w1, gpart, upart, N, K, s);
+    hipError_t e = launch_t<2, OUT_PART_PAIR>(p, s, stream);
+    if (e != hipSuccess)
+        return e;
+    const dim3 grid(static_cast<unsigned>((n / 4 + 255) / 256));  // four elements per thread
     switch (out) {
-    case OUT_F32_PAIR: return launch_t<2, OUT_F32_PAIR>(p, s.rounds, stream);
-    case OUT_H_SILU: return launch_t<2, OUT_H_SILU>(p, s.rounds, stream);
-    case OUT_H_GELU: return launch_t<2, OUT_H_GELU>(p, s.rounds, stream);
+    case OUT_F32_PAIR:
+        hipLaunchKernelGGL(smallm_reduce_pair_kernel<OUT_F32_PAIR>, grid, dim3(256), 0, stream, gpart, upart, s.parts,
+                           n, w0.scale2, w1.scale2, out0, static_cast<float *>(out1));
+        break;
+    case OUT_H_SILU:
+        hipLaunchKernelGGL(smallm_reduce_pair_kernel<OUT_H_SILU>, grid, dim3(256), 0, stream, gpart, upart, s.parts, n,
+                           w0.scale2, w1.scale2, out0, static_cast<float *>(nullptr));
+        break;
+    case OUT_H_GELU:
+        hipLaunchKernelGGL(smallm_reduce_pair_kernel<OUT_H_GELU>, grid, dim3(256), 0, stream, gpart, upart, s.parts, n,
+                           w0.scale2, w1.scale2, out0, static_cast<float *>(nullptr));
+        break;
     default: return hipErrorNotSupported;
     }
+    return hipGetLastError();
 }
 
 hipError_t launch_smallm_down(int M, const void *h, const WeightArg &w, void *out, float *partials, int K, int N,
@@ -116,17 +186,17 @@ hipError_t launch_smallm_down(int M, const void *h, const WeightArg &w, void *ou
 {
     if (!smallm_supported(M, K, N))
         return hipErrorNotSupported;
-    const SmallPlan s = plan(K, N);
+    const SmallPlan s = plan(K, N, M, 1);
     if (s.parts == 1) {
         const SmallParams p = params(M, h, w, w, out, nullptr, K, N, s);
-        return launch_t<1, OUT_BF16>(p, s.rounds, stream);
+        return launch_t<1, OUT_BF16>(p, s, stream);
     }
     const SmallParams p = params(M, h, w, w, partials, nullptr, K, N, s);
-    hipError_t e = launch_t<1, OUT_PART_F32>(p, s.rounds, stream);
+    hipError_t e = launch_t<1, OUT_PART_F32>(p, s, stream);
     if (e != hipSuccess)
         return e;
     const size_t n = static_cast<size_t>(M) * K;
-    hipLaunchKernelGGL(smallm_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(smallm_reduce_kernel, dim3(static_cast<unsigned>((n / 4 + 255) / 256)), dim3(256), 0, stream,
                        partials, s.parts, n, w.scale2, static_cast<uint16_t *>(out));
     return hipGetLastError();
 }
