@@ -136,7 +136,7 @@ def measured_traffic(workload):
     from w4a16_nvfp4_dense_amd import profiling
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_digest") != profiling.source_digest():
+    if t.get("source_digest") != profiling.source_digest(t.get("source_files")):
         log(f"[bench] {path} was measured on other kernel sources: traffic not reported")
         return None
     return t
@@ -505,6 +505,9 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated over")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="time the forward and the roofline kernel only (no trial median, read-ceiling or graph "
+                         "legs): for runs under a profiler")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 64 MiB device-to-device copy (untimed), the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -530,6 +533,33 @@ def main():
         bench_w4a4(args)
         return
     bench_nvfp4(args)
+
+
+def packed_weights(case, dev):
+    """One weight copy as a single device allocation: the codes and scales of
+    W_g, W_u and W_d back to back (each piece 256-byte aligned), so that the
+    bytes a forward streams are one contiguous range (W_g and W_u first) that
+    the read-ceiling leg can stream the same way. Returns (buffer, gate, up,
+    down) with DeviceWeights viewing into the buffer."""
+    import numpy as np
+    import torch
+    import w4a16_nvfp4_dense_amd as ffn
+
+    pieces = []
+    for w in (case.gate, case.up, case.down):
+        pieces += [w.codes, w.scales]
+    offs, at = [], 0
+    for a in pieces:
+        offs.append(at)
+        at = (at + a.nbytes + 255) // 256 * 256
+    host = np.zeros(at, dtype=np.uint8)
+    for a, o in zip(pieces, offs):
+        host[o:o + a.nbytes] = np.ascontiguousarray(a).reshape(-1)
+    buf = torch.from_numpy(host).to(dev)
+    views = [buf[o:o + a.nbytes].view(a.shape) for a, o in zip(pieces, offs)]
+    ws = [ffn.DeviceWeight(views[2 * i], views[2 * i + 1], float(w.scale2))
+          for i, w in enumerate((case.gate, case.up, case.down))]
+    return buf, ws[0], ws[1], ws[2], offs[4]
 
 
 def single_thread_oracle_us(trials=5):
@@ -573,10 +603,11 @@ def bench_nvfp4(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    copies = []
+    copies, bufs = [], []
     for _ in range(args.copies):
-        copies.append((ffn.DeviceWeight.from_host(case.gate, dev), ffn.DeviceWeight.from_host(case.up, dev),
-                       ffn.DeviceWeight.from_host(case.down, dev)))
+        buf, g, u, d, down_at = packed_weights(case, dev)
+        copies.append((g, u, d))
+        bufs.append((buf, down_at))
     x = ffn.bf16_from_bits(case.x_bits, dev)
     out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     ws_bytes = ffn.workspace_bytes(M, K, N)
@@ -627,9 +658,11 @@ def bench_nvfp4(args):
     log(f"[bench] {args.workload}: {us:.2f} us/forward, {gbs:.1f} GB/s algorithmic "
         f"({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f}); host wall {wall * 1e6 / args.steps:.2f} us/step")
     # Context: five more trials of 200 forwards each, median.
-    trials = [timed_ms(step, 200, stream) / 200 * 1e3 for _ in range(5)]
-    us_med5 = statistics.median(trials)
-    log(f"[bench] 5 trials of 200 forwards: median {us_med5:.2f} us (" + ", ".join(f"{t:.2f}" for t in trials) + ")")
+    trials = [] if args.profile_run else [timed_ms(step, 200, stream) / 200 * 1e3 for _ in range(5)]
+    us_med5 = statistics.median(trials) if trials else None
+    if trials:
+        log(f"[bench] 5 trials of 200 forwards: median {us_med5:.2f} us (" +
+            ", ".join(f"{t:.2f}" for t in trials) + ")")
 
     result = {
         "metric": METRIC,
@@ -652,7 +685,7 @@ def bench_nvfp4(args):
             "M": M, "K": K, "N": N, "act": fi.ACT_NAMES[act],
             "algorithmic_bytes_per_forward": nbytes["forward"],
         },
-        "us_per_forward_median5": round(us_med5, 3),
+        "us_per_forward_median5": None if us_med5 is None else round(us_med5, 3),
         "us_per_forward_trials": [round(t, 3) for t in trials],
     }
 
@@ -707,12 +740,16 @@ def bench_nvfp4(args):
         "algorithmic_bytes_per_launch": nbytes["dual_f32"],
     }
 
+    if args.profile_run:
+        print(json.dumps(result), flush=True)
+        return
+
     # Streaming-read ceiling (context, not `value`): a trivial kernel with the
-    # GEMVs' load width reading the same weight bytes, as one launch over all
-    # three weights and as two launches (W_g + W_u, then W_d), rotating copies.
-    one = [ffn.DiagRead([g.codes, g.scales, u.codes, u.scales, d.codes, d.scales]) for g, u, d in copies]
-    two = [(ffn.DiagRead([g.codes, g.scales, u.codes, u.scales]), ffn.DiagRead([d.codes, d.scales]))
-           for g, u, d in copies]
+    # GEMVs' load width reading the same weight bytes (each copy is one
+    # contiguous range), as one launch over all three weights and as two
+    # launches (W_g + W_u, then W_d), rotating copies.
+    one = [ffn.DiagRead([buf]) for buf, _ in bufs]
+    two = [(ffn.DiagRead([buf[:at]]), ffn.DiagRead([buf[at:]])) for buf, at in bufs]
     r1 = timed_ms(lambda i: one[i % nc].launch(stream), 200, stream, 20) / 200 * 1e3
 
     def two_step(i):

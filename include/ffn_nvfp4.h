@@ -38,9 +38,10 @@
  *     bit-identical outputs. Row m of a batched call is bit-identical to an
  *     M=1 call on that row for every M <= 8. Within each matrix-core arm (see
  *     the batch sizes below) a row's result does not depend on the other rows
- *     of the batch; the arms differ from each other and from the M <= 8 arm
- *     in rounding, and the 128-row arm's forward splits its reductions by the
- *     device's compute-unit count.
+ *     of the batch (in the small-batch arm, among batches with the same
+ *     number of 16-row token groups); the arms differ from each other and
+ *     from the M <= 8 arm in rounding, and the 128-row arm's forward splits
+ *     its reductions by the device's compute-unit count.
  *   - The functions hold no global mutable state and may be called from
  *     several host threads (on distinct output buffers), except
  *     ffn_nvfp4_forward_noalloc, whose per-device scratch array is shared by
@@ -88,26 +89,30 @@ typedef struct ffn_nvfp4_weight {
 
 /* Supported batch sizes:
  *   M = 0            empty call;
- *   1 <= M <= 8      the weight-streaming GEMV arm (each weight byte read once
- *                    for all M rows; dense_ffn.rs page, forward_k2 / forward_k3 /
+ *   1 <= M <= 8      the weight-streaming GEMV arm: one launch per projection
+ *                    for the whole batch, so each weight byte is read once for
+ *                    all M rows (dense_ffn.rs page, forward_k2 / forward_k3 /
  *                    forward_km);
  *   9 <= M <= 65536  the matrix-core arms (dense_ffn.rs page, forward_prefill:
  *                    weights dequantised to bf16 feeding bf16 matrix products
  *                    with fp32 accumulation). They need K and N in multiples
  *                    of 64 (else ERR_SHAPE) and scales 8-byte aligned (else
  *                    ERR_ALIGN).
- *     9 <= M <= 64, K and N multiples of 128: the small-batch arm, one launch
- *                    per projection, weights read once for all rows;
+ *     9 <= M <= 32, K and N multiples of 256: the small-batch arm, weights
+ *                    read and dequantised once for all rows (one token group
+ *                    of 16 rows up to M = 16, two above); its reductions are
+ *                    split in parts where a wave's activations do not fit its
+ *                    registers, finished by a reduction launch;
  *     otherwise      the 128-row arm, in blocks of 128 token rows, each block
  *                    reading the weights once.
  * Other M: ERR_BATCH. K and N: positive multiples of 32, at most 65536. */
 
 /* Bytes of device workspace ffn_nvfp4_forward needs for (M, K, N);
- * 0 if M = 0 or the shape is unsupported. For M <= 8 and for the small-batch
- * arm it holds h [M, N] bf16; for the 128-row arm, h for one block of up to
- * 128 rows plus the fp32 slots in which that arm leaves the pieces of split
- * reductions (about 64 MiB, whatever M). Its contents need no
- * initialisation. */
+ * 0 if M = 0 or the shape is unsupported. For M <= 8 it holds h [M, N] bf16;
+ * for the small-batch arm h and the fp32 partial sums of split reductions;
+ * for the 128-row arm, h for one block of up to 128 rows plus the fp32 slots
+ * in which that arm leaves the pieces of split reductions (about 64 MiB,
+ * whatever M). Its contents need no initialisation. */
 size_t ffn_nvfp4_workspace_bytes(int M, int K, int N);
 
 /* The whole FFN: out[M, K] (bf16) = W_d (act(W_g x) * (W_u x)) for
@@ -151,8 +156,9 @@ int ffn_nvfp4_forward_noalloc(const void *x, int M, int K, int N,
 
 /* Dual GEMV (one pass over x for both projections; dense_ffn.rs page,
  * DenseFfnLayer::forward, w4a16_gemv_dual). For M > 8 it runs the
- * small-batch arm when it applies, else the 128-row arm with one workgroup
- * per output tile (no workspace either way):
+ * small-batch arm when that arm covers the shape without splitting the
+ * reduction, else the 128-row arm with one workgroup per output tile (no
+ * workspace either way):
  *   gate_out[m, n] = scale2_g * sum_k W_g[n, k] x[m, k]
  *   up_out[m, n]   = scale2_u * sum_k W_u[n, k] x[m, k]
  *   x          device, bf16 [M, K], 16-byte aligned
