@@ -66,9 +66,9 @@ def assert_dual_close(got, ref, what):
 
 
 # Shapes: ragged block grids (K, N not multiples of 128), chunk counts that
-# leave lanes idle in the last step, 1 to 21 chunks per lane, batches split
-# into launches (4 + 1, 4 + 2, 4 + 3), activations in LDS pieces (M = 8 with
-# long down rows), one and two workgroups per compute unit.
+# leave lanes idle in the last step, 1 to 21 chunks per lane, every batch
+# size up to 8 (each in one launch per projection), activations in LDS pieces
+# (M = 8 with long down rows), one and two workgroups per compute unit.
 SMALL = [
     # (M, K, N, act, seed)
     (1, 256, 512, fi.ACT_SILU, 1),
@@ -76,9 +76,9 @@ SMALL = [
     (3, 400, 336, fi.ACT_GELU_TANH, 3),      # 25 / 21 chunks, ragged 128-blocks both ways
     (2, 1040, 1200, fi.ACT_SILU, 4),         # 65 / 75 chunks: one live lane in the last step
     (8, 2048, 3072, fi.ACT_SILU, 5),
-    (5, 1536, 2576, fi.ACT_GELU_TANH, 6),    # 4 + 1 rows
-    (6, 3072, 1040, fi.ACT_SILU, 7),         # 4 + 2 rows
-    (7, 1024, 6160, fi.ACT_GELU_TANH, 8),    # 4 + 3 rows
+    (5, 1536, 2576, fi.ACT_GELU_TANH, 6),    # 5 rows
+    (6, 3072, 1040, fi.ACT_SILU, 7),         # 6 rows
+    (7, 1024, 6160, fi.ACT_GELU_TANH, 8),    # 7 rows
     (4, 4096, 14336, fi.ACT_SILU, 9),        # down: 14 chunks per lane
     (8, 4096, 14336, fi.ACT_GELU_TANH, 10),  # down: activations staged in two pieces
     (8, 2064, 24576, fi.ACT_SILU, 11),       # down: 24 chunks per lane, three pieces
@@ -129,7 +129,7 @@ def test_fp8_format_coverage(act, M):
 
 def test_fp8_determinism_and_batch_rows():
     """Ten repeats are bit-identical; row m of a batch equals the M = 1 call on
-    that row, for batches of 2, 3, 5 and 8 (launch groups of 4 + 1 included)."""
+    that row, for batches of 2, 3, 5 and 8."""
     case = fi.make_fp8_ffn("fp8_det", 8, 2048, 6144, seed=21)
     L = Loaded(case)
     first = L.forward()
