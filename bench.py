@@ -39,6 +39,7 @@ WORKLOADS = {
     "decode_gelu_m1": (2, 1),
     "verify_silu_m2": (3, 2),
     "verify_silu_m3": (3, 3),
+    "verify_silu_m4": (3, 4),
     "verify_silu_m5": (3, 5),
     "verify_silu_m6": (3, 6),
     "verify_silu_m7": (3, 7),
