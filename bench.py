@@ -53,6 +53,7 @@ WORKLOADS = {
     # 33 <= M <= 64: the 128-row matrix-core arm (one or two token tiles)
     "smallbatch_silu_m48": (4, 48),
     "smallbatch_silu_m64": (4, 64),
+    "prefill_silu_m96": (4, 96),
 }
 SMALL_BATCH_MAX_M = 32  # above this the forward runs the 128-row matrix-core arm
 # The BF16 -> NVFP4 quantiser (ffn_nvfp4_quantize) on one weight of the decode
@@ -666,7 +667,10 @@ def bench_nvfp4(args):
             ", ".join(f"{t:.2f}" for t in trials) + ")")
 
     result = {
-        "metric": METRIC,
+        # the headline metric names its workload (decode SwiGLU M = 1); the
+        # other workloads name theirs
+        "metric": METRIC if args.workload == "decode_silu_m1" else
+        METRIC.replace("SwiGLU decode M=1", f"{'SwiGLU' if act == fi.ACT_SILU else 'GELU-tanh'} {args.workload}"),
         "value": round(gbs, 2),
         "unit": "GB/s",
         "us_per_forward": round(us, 3),

@@ -11,13 +11,15 @@ namespace ffn {
 
 namespace {
 
-// Ring stages: as many as fit in ~150 KB of LDS (the loads in flight per
-// compute unit are what bounds the streaming rate), at most 12.
+// Ring stages: 4 (three units in flight), or fewer if they do not fit in
+// ~150 KB of LDS. Measured on MI355X at 5120/17408 with 48 to 128 tokens:
+// 4 stages beat 3 (slower at 128 tokens) and 5 to 8 (the most that fit) by
+// 2 to 5 us per forward.
 template <int MT>
 constexpr int stages()
 {
     constexpr int s = (150 * 1024) / mfma_stage_bytes<MT>();
-    return s > 12 ? 12 : s;
+    return s > 4 ? 4 : s;
 }
 
 template <int MT, int NMAT, int IN, int OUT>

@@ -55,7 +55,7 @@ def _one(pattern: str) -> str:
 def stats_summary(trace_dir: str, top: int = 8) -> str:
     path = _one(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
     rows = list(csv.DictReader(open(path)))
-    out = ["kernel | calls | average us | min us | max us | share %"]
+    out = ["kernel | calls | average us | min us | max us | share %", "---|---|---|---|---|---"]
     for r in rows[:top]:
         name = r["Name"].replace("void ", "")
         name = name.split("(")[0] if "ffn::" in name else name[:60]
