@@ -68,6 +68,14 @@ SHAPES = [
     (45, 1024, 320, fi.ACT_SILU, 3),
     (128, 2048, 1024, fi.ACT_SILU, 4),
     (200, 768, 448, fi.ACT_GELU_TANH, 5),   # two token groups, two down blocks
+    # Wider N: rows per workgroup R = ceil(N / 256 compute units) on MI355X,
+    # in NF fragments of 32 B rows (gate and up interleaved); the last
+    # workgroup holds fewer rows when R does not divide N.
+    (40, 512, 5184, fi.ACT_SILU, 6),        # R = 21 (NF 2), last workgroup 18 rows
+    (130, 256, 9024, fi.ACT_GELU_TANH, 7),  # R = 36 (NF 3), last 24 rows, two token groups
+    (5, 256, 15424, fi.ACT_SILU, 8),        # R = 61 (NF 4), last 52 rows
+    (7, 256, 17984, fi.ACT_GELU_TANH, 9),   # R = 71 (NF 5), last 21 rows
+    (8, 256, 21504, fi.ACT_SILU, 10),       # R = 84 (NF 6, 3 ring stages), 256 workgroups
 ]
 
 

@@ -34,7 +34,6 @@ typedef uint32_t u32x2_w4_t __attribute__((ext_vector_type(2)));
 constexpr int kMxBlock = 32;
 constexpr int kW4Threads = 256;  // 4 waves
 constexpr int kW4TokensPerWave = 32;
-constexpr int kW4RowsPerTile = 32;
 constexpr int kW4TokensPerGroup = 4 * kW4TokensPerWave;
 
 // Shared exponent of a block with maximum magnitude amax (finite, >= 0).
@@ -152,22 +151,35 @@ struct W4a4Params {
     void *out0;  // fp32 gate [M, N], or bf16 h [M, N]
     float *out1;  // fp32 up [M, N]
     int M, N, K;
+    int R;  // weight rows of each projection per workgroup
 };
 
+// LDS stage of one 256-column piece for a workgroup with NF weight fragments
+// of 32 rows: A codes (128 token rows x 128 B), B codes (32 NF rows x 128 B),
+// A scales (128 rows x 8 B), B scales (32 NF rows x 8 B). B row b holds weight
+// row n0 + b / 2 of the gate (b even) or the up (b odd) projection, so the
+// gate and up outputs of one row land in neighbouring lanes. In a row's 128
+// code bytes the 16-byte chunk c sits at slot c ^ ((row / 2) % 8), so that
+// the 16 lanes of a ds_read_b128 phase (16 consecutive rows, one chunk) hit
+// 16 distinct 16-byte bank groups.
+template <int NF>
+struct W4Stage {
+    static constexpr int kACodes = 0;
+    static constexpr int kBCodes = 128 * 128;
+    static constexpr int kAScales = kBCodes + 32 * NF * 128;
+    static constexpr int kBScales = kAScales + 128 * 8;
+    static constexpr int kBytes = kBScales + 32 * NF * 8;
+};
+constexpr int kW4MaxFrags = 6;
+constexpr int kW4LdsMax = 160 * 1024;
 
-// LDS stage of one 256-column piece: A codes (128 token rows x 128 B), B codes
-// (32 gate rows, then 32 up rows, x 128 B), A scales (128 rows x 8 B), B
-// scales (64 rows x 8 B). In a row's 128 code bytes the 16-byte chunk c sits
-// at slot c ^ ((row / 2) % 8), so that the 16 lanes of a ds_read_b128 phase
-// (16 consecutive rows, one chunk) hit 16 distinct 16-byte bank groups.
-constexpr int kW4Stages = 3;
-constexpr int kW4ACodes = 0;
-constexpr int kW4BCodes = 128 * 128;
-constexpr int kW4AScales = kW4BCodes + 64 * 128;
-constexpr int kW4BScales = kW4AScales + 128 * 8;
-constexpr int kW4Stage = kW4BScales + 64 * 8;                 // 26112 B
-constexpr int kW4Dummy = kW4Stages * kW4Stage;                 // 256 B never read
-constexpr int kW4LdsBytes = kW4Dummy + 256;                    // 78592 B: two workgroups per CU
+// Ring stages: 4 (three pieces in flight), or as many as fit.
+template <int NF>
+constexpr int w4_stages()
+{
+    constexpr int s = (kW4LdsMax - 256) / W4Stage<NF>::kBytes;
+    return s > 4 ? 4 : s;
+}
 
 __device__ __forceinline__ int w4_slot(int row, int chunk)
 {
@@ -190,28 +202,46 @@ __device__ __forceinline__ void w4_scales(uint32_t (&s)[2], const FFN_LDS uint8_
     s[1] = static_cast<uint32_t>(s64 >> 32);
 }
 
-// Dual GEMM: workgroup (x, y) takes weight rows 32 x .. 32 x + 31 of both
-// projections and tokens 128 y .. 128 y + 127, wave w the token tile
-// 32 w .. 32 w + 31 for the whole reduction. Per 256-column piece the
-// workgroup stages the activation codes and scales and both projections'
-// codes and scales into a 3-stage LDS ring with direct global-to-LDS loads
-// (every load instruction reads 8 rows x 128 contiguous bytes; every wave
-// issues the same 8 loads per stage, one of them into a dummy area), one
-// piece ahead of the products; each wave then reads its operands in the
-// MFMA layout (ds_read_b128) and runs 8 products. Tokens past M re-read row
-// M - 1 and are not stored.
-template <int OUT>
+// The value of lane l ^ 1 (DPP quad permutation 1, 0, 3, 2).
+__device__ __forceinline__ float w4_pair_swap(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF,
+                                                                 false));
+}
+
+// Dual GEMM: workgroup (x, y) takes weight rows n0 = R x .. n0 + R - 1 of both
+// projections (2 R B rows, in NF fragments of 32) and tokens 128 y ..
+// 128 y + 127, wave w the token tile 32 w .. 32 w + 31 against all of the
+// workgroup's B rows, for the whole reduction. The host picks R so that the
+// grid has about one workgroup per compute unit: every workgroup then does the
+// same work in one round (with fixed 32-row tiles, 17408 rows made 544 tiles
+// for 512 resident slots, and the last 32 ran as a second round). Per
+// 256-column piece the workgroup stages the activation codes and scales and
+// the B rows' codes and scales into an S-stage LDS ring with direct
+// global-to-LDS loads (every code load reads 8 rows x 128 contiguous bytes;
+// every wave issues the same loads per piece, the spare scale loads into a
+// dummy area), S - 1 pieces ahead of the products; each wave then reads its
+// operands in the MFMA layout (ds_read_b128) and runs 4 NF products. Tokens
+// past M re-read row M - 1, B rows past the workgroup's rows re-read its last
+// row, and neither is stored.
+template <int OUT, int NF, int S>
 __global__ __launch_bounds__(kW4Threads) void w4a4_dual_kernel(const W4a4Params p)
 {
+    using St = W4Stage<NF>;
+    constexpr int SB = (NF + 3) / 4;     // B scale loads per wave
+    constexpr int LPP = 5 + NF + SB;     // loads per wave and piece
+    constexpr int kDummy = S * St::kBytes;
     extern __shared__ u32x4_t lds_raw[];
     FFN_LDS uint8_t *lds = (FFN_LDS uint8_t *)lds_raw;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tg0 = blockIdx.y * kW4TokensPerGroup;
-    const int n0 = blockIdx.x * kW4RowsPerTile;
+    const int n0 = blockIdx.x * p.R;
+    const int nlast = min(n0 + p.R, p.N) - 1;  // last weight row of this workgroup
     const int half = lane >> 5;
     const size_t kc = static_cast<size_t>(p.K) / 2, ke = static_cast<size_t>(p.K) / 32;
     const int pieces = p.K / 256;
+    auto brow = [&](int b) { return min(n0 + (b >> 1), nlast); };
 
     // Load sources of this lane (piece 0; piece q adds 128 q code bytes, 8 q
     // scale bytes). A codes: loads j = 0..3 cover rows 32 w + 8 j + lane / 8.
@@ -222,123 +252,153 @@ __global__ __launch_bounds__(kW4Threads) void w4a4_dual_kernel(const W4a4Params 
         const int tok = min(tg0 + R, p.M - 1);
         asrc[j] = p.xc + tok * kc + 16 * w4_slot(R, lane & 7);
     }
-    // B codes: loads j = 0, 1 cover rows 16 w + 8 j + lane / 8 (gate rows
-    // 0..31, up rows 32..63).
-    const uint8_t *bsrc[2];
+    // B codes: load i covers B rows 8 (NF w + i) + lane / 8.
+    const uint8_t *bsrc[NF];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int Rb = 16 * wave + 8 * j + (lane >> 3);
-        const uint8_t *base = Rb < 32 ? p.gc : p.uc;
-        bsrc[j] = base + (n0 + (Rb & 31)) * kc + 16 * w4_slot(Rb, lane & 7);
+    for (int i = 0; i < NF; ++i) {
+        const int b = 8 * (NF * wave + i) + (lane >> 3);
+        bsrc[i] = ((b & 1) ? p.uc : p.gc) + brow(b) * kc + 16 * w4_slot(b, lane & 7);
     }
-    // Scales: one dword per lane, rows 32 w + lane / 2 (A), and for waves 0
-    // and 1 the gate or up rows (B; waves 2 and 3 load a dummy).
+    // Scales: one dword per lane. A: rows 32 w + lane / 2. B: load j takes
+    // fragment f = w + 4 j, rows 32 f + lane / 2 (past NF: a dummy load).
     const int atok = min(tg0 + 32 * wave + (lane >> 1), p.M - 1);
     const uint8_t *assrc = p.xe + atok * ke + 4 * (lane & 1);
-    const uint8_t *bsbase = wave == 1 ? p.ue : p.ge;
-    const uint8_t *bssrc = bsbase + (n0 + (lane >> 1)) * ke + 4 * (lane & 1);
-    const bool bscale_wave = wave < 2;
+    const uint8_t *bssrc[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+        const int f = min(wave + 4 * j, NF - 1);
+        const int b = 32 * f + (lane >> 1);
+        bssrc[j] = ((b & 1) ? p.ue : p.ge) + brow(b) * ke + 4 * (lane & 1);
+    }
 
     auto issue = [&](int q, int st) {
-        FFN_LDS uint8_t *base = lds + st * kW4Stage;
+        FFN_LDS uint8_t *base = lds + st * St::kBytes;
         const size_t co = static_cast<size_t>(q) * 128, so = static_cast<size_t>(q) * 8;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(asrc[j] + co),
-                                             reinterpret_cast<FFN_LDS void *>(base + kW4ACodes +
+                                             reinterpret_cast<FFN_LDS void *>(base + St::kACodes +
                                                                               (32 * wave + 8 * j) * 128),
                                              16, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(bsrc[j] + co),
-                                             reinterpret_cast<FFN_LDS void *>(base + kW4BCodes +
-                                                                              (16 * wave + 8 * j) * 128),
+        for (int i = 0; i < NF; ++i)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(bsrc[i] + co),
+                                             reinterpret_cast<FFN_LDS void *>(base + St::kBCodes +
+                                                                              8 * (NF * wave + i) * 128),
                                              16, 0, 0);
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(assrc + so),
-                                         reinterpret_cast<FFN_LDS void *>(base + kW4AScales + 32 * wave * 8), 4, 0,
+                                         reinterpret_cast<FFN_LDS void *>(base + St::kAScales + 32 * wave * 8), 4, 0,
                                          0);
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const void *>(bssrc + so),
-            reinterpret_cast<FFN_LDS void *>(bscale_wave ? base + kW4BScales + 32 * wave * 8 : lds + kW4Dummy), 4,
-            0, 0);
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const int f = wave + 4 * j;
+            __builtin_amdgcn_global_load_lds(
+                reinterpret_cast<const void *>(bssrc[j] + so),
+                reinterpret_cast<FFN_LDS void *>(f < NF ? base + St::kBScales + 32 * f * 8 : lds + kDummy), 4, 0, 0);
+        }
     };
 
     // prologue: pieces 0 .. S - 2 (a piece past the end loads the last one
     // again, so every wait below has the same number of loads in flight)
 #pragma unroll
-    for (int k = 0; k < kW4Stages - 1; ++k)
+    for (int k = 0; k < S - 1; ++k)
         issue(min(k, pieces - 1), k);
 
-    w4_f32x16_t cg = {}, cu = {};
+    w4_f32x16_t acc[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+        acc[f] = w4_f32x16_t{};
     const int ar = 32 * wave + (lane & 31);  // this lane's A row in a stage
-    const int br = lane & 31;                // its B row (gate; up is 32 rows on)
+    const int br = lane & 31;                // its B row in every fragment
     for (int q = 0; q < pieces; ++q) {
-        const int st = q % kW4Stages;
-        wait_vmcnt<8 * (kW4Stages - 2)>();
+        const int st = q % S;
+        wait_vmcnt<LPP * (S - 2)>();
         lds_barrier();
-        issue(min(q + kW4Stages - 1, pieces - 1), (q + kW4Stages - 1) % kW4Stages);
-        const FFN_LDS uint8_t *base = lds + st * kW4Stage;
-        uint32_t sa[2], sg[2], su[2];
-        w4_scales(sa, base + kW4AScales + ar * 8, half);
-        w4_scales(sg, base + kW4BScales + br * 8, half);
-        w4_scales(su, base + kW4BScales + (32 + br) * 8, half);
+        issue(min(q + S - 1, pieces - 1), (q + S - 1) % S);
+        const FFN_LDS uint8_t *base = lds + st * St::kBytes;
+        uint32_t sa[2], sb[NF][2];
+        w4_scales(sa, base + St::kAScales + ar * 8, half);
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+            w4_scales(sb[f], base + St::kBScales + (32 * f + br) * 8, half);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int c = 2 * t + half;
-            const u32x4_t a = *reinterpret_cast<const FFN_LDS u32x4_t *>(base + kW4ACodes + ar * 128 +
+            const u32x4_t a = *reinterpret_cast<const FFN_LDS u32x4_t *>(base + St::kACodes + ar * 128 +
                                                                           16 * w4_slot(ar, c));
-            const u32x4_t g = *reinterpret_cast<const FFN_LDS u32x4_t *>(base + kW4BCodes + br * 128 +
-                                                                          16 * w4_slot(br, c));
-            const u32x4_t u = *reinterpret_cast<const FFN_LDS u32x4_t *>(base + kW4BCodes + (32 + br) * 128 +
-                                                                          16 * w4_slot(32 + br, c));
             const i32x8_t A = w4_operand(a);
-            if (t % 2 == 0) {
-                cg = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, w4_operand(g), cg, 4, 4, 0,
-                                                                     static_cast<int>(sa[t / 2]), 0,
-                                                                     static_cast<int>(sg[t / 2]));
-                cu = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, w4_operand(u), cu, 4, 4, 0,
-                                                                     static_cast<int>(sa[t / 2]), 0,
-                                                                     static_cast<int>(su[t / 2]));
-            } else {
-                cg = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, w4_operand(g), cg, 4, 4, 2,
-                                                                     static_cast<int>(sa[t / 2]), 2,
-                                                                     static_cast<int>(sg[t / 2]));
-                cu = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, w4_operand(u), cu, 4, 4, 2,
-                                                                     static_cast<int>(sa[t / 2]), 2,
-                                                                     static_cast<int>(su[t / 2]));
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                const int b = 32 * f + br;
+                const u32x4_t w = *reinterpret_cast<const FFN_LDS u32x4_t *>(base + St::kBCodes + b * 128 +
+                                                                              16 * w4_slot(b, c));
+                if (t % 2 == 0)
+                    acc[f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        A, w4_operand(w), acc[f], 4, 4, 0, static_cast<int>(sa[t / 2]), 0,
+                        static_cast<int>(sb[f][t / 2]));
+                else
+                    acc[f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        A, w4_operand(w), acc[f], 4, 4, 2, static_cast<int>(sa[t / 2]), 2,
+                        static_cast<int>(sb[f][t / 2]));
             }
         }
     }
     wait_vmcnt<0>();  // the trailing re-loads land before the workgroup ends
-    const int n = n0 + (lane & 31);
     const int t0 = tg0 + 32 * wave;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int row = t0 + 8 * (v / 4) + 4 * half + (v % 4);
-        if (row < p.M) {
-            const size_t o = static_cast<size_t>(row) * p.N + n;
+    for (int f = 0; f < NF; ++f) {
+        const int b = 32 * f + br;
+        const int n = n0 + (b >> 1);
+        const bool row_ok = n <= nlast;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int tok = t0 + 8 * (v / 4) + 4 * half + (v % 4);
+            const size_t o = static_cast<size_t>(tok) * p.N + n;
             if constexpr (OUT == OUT_F32_PAIR) {
-                static_cast<float *>(p.out0)[o] = p.s2g * cg[v];
-                p.out1[o] = p.s2u * cu[v];
+                if (row_ok && tok < p.M) {
+                    if (b & 1)
+                        p.out1[o] = p.s2u * acc[f][v];
+                    else
+                        static_cast<float *>(p.out0)[o] = p.s2g * acc[f][v];
+                }
             } else {
                 constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
-                static_cast<uint16_t *>(p.out0)[o] = to_bf16_bits(gate_act<A>(p.s2g * cg[v]) * (p.s2u * cu[v]));
+                const float u = w4_pair_swap(acc[f][v]);  // the up value of row n
+                if (!(b & 1) && row_ok && tok < p.M)
+                    static_cast<uint16_t *>(p.out0)[o] = to_bf16_bits(gate_act<A>(p.s2g * acc[f][v]) * (p.s2u * u));
             }
         }
     }
 }
 
-template <int OUT>
+template <int OUT, int NF>
 hipError_t launch_dual_t(const W4a4Params &p, dim3 grid, hipStream_t stream)
 {
-    auto kern = w4a4_dual_kernel<OUT>;
+    constexpr int S = w4_stages<NF>();
+    constexpr int lds = S * W4Stage<NF>::kBytes + 256;
+    static_assert(S >= 2 && lds <= kW4LdsMax, "LDS ring");
+    auto kern = w4a4_dual_kernel<OUT, NF, S>;
     static std::atomic<uint64_t> lds_done{0};
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), kW4LdsBytes, lds_done);
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds, lds_done);
     if (e != hipSuccess)
         return e;
     W4a4Params q = p;
     void *args[] = {&q};
-    return hipLaunchKernel(reinterpret_cast<const void *>(kern), grid, dim3(kW4Threads), args, kW4LdsBytes, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), grid, dim3(kW4Threads), args, lds, stream);
+}
+
+template <int OUT>
+hipError_t launch_dual_nf(const W4a4Params &p, int nf, dim3 grid, hipStream_t stream)
+{
+    switch (nf) {
+    case 1: return launch_dual_t<OUT, 1>(p, grid, stream);
+    case 2: return launch_dual_t<OUT, 2>(p, grid, stream);
+    case 3: return launch_dual_t<OUT, 3>(p, grid, stream);
+    case 4: return launch_dual_t<OUT, 4>(p, grid, stream);
+    case 5: return launch_dual_t<OUT, 5>(p, grid, stream);
+    case 6: return launch_dual_t<OUT, 6>(p, grid, stream);
+    default: return hipErrorNotSupported;
+    }
 }
 
 }  // namespace
@@ -370,14 +430,21 @@ hipError_t launch_mx_requant(const uint8_t *codes, const uint8_t *scales, int ro
 hipError_t launch_w4a4_dual(int M, OutKind out, const uint8_t *xc, const uint8_t *xe, const MxWeightArg &g,
                             const MxWeightArg &u, void *out0, float *out1, int N, int K, hipStream_t stream)
 {
-    if (M < 1 || N < kW4RowsPerTile || N % kW4RowsPerTile != 0 || K < 256 || K % 256 != 0)
+    if (M < 1 || N < 1 || K < 256 || K % 256 != 0)
         return hipErrorNotSupported;
-    W4a4Params p{xc, xe, g.codes, g.e8m0, u.codes, u.e8m0, g.scale2, u.scale2, out0, out1, M, N, K};
-    const dim3 grid(N / kW4RowsPerTile, (M + kW4TokensPerGroup - 1) / kW4TokensPerGroup);
+    // Rows per workgroup: N over the compute units (at least one fragment's
+    // worth, at most kW4MaxFrags fragments), so one round of about one
+    // workgroup per compute unit covers every row of a token group.
+    const int cus = device_cu_count();
+    int R = (N + cus - 1) / cus;
+    R = R < 16 ? 16 : (R > 16 * kW4MaxFrags ? 16 * kW4MaxFrags : R);
+    const int nf = (R + 15) / 16;
+    W4a4Params p{xc, xe, g.codes, g.e8m0, u.codes, u.e8m0, g.scale2, u.scale2, out0, out1, M, N, K, R};
+    const dim3 grid((N + R - 1) / R, (M + kW4TokensPerGroup - 1) / kW4TokensPerGroup);
     switch (out) {
-    case OUT_F32_PAIR: return launch_dual_t<OUT_F32_PAIR>(p, grid, stream);
-    case OUT_H_SILU: return launch_dual_t<OUT_H_SILU>(p, grid, stream);
-    case OUT_H_GELU: return launch_dual_t<OUT_H_GELU>(p, grid, stream);
+    case OUT_F32_PAIR: return launch_dual_nf<OUT_F32_PAIR>(p, nf, grid, stream);
+    case OUT_H_SILU: return launch_dual_nf<OUT_H_SILU>(p, nf, grid, stream);
+    case OUT_H_GELU: return launch_dual_nf<OUT_H_GELU>(p, nf, grid, stream);
     default: return hipErrorNotSupported;
     }
 }
