@@ -114,6 +114,34 @@ __device__ __forceinline__ void fp8_load_row(Fp8Row<IS, NMAT, fp8_scale_regs<I0,
     }
 }
 
+// Steps A .. B - 1 of row r into a whole row's registers (and, with SC, the
+// row's block scales).
+template <bool NT, int IT, int NMAT, int A, int B, bool SC>
+__device__ __forceinline__ void fp8_load_steps(Fp8Row<IT, NMAT, fp8_scale_regs<0, IT>()> &w, const Fp8Params &p,
+                                               int r, const RowGeom &rg)
+{
+    constexpr int NB = fp8_scale_regs<0, IT>();
+#pragma unroll
+    for (int t = 0; t < NMAT; ++t) {
+        const u32x4_t *cb = reinterpret_cast<const u32x4_t *>((t == 0 ? p.codes0 : p.codes1) +
+                                                              static_cast<size_t>(r) * static_cast<size_t>(p.cols));
+        const float *sb = (t == 0 ? p.bs0 : p.bs1) + static_cast<size_t>(r >> 7) * static_cast<size_t>(p.bcols);
+        if constexpr (SC) {
+#pragma unroll
+            for (int k = 0; k < NB; ++k)
+                w.bs[t][k] = sb[min(rg.lane + 64 * k, p.bcols - 1)];
+        }
+#pragma unroll
+        for (int i = A; i < B; ++i) {
+            const int c = (i == IT - 1) ? rg.clast : rg.lane + 64 * i;
+            if constexpr (NT)
+                w.wc[t][i] = __builtin_nontemporal_load(cb + c);
+            else
+                w.wc[t][i] = cb[c];
+        }
+    }
+}
+
 // The block scale of step i for this lane: grid block 8 i + lane / 8, held by
 // lane 8 (i % 8) + lane / 8 in register i / 8 - K0.
 template <int I0, int IS, int NB>
@@ -227,9 +255,14 @@ __device__ __forceinline__ void fp8_pieces(const Fp8Params &fp, u32x4_t *act, fl
         fp8_pieces<M, IT, NMAT, IN, W, P, p + 1>(fp, act, acc, g, G, rg);
 }
 
-// The down GEMV issues its first weight row only once its activations have
-// arrived (stage_act's LATE order): at the decode shape the 17 KB rows of the
-// whole grid would otherwise queue ahead of them (17.8 vs 18.7 us).
+// The down GEMV issues only the first kFp8FirstSteps steps of its first
+// weight row (and the row's block scales) with its activation loads, and the
+// rest once the activations have arrived: at the decode shape the 17 KB rows
+// of the whole grid would otherwise queue ahead of them (17.8 vs 18.7 us with
+// the whole row issued after the activations; with 2 of 17 steps issued
+// early the forward measures 44.22 vs 44.57 us at M = 1 and 46.05 vs
+// 46.74 us at M = 2). Rows of fewer than kFp8SplitMinSteps steps issue the
+// whole row after the activations.
 //
 // W waves per workgroup; wave g = wave * gridDim.x + blockIdx.x takes rows
 // g, g + G, ... (G = all waves of the grid). Dynamic LDS: M * IT * 2 KB, or
@@ -238,6 +271,9 @@ __device__ __forceinline__ void fp8_pieces(const Fp8Params &fp, u32x4_t *act, fl
 // first weight row before staging and streams codes non-temporally; the down
 // GEMV stages first (with the activation fused into the staging when its
 // input is gate and up) and uses cached loads, as the NVFP4 kernels do.
+constexpr int kFp8FirstSteps = 2;
+constexpr int kFp8SplitMinSteps = 6;
+
 template <int M, int IT, int NMAT, int IN, int OUT, int W, int P = 1>
 __global__ __launch_bounds__(64 * W) void fp8_gemv_kernel(const Fp8Params p)
 {
@@ -263,11 +299,21 @@ __global__ __launch_bounds__(64 * W) void fp8_gemv_kernel(const Fp8Params p)
     Fp8Row<IT, NMAT, fp8_scale_regs<0, IT>()> w;
     if (kWeightsFirst && g < p.rows)
         fp8_load_row<kNt, IT, NMAT>(w, p, g, rg);
-    stage_act<M, IT, IN, W, 0, 2, !kWeightsFirst>(act, p.in0, p.in1, p.cols, p.cpr, [&] {
-        if (!kWeightsFirst && g < p.rows)
-            fp8_load_row<kNt, IT, NMAT>(w, p, g, rg);
-    });
-    lds_barrier();
+    if constexpr (kWeightsFirst || IT < kFp8SplitMinSteps) {
+        stage_act<M, IT, IN, W, 0, 2, !kWeightsFirst>(act, p.in0, p.in1, p.cols, p.cpr, [&] {
+            if (!kWeightsFirst && g < p.rows)
+                fp8_load_row<kNt, IT, NMAT>(w, p, g, rg);
+        });
+        lds_barrier();
+    } else {
+        stage_act<M, IT, IN, W, 0, 2, false>(act, p.in0, p.in1, p.cols, p.cpr, [&] {
+            if (g < p.rows)
+                fp8_load_steps<kNt, IT, NMAT, 0, kFp8FirstSteps, true>(w, p, g, rg);
+        });
+        lds_barrier();
+        if (g < p.rows)
+            fp8_load_steps<kNt, IT, NMAT, kFp8FirstSteps, IT, false>(w, p, g, rg);
+    }
     for (int r = g; r < p.rows; r += G) {
         float acc[NMAT][M];
         fp8_row_dot<M, IT, NMAT>(acc, w, act, rg);
