@@ -224,21 +224,26 @@ __device__ __forceinline__ void fp8_row_dot(float (&acc)[NMAT][M], const Fp8Row<
     }
 }
 
+// Row registers of piece p of an IT-step row cut into P pieces.
+template <int IT, int NMAT, int P, int p>
+using Fp8PieceRow = Fp8Row<piece_steps<IT, P, p>(), NMAT,
+                           fp8_scale_regs<p * ((IT + P - 1) / P), piece_steps<IT, P, p>()>()>;
+
 // One piece of the staged kernel (steps I0 .. I0 + IS - 1 of every row), then
-// the next; as wave_pieces of the NVFP4 kernel.
+// the next; as wave_pieces of the NVFP4 kernel (the next piece's first row
+// goes out at the end of a piece, ahead of the barrier and the restaging).
 template <int M, int IT, int NMAT, int IN, int W, int P, int p>
 __device__ __forceinline__ void fp8_pieces(const Fp8Params &fp, u32x4_t *act, float (&acc)[kPieceMaxRows][NMAT][M],
-                                           int g, int G, const RowGeom &rg)
+                                           int g, int G, const RowGeom &rg, Fp8PieceRow<IT, NMAT, P, p> &w)
 {
     constexpr int IP = (IT + P - 1) / P;
     constexpr int I0 = p * IP;
-    constexpr int IS = (IT - I0 < IP) ? IT - I0 : IP;
+    constexpr int IS = piece_steps<IT, P, p>();
     constexpr bool kNt = NMAT == 2;
-    Fp8Row<IS, NMAT, fp8_scale_regs<I0, IS>()> w;
     if constexpr (p > 0)
         lds_barrier();
     stage_act<M, IS, IN, W, I0, 2>(act, fp.in0, fp.in1, fp.cols, fp.cpr, [&] {
-        if (g < fp.rows)
+        if (p == 0 && g < fp.rows)
             fp8_load_row<kNt, IT, NMAT, I0, IS>(w, fp, g, rg);
     });
     lds_barrier();
@@ -251,8 +256,12 @@ __device__ __forceinline__ void fp8_pieces(const Fp8Params &fp, u32x4_t *act, fl
         if (k + 1 < kPieceMaxRows && r + G < fp.rows)
             fp8_load_row<kNt, IT, NMAT, I0, IS>(w, fp, r + G, rg);
     }
-    if constexpr (p + 1 < P)
-        fp8_pieces<M, IT, NMAT, IN, W, P, p + 1>(fp, act, acc, g, G, rg);
+    if constexpr (p + 1 < P) {
+        Fp8PieceRow<IT, NMAT, P, p + 1> wn;
+        if (g < fp.rows)
+            fp8_load_row<kNt, IT, NMAT, I0 + IP, piece_steps<IT, P, p + 1>()>(wn, fp, g, rg);
+        fp8_pieces<M, IT, NMAT, IN, W, P, p + 1>(fp, act, acc, g, G, rg, wn);
+    }
 }
 
 // The down GEMV issues only the first kFp8FirstSteps steps of its first
@@ -286,7 +295,8 @@ __global__ __launch_bounds__(64 * W) void fp8_gemv_kernel(const Fp8Params p)
     const RowGeom rg = row_geom<IT>(p.cpr);
     if constexpr (P > 1) {
         float acc[kPieceMaxRows][NMAT][M];
-        fp8_pieces<M, IT, NMAT, IN, W, P, 0>(p, act, acc, g, G, rg);
+        Fp8PieceRow<IT, NMAT, P, 0> w0;
+        fp8_pieces<M, IT, NMAT, IN, W, P, 0>(p, act, acc, g, G, rg, w0);
 #pragma unroll
         for (int k = 0; k < kPieceMaxRows; ++k) {
             const int r = g + k * G;
