@@ -103,7 +103,7 @@ PrefillLayout prefill_layout(int M, int N)
     const int mb = M < ffn::kMfmaMaxM ? M : ffn::kMfmaMaxM;
     l.h = 0;
     l.partials = round256(static_cast<size_t>(mb) * N * 2);
-    l.total = l.partials + round256(ffn::mfma_partials_floats() * sizeof(float));
+    l.total = l.partials + round256(ffn::mfma_scratch_bytes());
     return l;
 }
 
@@ -187,7 +187,7 @@ hipError_t run_prefill_forward(int M, ffn::OutKind epi, const void *x, const ffn
     }
     const PrefillLayout l = prefill_layout(M, N);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    ffn::MfmaScratch scratch{reinterpret_cast<float *>(ws + l.partials)};
+    ffn::MfmaScratch scratch = ffn::mfma_scratch(ws + l.partials);
     void *h = ws + l.h;
     for (int m0 = 0; m0 < M; m0 += ffn::kMfmaMaxM) {
         const int mb = M - m0 < ffn::kMfmaMaxM ? M - m0 : ffn::kMfmaMaxM;

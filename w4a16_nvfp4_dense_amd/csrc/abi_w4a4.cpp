@@ -56,7 +56,7 @@ W4Layout layout(int M, int K, int N)
     l.h = l.xe + round256(static_cast<size_t>(M) * static_cast<size_t>(K / 32));
     l.dual_total = l.h;
     l.partials = l.h + round256(static_cast<size_t>(M) * static_cast<size_t>(N) * 2);
-    l.total = l.partials + round256(ffn::mfma_partials_floats() * sizeof(float));
+    l.total = l.partials + round256(ffn::mfma_scratch_bytes());
     return l;
 }
 
@@ -152,7 +152,7 @@ int ffn_w4a4_forward(const void *x, int M, int K, int N, const ffn_mxfp4_weight 
         return FFN_NVFP4_ERR_LAUNCH;
     // The down projection on the W4A16 matrix-core arm, in blocks of up to
     // 128 token rows (stream-K partial slots in the workspace).
-    ffn::MfmaScratch scratch{reinterpret_cast<float *>(ws + l.partials)};
+    ffn::MfmaScratch scratch = ffn::mfma_scratch(ws + l.partials);
     const ffn::WeightArg d{down->codes, down->scales, down->scale2};
     for (int m0 = 0; m0 < M; m0 += ffn::kMfmaMaxM) {
         const int mb = M - m0 < ffn::kMfmaMaxM ? M - m0 : ffn::kMfmaMaxM;

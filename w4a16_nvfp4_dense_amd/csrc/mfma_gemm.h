@@ -40,11 +40,25 @@
 // [floor(g U / G), floor((g + 1) U / G))), so all compute units finish
 // together whatever the tile count. A workgroup that holds a whole tile runs
 // the epilogue itself; the pieces of a tile split between workgroups go to
-// fp32 slots of the workspace, and mfma_reduce_kernel, launched next, adds
-// them in k order and runs the same epilogue. No workgroup waits for or
-// signals another (device-scope fences inside the GEMM would write back and
-// invalidate the L2 that keeps the activation block resident). With G = T
-// every workgroup owns exactly one whole tile and no slot is touched.
+// fp32 slots of the workspace. With G = T every workgroup owns exactly one
+// whole tile and no slot is touched. Split tiles are finished in one of two
+// ways:
+//  - the down GEMM (a tile shared by ~13 workgroups at 128 tokens): by
+//    mfma_reduce_kernel, launched next, which adds the pieces in k order and
+//    runs the same epilogue;
+//  - the dual GEMM (a tile shared by 2-3 workgroups; FIX): inside the launch.
+//    Each workgroup walks its range downwards, so a lower workgroup reaches
+//    its piece of a shared tile (the top of its range) first and the highest
+//    one (whose range starts inside the tile) reaches it last. The lower ones
+//    store their pieces with device-coherent 16-byte stores (sc1: written
+//    through to memory, past the XCD's L2) and then set one ready word per
+//    wave to the launch's tag; the highest waits for those words, reads the
+//    pieces with device-coherent loads, adds them nearest first and runs the
+//    epilogue. A workgroup only ever waits for lower-numbered ones, which
+//    were dispatched first and wait only for lower ones still, so the waits
+//    end even when not all workgroups are resident at once. No fence is
+//    used: a release fence writes back the XCD's whole L2, which holds the
+//    activation block.
 #pragma once
 
 #include "kernels.h"
@@ -69,6 +83,8 @@ struct MfmaParams {
     void *out0;
     void *out1;
     float *partials;   // 2 G slots of partial tiles (stream-K only)
+    unsigned long long *flags;  // 4 ready words per slot (in-kernel finishing only)
+    unsigned long long tag;     // this launch's ready value (nonzero)
     int M;             // token rows, 1 <= M <= 32 * MT
     int rows;          // weight rows (output columns)
     int cols;          // reduction length, a multiple of 64
@@ -146,6 +162,27 @@ __device__ __forceinline__ int opaque_lane(int x)
     return x;
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (word 3: the raw-buffer
+// format bits of gfx9 devices), and a 16-byte store through it with the
+// device-scope cache policy (sc1, as agent-scope atomic stores use), so that
+// once it has completed another compute unit's agent-scope loads see it.
+// (As two 8-byte agent-scope atomic stores, which leave half lines to merge
+// below the L2, the prefill forward measured 9 us slower.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(void *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void store_device_coherent(__amdgpu_buffer_rsrc_t r, int byte_off, const f32x4_t &v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, byte_off, 0, 16 /* sc1 */);
+}
+// The matching 16-byte load (device-scope cache policy: not served by a
+// stale line of this compute unit's caches).
+__device__ __forceinline__ f32x4_t load_device_coherent(__amdgpu_buffer_rsrc_t r, int byte_off)
+{
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */));
+}
+
 // Epilogue of one accumulator position. Accumulator (f, mt, v) of lane
 // `lane` of wave `wave` holds D[m, row] with m = 32 mt + 8 (v / 4) + 4 (lane /
 // 32) + v % 4 and row = row lane % 32 of fragment f. (y0, y1) are fragments 0
@@ -183,7 +220,7 @@ __device__ __forceinline__ void emit_pair(const MfmaParams &p, int rows, int M, 
     }
 }
 
-template <int MT, int NMAT, int IN, int OUT, int S>
+template <int MT, int NMAT, int IN, int OUT, int S, bool FIX = false>
 __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaParams p)
 {
     static_assert(MT >= 1 && MT <= 4, "token tiles");
@@ -220,6 +257,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaPa
         const int row = t * ROWS_TILE + wave * ROWS_WAVE + (NMAT == 2 ? 0 : f * 32) + rr;
         return min(row, p.rows - 1);
     };
+
+    // The unit of step j: increasing, or with in-kernel finishing (FIX)
+    // decreasing, so that of the workgroups sharing a tile the highest one
+    // reaches its piece of it last and the lower ones write theirs earlier.
+    auto unit_at = [&](int jj) { return FIX ? u_begin + n - 1 - jj : u_begin + jj; };
 
     // Activation slot P (16 bytes) of a stage holds row P / 8, 16-byte piece
     // (P % 8) ^ ((row / 2) % 8) of the unit. A row is 128 bytes, so even rows
@@ -341,7 +383,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaPa
     // F0 holds the weights of the next unit to multiply.
     const int npre = min(n, S - 1);
     for (int j = 0; j < npre; ++j)
-        issue(u_begin + j, j);
+        issue(unit_at(j), j);
     Frags F0, F1;
     wait_units<S - 2, L>(min(S - 2, n - 1));
     lds_barrier();
@@ -352,7 +394,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaPa
         // ... in every wave, and every wave is done with unit j - 1's stage
         lds_barrier();
         if (j + S - 1 < n)
-            issue(u_begin + j + S - 1, (j + S - 1) % S);
+            issue(unit_at(j + S - 1), (j + S - 1) % S);
         load_weights((j + 1) % S, nxt);  // past the end: a harmless re-read
         mfma_unit(j % S, cur);
         // The compiler interleaves the next unit's dequantisation with these
@@ -361,13 +403,65 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaPa
         // tokens with the 4-stage ring.)
     };
 
+    // FIX: finish tile t, whose top unit this workgroup's current piece
+    // holds (acc): add the lower workgroups' pieces of the tile to it, the
+    // nearest first (a fixed order: a tile's sum depends only on the shape),
+    // each piece's loads all in flight before its additions.
+    auto finish = [&](int t) {
+        const int g_lo = sk_owner(static_cast<long long>(t) * KU, U, G);
+        for (int gg = g - 1; gg >= g_lo; --gg) {
+            const int slot = 2 * gg + (t == sk_begin(gg, U, G) / KU ? 0 : 1);
+            unsigned long long *flag = p.flags + 4 * slot + wave;
+            // bounded wait: a correct launch never reaches the limit
+            for (int spin = 0; spin < (1 << 22); ++spin) {
+                // (every lane reads the same word: take the first lane's, a uniform exit)
+                const bool ready = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.tag;
+                if (__builtin_amdgcn_readfirstlane(static_cast<int>(ready)))
+                    break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            __hip_atomic_store(flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const __amdgpu_buffer_rsrc_t rsrc = raw_buffer(slot_ptr(gg, t), SLOT / kMfmaWaves * 4);
+            f32x4_t v[2][MT][4];
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        v[f][mt][q4] = load_device_coherent(
+                            rsrc, (((f * MT + mt) * 4 + q4) * 64 + opaque_lane(lane)) * 16);
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            acc[f][mt][4 * q4 + c] += v[f][mt][q4][c];
+        }
+        store_out(t);
+    };
+
     // Pieces: maximal runs of this workgroup's units inside one tile. The
     // ring runs on across pieces; the accumulators only live inside one.
     int j = 0;
+    int fin_t = -1;       // FIX: the tile this workgroup finishes after its loop
+    int wrote = 0;        // FIX: slots it wrote (bit 0: slot 2 g, bit 1: 2 g + 1), published at the end
     while (j < n) {
-        const int t = (u_begin + j) / KU;
-        const int ku0 = u_begin + j - t * KU;
-        const int len = min(KU - ku0, n - j);
+        int t, ku0, len;
+        if constexpr (FIX) {
+            const int top = u_begin + n - 1 - j;
+            t = top / KU;
+            const int lo = max(u_begin, t * KU);
+            ku0 = lo - t * KU;
+            len = top - lo + 1;
+        } else {
+            t = (u_begin + j) / KU;
+            ku0 = u_begin + j - t * KU;
+            len = min(KU - ku0, n - j);
+        }
 #pragma unroll
         for (int f = 0; f < 2; ++f)
 #pragma unroll
@@ -389,18 +483,53 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaPa
             store_out(t);
             continue;
         }
+        if constexpr (FIX) {
+            // A piece that holds its tile's top unit without being the whole
+            // tile starts inside the tile, so at the range's first unit: in
+            // decreasing order it is the workgroup's last piece. The tile is
+            // finished after the ready words of this workgroup are set.
+            if (ku0 + len == KU) {
+                fin_t = t;
+                break;
+            }
+        }
         // A piece of a tile shared with other workgroups: to its slot, for
-        // mfma_reduce_kernel.
-        f32x4_t *mine = reinterpret_cast<f32x4_t *>(slot_ptr(g, t)) + opaque_lane(lane);
+        // mfma_reduce_kernel or (FIX) the workgroup that finishes the tile.
+        float *part = slot_ptr(g, t);
+        f32x4_t *mine = reinterpret_cast<f32x4_t *>(part) + opaque_lane(lane);
+        const __amdgpu_buffer_rsrc_t rsrc = raw_buffer(part, SLOT / kMfmaWaves * 4);
 #pragma unroll
         for (int f = 0; f < 2; ++f)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    mine[((f * MT + mt) * 4 + q4) * 64] =
-                        f32x4_t{acc[f][mt][4 * q4], acc[f][mt][4 * q4 + 1], acc[f][mt][4 * q4 + 2],
-                                acc[f][mt][4 * q4 + 3]};
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4_t v = {acc[f][mt][4 * q4], acc[f][mt][4 * q4 + 1], acc[f][mt][4 * q4 + 2],
+                                       acc[f][mt][4 * q4 + 3]};
+                    const int idx = ((f * MT + mt) * 4 + q4) * 64;
+                    if constexpr (FIX)  // read by another compute unit in this launch
+                        store_device_coherent(rsrc, (idx + opaque_lane(lane)) * 16, v);
+                    else
+                        mine[idx] = v;
+                }
+        if constexpr (FIX)
+            wrote |= (t == sk_begin(g, U, G) / KU) ? 1 : 2;
+    }
+    if constexpr (FIX) {
+        // Publish this wave's part of the slot written above once its
+        // device-coherent stores have completed (nothing else is in flight at
+        // the end of the range). (A release fence instead, which writes the
+        // XCD's L2 back, measured 21 us slower per forward.)
+        if (wrote != 0) {
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                if (wrote & (1 << b))
+                    __hip_atomic_store(p.flags + 4 * (2 * g + b) + wave, p.tag, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (fin_t >= 0)
+            finish(fin_t);
     }
 }
 

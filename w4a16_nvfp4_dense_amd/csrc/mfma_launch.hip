@@ -22,11 +22,11 @@ constexpr int stages()
     return s > 4 ? 4 : s;
 }
 
-template <int MT, int NMAT, int IN, int OUT>
+template <int MT, int NMAT, int IN, int OUT, bool FIX = false>
 hipError_t launch_t(MfmaParams p, int G, hipStream_t stream)
 {
     constexpr int S = stages<MT>();
-    auto kern = mfma_gemm_kernel<MT, NMAT, IN, OUT, S>;
+    auto kern = mfma_gemm_kernel<MT, NMAT, IN, OUT, S, FIX>;
     const int lds = S * mfma_stage_bytes<MT>();
     static std::atomic<uint64_t> lds_done{0};
     hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds, lds_done);
@@ -36,10 +36,17 @@ hipError_t launch_t(MfmaParams p, int G, hipStream_t stream)
     return hipLaunchKernel(reinterpret_cast<const void *>(kern), dim3(G), dim3(kMfmaWaves * 64), args, lds, stream);
 }
 
-// The GEMM, then (stream-K) the reduction of the split tiles.
+// The GEMM, then (stream-K) the reduction of the split tiles. The dual GEMM
+// finishes its split tiles in the kernel when the scratch has ready words:
+// the workgroup holding a tile's last unit adds the lower workgroups' pieces
+// once their ready words carry this launch's tag.
 template <int MT, int NMAT, int IN, int OUT>
 hipError_t launch_gemm_reduce(const MfmaParams &p, int G, hipStream_t stream)
 {
+    if constexpr (NMAT == 2) {
+        if (p.partials != nullptr && p.flags != nullptr)
+            return launch_t<MT, NMAT, IN, OUT, true>(p, G, stream);
+    }
     hipError_t e = launch_t<MT, NMAT, IN, OUT>(p, G, stream);
     if (e != hipSuccess || p.partials == nullptr)
         return e;
@@ -60,6 +67,18 @@ hipError_t launch_mt(const MfmaParams &p, int G, hipStream_t stream)
     }
 }
 
+// A nonzero 64-bit tag per launch (a counter through a 64-bit mix), so that
+// ready words left in a reused workspace by other data almost never equal it.
+unsigned long long next_tag()
+{
+    static std::atomic<unsigned long long> counter{0};
+    unsigned long long z = counter.fetch_add(1, std::memory_order_relaxed) + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return z != 0 ? z : 1;
+}
+
 // Grid and stream-K bookkeeping for one GEMM. With a workspace the grid is
 // one workgroup per compute unit (capped at kMfmaMaxGrid) and a reduction
 // launch finishes the split tiles; without one it is one workgroup per tile.
@@ -78,6 +97,8 @@ void plan(MfmaParams &p, int nmat, const MfmaScratch *ws, int &G)
     if (G <= p.tiles && p.units % G == 0 && (p.units / G) % p.units_per_tile == 0)
         return;  // every workgroup owns whole tiles
     p.partials = ws->partials;
+    p.flags = ws->flags;
+    p.tag = next_tag();
 }
 
 MfmaParams params(int M, const void *in0, const float *in1, const WeightArg &w0, const WeightArg &w1, void *out0,
@@ -105,6 +126,22 @@ MfmaParams params(int M, const void *in0, const float *in1, const WeightArg &w0,
 size_t mfma_partials_floats()
 {
     return static_cast<size_t>(2) * kMfmaMaxGrid * mfma_slot_floats<4>();
+}
+
+size_t mfma_flag_words()
+{
+    return static_cast<size_t>(2) * kMfmaMaxGrid * kMfmaWaves;
+}
+
+size_t mfma_scratch_bytes()
+{
+    return mfma_partials_floats() * sizeof(float) + mfma_flag_words() * sizeof(unsigned long long);
+}
+
+MfmaScratch mfma_scratch(void *base)
+{
+    float *partials = static_cast<float *>(base);
+    return MfmaScratch{partials, reinterpret_cast<unsigned long long *>(partials + mfma_partials_floats())};
 }
 
 hipError_t launch_mfma_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1,
