@@ -102,14 +102,15 @@ typedef struct ffn_nvfp4_weight {
  *                    read and dequantised once for all rows (one token group
  *                    of 16 rows up to M = 16, two above); its reductions are
  *                    split in parts where a wave's activations do not fit its
- *                    registers, finished by a reduction launch;
+ *                    registers, finished inside the same launch;
  *     otherwise      the 128-row arm, in blocks of 128 token rows, each block
  *                    reading the weights once.
  * Other M: ERR_BATCH. K and N: positive multiples of 32, at most 65536. */
 
 /* Bytes of device workspace ffn_nvfp4_forward needs for (M, K, N);
  * 0 if M = 0 or the shape is unsupported. For M <= 8 it holds h [M, N] bf16;
- * for the small-batch arm h and the fp32 partial sums of split reductions;
+ * for the small-batch arm h, the fp32 partial sums of split reductions and
+ * their ready words (a few KB);
  * for the 128-row arm, h for one block of up to 128 rows plus the fp32 slots
  * in which that arm leaves the pieces of split reductions (about 64 MiB,
  * whatever M). Its contents need no initialisation. */

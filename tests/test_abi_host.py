@@ -96,15 +96,19 @@ def test_version_strerror_workspace():
     assert ffn.workspace_bytes(1, 250, 512) == 0
     # small-batch arm (9 <= M <= 32, K and N multiples of 256): h, the down
     # projection's partial sums when its reduction is split (N = 17408: 4
-    # parts), and the dual projection's when its reduction is split (two
-    # token groups at K = 5120: 2 parts)
+    # parts), the dual projection's when its reduction is split (two token
+    # groups at K = 5120: 2 parts), and 4 ready words of 8 bytes per workgroup
+    # of the larger split grid (about one workgroup per compute unit; 256
+    # compute units assumed where no device is visible)
     r256 = lambda b: (b + 255) // 256 * 256
+    flags = lambda grid: r256(4 * 8 * grid)
     assert ffn.workspace_bytes(9, 256, 512) == 9 * 512 * 2
-    assert ffn.workspace_bytes(16, 5120, 17408) == 16 * 17408 * 2 + 4 * 16 * 5120 * 4
+    assert ffn.workspace_bytes(16, 5120, 17408) == 16 * 17408 * 2 + 4 * 16 * 5120 * 4 + flags(4 * 64)
     assert ffn.workspace_bytes(17, 5120, 17408) == (r256(17 * 17408 * 2) + 4 * 17 * 5120 * 4
-                                                    + 2 * 2 * 17 * 17408 * 4)
-    assert ffn.workspace_bytes(32, 4096, 8192) == r256(32 * 8192 * 2) + 2 * 32 * 4096 * 4
-    assert ffn.workspace_bytes(16, 5376, 512) == r256(16 * 512 * 2) + 2 * 2 * 16 * 512 * 4
+                                                    + 2 * 2 * 17 * 17408 * 4 + flags(256))
+    assert ffn.workspace_bytes(32, 4096, 8192) == r256(32 * 8192 * 2) + 2 * 32 * 4096 * 4 + flags(2 * 128)
+    # dual reduction in 2 parts over 32 row tiles (512 rows): a grid of 64
+    assert ffn.workspace_bytes(16, 5376, 512) == r256(16 * 512 * 2) + 2 * 2 * 16 * 512 * 4 + flags(2 * 32)
     # 128-row matrix-core arm (M > 32, or K or N not a multiple of 256): h for
     # one block of 128 rows and the partial slots
     ws33 = ffn.workspace_bytes(33, 256, 512)

@@ -78,14 +78,15 @@ struct PrefillLayout {
 
 // Batches of 9 to 32 rows take the small-batch arm when it covers the shape;
 // its workspace is h, the down projection's partial sums and, when the dual
-// projection's reduction is split in parts, its partial sums.
+// projection's reduction is split in parts, its partial sums, then the ready
+// words of the split reductions.
 bool small_arm(int M, int K, int N)
 {
     return M > kMaxGemvM && ffn::smallm_supported(M, K, N);
 }
 
 struct SmallLayout {
-    size_t down_partials, dual_partials, total;
+    size_t down_partials, dual_partials, flags, total;
 };
 
 SmallLayout small_layout(int M, int K, int N)
@@ -93,7 +94,8 @@ SmallLayout small_layout(int M, int K, int N)
     SmallLayout l{};
     l.down_partials = round256(static_cast<size_t>(M) * static_cast<size_t>(N) * 2);
     l.dual_partials = l.down_partials + round256(ffn::smallm_partial_floats(M, K, N) * sizeof(float));
-    l.total = l.dual_partials + round256(ffn::smallm_dual_partial_floats(M, K, N) * sizeof(float));
+    l.flags = l.dual_partials + round256(ffn::smallm_dual_partial_floats(M, K, N) * sizeof(float));
+    l.total = l.flags + round256(ffn::smallm_flag_words(M, K, N) * sizeof(unsigned long long));
     return l;
 }
 
@@ -145,7 +147,8 @@ hipError_t run_prefill_dual(int M, const void *x, const ffn::WeightArg &g, const
     // The dual entry has no workspace: the small-batch arm only when its
     // reduction is not split.
     if (small_arm(M, K, N) && !ffn::smallm_dual_split(M, K, N))
-        return ffn::launch_smallm_dual(M, ffn::OUT_F32_PAIR, x, g, u, gate_out, up_out, nullptr, N, K, stream);
+        return ffn::launch_smallm_dual(M, ffn::OUT_F32_PAIR, x, g, u, gate_out, up_out, nullptr, nullptr, N, K,
+                                       stream);
     for (int m0 = 0; m0 < M; m0 += ffn::kMfmaMaxM) {
         const int mb = M - m0 < ffn::kMfmaMaxM ? M - m0 : ffn::kMfmaMaxM;
         const size_t xo = static_cast<size_t>(m0) * K, oo = static_cast<size_t>(m0) * N;
@@ -178,12 +181,13 @@ hipError_t run_prefill_forward(int M, ffn::OutKind epi, const void *x, const ffn
     if (small_arm(M, K, N)) {
         const SmallLayout l = small_layout(M, K, N);
         uint8_t *ws = static_cast<uint8_t *>(workspace);
+        unsigned long long *flags = reinterpret_cast<unsigned long long *>(ws + l.flags);
         hipError_t e = ffn::launch_smallm_dual(M, epi, x, g, u, workspace, nullptr,
-                                               reinterpret_cast<float *>(ws + l.dual_partials), N, K, stream);
+                                               reinterpret_cast<float *>(ws + l.dual_partials), flags, N, K, stream);
         if (e != hipSuccess)
             return e;
-        return ffn::launch_smallm_down(M, workspace, d, out, reinterpret_cast<float *>(ws + l.down_partials), K, N,
-                                       stream);
+        return ffn::launch_smallm_down(M, workspace, d, out, reinterpret_cast<float *>(ws + l.down_partials), flags,
+                                       K, N, stream);
     }
     const PrefillLayout l = prefill_layout(M, N);
     uint8_t *ws = static_cast<uint8_t *>(workspace);

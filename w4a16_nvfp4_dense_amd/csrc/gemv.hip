@@ -29,6 +29,9 @@
 // combined by a fixed DPP tree within the wave; there is no cross-wave
 // shared-memory reduction and no atomics, so results are bit-reproducible,
 // and a row's result does not depend on M.
+#include <atomic>
+#include <cstdint>
+
 #include "kernels.h"
 #include "nvfp4_device.h"
 
@@ -280,6 +283,17 @@ int device_cu_count()
         __atomic_store_n(&counts[dev], n, __ATOMIC_RELAXED);
     }
     return n;
+}
+
+unsigned long long launch_tag()
+{
+    static std::atomic<unsigned long long> counter{0};
+    unsigned long long z = counter.fetch_add(1, std::memory_order_relaxed) +
+                           reinterpret_cast<uintptr_t>(&counter) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;  // splitmix64 finaliser
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return z != 0 ? z : 1;
 }
 
 // Lanes per row as a function of the reduction length only: the smallest of

@@ -47,8 +47,6 @@ enum OutKind : int {
     OUT_BF16 = 1,      // one projection: out0 = bf16(s2_0 * y0) [M, rows]
     OUT_H_SILU = 2,    // two projections: out0 = bf16(SiLU(s2_0 y0) * s2_1 y1) [M, rows]
     OUT_H_GELU = 3,    // same with GELU-tanh
-    OUT_PART_F32 = 4,  // one projection, a piece of a split reduction: out0 = y0 (fp32, unscaled)
-    OUT_PART_PAIR = 5, // two projections, pieces of split reductions: out0 = y0, out1 = y1 (fp32, unscaled)
 };
 
 // Streaming GEMV over NVFP4 weights for 1 <= M <= 8 activation rows:
@@ -75,6 +73,12 @@ hipError_t launch_wave_down(int M, InKind in, const void *in0, const float *in1,
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
+
+// A nonzero 64-bit tag per launch for the ready words of in-kernel exchanges
+// (a counter and this library's address through a 64-bit mix), so that a
+// ready word left in a reused workspace by other data or another launch
+// almost never equals it.
+unsigned long long launch_tag();
 
 // Lanes that share one weight row for a reduction of `cpr` 32-column chunks
 // (8, 16, 32 or 64); the row-streaming kernels require 64.

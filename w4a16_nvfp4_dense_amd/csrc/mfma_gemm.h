@@ -162,27 +162,6 @@ __device__ __forceinline__ int opaque_lane(int x)
     return x;
 }
 
-// Raw buffer resource over `bytes` bytes at `base` (word 3: the raw-buffer
-// format bits of gfx9 devices), and a 16-byte store through it with the
-// device-scope cache policy (sc1, as agent-scope atomic stores use), so that
-// once it has completed another compute unit's agent-scope loads see it.
-// (As two 8-byte agent-scope atomic stores, which leave half lines to merge
-// below the L2, the prefill forward measured 9 us slower.)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(void *base, int bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
-}
-__device__ __forceinline__ void store_device_coherent(__amdgpu_buffer_rsrc_t r, int byte_off, const f32x4_t &v)
-{
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, byte_off, 0, 16 /* sc1 */);
-}
-// The matching 16-byte load (device-scope cache policy: not served by a
-// stale line of this compute unit's caches).
-__device__ __forceinline__ f32x4_t load_device_coherent(__amdgpu_buffer_rsrc_t r, int byte_off)
-{
-    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */));
-}
-
 // Epilogue of one accumulator position. Accumulator (f, mt, v) of lane
 // `lane` of wave `wave` holds D[m, row] with m = 32 mt + 8 (v / 4) + 4 (lane /
 // 32) + v % 4 and row = row lane % 32 of fragment f. (y0, y1) are fragments 0
@@ -410,16 +389,8 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void mfma_gemm_kernel(const MfmaPa
     auto finish = [&](int t) {
         const int g_lo = sk_owner(static_cast<long long>(t) * KU, U, G);
         for (int gg = g - 1; gg >= g_lo; --gg) {
-            const int slot = 2 * gg + (t == sk_begin(gg, U, G) / KU ? 0 : 1);
-            unsigned long long *flag = p.flags + 4 * slot + wave;
-            // bounded wait: a correct launch never reaches the limit
-            for (int spin = 0; spin < (1 << 22); ++spin) {
-                // (every lane reads the same word: take the first lane's, a uniform exit)
-                const bool ready = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.tag;
-                if (__builtin_amdgcn_readfirstlane(static_cast<int>(ready)))
-                    break;
-                __builtin_amdgcn_s_sleep(1);
-            }
+            unsigned long long *flag = p.flags + 4 * (2 * gg + (t == sk_begin(gg, U, G) / KU ? 0 : 1)) + wave;
+            wait_ready([&](int) { return flag; }, 1, p.tag);
             __hip_atomic_store(flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const __amdgpu_buffer_rsrc_t rsrc = raw_buffer(slot_ptr(gg, t), SLOT / kMfmaWaves * 4);
             f32x4_t v[2][MT][4];

@@ -67,18 +67,6 @@ hipError_t launch_mt(const MfmaParams &p, int G, hipStream_t stream)
     }
 }
 
-// A nonzero 64-bit tag per launch (a counter through a 64-bit mix), so that
-// ready words left in a reused workspace by other data almost never equal it.
-unsigned long long next_tag()
-{
-    static std::atomic<unsigned long long> counter{0};
-    unsigned long long z = counter.fetch_add(1, std::memory_order_relaxed) + 0x9E3779B97F4A7C15ull;
-    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-    z ^= z >> 31;
-    return z != 0 ? z : 1;
-}
-
 // Grid and stream-K bookkeeping for one GEMM. With a workspace the grid is
 // one workgroup per compute unit (capped at kMfmaMaxGrid) and a reduction
 // launch finishes the split tiles; without one it is one workgroup per tile.
@@ -98,7 +86,7 @@ void plan(MfmaParams &p, int nmat, const MfmaScratch *ws, int &G)
         return;  // every workgroup owns whole tiles
     p.partials = ws->partials;
     p.flags = ws->flags;
-    p.tag = next_tag();
+    p.tag = launch_tag();
 }
 
 MfmaParams params(int M, const void *in0, const float *in1, const WeightArg &w0, const WeightArg &w1, void *out0,

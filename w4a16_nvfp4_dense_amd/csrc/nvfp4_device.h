@@ -107,6 +107,66 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Exchange between the workgroups of one launch, without a fence. Data moves
+// with stores and loads that carry the device-scope cache policy (sc1, as
+// agent-scope atomics use): a store is written through the XCD's L2 to
+// memory, a load is not served by a line another XCD may have changed. A
+// writer publishes with an agent-scope atomic store of the launch's tag to a
+// ready word once its own stores have completed (s_waitcnt vmcnt(0)); the
+// reader waits for the tag. (A release fence instead writes back the XCD's
+// whole L2, which holds what the GEMMs keep resident: 21 us slower per
+// prefill forward; 8-byte atomic stores for the data, which leave half lines
+// to merge below the L2, 9 us slower.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void *base, int bytes)
+{
+    // word 3: the raw-buffer format bits of gfx9 devices
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void store_device_coherent(__amdgpu_buffer_rsrc_t r, int byte_off, const f32x4_t &v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, byte_off, 0, 16 /* sc1 */);
+}
+__device__ __forceinline__ f32x4_t load_device_coherent(__amdgpu_buffer_rsrc_t r, int byte_off)
+{
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */));
+}
+__device__ __forceinline__ void store_device_coherent(__amdgpu_buffer_rsrc_t r, int byte_off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 16 /* sc1 */);
+}
+__device__ __forceinline__ float load_device_coherent_f32(__amdgpu_buffer_rsrc_t r, int byte_off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 16 /* sc1 */));
+}
+
+// Waits (bounded: a correct launch never reaches the limit) until the n ready
+// words word(0) .. word(n - 1) all hold `tag`. A poll has the loads of up to
+// 8 words in flight together. Every lane reads the same words and the first
+// lane's result decides, so the exit is uniform. (Both callers wait for one
+// word at a time: for the pieces of one tile, polling all words at once
+// measured 0.2-1.2 us slower per forward.)
+template <typename WordAt>
+__device__ __forceinline__ void wait_ready(WordAt word, int n, unsigned long long tag)
+{
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+        bool ready = true;
+        for (int k0 = 0; k0 < n; k0 += 8) {
+            unsigned long long v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (k0 + k < n)
+                    v[k] = __hip_atomic_load(word(k0 + k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (k0 + k < n)
+                    ready = ready && v[k] == tag;
+        }
+        if (__builtin_amdgcn_readfirstlane(static_cast<int>(ready)))
+            break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 // Workgroup barrier for LDS only: waits for this wave's LDS traffic and meets
 // the other waves, without the vector-memory drain of __syncthreads() (which
 // would also wait for global loads still in flight for later use).

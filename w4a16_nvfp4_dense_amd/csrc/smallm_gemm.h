@@ -49,15 +49,18 @@
 // activations fit in registers: 5 rounds, 4 for the dual GEMM with two token
 // groups) and
 // tiles [g T / G, (g + 1) T / G) with g = w / P, T tiles and G = gridDim / P
-// groups. With P = 1 the epilogue writes finished outputs; with P > 1 it
-// writes the part's fp32 sums and smallm_reduce_kernel (down) or
-// smallm_reduce_pair_kernel (dual, with the activation epilogue) adds the
-// parts in order. (Adding them in the kernel,
-// by the last of a group's workgroups to finish, measured no faster: the
-// exchange between XCDs costs the same round trips as a second launch.) No
-// workgroup waits for another, the order of every sum is fixed, and a token
-// row's result does not depend on the other rows of the batch within one
-// token-group count (the count sets the parts, hence the order of the sums).
+// groups. With P = 1 the epilogue writes finished outputs. With P > 1
+// (SPLIT) every workgroup stores its part's fp32 sums of its tiles with
+// device-coherent stores; the lower parts' workgroups then set their ready
+// words, and the last part's workgroup (the highest id of the P, so it waits
+// only for workgroups dispatched before it, which wait for nobody) adds the
+// parts in order, part 0 first, and runs the epilogue. (A first version that
+// let the last workgroup to finish add the parts, behind device-scope
+// release/acquire fences, measured slower than a separate reduction launch:
+// the fences write back and invalidate the XCD's L2.) The order of every sum
+// is fixed, and a token row's result does not depend on the other rows of the
+// batch within one token-group count (the count sets the parts, hence the
+// order of the sums).
 #pragma once
 
 #include "kernels.h"
@@ -91,6 +94,10 @@ struct SmallParams {
     int cols;    // reduction length, a multiple of 256
     int parts;   // P
     int groups;  // G: workgroups per part
+    float *part0;  // P x [M, rows] fp32 pieces of the first projection (split reductions)
+    float *part1;  // the same for the second projection
+    unsigned long long *flags;  // 4 ready words per workgroup (split reductions)
+    unsigned long long tag;     // this launch's ready value (nonzero)
 };
 
 // LDS of one ring stage: codes [NMAT][2 row halves][4 column blocks][8 rows]
@@ -118,7 +125,7 @@ constexpr int sm_lds_bytes()
     return kSmStages * sm_stage_bytes<NMAT>() + sm_red_bytes<NMAT>() + 1280;
 }
 
-template <int NMAT, int OUT, int NR, int TG>
+template <int NMAT, int OUT, int NR, int TG, bool SPLIT>
 __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallParams p)
 {
     static_assert(NR >= 1 && NR <= kSmMaxRounds, "rounds");
@@ -153,6 +160,7 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
     const int total = ntiles * nrounds;                  // rounds of this workgroup
     const size_t row_codes = static_cast<size_t>(cols) / 2;
     const size_t row_scales = static_cast<size_t>(cols) / 16;
+    const int piece_bytes = P * M * p.rows * 4;  // one projection's pieces (< 2^31, checked by the launcher)
 
     // Loads of one round: codes (16 rows x 512 bytes per projection) and
     // scales (16 x 64 bytes per projection). Every wave issues exactly two
@@ -351,87 +359,113 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
                 if (m < M) {
                     const int row = (ta + tt) * kSmRows + rr;
                     const size_t o = static_cast<size_t>(m) * p.rows + row;
-                    if constexpr (OUT == OUT_F32_PAIR) {
+                    if constexpr (SPLIT) {
+                        // this part's piece, for the last part's workgroup (any XCD)
+                        const int po = (part * M * p.rows + static_cast<int>(o)) * 4;
+                        store_device_coherent(raw_buffer(p.part0, piece_bytes), po, y[0]);
+                        if constexpr (NMAT == 2)
+                            store_device_coherent(raw_buffer(p.part1, piece_bytes), po, y[1]);
+                    } else if constexpr (OUT == OUT_F32_PAIR) {
                         static_cast<float *>(p.out0)[o] = y[0] * p.s2_0;
                         static_cast<float *>(p.out1)[o] = y[NMAT - 1] * p.s2_1;
                     } else if constexpr (OUT == OUT_H_SILU || OUT == OUT_H_GELU) {
                         constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
                         static_cast<uint16_t *>(p.out0)[o] =
                             to_bf16_bits(gate_act<A>(y[0] * p.s2_0) * (y[NMAT - 1] * p.s2_1));
-                    } else if constexpr (OUT == OUT_BF16) {
-                        static_cast<uint16_t *>(p.out0)[o] = to_bf16_bits(y[0] * p.s2_0);
-                    } else if constexpr (OUT == OUT_PART_PAIR) {
-                        const size_t po = static_cast<size_t>(part) * M * p.rows + o;
-                        static_cast<float *>(p.out0)[po] = y[0];
-                        static_cast<float *>(p.out1)[po] = y[NMAT - 1];
                     } else {
-                        static_cast<float *>(p.out0)[static_cast<size_t>(part) * M * p.rows + o] = y[0];
+                        static_cast<uint16_t *>(p.out0)[o] = to_bf16_bits(y[0] * p.s2_0);
                     }
                 }
             }
         }
     }
 
-}
+    if constexpr (SPLIT) {
+        // The P workgroups blockIdx.x - part .. + P - 1 hold the parts of the
+        // same tiles; waves 0-3 stored this workgroup's pieces. The lower
+        // parts publish theirs once those stores have completed (nothing else
+        // they issued matters: the ring's trailing loads only fill LDS).
+        if (part != P - 1) {
+            if (q < 4) {
+                wait_vmcnt<0>();
+                __hip_atomic_store(p.flags + 4 * blockIdx.x + q, p.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            return;
+        }
+        // The last part's workgroup finishes the tiles. Wave q adds up the
+        // elements that wave q % 4 of every part stored, for the (tile, token
+        // group) items q / 4, q / 4 + 4, ... It waits only for lower-numbered
+        // workgroups, which were dispatched first and wait for nobody.
+        wait_vmcnt<0>();
+        __syncthreads();  // this workgroup's own pieces have been stored
+        const int qw = q & 3;
+        const int g0 = blockIdx.x - part;
+        // (one word at a time: polling all of them at once measured no faster)
+        for (int pp = 0; pp < P - 1; ++pp)
+            wait_ready([&](int) { return p.flags + 4 * (g0 + pp) + qw; }, 1, p.tag);
+        __syncthreads();  // every wave has seen its words: clear them
+        if (q < 4)
+            for (int pp = 0; pp < P - 1; ++pp)
+                __hip_atomic_store(p.flags + 4 * (g0 + pp) + q, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-// The parts' sums of four consecutive elements e .. e + 3 (e a multiple of
-// 4, n too): every load of a batch of up to 8 parts is issued before the
-// first addition, and the parts are added in order (part 0 first).
-__device__ __forceinline__ f32x4_t sum_parts4(const float *part, int parts, size_t n, size_t e)
-{
-    constexpr int B = 8;
-    f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k0 = 0; k0 < parts; k0 += B) {
-        f32x4_t v[B];
+        const int tid2 = 64 * qw + lane;  // the storing thread of these elements
+        const int mo = tid2 >> 4;         // token within its group
+        const int rr = tid2 & 15;
+        const __amdgpu_buffer_rsrc_t rsrc[2] = {raw_buffer(p.part0, piece_bytes),
+                                                raw_buffer(NMAT == 2 ? p.part1 : p.part0, piece_bytes)};
+        const int part_bytes = M * p.rows * 4;
+        const int items = ntiles * TG;
+        constexpr int IG = 4;  // items per thread and batch
+        constexpr int PC = 4;  // parts per batch (all loads of a batch in flight before its additions)
+        for (int k0 = q >> 2; k0 < items; k0 += 4 * IG) {
+            int off[IG];
+            bool ok[IG];
 #pragma unroll
-        for (int k = 0; k < B; ++k)
-            if (k0 + k < parts)
-                v[k] = *reinterpret_cast<const f32x4_t *>(part + static_cast<size_t>(k0 + k) * n + e);
+            for (int i = 0; i < IG; ++i) {
+                const int k = k0 + 4 * i;
+                const int tt = k / TG;
+                const int m = 16 * (k - tt * TG) + mo;
+                ok[i] = k < items && m < M;
+                off[i] = ok[i] ? (m * p.rows + (ta + tt) * kSmRows + rr) * 4 : 0;  // 0: a valid, unused read
+            }
+            float sum[IG][NMAT];
+            for (int p0 = 0; p0 < P; p0 += PC) {
+                float v[IG][PC][NMAT];
 #pragma unroll
-        for (int k = 0; k < B; ++k)
-            if (k0 + k < parts)
-                a = (k0 + k == 0) ? v[k] : a + v[k];
-    }
-    return a;
-}
-
-// out[m, j] = bf16(s2 * sum_p part[p, m, j]), the parts added in order; four
-// elements per thread (n is a multiple of 4).
-__global__ __launch_bounds__(256) void smallm_reduce_kernel(const float *part, int parts, size_t n, float s2,
-                                                            uint16_t *out)
-{
-    const size_t e = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
-    if (e >= n)
-        return;
-    const f32x4_t a = sum_parts4(part, parts, n, e);
-    *reinterpret_cast<u32x2_t *>(out + e) = u32x2_t{pack_bf16x2(a[0] * s2, a[1] * s2), pack_bf16x2(a[2] * s2, a[3] * s2)};
-}
-
-// The dual projection split in parts: g = sum_p gpart[p, m, n], u likewise
-// (parts added in order), then the same epilogue as an unsplit tile: the fp32
-// pair s2_g g, s2_u u, or h = bf16(act(s2_g g) * (s2_u u)). Four elements per
-// thread (n is a multiple of 4).
-template <int OUT>
-__global__ __launch_bounds__(256) void smallm_reduce_pair_kernel(const float *gpart, const float *upart, int parts,
-                                                                 size_t n, float s2_g, float s2_u, void *out0,
-                                                                 float *out1)
-{
-    const size_t e = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
-    if (e >= n)
-        return;
-    const f32x4_t g = sum_parts4(gpart, parts, n, e);
-    const f32x4_t u = sum_parts4(upart, parts, n, e);
-    if constexpr (OUT == OUT_F32_PAIR) {
-        *reinterpret_cast<f32x4_t *>(static_cast<float *>(out0) + e) = g * s2_g;
-        *reinterpret_cast<f32x4_t *>(out1 + e) = u * s2_u;
-    } else {
-        constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
-        float h[4];
+                for (int i = 0; i < IG; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            h[i] = gate_act<A>(g[i] * s2_g) * (u[i] * s2_u);
-        *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(out0) + e) =
-            u32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+                    for (int c = 0; c < PC; ++c)
+#pragma unroll
+                        for (int f = 0; f < NMAT; ++f)
+                            if (p0 + c < P)
+                                v[i][c][f] = load_device_coherent_f32(rsrc[f], off[i] + (p0 + c) * part_bytes);
+                // the parts in order, part 0 first
+#pragma unroll
+                for (int i = 0; i < IG; ++i)
+#pragma unroll
+                    for (int c = 0; c < PC; ++c)
+#pragma unroll
+                        for (int f = 0; f < NMAT; ++f)
+                            if (p0 + c < P)
+                                sum[i][f] = (p0 + c == 0) ? v[i][c][f] : sum[i][f] + v[i][c][f];
+            }
+#pragma unroll
+            for (int i = 0; i < IG; ++i) {
+                if (!ok[i])
+                    continue;
+                const size_t o = static_cast<size_t>(off[i] / 4);
+                if constexpr (OUT == OUT_F32_PAIR) {
+                    static_cast<float *>(p.out0)[o] = sum[i][0] * p.s2_0;
+                    static_cast<float *>(p.out1)[o] = sum[i][NMAT - 1] * p.s2_1;
+                } else if constexpr (OUT == OUT_H_SILU || OUT == OUT_H_GELU) {
+                    constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
+                    static_cast<uint16_t *>(p.out0)[o] =
+                        to_bf16_bits(gate_act<A>(sum[i][0] * p.s2_0) * (sum[i][NMAT - 1] * p.s2_1));
+                } else {
+                    static_cast<uint16_t *>(p.out0)[o] = to_bf16_bits(sum[i][0] * p.s2_0);
+                }
+            }
+        }
     }
 }
 

@@ -25,13 +25,22 @@ size_t smallm_partial_floats(int M, int K, int N);
 // fp32 floats of the dual GEMM's partial sums (0 when it needs none).
 size_t smallm_dual_partial_floats(int M, int K, int N);
 
+// 64-bit ready words that a split reduction of either GEMM uses (0 when
+// neither is split): 4 per workgroup, set to a per-launch tag by the
+// workgroups of the lower parts and cleared by the one that finishes their
+// tiles, so they need no initialisation; the two GEMMs of a forward may share
+// them (stream-ordered).
+size_t smallm_flag_words(int M, int K, int N);
+
 // Dual GEMM (gate and up; out = OUT_F32_PAIR or OUT_H_*); `partials` holds
-// smallm_dual_partial_floats(M, K, N) floats (may be null when that is 0).
+// smallm_dual_partial_floats(M, K, N) floats and `flags` smallm_flag_words()
+// words (both may be null when the reduction is not split).
 hipError_t launch_smallm_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1,
-                              void *out0, void *out1, float *partials, int N, int K, hipStream_t stream);
-// Down GEMM: out[M, K] bf16 from h[M, N] bf16; `partials` holds
-// smallm_partial_floats(M, K, N) floats.
-hipError_t launch_smallm_down(int M, const void *h, const WeightArg &w, void *out, float *partials, int K, int N,
+                              void *out0, void *out1, float *partials, unsigned long long *flags, int N, int K,
                               hipStream_t stream);
+// Down GEMM: out[M, K] bf16 from h[M, N] bf16; `partials` holds
+// smallm_partial_floats(M, K, N) floats, `flags` as above.
+hipError_t launch_smallm_down(int M, const void *h, const WeightArg &w, void *out, float *partials,
+                              unsigned long long *flags, int K, int N, hipStream_t stream);
 
 }  // namespace ffn

@@ -55,18 +55,18 @@ bool shape_ok(int rows, int cols)
     return rows > 0 && rows % kSmRows == 0 && cols > 0 && cols % 256 == 0;
 }
 
-template <int NMAT, int OUT, int TG>
+template <int NMAT, int OUT, int TG, bool SPLIT>
 hipError_t launch_tg(const SmallParams &p, int rounds, hipStream_t stream)
 {
     const void *kern = nullptr;
     switch (rounds) {
-    case 1: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 1, TG>); break;
-    case 2: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 2, TG>); break;
-    case 3: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 3, TG>); break;
-    case 4: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 4, TG>); break;
+    case 1: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 1, TG, SPLIT>); break;
+    case 2: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 2, TG, SPLIT>); break;
+    case 3: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 3, TG, SPLIT>); break;
+    case 4: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 4, TG, SPLIT>); break;
     case 5:
         if constexpr (TG == 1 || NMAT == 1) {
-            kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 5, TG>);
+            kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 5, TG, SPLIT>);
             break;
         }
         return hipErrorNotSupported;
@@ -84,15 +84,17 @@ hipError_t launch_tg(const SmallParams &p, int rounds, hipStream_t stream)
 template <int NMAT, int OUT>
 hipError_t launch_t(const SmallParams &p, const SmallPlan &s, hipStream_t stream)
 {
+    const bool split = s.parts > 1;
     switch (s.tg) {
-    case 1: return launch_tg<NMAT, OUT, 1>(p, s.rounds, stream);
-    case 2: return launch_tg<NMAT, OUT, 2>(p, s.rounds, stream);
+    case 1: return split ? launch_tg<NMAT, OUT, 1, true>(p, s.rounds, stream) : launch_tg<NMAT, OUT, 1, false>(p, s.rounds, stream);
+    case 2: return split ? launch_tg<NMAT, OUT, 2, true>(p, s.rounds, stream) : launch_tg<NMAT, OUT, 2, false>(p, s.rounds, stream);
     default: return hipErrorNotSupported;
     }
 }
 
 SmallParams params(int M, const void *in0, const WeightArg &w0, const WeightArg &w1, void *out0, void *out1,
-                   int rows, int cols, const SmallPlan &s)
+                   int rows, int cols, const SmallPlan &s, float *part0, float *part1,
+                   unsigned long long *flags)
 {
     SmallParams p{};
     p.in0 = in0;
@@ -109,6 +111,10 @@ SmallParams params(int M, const void *in0, const WeightArg &w0, const WeightArg 
     p.cols = cols;
     p.parts = s.parts;
     p.groups = s.groups;
+    p.part0 = part0;
+    p.part1 = part1;
+    p.flags = flags;
+    p.tag = s.parts > 1 ? launch_tag() : 0;
     return p;
 }
 
@@ -136,69 +142,48 @@ size_t smallm_dual_partial_floats(int M, int K, int N)
     return s.parts > 1 ? static_cast<size_t>(2) * s.parts * M * N : 0;
 }
 
-hipError_t launch_smallm_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1,
-                              void *out0, void *out1, float *partials, int N, int K, hipStream_t stream)
+size_t smallm_flag_words(int M, int K, int N)
 {
-    if (!smallm_supported(M, K, N))
-        return hipErrorNotSupported;
-    const SmallPlan s = plan(N, K, M, 2);
-    if (s.parts == 1) {
-        const SmallParams p = params(M, x, w0, w1, out0, out1, N, K, s);
-        switch (out) {
-        case OUT_F32_PAIR: return launch_t<2, OUT_F32_PAIR>(p, s, stream);
-        case OUT_H_SILU: return launch_t<2, OUT_H_SILU>(p, s, stream);
-        case OUT_H_GELU: return launch_t<2, OUT_H_GELU>(p, s, stream);
-        default: return hipErrorNotSupported;
-        }
-    }
-    // The reduction in parts: both projections' partial sums, then one pass
-    // that adds them in order and runs the epilogue.
-    if (partials == nullptr)
-        return hipErrorNotSupported;
-    const size_t n = static_cast<size_t>(M) * N;
-    float *gpart = partials;
-    float *upart = partials + static_cast<size_t>(s.parts) * n;
-    const SmallParams p = params(M, x, w0, w1, gpart, upart, N, K, s);
-    hipError_t e = launch_t<2, OUT_PART_PAIR>(p, s, stream);
-    if (e != hipSuccess)
-        return e;
-    const dim3 grid(static_cast<unsigned>((n / 4 + 255) / 256));  // four elements per thread
-    switch (out) {
-    case OUT_F32_PAIR:
-        hipLaunchKernelGGL(smallm_reduce_pair_kernel<OUT_F32_PAIR>, grid, dim3(256), 0, stream, gpart, upart, s.parts,
-                           n, w0.scale2, w1.scale2, out0, static_cast<float *>(out1));
-        break;
-    case OUT_H_SILU:
-        hipLaunchKernelGGL(smallm_reduce_pair_kernel<OUT_H_SILU>, grid, dim3(256), 0, stream, gpart, upart, s.parts, n,
-                           w0.scale2, w1.scale2, out0, static_cast<float *>(nullptr));
-        break;
-    case OUT_H_GELU:
-        hipLaunchKernelGGL(smallm_reduce_pair_kernel<OUT_H_GELU>, grid, dim3(256), 0, stream, gpart, upart, s.parts, n,
-                           w0.scale2, w1.scale2, out0, static_cast<float *>(nullptr));
-        break;
-    default: return hipErrorNotSupported;
-    }
-    return hipGetLastError();
+    const SmallPlan d = plan(N, K, M, 2), w = plan(K, N, M, 1);
+    const int grid = std::max(d.parts > 1 ? d.parts * d.groups : 0, w.parts > 1 ? w.parts * w.groups : 0);
+    return static_cast<size_t>(4) * grid;
 }
 
-hipError_t launch_smallm_down(int M, const void *h, const WeightArg &w, void *out, float *partials, int K, int N,
+hipError_t launch_smallm_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1,
+                              void *out0, void *out1, float *partials, unsigned long long *flags, int N, int K,
                               hipStream_t stream)
 {
     if (!smallm_supported(M, K, N))
         return hipErrorNotSupported;
-    const SmallPlan s = plan(K, N, M, 1);
-    if (s.parts == 1) {
-        const SmallParams p = params(M, h, w, w, out, nullptr, K, N, s);
-        return launch_t<1, OUT_BF16>(p, s, stream);
+    const SmallPlan s = plan(N, K, M, 2);
+    // A reduction split in parts: both projections' pieces, finished by the
+    // last part's workgroup of each tile group.
+    float *gpart = nullptr, *upart = nullptr;
+    if (s.parts > 1) {
+        if (partials == nullptr || flags == nullptr)
+            return hipErrorNotSupported;
+        gpart = partials;
+        upart = partials + static_cast<size_t>(s.parts) * M * N;
     }
-    const SmallParams p = params(M, h, w, w, partials, nullptr, K, N, s);
-    hipError_t e = launch_t<1, OUT_PART_F32>(p, s, stream);
-    if (e != hipSuccess)
-        return e;
-    const size_t n = static_cast<size_t>(M) * K;
-    hipLaunchKernelGGL(smallm_reduce_kernel, dim3(static_cast<unsigned>((n / 4 + 255) / 256)), dim3(256), 0, stream,
-                       partials, s.parts, n, w.scale2, static_cast<uint16_t *>(out));
-    return hipGetLastError();
+    const SmallParams p = params(M, x, w0, w1, out0, out1, N, K, s, gpart, upart, flags);
+    switch (out) {
+    case OUT_F32_PAIR: return launch_t<2, OUT_F32_PAIR>(p, s, stream);
+    case OUT_H_SILU: return launch_t<2, OUT_H_SILU>(p, s, stream);
+    case OUT_H_GELU: return launch_t<2, OUT_H_GELU>(p, s, stream);
+    default: return hipErrorNotSupported;
+    }
+}
+
+hipError_t launch_smallm_down(int M, const void *h, const WeightArg &w, void *out, float *partials,
+                              unsigned long long *flags, int K, int N, hipStream_t stream)
+{
+    if (!smallm_supported(M, K, N))
+        return hipErrorNotSupported;
+    const SmallPlan s = plan(K, N, M, 1);
+    if (s.parts > 1 && (partials == nullptr || flags == nullptr))
+        return hipErrorNotSupported;
+    const SmallParams p = params(M, h, w, w, out, nullptr, K, N, s, partials, partials, flags);
+    return launch_t<1, OUT_BF16>(p, s, stream);
 }
 
 }  // namespace ffn
