@@ -97,11 +97,11 @@ def test_version_strerror_workspace():
     # small-batch arm (9 <= M <= 32, K and N multiples of 256): h, the down
     # projection's partial sums when its reduction is split (N = 17408: 4
     # parts), the dual projection's when its reduction is split (two token
-    # groups at K = 5120: 2 parts), and 4 ready words of 8 bytes per workgroup
+    # groups at K = 5120: 2 parts), and one 8-byte ready word per workgroup
     # of the larger split grid (about one workgroup per compute unit; 256
     # compute units assumed where no device is visible)
     r256 = lambda b: (b + 255) // 256 * 256
-    flags = lambda grid: r256(4 * 8 * grid)
+    flags = lambda grid: r256(8 * grid)
     assert ffn.workspace_bytes(9, 256, 512) == 9 * 512 * 2
     assert ffn.workspace_bytes(16, 5120, 17408) == 16 * 17408 * 2 + 4 * 16 * 5120 * 4 + flags(4 * 64)
     assert ffn.workspace_bytes(17, 5120, 17408) == (r256(17 * 17408 * 2) + 4 * 17 * 5120 * 4

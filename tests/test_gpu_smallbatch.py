@@ -70,20 +70,20 @@ def test_smallbatch_dual_entry(M, K, N, act, seed):
 
 def test_smallbatch_workspace():
     """The small-batch arm keeps h = act(gate) * up and, when a projection's
-    reduction is split, its fp32 partial sums and 4 ready words (8 bytes) per
-    workgroup of the split grid."""
+    reduction is split, its fp32 partial sums and one ready word (8 bytes)
+    per workgroup of the split grid."""
     r256 = lambda b: (b + 255) // 256 * 256
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert ffn.workspace_bytes(9, 256, 512) == r256(9 * 512 * 2)
     # N = 17408: 68 blocks of 256 columns in parts of at most 20: 4 parts,
     # cus / 4 groups of tiles
     assert ffn.workspace_bytes(16, 5120, 17408) == (r256(16 * 17408 * 2) + 4 * 16 * 5120 * 4
-                                                    + r256(4 * 8 * 4 * (cus // 4)))
+                                                    + r256(8 * 4 * (cus // 4)))
     # two token groups: the dual projection's reduction in 2 parts (K = 5120),
     # the down projection's in 4
     assert ffn.workspace_bytes(17, 5120, 17408) == (r256(17 * 17408 * 2) + 4 * 17 * 5120 * 4
                                                     + 2 * 2 * 17 * 17408 * 4
-                                                    + r256(4 * 8 * max(2 * (cus // 2), 4 * (cus // 4))))
+                                                    + r256(8 * max(2 * (cus // 2), 4 * (cus // 4))))
     # M = 33, or K or N not a multiple of 256: the 128-row arm with its
     # partial slots
     assert ffn.workspace_bytes(33, 5120, 17408) > 32 << 20

@@ -96,7 +96,7 @@ struct SmallParams {
     int groups;  // G: workgroups per part
     float *part0;  // P x [M, rows] fp32 pieces of the first projection (split reductions)
     float *part1;  // the same for the second projection
-    unsigned long long *flags;  // 4 ready words per workgroup (split reductions)
+    unsigned long long *flags;  // one ready word per workgroup (split reductions)
     unsigned long long tag;     // this launch's ready value (nonzero)
 };
 
@@ -109,20 +109,20 @@ constexpr int sm_stage_bytes()
     return NMAT * kSmRows * (kSmRound / 2 + kSmRound / 16);
 }
 
-// LDS of the reduction area: [16 waves][NMAT] accumulator sets of 64 lanes x
-// 16 B, then [NMAT][2][256] half sums.
-template <int NMAT>
+// LDS of the reduction area: [TG token groups][16 waves][NMAT] accumulator
+// sets of 64 lanes x 16 B.
+template <int NMAT, int TG>
 constexpr int sm_red_bytes()
 {
-    return kSmWaves * NMAT * 1024 + NMAT * 2 * 256 * 4;
+    return TG * kSmWaves * NMAT * 1024;
 }
 
 // Ring, reduction area (the waves' accumulators and the two half sums), and
 // 1280 bytes that the dummy loads write and nothing reads.
-template <int NMAT>
+template <int NMAT, int TG>
 constexpr int sm_lds_bytes()
 {
-    return kSmStages * sm_stage_bytes<NMAT>() + sm_red_bytes<NMAT>() + 1280;
+    return kSmStages * sm_stage_bytes<NMAT>() + sm_red_bytes<NMAT, TG>() + 1280;
 }
 
 template <int NMAT, int OUT, int NR, int TG, bool SPLIT>
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
     const uint32_t sdword = scale_wave ? 4 * ((lane & 15) ^ (q & 3)) : 0;
     const uint32_t clast = static_cast<uint32_t>(row_codes) - 16;
     const uint32_t slast = static_cast<uint32_t>(row_scales) - 4;
-    constexpr int DUMMY = S * STAGE + sm_red_bytes<NMAT>();  // 1 KB + 256 B never read
+    constexpr int DUMMY = S * STAGE + sm_red_bytes<NMAT, TG>();  // 1 KB + 256 B never read
     auto issue = [&](const uint8_t *cb, const uint8_t *sb, int i, int st) {
         const uint32_t u0 = static_cast<uint32_t>(ua + kSmWaves * i);  // first unit of the round
         FFN_LDS uint8_t *base = lds + st * STAGE;
@@ -287,6 +287,57 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
     const int code_off = (4 * (r >> 3) + (q >> 2)) * 1024 + (r & 7) * 128 +
                          16 * ((2 * (q & 3) + (g >> 1)) ^ ((r >> 1) & 7)) + 8 * (g & 1);
     const int scale_off = CODES + r * 64 + 4 * (q ^ (r >> 2));
+    // Tile tt's sums from the 16 waves' accumulators in the reduction area,
+    // and its epilogue. Thread pair (2 j, 2 j + 1) takes output j = (t, o),
+    // o = 16 m + rr (accumulator m % 4 of lane 16 (m / 4) + rr of every
+    // wave): each thread adds waves 8 h .. 8 h + 7 in order (h = tid % 2),
+    // and the even thread adds the two halves, half 0 first.
+    const FFN_LDS float *redf = reinterpret_cast<const FFN_LDS float *>(red);
+    auto finish_tile = [&](int tt) {
+        const int j = tid >> 1;
+        const int h = tid & 1;
+        if (j >= TG * 256)
+            return;
+        const int t = j >> 8;
+        const int o = j & 255;
+        const int ml = o >> 4;
+        const int rr = o & 15;
+        const int at = (16 * (ml >> 2) + rr) * 4 + (ml & 3);
+        float y[NMAT];
+#pragma unroll
+        for (int f = 0; f < NMAT; ++f) {
+            float a = redf[((t * kSmWaves + 8 * h) * NMAT + f) * 256 + at];
+#pragma unroll
+            for (int w = 1; w < 8; ++w)
+                a += redf[((t * kSmWaves + 8 * h + w) * NMAT + f) * 256 + at];
+            // the partner thread's half (lanes 2 j and 2 j + 1)
+            const float b = __builtin_bit_cast(
+                float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, true));
+            y[f] = a + b;  // in the even thread: half 0 + half 1
+        }
+        const int m = 16 * t + ml;
+        if (h != 0 || m >= M)
+            return;
+        const int row = (ta + tt) * kSmRows + rr;
+        const size_t o_out = static_cast<size_t>(m) * p.rows + row;
+        if constexpr (SPLIT) {
+            // this part's piece, for the last part's workgroup (any XCD)
+            const int po = (part * M * p.rows + static_cast<int>(o_out)) * 4;
+            store_device_coherent(raw_buffer(p.part0, piece_bytes), po, y[0]);
+            if constexpr (NMAT == 2)
+                store_device_coherent(raw_buffer(p.part1, piece_bytes), po, y[1]);
+        } else if constexpr (OUT == OUT_F32_PAIR) {
+            static_cast<float *>(p.out0)[o_out] = y[0] * p.s2_0;
+            static_cast<float *>(p.out1)[o_out] = y[NMAT - 1] * p.s2_1;
+        } else if constexpr (OUT == OUT_H_SILU || OUT == OUT_H_GELU) {
+            constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
+            static_cast<uint16_t *>(p.out0)[o_out] =
+                to_bf16_bits(gate_act<A>(y[0] * p.s2_0) * (y[NMAT - 1] * p.s2_1));
+        } else {
+            static_cast<uint16_t *>(p.out0)[o_out] = to_bf16_bits(y[0] * p.s2_0);
+        }
+    };
+
     int st = 0;  // ring stage of the round being multiplied
     for (int tt = 0; tt < ntiles; ++tt) {
 #pragma unroll
@@ -298,6 +349,9 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
             wait_vmcnt<2 * (S - 2)>();
             lds_barrier();
             issue_next();
+            // the previous tile's partial sums were written before this barrier
+            if (i == 0 && tt > 0)
+                finish_tile(tt - 1);
             if (kSmWaves * i + q < nu) {
                 const FFN_LDS uint8_t *base = lds + st * STAGE;
 #pragma unroll
@@ -321,100 +375,60 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
                 st = 0;
         }
 
-        // Tile done: for each token group, add the 16 waves' accumulators,
-        // waves 0-7 and 8-15 in order by separate threads, then the two
-        // halves (the reduction area is reused group after group).
+        // Tile done: this wave's accumulators to the reduction area, added up
+        // during the next tile's first round (after the loop for the last
+        // tile), so that no extra barrier is needed and the epilogue's stores
+        // have a round to complete. A tile of one round has no barrier between
+        // the previous tile's sums, read in that round, and these writes.
+        if (nrounds == 1)
+            lds_barrier();
 #pragma unroll
-        for (int t = 0; t < TG; ++t) {
+        for (int t = 0; t < TG; ++t)
 #pragma unroll
             for (int f = 0; f < NMAT; ++f) {
-                red[(q * NMAT + f) * 64 + lane] = acc[f][t];
+                red[((t * kSmWaves + q) * NMAT + f) * 64 + lane] = acc[f][t];
                 acc[f][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             }
-            lds_barrier();
-            const FFN_LDS float *redf = reinterpret_cast<const FFN_LDS float *>(red);
-            FFN_LDS float *half = reinterpret_cast<FFN_LDS float *>(red + kSmWaves * NMAT * 64);
-            if (tid < NMAT * 512) {
-                // job (f, h, o): output o = 16 m + rr (accumulator m % 4 of lane
-                // 16 (m / 4) + rr), waves 8 h .. 8 h + 7 of projection f
-                const int o = tid & 255;
-                const int h = (tid >> 8) & 1;
-                const int f = tid >> 9;
-                const int m = o >> 4;
-                const int at = (16 * (m >> 2) + (o & 15)) * 4 + (m & 3);
-                float a = redf[((8 * h) * NMAT + f) * 256 + at];
-#pragma unroll
-                for (int w = 1; w < 8; ++w)
-                    a += redf[((8 * h + w) * NMAT + f) * 256 + at];
-                half[(f * 2 + h) * 256 + o] = a;
-            }
-            lds_barrier();
-            if (tid < 256) {
-                const int m = 16 * t + (tid >> 4);
-                const int rr = tid & 15;
-                float y[NMAT];
-#pragma unroll
-                for (int f = 0; f < NMAT; ++f)
-                    y[f] = half[(f * 2) * 256 + tid] + half[(f * 2 + 1) * 256 + tid];
-                if (m < M) {
-                    const int row = (ta + tt) * kSmRows + rr;
-                    const size_t o = static_cast<size_t>(m) * p.rows + row;
-                    if constexpr (SPLIT) {
-                        // this part's piece, for the last part's workgroup (any XCD)
-                        const int po = (part * M * p.rows + static_cast<int>(o)) * 4;
-                        store_device_coherent(raw_buffer(p.part0, piece_bytes), po, y[0]);
-                        if constexpr (NMAT == 2)
-                            store_device_coherent(raw_buffer(p.part1, piece_bytes), po, y[1]);
-                    } else if constexpr (OUT == OUT_F32_PAIR) {
-                        static_cast<float *>(p.out0)[o] = y[0] * p.s2_0;
-                        static_cast<float *>(p.out1)[o] = y[NMAT - 1] * p.s2_1;
-                    } else if constexpr (OUT == OUT_H_SILU || OUT == OUT_H_GELU) {
-                        constexpr int A = (OUT == OUT_H_SILU) ? ACT_SILU : ACT_GELU_TANH;
-                        static_cast<uint16_t *>(p.out0)[o] =
-                            to_bf16_bits(gate_act<A>(y[0] * p.s2_0) * (y[NMAT - 1] * p.s2_1));
-                    } else {
-                        static_cast<uint16_t *>(p.out0)[o] = to_bf16_bits(y[0] * p.s2_0);
-                    }
-                }
-            }
-        }
     }
+    lds_barrier();
+    finish_tile(ntiles - 1);
 
     if constexpr (SPLIT) {
         // The P workgroups blockIdx.x - part .. + P - 1 hold the parts of the
-        // same tiles; waves 0-3 stored this workgroup's pieces. The lower
-        // parts publish theirs once those stores have completed (nothing else
-        // they issued matters: the ring's trailing loads only fill LDS).
+        // same tiles. Every wave waits for its own piece stores (nothing else
+        // it issued matters: the ring's trailing loads only fill LDS); once
+        // all have, a lower part's workgroup publishes its pieces.
+        wait_vmcnt<0>();
+        __syncthreads();
         if (part != P - 1) {
-            if (q < 4) {
-                wait_vmcnt<0>();
-                __hip_atomic_store(p.flags + 4 * blockIdx.x + q, p.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            if (q == 0)
+                __hip_atomic_store(p.flags + blockIdx.x, p.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return;
         }
-        // The last part's workgroup finishes the tiles. Wave q adds up the
-        // elements that wave q % 4 of every part stored, for the (tile, token
-        // group) items q / 4, q / 4 + 4, ... It waits only for lower-numbered
-        // workgroups, which were dispatched first and wait for nobody.
-        wait_vmcnt<0>();
-        __syncthreads();  // this workgroup's own pieces have been stored
-        const int qw = q & 3;
+        // The last part's workgroup finishes the tiles: thread (q, lane) takes
+        // element (token 16 t + tid2 / 16, row tid2 % 16) with tid2 = 64 (q %
+        // 4) + lane of the (tile, token group) items q / 4, q / 4 + 4, ... It
+        // waits only for lower-numbered workgroups, which were dispatched
+        // first and wait for nobody.
         const int g0 = blockIdx.x - part;
         // (one word at a time: polling all of them at once measured no faster)
         for (int pp = 0; pp < P - 1; ++pp)
-            wait_ready([&](int) { return p.flags + 4 * (g0 + pp) + qw; }, 1, p.tag);
-        __syncthreads();  // every wave has seen its words: clear them
-        if (q < 4)
+            wait_ready([&](int) { return p.flags + g0 + pp; }, 1, p.tag);
+        __syncthreads();  // every wave has seen the words: clear them
+        if (q == 0)
             for (int pp = 0; pp < P - 1; ++pp)
-                __hip_atomic_store(p.flags + 4 * (g0 + pp) + q, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(p.flags + g0 + pp, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-        const int tid2 = 64 * qw + lane;  // the storing thread of these elements
-        const int mo = tid2 >> 4;         // token within its group
+        const int tid2 = 64 * (q & 3) + lane;
+        const int mo = tid2 >> 4;  // token within its group
         const int rr = tid2 & 15;
         const __amdgpu_buffer_rsrc_t rsrc[2] = {raw_buffer(p.part0, piece_bytes),
                                                 raw_buffer(NMAT == 2 ? p.part1 : p.part0, piece_bytes)};
         const int part_bytes = M * p.rows * 4;
         const int items = ntiles * TG;
+        // (Measured and not kept: 8 items per batch, which spills the
+        // two-group kernel's registers, and the last part's own pieces kept in
+        // this XCD's L2 with plain stores and loads: 1-2 us slower each.)
         constexpr int IG = 4;  // items per thread and batch
         constexpr int PC = 4;  // parts per batch (all loads of a batch in flight before its additions)
         for (int k0 = q >> 2; k0 < items; k0 += 4 * IG) {

@@ -26,7 +26,7 @@ size_t smallm_partial_floats(int M, int K, int N);
 size_t smallm_dual_partial_floats(int M, int K, int N);
 
 // 64-bit ready words that a split reduction of either GEMM uses (0 when
-// neither is split): 4 per workgroup, set to a per-launch tag by the
+// neither is split): one per workgroup, set to a per-launch tag by the
 // workgroups of the lower parts and cleared by the one that finishes their
 // tiles, so they need no initialisation; the two GEMMs of a forward may share
 // them (stream-ordered).

@@ -72,7 +72,7 @@ hipError_t launch_tg(const SmallParams &p, int rounds, hipStream_t stream)
         return hipErrorNotSupported;
     default: return hipErrorNotSupported;
     }
-    constexpr int lds = sm_lds_bytes<NMAT>();
+    constexpr int lds = sm_lds_bytes<NMAT, TG>();
     static std::atomic<uint64_t> lds_done[kSmMaxRounds];  // per rounds instantiation
     hipError_t e = allow_lds(kern, lds, lds_done[rounds - 1]);
     if (e != hipSuccess)
@@ -146,7 +146,7 @@ size_t smallm_flag_words(int M, int K, int N)
 {
     const SmallPlan d = plan(N, K, M, 2), w = plan(K, N, M, 1);
     const int grid = std::max(d.parts > 1 ? d.parts * d.groups : 0, w.parts > 1 ? w.parts * w.groups : 0);
-    return static_cast<size_t>(4) * grid;
+    return static_cast<size_t>(grid);
 }
 
 hipError_t launch_smallm_dual(int M, OutKind out, const void *x, const WeightArg &w0, const WeightArg &w1,
