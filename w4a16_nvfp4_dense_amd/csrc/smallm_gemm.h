@@ -125,7 +125,10 @@ constexpr int sm_lds_bytes()
     return kSmStages * sm_stage_bytes<NMAT>() + sm_red_bytes<NMAT, TG>() + 1280;
 }
 
-template <int NMAT, int OUT, int NR, int TG, bool SPLIT>
+// PARTIAL: the batch leaves tokens of its last group empty (M < 16 TG); the
+// reduction then skips their partial sums (a separate instantiation: the
+// per-lane tests cost full groups 0.4-0.6 us per forward).
+template <int NMAT, int OUT, int NR, int TG, bool SPLIT, bool PARTIAL>
 __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallParams p)
 {
     static_assert(NR >= 1 && NR <= kSmMaxRounds, "rounds");
@@ -296,12 +299,13 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
     auto finish_tile = [&](int tt) {
         const int j = tid >> 1;
         const int h = tid & 1;
-        if (j >= TG * 256)
-            return;
         const int t = j >> 8;
         const int o = j & 255;
         const int ml = o >> 4;
         const int rr = o & 15;
+        const int m = 16 * t + ml;
+        if (j >= TG * 256 || (PARTIAL && m >= M))  // (the pair of threads leaves together)
+            return;
         const int at = (16 * (ml >> 2) + rr) * 4 + (ml & 3);
         float y[NMAT];
 #pragma unroll
@@ -315,8 +319,7 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
                 float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, true));
             y[f] = a + b;  // in the even thread: half 0 + half 1
         }
-        const int m = 16 * t + ml;
-        if (h != 0 || m >= M)
+        if (h != 0)
             return;
         const int row = (ta + tt) * kSmRows + rr;
         const size_t o_out = static_cast<size_t>(m) * p.rows + row;
@@ -382,11 +385,14 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
         // the previous tile's sums, read in that round, and these writes.
         if (nrounds == 1)
             lds_barrier();
+        // (a lane's 4 accumulators are tokens 16 t + 4 (lane / 16) .. + 3:
+        // lanes whose tokens all lie past the batch write nothing)
 #pragma unroll
         for (int t = 0; t < TG; ++t)
 #pragma unroll
             for (int f = 0; f < NMAT; ++f) {
-                red[((t * kSmWaves + q) * NMAT + f) * 64 + lane] = acc[f][t];
+                if (!PARTIAL || 16 * t + 4 * (lane >> 4) < M)
+                    red[((t * kSmWaves + q) * NMAT + f) * 64 + lane] = acc[f][t];
                 acc[f][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             }
     }

@@ -55,18 +55,18 @@ bool shape_ok(int rows, int cols)
     return rows > 0 && rows % kSmRows == 0 && cols > 0 && cols % 256 == 0;
 }
 
-template <int NMAT, int OUT, int TG, bool SPLIT>
+template <int NMAT, int OUT, int TG, bool SPLIT, bool PARTIAL>
 hipError_t launch_tg(const SmallParams &p, int rounds, hipStream_t stream)
 {
     const void *kern = nullptr;
     switch (rounds) {
-    case 1: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 1, TG, SPLIT>); break;
-    case 2: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 2, TG, SPLIT>); break;
-    case 3: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 3, TG, SPLIT>); break;
-    case 4: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 4, TG, SPLIT>); break;
+    case 1: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 1, TG, SPLIT, PARTIAL>); break;
+    case 2: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 2, TG, SPLIT, PARTIAL>); break;
+    case 3: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 3, TG, SPLIT, PARTIAL>); break;
+    case 4: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 4, TG, SPLIT, PARTIAL>); break;
     case 5:
         if constexpr (TG == 1 || NMAT == 1) {
-            kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 5, TG, SPLIT>);
+            kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 5, TG, SPLIT, PARTIAL>);
             break;
         }
         return hipErrorNotSupported;
@@ -81,13 +81,20 @@ hipError_t launch_tg(const SmallParams &p, int rounds, hipStream_t stream)
     return hipLaunchKernel(kern, dim3(p.parts * p.groups), dim3(kSmWaves * 64), args, lds, stream);
 }
 
+template <int NMAT, int OUT, int TG, bool SPLIT>
+hipError_t launch_split(const SmallParams &p, int rounds, hipStream_t stream)
+{
+    return p.M < 16 * TG ? launch_tg<NMAT, OUT, TG, SPLIT, true>(p, rounds, stream)
+                         : launch_tg<NMAT, OUT, TG, SPLIT, false>(p, rounds, stream);
+}
+
 template <int NMAT, int OUT>
 hipError_t launch_t(const SmallParams &p, const SmallPlan &s, hipStream_t stream)
 {
     const bool split = s.parts > 1;
     switch (s.tg) {
-    case 1: return split ? launch_tg<NMAT, OUT, 1, true>(p, s.rounds, stream) : launch_tg<NMAT, OUT, 1, false>(p, s.rounds, stream);
-    case 2: return split ? launch_tg<NMAT, OUT, 2, true>(p, s.rounds, stream) : launch_tg<NMAT, OUT, 2, false>(p, s.rounds, stream);
+    case 1: return split ? launch_split<NMAT, OUT, 1, true>(p, s.rounds, stream) : launch_split<NMAT, OUT, 1, false>(p, s.rounds, stream);
+    case 2: return split ? launch_split<NMAT, OUT, 2, true>(p, s.rounds, stream) : launch_split<NMAT, OUT, 2, false>(p, s.rounds, stream);
     default: return hipErrorNotSupported;
     }
 }
