@@ -40,6 +40,12 @@ SMALL_BATCH = [
     (32, 5120, 6144, fi.ACT_GELU_TANH, 66),
     # one token group with the dual projection split (K above 5120)
     (12, 5376, 1024, fi.ACT_SILU, 67),
+    # down projections in more parts than the finishing workgroup loads in
+    # one batch (4): 5 parts (N = 21504) with one and two token groups, and
+    # 13 parts (N = 65536: three full batches and one part)
+    (12, 512, 21504, fi.ACT_GELU_TANH, 69),
+    (20, 256, 21504, fi.ACT_SILU, 70),
+    (9, 256, 65536, fi.ACT_SILU, 71),
 ]
 IDS = [f"m{m}_k{k}_n{n}_a{a}" for m, k, n, a, _ in SMALL_BATCH]
 
