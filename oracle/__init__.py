@@ -109,6 +109,13 @@ class Oracle:
         lib.oracle_w4a4_ffn.restype = _I
         lib.oracle_w4a4_ffn.argtypes = [_P, _I, _I, _I, _I, _P, _P, ctypes.c_float, _P, _P, ctypes.c_float,
                                         _P, _P, ctypes.c_float, _P]
+        lib.oracle_bf16_round_bits.restype = ctypes.c_uint16
+        lib.oracle_bf16_round_bits.argtypes = [ctypes.c_double]
+        lib.oracle_w4a4_down.restype = _I
+        lib.oracle_w4a4_down.argtypes = [_P, _I, _I, _I, _P, _P, ctypes.c_float, _P]
+        lib.oracle_w4a4_ffn_fp4.restype = _I
+        lib.oracle_w4a4_ffn_fp4.argtypes = [_P, _I, _I, _I, _I, _P, _P, ctypes.c_float, _P, _P, ctypes.c_float,
+                                            _P, _P, ctypes.c_float, _P]
         self.lib = lib
         self.path = lib_path
 
@@ -349,6 +356,36 @@ class Oracle:
         return out
 
 
+    def bf16_round_bits(self, v: float) -> int:
+        return int(self.lib.oracle_bf16_round_bits(float(v)))
+
+    def w4a4_down(self, h_bits: np.ndarray, down_mx) -> np.ndarray:
+        """scale2_d * (mx(h) . mx(W_d)) for bf16 h [M, N] (bit patterns) and an
+        MXFP4 down weight [K, N]."""
+        h = _c(h_bits, np.uint16)
+        M, N = h.shape
+        dc, de = _c(down_mx.codes, np.uint8), _c(down_mx.e8m0, np.uint8)
+        K = dc.shape[0]
+        out = np.empty((M, K), dtype=np.float64)
+        rc = self.lib.oracle_w4a4_down(_ptr(h), M, N, K, _ptr(dc), _ptr(de), float(down_mx.scale2), _ptr(out))
+        if rc != 0:
+            raise MemoryError("oracle_w4a4_down")
+        return out
+
+    def w4a4_ffn_fp4(self, case, gate_mx, up_mx, down_mx, rows: Optional[np.ndarray] = None) -> np.ndarray:
+        x = _c(case.x_bits if rows is None else case.x_bits[np.asarray(rows)], np.uint16)
+        M = x.shape[0]
+        gc, ge, uc, ue, dc, de = (_c(t, np.uint8) for t in (gate_mx.codes, gate_mx.e8m0, up_mx.codes, up_mx.e8m0,
+                                                             down_mx.codes, down_mx.e8m0))
+        out = np.empty((M, case.K), dtype=np.float64)
+        rc = self.lib.oracle_w4a4_ffn_fp4(_ptr(x), M, case.K, case.N, int(case.act), _ptr(gc), _ptr(ge),
+                                          float(gate_mx.scale2), _ptr(uc), _ptr(ue), float(up_mx.scale2), _ptr(dc),
+                                          _ptr(de), float(down_mx.scale2), _ptr(out))
+        if rc != 0:
+            raise MemoryError("oracle_w4a4_ffn_fp4")
+        return out
+
+
 _default: Optional[Oracle] = None
 
 
@@ -437,6 +474,14 @@ def w4a4_dual(case, gate_mx, up_mx):
 
 def w4a4_ffn(case, gate_mx, up_mx, rows=None) -> np.ndarray:
     return default().w4a4_ffn(case, gate_mx, up_mx, rows)
+
+
+def w4a4_down(h_bits, down_mx) -> np.ndarray:
+    return default().w4a4_down(h_bits, down_mx)
+
+
+def w4a4_ffn_fp4(case, gate_mx, up_mx, down_mx, rows=None) -> np.ndarray:
+    return default().w4a4_ffn_fp4(case, gate_mx, up_mx, down_mx, rows)
 
 
 def ulp_bf16(v: np.ndarray) -> np.ndarray:

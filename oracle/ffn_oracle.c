@@ -95,6 +95,37 @@ double oracle_bf16_value(uint16_t bits)
     return (double)f;
 }
 
+/* The bf16 nearest to v (ties to even), as its bit pattern: bf16 keeps 8
+ * significant bits of an fp32, so v is rounded once, directly from double,
+ * at the bf16 spacing of its binade (2^-133 below the smallest normal);
+ * magnitudes that round past the largest finite bf16 give infinity. */
+uint16_t oracle_bf16_round_bits(double v)
+{
+    const double mag = fabs(v);
+    double r;
+    if (mag == 0.0) {
+        r = 0.0;
+    } else {
+        int e;
+        frexp(mag, &e); /* mag in [2^(e-1), 2^e) */
+        int q = e - 8;  /* spacing of 8 significant bits */
+        if (q < -133)
+            q = -133;
+        const double scaled = ldexp(mag, -q);
+        double n = floor(scaled);
+        const double frac = scaled - n;
+        if (frac > 0.5 || (frac == 0.5 && fmod(n, 2.0) != 0.0))
+            n += 1.0;
+        r = ldexp(n, q);
+    }
+    const float f = (float)r; /* exact: at most 8 significant bits, or infinity */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if (v < 0.0 || (v == 0.0 && signbit(v)))
+        u |= 0x80000000u;
+    return (uint16_t)(u >> 16);
+}
+
 /* SiLU(g) = g * sigmoid(g) = g / (1 + e^-g). */
 double oracle_silu(double g)
 {
@@ -449,8 +480,9 @@ int oracle_fp8_ffn(const uint16_t *x_bits, int M, int K, int N, int act,
  *   - weights: requantised once from NVFP4, v = e2m1(code) * e4m3(scale)
  *     (exact); scale2 is not folded in: it multiplies the projection's sum;
  *   - products of two MXFP4 values are exact; sums are taken in double.
- * The down projection stays on the W4A16 path (oracle_down). Inputs and
- * scales must be finite. */
+ * The hybrid FFN keeps the down projection on the W4A16 path (oracle_down);
+ * the all-W4A4 FFN rounds h to bf16 and quantises it like the activations
+ * (oracle_w4a4_down). Inputs and scales must be finite. */
 
 double oracle_mx_value(int code, int e8m0)
 {
@@ -565,6 +597,50 @@ int oracle_w4a4_dual(const uint16_t *x_bits, int M, int K, int N, const uint8_t 
     }
     free(xc);
     free(xs);
+    return rc;
+}
+
+/* The down projection on 4 bits: out = scale2_d * (mx(h) . mx(W_d)) for bf16
+ * h [M, N] (quantised as the activations are) and an MXFP4 W_d [K, N]. */
+int oracle_w4a4_down(const uint16_t *h_bits, int M, int N, int K, const uint8_t *d_codes, const uint8_t *d_e8m0,
+                     float d_scale2, double *out)
+{
+    uint8_t *hc = (uint8_t *)malloc((size_t)M * (size_t)(N / 2));
+    uint8_t *hs = (uint8_t *)malloc((size_t)M * (size_t)(N / 32));
+    int rc = -1;
+    if (hc && hs && oracle_mx_quantize_bf16(h_bits, M, N, hc, hs) == 0) {
+        oracle_mx_linear_f64(hc, hs, M, N, d_codes, d_e8m0, K, out);
+        for (size_t i = 0; i < (size_t)M * (size_t)K; ++i)
+            out[i] *= (double)d_scale2;
+        rc = 0;
+    }
+    free(hc);
+    free(hs);
+    return rc;
+}
+
+/* The all-W4A4 FFN: W4A4 gate and up, h = bf16(act(gate) * up) (the down
+ * input is a bf16 tensor, quantised to 4 bits like the activations), then
+ * the down projection on 4 bits. */
+int oracle_w4a4_ffn_fp4(const uint16_t *x_bits, int M, int K, int N, int act, const uint8_t *g_codes,
+                        const uint8_t *g_e8m0, float g_scale2, const uint8_t *u_codes, const uint8_t *u_e8m0,
+                        float u_scale2, const uint8_t *d_codes, const uint8_t *d_e8m0, float d_scale2, double *out)
+{
+    size_t mn = (size_t)M * (size_t)N;
+    double *gate = (double *)malloc(sizeof(double) * mn);
+    double *up = (double *)malloc(sizeof(double) * mn);
+    uint16_t *h = (uint16_t *)malloc(sizeof(uint16_t) * mn);
+    int rc = -1;
+    if (gate && up && h &&
+        oracle_w4a4_dual(x_bits, M, K, N, g_codes, g_e8m0, g_scale2, u_codes, u_e8m0, u_scale2, gate, up) == 0) {
+        oracle_gated_act(act, gate, up, mn, gate);
+        for (size_t i = 0; i < mn; ++i)
+            h[i] = oracle_bf16_round_bits(gate[i]);
+        rc = oracle_w4a4_down(h, M, N, K, d_codes, d_e8m0, d_scale2, out);
+    }
+    free(gate);
+    free(up);
+    free(h);
     return rc;
 }
 

@@ -688,6 +688,89 @@ def pin_w4a4_matches_numpy(orc):
         np.testing.assert_array_equal(orc.w4a4_ffn(case, gm, um, rows=np.array([1])), out[1:2])
 
 
+def _bf16_bits_of_f32(f):
+    """float32 -> bf16 bit patterns, nearest with ties to even (the usual
+    integer form: add 0x7FFF plus the kept lowest bit, truncate), for finite
+    values."""
+    u = np.asarray(f, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def pin_bf16_round(orc):
+    """The oracle's bf16 rounding (h of the all-W4A4 FFN): ties to even at the
+    binade's spacing, signed zero, the subnormal spacing 2^-133, overflow to
+    infinity past halfway above the largest finite bf16; and, on float32
+    inputs (where one rounding from double equals one from float32), the
+    integer rounding of the bit pattern."""
+    r = orc.bf16_round_bits
+    assert r(1.0) == 0x3F80
+    assert r(1.0 + 2.0 ** -8) == 0x3F80          # tie: even (1.0) wins
+    assert r(1.0 + 3 * 2.0 ** -8) == 0x3F82      # tie: even (1 + 2^-6) wins
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -20) == 0x3F81
+    assert r(-2.5) == 0xC020
+    assert r(0.0) == 0x0000 and r(-0.0) == 0x8000
+    assert r(2.0 ** -133) == 0x0001 and r(2.0 ** -134) == 0x0000 and r(0.75 * 2.0 ** -133) == 0x0001
+    big = float(np.uint32(0x7F7F0000).view(np.float32))  # the largest finite bf16, 3.3895e38
+    assert r(big) == 0x7F7F and r(3.38e38) == 0x7F7E      # below the midpoint 3.3829e38 to 0x7F7F
+    assert r(3.4e38) == 0x7F80 and r(-3.4e38) == 0xFF80   # past halfway to 2^128
+    rng = np.random.default_rng(78)
+    f = (rng.normal(size=4000) * np.exp(rng.uniform(-40, 40, size=4000))).astype(np.float32)
+    want = _bf16_bits_of_f32(f)
+    got = np.array([r(float(v)) for v in f], dtype=np.uint16)
+    np.testing.assert_array_equal(got, want)
+
+
+def _random_mx(rng, rows, cols, scale2):
+    codes = rng.integers(0, 256, size=(rows, cols // 2)).astype(np.uint8)
+    e8m0 = rng.integers(120, 131, size=(rows, cols // 32)).astype(np.uint8)
+    return fi.MxWeight(codes, e8m0, scale2)
+
+
+def pin_w4a4_down(orc):
+    """The down projection on 4 bits. h already on each block's MXFP4 grid
+    (largest magnitude 4 or 6 times 2^s): quantising it is the identity, and
+    the result is scale2 times numpy's float64 product of h with the
+    independently decoded MXFP4 weight. General h: the same with h replaced
+    by the quantiser's output (the quantiser is pinned above)."""
+    rng = np.random.default_rng(79)
+    M, N, K = 3, 256, 96
+    w = _random_mx(rng, K, N, 0.625)
+    wd = _mx_decode(w.codes, w.e8m0)
+    hc = rng.integers(0, 16, size=(M, N)).astype(np.uint8)
+    hc[:, ::32] = rng.choice([6, 7, 14, 15], size=(M, N // 32))
+    hs = rng.integers(-8, 8, size=(M, N // 32))
+    hv = _e2m1_table()[hc] * np.repeat(np.ldexp(1.0, hs), 32, axis=1)
+    h_bits = fi.f32_to_bf16_bits(hv.astype(np.float32))
+    assert np.array_equal(fi.bf16_bits_to_f32(h_bits).astype(np.float64), hv)
+    got = orc.w4a4_down(h_bits, w)
+    ref = 0.625 * (hv @ wd.T)
+    assert np.all(np.abs(got - ref) <= 1e-12 * (np.abs(hv) @ np.abs(wd).T))
+    h_bits = fi.f32_to_bf16_bits(rng.normal(size=(M, N)).astype(np.float32))
+    qc, qe = orc.mx_quantize_bf16(h_bits)
+    ha = _mx_decode(qc, qe)
+    got = orc.w4a4_down(h_bits, w)
+    assert np.all(np.abs(got - 0.625 * (ha @ wd.T)) <= 1e-12 * (np.abs(ha) @ np.abs(wd).T))
+
+
+def pin_w4a4_ffn_fp4(orc):
+    """The all-W4A4 FFN, through exact symmetries that a dropped or misplaced
+    term breaks: negating W_d (sign bits of its codes) or W_u negates the
+    output exactly (h = act(gate) * up is odd in up, and bf16 rounding and
+    MXFP4 quantisation keep signs), and doubling scale2_d doubles it; its
+    rows do not depend on the other rows."""
+    for act in (fi.ACT_SILU, fi.ACT_GELU_TANH):
+        case = fi.make_small(3, 256, 512, act=act, seed=80, scale2=0.5)
+        gm, um, dm = orc.mx_requant(case.gate), orc.mx_requant(case.up), orc.mx_requant(case.down)
+        out = orc.w4a4_ffn_fp4(case, gm, um, dm)
+        assert np.isfinite(out).all() and np.abs(out).max() > 0
+        neg = lambda w: fi.MxWeight((w.codes ^ 0x88).astype(np.uint8), w.e8m0, w.scale2)
+        np.testing.assert_array_equal(orc.w4a4_ffn_fp4(case, gm, um, neg(dm)), -out)
+        np.testing.assert_array_equal(orc.w4a4_ffn_fp4(case, gm, neg(um), dm), -out)
+        d2 = fi.MxWeight(dm.codes, dm.e8m0, 2 * dm.scale2)
+        np.testing.assert_array_equal(orc.w4a4_ffn_fp4(case, gm, um, d2), 2 * out)
+        np.testing.assert_array_equal(orc.w4a4_ffn_fp4(case, gm, um, dm, rows=np.array([2])), out[2:3])
+
+
 PINS = [pin_e2m1_table, pin_e4m3_vs_torch, pin_e4m3_anchors_and_order, pin_byte_nibble_order,
         pin_scale_blocks, pin_dequant_independent, pin_activations, pin_gated_act,
         pin_one_hot_selects, pin_down_orientation, pin_ternary_exact_vs_numpy,
@@ -696,7 +779,7 @@ PINS = [pin_e2m1_table, pin_e4m3_vs_torch, pin_e4m3_anchors_and_order, pin_byte_
         pin_quantize_exact_roundtrip, pin_quantize_error_bound, pin_fp8_block_indexing,
         pin_fp8_dequant_vs_torch, pin_fp8_exact_vs_numpy, pin_fp8_fraction_bound, pin_fp8_ffn_composition,
         pin_mx_exponent_rule, pin_mx_quantize_nearest, pin_mx_grid_roundtrip, pin_mx_requant,
-        pin_w4a4_reduces_to_w4a16, pin_w4a4_matches_numpy]
+        pin_w4a4_reduces_to_w4a16, pin_w4a4_matches_numpy, pin_bf16_round, pin_w4a4_down, pin_w4a4_ffn_fp4]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
