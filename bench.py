@@ -65,10 +65,12 @@ QUANT_METRIC = "µs per BF16->NVFP4 weight quantise + achieved HBM GB/s (% of pe
 FP8_WORKLOADS = {"fp8_decode_silu_m1": 1, "fp8_verify_silu_m2": 2, "fp8_verify_silu_m3": 3,
                  "fp8_verify_silu_m8": 8}
 FP8_METRIC = "µs/FFN forward + achieved HBM GB/s (% of peak), block-scaled FP8 SwiGLU"
-# The W4A4 prefill arm (ffn_w4a4_forward: MXFP4 gate/up on FP4 matrix cores,
-# NVFP4 down on the bf16 arm) on the prefill shape; its own line.
-W4A4_WORKLOADS = {"w4a4_prefill_silu_m128": 128}
+# The W4A4 prefill arm on the prefill shape, each its own line: the hybrid
+# (ffn_w4a4_forward: MXFP4 gate/up on FP4 matrix cores, NVFP4 down on the bf16
+# arm) and all three projections on 4 bits (ffn_w4a4_forward_fp4).
+W4A4_WORKLOADS = {"w4a4_prefill_silu_m128": (128, False), "w4a4fp4_prefill_silu_m128": (128, True)}
 W4A4_METRIC = "µs/FFN forward + achieved TFLOP/s, W4A4 (MXFP4 gate/up) prefill SwiGLU"
+W4A4_FP4_METRIC = "µs/FFN forward + achieved TFLOP/s, W4A4 (MXFP4 gate/up/down) prefill SwiGLU"
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 
@@ -301,7 +303,7 @@ def bench_w4a4(args):
     import w4a16_nvfp4_dense_amd as ffn
 
     lib = ffn.load()
-    M = W4A4_WORKLOADS[args.workload]
+    M, fp4 = W4A4_WORKLOADS[args.workload]
     case = fi.make_config(4, M=M)
     K, N, act = case.K, case.N, case.act
     dev = torch.device("cuda:0")
@@ -309,14 +311,16 @@ def bench_w4a4(args):
     copies = []
     for _ in range(args.copies):
         g, u, d = (ffn.DeviceWeight.from_host(w, dev) for w in (case.gate, case.up, case.down))
-        copies.append((ffn.w4a4_prepare_weight(g), ffn.w4a4_prepare_weight(u), d))
+        copies.append((ffn.w4a4_prepare_weight(g), ffn.w4a4_prepare_weight(u),
+                       ffn.w4a4_prepare_weight(d) if fp4 else d))
     torch.cuda.synchronize()
     structs = [(g.struct(), u.struct(), d.struct()) for g, u, d in copies]
     refs = [tuple(ctypes.byref(x) for x in st) for st in structs]
     x = ffn.bf16_from_bits(case.x_bits, dev)
     out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    ws_bytes = ffn.w4a4_workspace_bytes(M, K, N)
+    ws_bytes = ffn.w4a4_fp4_workspace_bytes(M, K, N) if fp4 else ffn.w4a4_workspace_bytes(M, K, N)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    h_in = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     gate_out = torch.empty((M, N), dtype=torch.float32, device=dev)
     up_out = torch.empty((M, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -325,9 +329,16 @@ def bench_w4a4(args):
 
     def step(i):
         g, u, d = refs[i % nc]
-        rc = lib.ffn_w4a4_forward(x.data_ptr(), M, K, N, g, u, d, act, ws.data_ptr(), ws_bytes, out.data_ptr(), sh)
+        fn = lib.ffn_w4a4_forward_fp4 if fp4 else lib.ffn_w4a4_forward
+        rc = fn(x.data_ptr(), M, K, N, g, u, d, act, ws.data_ptr(), ws_bytes, out.data_ptr(), sh)
         if rc:
-            raise ffn.FfnError(rc, "ffn_w4a4_forward")
+            raise ffn.FfnError(rc, "ffn_w4a4_forward_fp4" if fp4 else "ffn_w4a4_forward")
+
+    def down4(i):
+        _, _, d = refs[i % nc]
+        rc = lib.ffn_w4a4_down_gemm(h_in.data_ptr(), M, N, K, d, out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
+        if rc:
+            raise ffn.FfnError(rc, "ffn_w4a4_down_gemm")
 
     def dual(i):
         g, u, _ = refs[i % nc]
@@ -354,6 +365,11 @@ def bench_w4a4(args):
     flops = 2.0 * 3 * M * K * N
     tflops = flops / (us * 1e-6) / 1e12
     dual_us = timed(dual, steps) / steps * 1e3
+    down_us = None
+    if fp4:
+        h_in.copy_(ffn.bf16_from_bits(fi.f32_to_bf16_bits(np.random.default_rng(5).normal(
+            size=(M, N)).astype(np.float32)), dev))
+        down_us = timed(down4, steps) / steps * 1e3
     dual_flops = 2.0 * 2 * M * K * N
     dual_tflops = dual_flops / (dual_us * 1e-6) / 1e12
     # the dual entry's bytes: both MXFP4 weights (codes + E8M0 per 32), x in
@@ -361,20 +377,27 @@ def bench_w4a4(args):
     dual_bytes = 2 * N * K // 2 + 2 * N * K // 32 + 2 * M * K + 8 * M * N
     dual_gbs = dual_bytes / (dual_us * 1e-6) / 1e9
     bound = roofline_bound(dual_flops, dual_bytes, MFMA_FP4_PEAK_TFLOPS)
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic("w4a4_prefill_silu_m128")  # the same dual entry in both workloads
     log(f"[bench] {args.workload}: {us:.2f} us/forward, {tflops:.1f} TFLOP/s; W4A4 dual GEMM (with the activation "
         f"quantisation) {dual_us:.2f} us, {dual_tflops:.1f} TFLOP/s ({100 * dual_tflops / MFMA_FP4_PEAK_TFLOPS:.1f}% "
         f"of the FP4 peak)")
+    if fp4:
+        down_bytes = K * N // 2 + K * N // 32 + 2 * M * N + 2 * M * K
+        log(f"[bench] W4A4 down GEMM entry (with the quantisation of h): {down_us:.2f} us, "
+            f"{2.0 * M * K * N / (down_us * 1e-6) / 1e12:.1f} TFLOP/s, {down_bytes / (down_us * 1e-6) / 1e9:.1f} GB/s")
+    down_desc = "MXFP4 down requantised from NVFP4, h quantised to MXFP4" if fp4 else "NVFP4 down"
     result = {
-        "metric": W4A4_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "us_per_forward": round(us, 3),
+        "metric": W4A4_FP4_METRIC if fp4 else W4A4_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s",
+        "us_per_forward": round(us, 3),
         "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp4 (gate/up), bf16 (down)",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4" if fp4 else "fp4 (gate/up), bf16 (down)",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: gated FFN forward, M={M}, hidden K={K}, intermediate N={N}, "
-                               f"act={fi.ACT_NAMES[act]}, MXFP4 gate/up requantised from NVFP4, NVFP4 down, "
+                               f"act={fi.ACT_NAMES[act]}, MXFP4 gate/up requantised from NVFP4, {down_desc}, "
                                f"rotated over {nc} copies",
                    "M": M, "K": K, "N": N, "act": fi.ACT_NAMES[act], "flops_per_forward": flops},
-        "roofline": {"kernel": "W4A4 dual GEMM entry (ffn_w4a4_dual_gemm: mx_quant_bf16_kernel + w4a4_dual_kernel, "
+        "roofline": {"kernel": "W4A4 dual GEMM entry (ffn_w4a4_dual_gemm: mx_quant_bf16_kernel + w4a4_gemm_kernel, "
                                "fp32 gate and up out)",
                      "bound": bound,
                      "achieved": round(dual_gbs if bound == "hbm" else dual_tflops, 2),
@@ -389,17 +412,21 @@ def bench_w4a4(args):
                      "tflops": round(dual_tflops, 2),
                      "frac_of_fp4_peak": round(dual_tflops / MFMA_FP4_PEAK_TFLOPS, 4)},
     }
+    if fp4:
+        result["down_gemm_us"] = round(down_us, 3)
     if not args.no_cpu_baseline:
         import oracle
         orc = oracle.default()
         gm, um = orc.mx_requant(case.gate), orc.mx_requant(case.up)
+        dm = orc.mx_requant(case.down) if fp4 else None
         rows = np.array([0])
         sub = case.with_x(case.x_bits[rows])
-        orc.w4a4_ffn(sub, gm, um)
+        one = (lambda: orc.w4a4_ffn_fp4(sub, gm, um, dm)) if fp4 else (lambda: orc.w4a4_ffn(sub, gm, um))
+        one()
         n = 0
         t0 = time.perf_counter()
         while True:
-            orc.w4a4_ffn(sub, gm, um)
+            one()
             n += 1
             el = time.perf_counter() - t0
             if el >= args.cpu_seconds:
@@ -408,7 +435,8 @@ def bench_w4a4(args):
         result["cpu_baseline"] = {"value": round(n * row_flops / el / 1e12, 6), "unit": "TFLOP/s",
                                   "us_per_token_row": round(el / n * 1e6, 1), "cores": orc.num_threads(),
                                   "kind": "oracle",
-                                  "sample": f"{n} single-token-row W4A4 forwards of the same weights (fp64 C oracle, "
+                                  "sample": f"{n} single-token-row {'all-4-bit ' if fp4 else ''}W4A4 forwards of the same "
+                                            f"weights (fp64 C oracle, "
                                             f"OpenMP over outputs), {el:.1f} s"}
     print(json.dumps(result), flush=True)
 

@@ -3,10 +3,15 @@
  * matrix cores).
  *
  * The pages run a lossy W4A4 prefill for the dense FFN: 4-bit weights against
- * bf16 activations quantised to 4 bits on every call, for gate and up only;
- * the heavy-tailed down projection stays on the W4A16 path, and each
- * projection's per-tensor scale2 multiplies its products (dense_ffn.rs page,
- * the W4A4 native-FP4 prefill and the NVFP4 W4A4 MMQ arm of forward_prefill).
+ * bf16 activations quantised to 4 bits on every call, each projection's
+ * per-tensor scale2 multiplying its products (dense_ffn.rs page, the W4A4
+ * native-FP4 prefill and the NVFP4 W4A4 MMQ arm of forward_prefill). Two
+ * forms are offered, as the pages describe both:
+ *   - ffn_w4a4_forward: gate and up on 4 bits, the heavy-tailed down
+ *     projection kept on the W4A16 path (the MMQ arm's hybrid);
+ *   - ffn_w4a4_forward_fp4: all three projections on 4 bits, h quantised like
+ *     the activations before the down projection (the native-FP4 prefill,
+ *     which quantises the down input too).
  *
  * gfx950's FP4 matrix instruction (v_mfma_scale_f32_32x32x64_f8f6f4) takes one
  * power-of-two (E8M0) scale per 32 consecutive elements of each operand row,
@@ -86,6 +91,38 @@ int ffn_w4a4_dual_gemm(const void *x, int M, int K, int N, const ffn_mxfp4_weigh
 int ffn_w4a4_forward(const void *x, int M, int K, int N, const ffn_mxfp4_weight *gate,
                      const ffn_mxfp4_weight *up, const ffn_nvfp4_weight *down, int act, void *workspace,
                      size_t workspace_bytes, void *out, hipStream_t stream);
+
+/* Bytes of device workspace ffn_w4a4_down_gemm and ffn_w4a4_forward_fp4 need
+ * for (M, K, N): mx(x), h [M, N] bf16, mx(h), and the down projection's fp32
+ * partial sums and ready words when its reduction is split over the compute
+ * units (about 8 MB at K = 5120; one block of 128 token rows at a time);
+ * each part rounded up to 256 bytes. 0 if M = 0 or the shape is unsupported
+ * (as ffn_w4a4_dual_gemm, and N a multiple of 256). Contents need no
+ * initialisation. */
+size_t ffn_w4a4_fp4_workspace_bytes(int M, int K, int N);
+
+/* W4A4 down GEMM: out[M, K] (bf16) = scale2_d * (mx(h) . mx(W_d)), the
+ * products exact and summed in fp32 (dense_ffn.rs page, the native-FP4
+ * prefill's down projection on the quantised down input).
+ *   h          device, bf16 [M, N], 16-byte aligned
+ *   down       host struct of an MXFP4 weight [K, N]
+ *   out        device, bf16 [M, K], 16-byte aligned
+ *   workspace  device, >= ffn_w4a4_fp4_workspace_bytes(M, K, N) bytes,
+ *              16-byte aligned; clobbered (holds mx(h) and partial sums)
+ * M: 0 .. 65536; K a positive multiple of 256 and N of 256, both at most
+ * 65536 (else FFN_NVFP4_ERR_SHAPE). Calls that share a workspace must not
+ * overlap (one stream). */
+int ffn_w4a4_down_gemm(const void *h, int M, int N, int K, const ffn_mxfp4_weight *down, void *out,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The all-W4A4 FFN: out[M, K] (bf16) = down GEMM of h = bf16(act(gate) * up)
+ * with gate and up from the W4A4 dual GEMM (the h epilogue of
+ * ffn_w4a4_dual_gemm's products) and the down GEMM as ffn_w4a4_down_gemm.
+ * `down` is an MXFP4 weight [K, N] (ffn_w4a4_prepare_weight of the NVFP4
+ * down projection). Shapes and workspace as ffn_w4a4_down_gemm. */
+int ffn_w4a4_forward_fp4(const void *x, int M, int K, int N, const ffn_mxfp4_weight *gate,
+                         const ffn_mxfp4_weight *up, const ffn_mxfp4_weight *down, int act, void *workspace,
+                         size_t workspace_bytes, void *out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

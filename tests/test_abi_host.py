@@ -46,7 +46,8 @@ def test_exports_every_header_symbol():
     assert set(fp8) == {"ffn_fp8_forward", "ffn_fp8_dual_gemv", "ffn_fp8_down_gemv", "ffn_fp8_workspace_bytes"}
     w4 = ffn.header_functions(ffn.W4A4_HEADER_PATH)
     assert set(w4) == {"ffn_w4a4_prepare_weight", "ffn_w4a4_workspace_bytes", "ffn_w4a4_dual_gemm",
-                       "ffn_w4a4_forward"}
+                       "ffn_w4a4_forward", "ffn_w4a4_fp4_workspace_bytes", "ffn_w4a4_down_gemm",
+                       "ffn_w4a4_forward_fp4"}
     diag = ffn.header_functions(ffn.DIAG_HEADER_PATH)
     assert set(diag) == {"ffn_diag_read"}
     for n in list(names) + list(fp8) + list(w4) + list(diag):
@@ -362,6 +363,56 @@ def test_w4a4_validation(call):
     else:
         assert w4dual(go=0) == ffn.ERR_NULL
         assert w4dual(ws=0) == ffn.ERR_NULL
+
+
+def w4fp4(x=FAKE, M=1, K=256, N=256, g=None, u=None, d=None, act=0, ws=FAKE + 0x200000, wsb=1 << 24,
+          out=FAKE + 0x400000):
+    g, u, d = g or MX(), u or MX(), d or MX()
+    return ffn.load().ffn_w4a4_forward_fp4(x, M, K, N, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), act,
+                                           ws, wsb, out, 0)
+
+
+def w4down(h=FAKE, M=1, N=256, K=256, d=None, out=FAKE + 0x400000, ws=FAKE + 0x200000, wsb=1 << 24):
+    d = d or MX()
+    return ffn.load().ffn_w4a4_down_gemm(h, M, N, K, ctypes.byref(d), out, ws, wsb, 0)
+
+
+def test_w4a4_fp4_workspace_bytes():
+    """mx(x), h, mx(h), the down projection's partial sums and ready words:
+    at K = 5120 the reduction is split in 3 parts over 80 row blocks of 64
+    (256 compute units assumed where no device is visible)."""
+    r = lambda b: (b + 255) // 256 * 256
+    M, K, N = 128, 5120, 17408
+    want = (r(M * K // 2) + r(M * K // 32) + r(M * N * 2) + r(M * N // 2) + r(M * N // 32)
+            + r(3 * 128 * K * 4) + r(3 * 80 * 8))
+    assert ffn.w4a4_fp4_workspace_bytes(M, K, N) == want
+    # one 256-column piece: no split, no partial sums
+    assert ffn.w4a4_fp4_workspace_bytes(1, 256, 256) == r(128) + r(8) + r(512) + r(128) + r(8)
+    assert ffn.w4a4_fp4_workspace_bytes(1, 256, 320) == 0   # N must be a multiple of 256 here
+    assert ffn.w4a4_fp4_workspace_bytes(0, 256, 256) == 0
+
+
+@pytest.mark.parametrize("call", [w4fp4, w4down])
+def test_w4a4_fp4_validation(call):
+    wkey = "d" if call is w4down else "g"
+    assert call(**{wkey: MX(codes=0)}) == ffn.ERR_NULL
+    assert call(**{wkey: MX(codes=FAKE + 8)}) == ffn.ERR_ALIGN
+    assert call(**{wkey: MX(scale2=float("inf"))}) == ffn.ERR_SCALE2
+    assert call(d=MX(scales=FAKE + 0x10004)) == ffn.ERR_ALIGN
+    for K, N in ((128, 256), (256, 320), (256, 64), (0, 256), (65792, 256)):
+        assert call(K=K, N=N) == ffn.ERR_SHAPE, (K, N)
+    assert call(M=-1) == ffn.ERR_BATCH
+    assert call(wsb=100) == ffn.ERR_WORKSPACE
+    assert call(ws=0) == ffn.ERR_NULL
+    assert call(out=FAKE + 8) == ffn.ERR_ALIGN
+    if call is w4fp4:
+        assert w4fp4(act=3) == ffn.ERR_ACT
+        assert w4fp4(M=0, x=0) == ffn.OK
+        assert w4fp4(x=0) == ffn.ERR_NULL
+    else:
+        assert w4down(M=0, h=0) == ffn.OK
+        assert w4down(h=0) == ffn.ERR_NULL
+        assert w4down(h=FAKE + 8) == ffn.ERR_ALIGN
 
 
 def test_w4a4_prepare_validation():

@@ -110,6 +110,15 @@ def test_w4a4_checks_weights():
     w = ffn.DeviceWeight(Fake((N, K // 2)), Fake((N, K // 32)), 1.0)
     with pytest.raises(ValueError, match="w.scales"):
         ffn.w4a4_prepare_weight(w)
+    # all three projections on 4 bits: the down weight is MXFP4 [K, N]
+    with pytest.raises(ValueError, match="down"):
+        ffn.w4a4_forward_fp4(x_of(), g, u, mx(N, K), out=Fake((M, K), torch.bfloat16), workspace=Fake((1,)))
+    with pytest.raises(ValueError, match="down"):
+        ffn.w4a4_down_gemm(Fake((M, N), torch.bfloat16), mx(K, N + 32), out=Fake((M, K), torch.bfloat16),
+                           workspace=Fake((1,)))
+    with pytest.raises(ValueError, match="h"):
+        ffn.w4a4_down_gemm(Fake((M, N), torch.float32), mx(K, N), out=Fake((M, K), torch.bfloat16),
+                           workspace=Fake((1,)))
 
 
 def test_fp8_checks_weights():

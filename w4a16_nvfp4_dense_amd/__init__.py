@@ -34,6 +34,9 @@ and the W4A4 prefill arm over MXFP4 operands (``include/ffn_w4a4.h``):
 * :func:`w4a4_dual_gemm`  -- ``ffn_w4a4_dual_gemm``
 * :func:`w4a4_forward`    -- ``ffn_w4a4_forward``
 * :func:`w4a4_workspace_bytes` -- ``ffn_w4a4_workspace_bytes``
+* :func:`w4a4_down_gemm`  -- ``ffn_w4a4_down_gemm`` (the down projection on 4 bits)
+* :func:`w4a4_forward_fp4` -- ``ffn_w4a4_forward_fp4`` (all three projections on 4 bits)
+* :func:`w4a4_fp4_workspace_bytes` -- ``ffn_w4a4_fp4_workspace_bytes``
 """
 from __future__ import annotations
 
@@ -141,6 +144,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ffn_diag_read.argtypes = [ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_size_t), _I, _P, _P]
     lib.ffn_w4a4_forward.restype = _I
     lib.ffn_w4a4_forward.argtypes = [_P, _I, _I, _I, _MP, _MP, _WP, _I, _P, ctypes.c_size_t, _P, _P]
+    lib.ffn_w4a4_fp4_workspace_bytes.restype = ctypes.c_size_t
+    lib.ffn_w4a4_fp4_workspace_bytes.argtypes = [_I, _I, _I]
+    lib.ffn_w4a4_down_gemm.restype = _I
+    lib.ffn_w4a4_down_gemm.argtypes = [_P, _I, _I, _I, _MP, _P, _P, ctypes.c_size_t, _P]
+    lib.ffn_w4a4_forward_fp4.restype = _I
+    lib.ffn_w4a4_forward_fp4.argtypes = [_P, _I, _I, _I, _MP, _MP, _MP, _I, _P, ctypes.c_size_t, _P, _P]
     _lib = lib
     return lib
 
@@ -616,6 +625,62 @@ def w4a4_forward(x, gate: MxDeviceWeight, up: MxDeviceWeight, down: DeviceWeight
                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), out.data_ptr(),
                                  _stream_handle(stream))
     _check(rc, "ffn_w4a4_forward")
+    _record(stream, *fresh)
+    return out
+
+
+def w4a4_fp4_workspace_bytes(M: int, K: int, N: int) -> int:
+    return int(load().ffn_w4a4_fp4_workspace_bytes(int(M), int(K), int(N)))
+
+
+def w4a4_down_gemm(h, down: MxDeviceWeight, out=None, workspace=None, stream=None):
+    """out[M, K] (bf16) = scale2 * (mx(h) . mx(W_d)) for h [M, N] bf16 and an
+    MXFP4 down weight [K, N]."""
+    import torch
+    M, N = h.shape
+    K = down.rows
+    _check_tensor(h, torch.bfloat16, (M, N), "h")
+    _check_mx_weight(down, K, N, "down", h.device)
+    fresh = []
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=h.device)
+        fresh.append(out)
+    _check_tensor(out, torch.bfloat16, (M, K), "out", h.device)
+    if workspace is None:
+        workspace = torch.empty(max(w4a4_fp4_workspace_bytes(M, K, N), 1), dtype=torch.uint8, device=h.device)
+        fresh.append(workspace)
+    d = down.struct()
+    rc = load().ffn_w4a4_down_gemm(h.data_ptr(), M, N, K, ctypes.byref(d), out.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _check(rc, "ffn_w4a4_down_gemm")
+    _record(stream, *fresh)
+    return out
+
+
+def w4a4_forward_fp4(x, gate: MxDeviceWeight, up: MxDeviceWeight, down: MxDeviceWeight, act: int = ACT_SILU,
+                     out=None, workspace=None, stream=None):
+    """out[M, K] (bf16): all three projections on 4 bits (MXFP4 weights and
+    activations, h quantised before the down projection)."""
+    import torch
+    M, K = x.shape
+    N = gate.rows
+    _check_tensor(x, torch.bfloat16, (M, K), "x")
+    _check_mx_weight(gate, N, K, "gate", x.device)
+    _check_mx_weight(up, N, K, "up", x.device)
+    _check_mx_weight(down, K, N, "down", x.device)
+    fresh = []
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
+        fresh.append(out)
+    _check_tensor(out, torch.bfloat16, (M, K), "out", x.device)
+    if workspace is None:
+        workspace = torch.empty(max(w4a4_fp4_workspace_bytes(M, K, N), 1), dtype=torch.uint8, device=x.device)
+        fresh.append(workspace)
+    g, u, d = gate.struct(), up.struct(), down.struct()
+    rc = load().ffn_w4a4_forward_fp4(x.data_ptr(), M, K, N, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                                     int(act), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                     out.data_ptr(), _stream_handle(stream))
+    _check(rc, "ffn_w4a4_forward_fp4")
     _record(stream, *fresh)
     return out
 

@@ -129,4 +129,15 @@ hipError_t launch_mx_requant(const uint8_t *codes, const uint8_t *scales, int ro
 hipError_t launch_w4a4_dual(int M, OutKind out, const uint8_t *xc, const uint8_t *xe, const MxWeightArg &g,
                             const MxWeightArg &u, void *out0, float *out1, int N, int K, hipStream_t stream);
 
+// W4A4 down GEMM for one token group (1 <= M <= 128): out[M, rows] (bf16) =
+// scale2 * (mx(h) . mx(W)) for MXFP4 h [M, cols] and W [rows, cols], cols a
+// multiple of 256. The reduction is split in parts when that fills the
+// device better; `part` then holds w4a4_down_partial_floats(rows, cols)
+// floats and `flags` w4a4_down_flag_words(rows, cols) words (no
+// initialisation needed; calls on one stream may share them).
+size_t w4a4_down_partial_floats(int rows, int cols);
+size_t w4a4_down_flag_words(int rows, int cols);
+hipError_t launch_w4a4_down(int M, const uint8_t *hc, const uint8_t *he, const MxWeightArg &d, uint16_t *out,
+                            int rows, int cols, float *part, unsigned long long *flags, hipStream_t stream);
+
 }  // namespace ffn

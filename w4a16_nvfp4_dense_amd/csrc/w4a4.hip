@@ -1,8 +1,10 @@
 // w4a4.hip -- the W4A4 prefill arm on gfx950's FP4 matrix cores: gate and up
 // from 4-bit weights against activations quantised to 4 bits on every call,
-// the down projection left on the W4A16 arm (dense_ffn.rs page, the W4A4
-// native-FP4 prefill and the NVFP4 W4A4 MMQ arm of forward_prefill, which
-// keeps the heavy-tailed down projection at higher precision).
+// and the down projection either left on the W4A16 arm (the NVFP4 W4A4 MMQ
+// arm of forward_prefill keeps the heavy-tailed down projection at higher
+// precision) or run here too against h quantised to 4 bits (the W4A4
+// native-FP4 prefill quantises the down input and runs all three GEMMs on FP4
+// products) (dense_ffn.rs page, forward_prefill).
 //
 // Scale format. v_mfma_scale_f32_32x32x64_f8f6f4 multiplies E2M1 operands
 // with one E8M0 (power-of-two) scale per 32 consecutive elements of each
@@ -140,6 +142,8 @@ __global__ __launch_bounds__(256) void mx_requant_kernel(const uint8_t *codes, c
     mx_store_block(v, mx_codes + t * (kMxBlock / 2), mx_e8m0 + t);
 }
 
+// N: weight rows (outputs per token), K: reduction length. The down GEMM
+// (DOWN) uses the gate fields for its one weight and out0 for bf16 out.
 struct W4a4Params {
     const uint8_t *xc;  // MXFP4 activations [M, K/2], [M, K/32]
     const uint8_t *xe;
@@ -148,10 +152,14 @@ struct W4a4Params {
     const uint8_t *uc;
     const uint8_t *ue;
     float s2g, s2u;
-    void *out0;  // fp32 gate [M, N], or bf16 h [M, N]
+    void *out0;  // fp32 gate [M, N], or bf16 h [M, N], or (DOWN) bf16 out [M, N]
     float *out1;  // fp32 up [M, N]
     int M, N, K;
     int R;  // weight rows of each projection per workgroup
+    int P;  // DOWN: parts of the reduction (consecutive workgroups of a row block)
+    float *part;                // DOWN, P > 1: P x [M, N] fp32 pieces (unscaled)
+    unsigned long long *flags;  // DOWN, P > 1: one ready word per workgroup
+    unsigned long long tag;     // this launch's ready value (nonzero)
 };
 
 // LDS stage of one 256-column piece for a workgroup with NF weight fragments
@@ -224,8 +232,16 @@ __device__ __forceinline__ float w4_pair_swap(float v)
 // operands in the MFMA layout (ds_read_b128) and runs 4 NF products. Tokens
 // past M re-read row M - 1, B rows past the workgroup's rows re-read its last
 // row, and neither is stored.
-template <int OUT, int NF, int S>
-__global__ __launch_bounds__(kW4Threads) void w4a4_dual_kernel(const W4a4Params p)
+//
+// DOWN: one weight, B row b is row n0 + b of it, and workgroup x takes row
+// block x / P and part x % P of the reduction (256-column pieces q0 .. q1 - 1
+// with q0 = part pieces / P); one token group (M <= 128). With P > 1 the
+// lower parts store their fp32 sums with device-coherent stores and set a
+// ready word; the last part (the highest id of the block, so it waits only
+// for workgroups dispatched before it) adds them in part order and its own
+// sums last, then writes bf16 s2 * sum.
+template <bool DOWN, int OUT, int NF, int S, bool SPLIT>
+__global__ __launch_bounds__(kW4Threads) void w4a4_gemm_kernel(const W4a4Params p)
 {
     using St = W4Stage<NF>;
     constexpr int SB = (NF + 3) / 4;     // B scale loads per wave
@@ -236,12 +252,16 @@ __global__ __launch_bounds__(kW4Threads) void w4a4_dual_kernel(const W4a4Params 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tg0 = blockIdx.y * kW4TokensPerGroup;
-    const int n0 = blockIdx.x * p.R;
+    const int P = DOWN ? p.P : 1;
+    const int rb = DOWN ? static_cast<int>(blockIdx.x) / P : static_cast<int>(blockIdx.x);
+    const int part = DOWN ? static_cast<int>(blockIdx.x) - rb * P : 0;
+    const int n0 = rb * p.R;
     const int nlast = min(n0 + p.R, p.N) - 1;  // last weight row of this workgroup
     const int half = lane >> 5;
     const size_t kc = static_cast<size_t>(p.K) / 2, ke = static_cast<size_t>(p.K) / 32;
-    const int pieces = p.K / 256;
-    auto brow = [&](int b) { return min(n0 + (b >> 1), nlast); };
+    const int q0 = part * (p.K / 256) / P;               // first piece of this part
+    const int pieces = (part + 1) * (p.K / 256) / P - q0;  // >= 1 (P <= K / 256)
+    auto brow = [&](int b) { return DOWN ? min(n0 + b, nlast) : min(n0 + (b >> 1), nlast); };
 
     // Load sources of this lane (piece 0; piece q adds 128 q code bytes, 8 q
     // scale bytes). A codes: loads j = 0..3 cover rows 32 w + 8 j + lane / 8.
@@ -250,25 +270,25 @@ __global__ __launch_bounds__(kW4Threads) void w4a4_dual_kernel(const W4a4Params 
     for (int j = 0; j < 4; ++j) {
         const int R = 32 * wave + 8 * j + (lane >> 3);
         const int tok = min(tg0 + R, p.M - 1);
-        asrc[j] = p.xc + tok * kc + 16 * w4_slot(R, lane & 7);
+        asrc[j] = p.xc + tok * kc + 16 * w4_slot(R, lane & 7) + 128 * q0;
     }
     // B codes: load i covers B rows 8 (NF w + i) + lane / 8.
     const uint8_t *bsrc[NF];
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
         const int b = 8 * (NF * wave + i) + (lane >> 3);
-        bsrc[i] = ((b & 1) ? p.uc : p.gc) + brow(b) * kc + 16 * w4_slot(b, lane & 7);
+        bsrc[i] = ((!DOWN && (b & 1)) ? p.uc : p.gc) + brow(b) * kc + 16 * w4_slot(b, lane & 7) + 128 * q0;
     }
     // Scales: one dword per lane. A: rows 32 w + lane / 2. B: load j takes
     // fragment f = w + 4 j, rows 32 f + lane / 2 (past NF: a dummy load).
     const int atok = min(tg0 + 32 * wave + (lane >> 1), p.M - 1);
-    const uint8_t *assrc = p.xe + atok * ke + 4 * (lane & 1);
+    const uint8_t *assrc = p.xe + atok * ke + 4 * (lane & 1) + 8 * q0;
     const uint8_t *bssrc[SB];
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
         const int f = min(wave + 4 * j, NF - 1);
         const int b = 32 * f + (lane >> 1);
-        bssrc[j] = ((b & 1) ? p.ue : p.ge) + brow(b) * ke + 4 * (lane & 1);
+        bssrc[j] = ((!DOWN && (b & 1)) ? p.ue : p.ge) + brow(b) * ke + 4 * (lane & 1) + 8 * q0;
     }
 
     auto issue = [&](int q, int st) {
@@ -345,6 +365,82 @@ __global__ __launch_bounds__(kW4Threads) void w4a4_dual_kernel(const W4a4Params 
     }
     wait_vmcnt<0>();  // the trailing re-loads land before the workgroup ends
     const int t0 = tg0 + 32 * wave;
+    if constexpr (DOWN) {
+        // accumulator v of fragment f: token t0 + 8 (v / 4) + 4 half + v % 4,
+        // output row n0 + 32 f + br; its offset in an [M, N] array (0, a
+        // valid and unused one, past the rows or the tokens)
+        auto elem = [&](int f, int v) {
+            const int n = n0 + 32 * f + br;
+            const int tok = t0 + 8 * (v / 4) + 4 * half + (v % 4);
+            return (n <= nlast && tok < p.M) ? tok * p.N + n : -1;
+        };
+        if constexpr (SPLIT) {
+            const int part_bytes = p.M * p.N * 4;  // <= 128 x 65536 x 4
+            if (part != P - 1) {
+                const __amdgpu_buffer_rsrc_t rs = raw_buffer(p.part + static_cast<size_t>(part) * p.M * p.N,
+                                                             part_bytes);
+#pragma unroll
+                for (int f = 0; f < NF; ++f)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int e = elem(f, v);
+                        if (e >= 0)
+                            store_device_coherent(rs, 4 * e, acc[f][v]);
+                    }
+                wait_vmcnt<0>();
+                __syncthreads();
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(p.flags + blockIdx.x, p.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                return;
+            }
+            const int g0 = static_cast<int>(blockIdx.x) - part;
+            for (int pp = 0; pp < P - 1; ++pp)
+                wait_ready([&](int) { return p.flags + g0 + pp; }, 1, p.tag);
+            __syncthreads();  // every wave has seen the words: clear them
+            if (threadIdx.x == 0)
+                for (int pp = 0; pp < P - 1; ++pp)
+                    __hip_atomic_store(p.flags + g0 + pp, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            constexpr int PC = 2;  // parts per batch (all loads of a batch in flight before its additions)
+            float sum[NF][16];
+            for (int p0 = 0; p0 < P - 1; p0 += PC) {
+                float v_[PC][NF][16];
+#pragma unroll
+                for (int c = 0; c < PC; ++c) {
+                    if (p0 + c >= P - 1)
+                        continue;
+                    const __amdgpu_buffer_rsrc_t rs =
+                        raw_buffer(p.part + static_cast<size_t>(p0 + c) * p.M * p.N, part_bytes);
+#pragma unroll
+                    for (int f = 0; f < NF; ++f)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            v_[c][f][v] = load_device_coherent_f32(rs, 4 * max(elem(f, v), 0));
+                }
+#pragma unroll
+                for (int c = 0; c < PC; ++c)
+#pragma unroll
+                    for (int f = 0; f < NF; ++f)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            if (p0 + c < P - 1)
+                                sum[f][v] = (p0 + c == 0) ? v_[c][f][v] : sum[f][v] + v_[c][f][v];
+            }
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[f][v] = sum[f][v] + acc[f][v];  // this workgroup's part last
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int e = elem(f, v);
+                if (e >= 0)
+                    static_cast<uint16_t *>(p.out0)[e] = to_bf16_bits(p.s2g * acc[f][v]);
+            }
+        return;
+    }
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
         const int b = 32 * f + br;
@@ -371,13 +467,13 @@ __global__ __launch_bounds__(kW4Threads) void w4a4_dual_kernel(const W4a4Params 
     }
 }
 
-template <int OUT, int NF>
-hipError_t launch_dual_t(const W4a4Params &p, dim3 grid, hipStream_t stream)
+template <bool DOWN, int OUT, int NF, bool SPLIT>
+hipError_t launch_gemm_t(const W4a4Params &p, dim3 grid, hipStream_t stream)
 {
     constexpr int S = w4_stages<NF>();
     constexpr int lds = S * W4Stage<NF>::kBytes + 256;
     static_assert(S >= 2 && lds <= kW4LdsMax, "LDS ring");
-    auto kern = w4a4_dual_kernel<OUT, NF, S>;
+    auto kern = w4a4_gemm_kernel<DOWN, OUT, NF, S, SPLIT>;
     static std::atomic<uint64_t> lds_done{0};
     hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds, lds_done);
     if (e != hipSuccess)
@@ -391,14 +487,29 @@ template <int OUT>
 hipError_t launch_dual_nf(const W4a4Params &p, int nf, dim3 grid, hipStream_t stream)
 {
     switch (nf) {
-    case 1: return launch_dual_t<OUT, 1>(p, grid, stream);
-    case 2: return launch_dual_t<OUT, 2>(p, grid, stream);
-    case 3: return launch_dual_t<OUT, 3>(p, grid, stream);
-    case 4: return launch_dual_t<OUT, 4>(p, grid, stream);
-    case 5: return launch_dual_t<OUT, 5>(p, grid, stream);
-    case 6: return launch_dual_t<OUT, 6>(p, grid, stream);
+    case 1: return launch_gemm_t<false, OUT, 1, false>(p, grid, stream);
+    case 2: return launch_gemm_t<false, OUT, 2, false>(p, grid, stream);
+    case 3: return launch_gemm_t<false, OUT, 3, false>(p, grid, stream);
+    case 4: return launch_gemm_t<false, OUT, 4, false>(p, grid, stream);
+    case 5: return launch_gemm_t<false, OUT, 5, false>(p, grid, stream);
+    case 6: return launch_gemm_t<false, OUT, 6, false>(p, grid, stream);
     default: return hipErrorNotSupported;
     }
+}
+
+// Down GEMM split: row blocks of kW4DownRows rows, and as many parts of the
+// reduction as fill about one workgroup per compute unit (at most
+// kW4MaxParts, at most one per 256-column piece).
+constexpr int kW4DownFrags = 2;
+constexpr int kW4DownRows = 32 * kW4DownFrags;
+constexpr int kW4MaxParts = 8;
+
+int w4_down_parts(int rows, int cols)
+{
+    const int blocks = (rows + kW4DownRows - 1) / kW4DownRows;
+    int P = device_cu_count() / blocks;
+    P = P < 1 ? 1 : (P > kW4MaxParts ? kW4MaxParts : P);
+    return P > cols / 256 ? cols / 256 : P;
 }
 
 }  // namespace
@@ -439,7 +550,8 @@ hipError_t launch_w4a4_dual(int M, OutKind out, const uint8_t *xc, const uint8_t
     int R = (N + cus - 1) / cus;
     R = R < 16 ? 16 : (R > 16 * kW4MaxFrags ? 16 * kW4MaxFrags : R);
     const int nf = (R + 15) / 16;
-    W4a4Params p{xc, xe, g.codes, g.e8m0, u.codes, u.e8m0, g.scale2, u.scale2, out0, out1, M, N, K, R};
+    W4a4Params p{xc, xe, g.codes, g.e8m0, u.codes, u.e8m0, g.scale2, u.scale2, out0, out1, M, N, K, R, 1, nullptr,
+                 nullptr, 0};
     const dim3 grid((N + R - 1) / R, (M + kW4TokensPerGroup - 1) / kW4TokensPerGroup);
     switch (out) {
     case OUT_F32_PAIR: return launch_dual_nf<OUT_F32_PAIR>(p, nf, grid, stream);
@@ -447,6 +559,33 @@ hipError_t launch_w4a4_dual(int M, OutKind out, const uint8_t *xc, const uint8_t
     case OUT_H_GELU: return launch_dual_nf<OUT_H_GELU>(p, nf, grid, stream);
     default: return hipErrorNotSupported;
     }
+}
+
+size_t w4a4_down_partial_floats(int rows, int cols)
+{
+    const int P = w4_down_parts(rows, cols);
+    return P > 1 ? static_cast<size_t>(P) * kW4TokensPerGroup * rows : 0;
+}
+
+size_t w4a4_down_flag_words(int rows, int cols)
+{
+    const int P = w4_down_parts(rows, cols);
+    return P > 1 ? static_cast<size_t>(P) * ((rows + kW4DownRows - 1) / kW4DownRows) : 0;
+}
+
+hipError_t launch_w4a4_down(int M, const uint8_t *hc, const uint8_t *he, const MxWeightArg &d, uint16_t *out,
+                            int rows, int cols, float *part, unsigned long long *flags, hipStream_t stream)
+{
+    if (M < 1 || M > kW4TokensPerGroup || rows < 1 || cols < 256 || cols % 256 != 0)
+        return hipErrorNotSupported;
+    const int P = w4_down_parts(rows, cols);
+    if (P > 1 && (part == nullptr || flags == nullptr))
+        return hipErrorNotSupported;
+    W4a4Params p{hc, he, d.codes, d.e8m0, nullptr, nullptr, d.scale2, 0.0f, out, nullptr, M, rows, cols,
+                 kW4DownRows, P, part, flags, P > 1 ? launch_tag() : 0};
+    const dim3 grid(((rows + kW4DownRows - 1) / kW4DownRows) * P, 1);
+    return P > 1 ? launch_gemm_t<true, OUT_BF16, kW4DownFrags, true>(p, grid, stream)
+                 : launch_gemm_t<true, OUT_BF16, kW4DownFrags, false>(p, grid, stream);
 }
 
 }  // namespace ffn
