@@ -426,3 +426,21 @@ def test_w4a4_prepare_validation():
     assert call(rows=0) == ffn.ERR_SHAPE
     assert call(mc=FAKE + 0x200008) == ffn.ERR_ALIGN
     assert call(wt=W(scales=FAKE + 0x10001)) == ffn.ERR_ALIGN
+
+
+def test_traffic_summaries_match_sources():
+    """Every committed HBM-counter summary names the kernel sources it was
+    measured on by digest; bench.py reports its traffic only while they
+    match. A source change that leaves the kernel's instructions unchanged
+    must re-stamp the digest (after checking the assembly), any other must
+    re-take the counters: either way this keeps the reported traffic alive."""
+    import glob
+    import json
+    import os
+    from w4a16_nvfp4_dense_amd import profiling
+    files = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                          "profiles", "traffic_*.json")))
+    assert files
+    for f in files:
+        t = json.load(open(f))
+        assert t["source_digest"] == profiling.source_digest(t.get("source_files")), os.path.basename(f)
