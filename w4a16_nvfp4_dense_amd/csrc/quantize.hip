@@ -23,11 +23,16 @@
 //   quantize_absmax_kernel: per-workgroup maxima of |w| (taken on the bf16 bit
 //                    patterns: for finite values the magnitude order is the
 //                    unsigned order of the low 15 bits), written to the
-//                    workspace, with the same traversal as the quantise pass;
-//   quantize_kernel: every workgroup reduces those maxima (a few KB from L2),
-//                    then each thread encodes one 16-element block at a time:
-//                    32 bytes in (two 16-byte loads), 8 code bytes and 1 scale
-//                    byte out, so a wave reads 2 KB and writes 512 + 64 bytes
+//                    workspace; two workgroups per compute unit, each thread
+//                    with four 16-element blocks (eight 16-byte loads) in
+//                    flight per step;
+//   quantize_kernel: every workgroup reduces those maxima (2 KB from L2, one
+//                    per absmax workgroup; fewer of them shorten this prologue
+//                    that delays every workgroup's stream), then each thread
+//                    encodes one 16-element block at a time: 32 bytes in (two
+//                    16-byte loads, issued one block ahead so the first ones
+//                    overlap the prologue), 8 code bytes and 1 scale byte out,
+//                    so a wave reads 2 KB and writes 512 + 64 bytes
 //                    contiguously.
 #include <hip/hip_runtime.h>
 
@@ -42,6 +47,8 @@ namespace ffn {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kAbsmaxInFlight = 4;  // 16-element blocks per thread and step of the absmax pass
+constexpr int kAbsmaxGroupsPerCu = 2;
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits)
 {
@@ -96,16 +103,22 @@ __global__ __launch_bounds__(kThreads) void quantize_absmax_kernel(const u32x4_t
 {
     __shared__ uint32_t sh[kThreads / 64];
     uint32_t m = 0;
-    // the quantise pass's traversal: one 16-element block (32 bytes) per thread and step
-    for (size_t b = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; b < nblocks;
-         b += static_cast<size_t>(gridDim.x) * kThreads) {
-        const u32x4_t v0 = w[2 * b];
-        const u32x4_t v1 = w[2 * b + 1];
+    const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
+    for (size_t b0 = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; b0 < nblocks;
+         b0 += kAbsmaxInFlight * stride) {
+        u32x4_t v[2 * kAbsmaxInFlight];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            m = max(m, max(v0[q] & 0x7FFFu, (v0[q] >> 16) & 0x7FFFu));
-            m = max(m, max(v1[q] & 0x7FFFu, (v1[q] >> 16) & 0x7FFFu));
+        for (int k = 0; k < kAbsmaxInFlight; ++k) {
+            // past the end, block b0 again (the maximum is unchanged by a repeat)
+            const size_t b = b0 + k * stride < nblocks ? b0 + k * stride : b0;
+            v[2 * k] = w[2 * b];
+            v[2 * k + 1] = w[2 * b + 1];
         }
+#pragma unroll
+        for (int k = 0; k < 2 * kAbsmaxInFlight; ++k)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                m = max(m, max(v[k][q] & 0x7FFFu, (v[k][q] >> 16) & 0x7FFFu));
     }
     m = workgroup_max(m, sh);
     if (threadIdx.x == 0)
@@ -117,6 +130,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t *w, si
                                                             float *scale2_out)
 {
     __shared__ uint32_t sh[kThreads / 64];
+    const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
+    size_t b = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+    u32x4_t n0 = {0u, 0u, 0u, 0u}, n1 = {0u, 0u, 0u, 0u};  // the next block's 32 bytes
+    if (b < nblocks) {
+        n0 = w[2 * b];
+        n1 = w[2 * b + 1];
+    }
     uint32_t m = 0;
     for (int i = threadIdx.x; i < npartial; i += kThreads)
         m = max(m, partial[i]);
@@ -126,10 +146,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t *w, si
     if (blockIdx.x == 0 && threadIdx.x == 0)
         *scale2_out = amax == 0.0f ? 0.0f : scale2;
     const float d = scale2 * 6.0f;
-    for (size_t b = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; b < nblocks;
-         b += static_cast<size_t>(gridDim.x) * kThreads) {
-        const u32x4_t v0 = w[2 * b];
-        const u32x4_t v1 = w[2 * b + 1];
+    for (; b < nblocks; b += stride) {
+        const u32x4_t v0 = n0;
+        const u32x4_t v1 = n1;
+        if (b + stride < nblocks) {
+            n0 = w[2 * (b + stride)];
+            n1 = w[2 * (b + stride) + 1];
+        }
         uint32_t bits[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -165,13 +188,22 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t *w, si
 
 namespace {
 
-// Workgroups of either pass: a few per compute unit (each quantise workgroup
-// first re-reduces the absmax pass's per-workgroup maxima), at most
+// Workgroups of the quantise pass: a few per compute unit, at most
 // kQuantizeMaxPartials.
 int quantize_blocks(size_t nblocks)
 {
     const size_t want = (nblocks + kThreads - 1) / kThreads;
     const size_t cap = std::min<size_t>(kQuantizeMaxPartials, static_cast<size_t>(device_cu_count()) * 8);
+    return static_cast<int>(std::max<size_t>(1, std::min(want, cap)));
+}
+
+// Workgroups of the absmax pass, one partial maximum each: kAbsmaxGroupsPerCu
+// per compute unit, at most kQuantizeMaxPartials.
+int absmax_blocks(size_t nblocks)
+{
+    const size_t want = (nblocks + kThreads - 1) / kThreads;
+    const size_t cap =
+        std::min<size_t>(kQuantizeMaxPartials, static_cast<size_t>(device_cu_count()) * kAbsmaxGroupsPerCu);
     return static_cast<int>(std::max<size_t>(1, std::min(want, cap)));
 }
 
@@ -181,14 +213,15 @@ hipError_t launch_quantize(const void *w, int rows, int cols, uint8_t *codes, ui
                            uint32_t *partial, hipStream_t stream)
 {
     const size_t nblocks = static_cast<size_t>(rows) * static_cast<size_t>(cols) / 16;  // 16-element blocks
+    const int ga = absmax_blocks(nblocks);
     const int g = quantize_blocks(nblocks);
-    hipLaunchKernelGGL(quantize_absmax_kernel, dim3(g), dim3(kThreads), 0, stream, static_cast<const u32x4_t *>(w),
+    hipLaunchKernelGGL(quantize_absmax_kernel, dim3(ga), dim3(kThreads), 0, stream, static_cast<const u32x4_t *>(w),
                        nblocks, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(quantize_kernel, dim3(g), dim3(kThreads), 0, stream, static_cast<const u32x4_t *>(w), nblocks,
-                       partial, g, reinterpret_cast<uint2 *>(codes), scales, scale2);
+                       partial, ga, reinterpret_cast<uint2 *>(codes), scales, scale2);
     return hipGetLastError();
 }
 
