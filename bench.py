@@ -45,17 +45,19 @@ WORKLOADS = {
     "verify_silu_m7": (3, 7),
     "verify_silu_m8": (3, 8),
     "prefill_silu_m128": (4, 128),
-    # small batches (9 <= M <= 32) on the prefill shapes: the small-batch arm
+    # small batches (9 <= M <= 40) on the prefill shapes: the small-batch arm
     "smallbatch_silu_m9": (4, 9),
     "smallbatch_silu_m16": (4, 16),
     "smallbatch_silu_m17": (4, 17),
     "smallbatch_silu_m32": (4, 32),
-    # 33 <= M <= 64: the 128-row matrix-core arm (one or two token tiles)
+    "smallbatch_silu_m33": (4, 33),
+    "smallbatch_silu_m40": (4, 40),
+    # 41 <= M <= 64: the 128-row matrix-core arm (one or two token tiles)
     "smallbatch_silu_m48": (4, 48),
     "smallbatch_silu_m64": (4, 64),
     "prefill_silu_m96": (4, 96),
 }
-SMALL_BATCH_MAX_M = 32  # above this the forward runs the 128-row matrix-core arm
+SMALL_BATCH_MAX_M = 40  # above this the forward runs the 128-row matrix-core arm
 # The BF16 -> NVFP4 quantiser (ffn_nvfp4_quantize) on one weight of the decode
 # gate/up shape; timed like the forward, reported on its own line.
 QUANT_WORKLOADS = {"quantize_17408x5120": (17408, 5120)}

@@ -98,11 +98,12 @@ typedef struct ffn_nvfp4_weight {
  *                    with fp32 accumulation). They need K and N in multiples
  *                    of 64 (else ERR_SHAPE) and scales 8-byte aligned (else
  *                    ERR_ALIGN).
- *     9 <= M <= 32, K and N multiples of 256: the small-batch arm, weights
+ *     9 <= M <= 40, K and N multiples of 256: the small-batch arm, weights
  *                    read and dequantised once for all rows (one token group
- *                    of 16 rows up to M = 16, two above); its reductions are
- *                    split in parts where a wave's activations do not fit its
- *                    registers, finished inside the same launch;
+ *                    of 16 rows up to M = 16, two up to 32, three above); its
+ *                    reductions are split in parts where a wave's
+ *                    activations do not fit its registers, finished inside
+ *                    the same launch;
  *     otherwise      the 128-row arm, in blocks of 128 token rows, each block
  *                    reading the weights once.
  * Other M: ERR_BATCH. K and N: positive multiples of 32, at most 65536. */

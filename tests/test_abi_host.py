@@ -95,7 +95,7 @@ def test_version_strerror_workspace():
     assert ffn.workspace_bytes(8, 5120, 17408) == 8 * 17408 * 2
     assert ffn.workspace_bytes(0, 256, 512) == 0
     assert ffn.workspace_bytes(1, 250, 512) == 0
-    # small-batch arm (9 <= M <= 32, K and N multiples of 256): h, the down
+    # small-batch arm (9 <= M <= 40, K and N multiples of 256): h, the down
     # projection's partial sums when its reduction is split (N = 17408: 4
     # parts), the dual projection's when its reduction is split (two token
     # groups at K = 5120: 2 parts), and one 8-byte ready word per workgroup
@@ -110,10 +110,16 @@ def test_version_strerror_workspace():
     assert ffn.workspace_bytes(32, 4096, 8192) == r256(32 * 8192 * 2) + 2 * 32 * 4096 * 4 + flags(2 * 128)
     # dual reduction in 2 parts over 32 row tiles (512 rows): a grid of 64
     assert ffn.workspace_bytes(16, 5376, 512) == r256(16 * 512 * 2) + 2 * 2 * 16 * 512 * 4 + flags(2 * 32)
-    # 128-row matrix-core arm (M > 32, or K or N not a multiple of 256): h for
+    # three token groups (33 <= M <= 40): the dual reduction in parts of at
+    # most 2 rounds (K = 5120: 3 parts, 256 // 3 = 85 tile groups), the down
+    # reduction in parts of at most 3 (N = 17408: 6 parts, 42 groups)
+    assert ffn.workspace_bytes(33, 5120, 17408) == (r256(33 * 17408 * 2) + 6 * 33 * 5120 * 4
+                                                    + 2 * 3 * 33 * 17408 * 4 + flags(max(3 * 85, 6 * 42)))
+    assert ffn.workspace_bytes(40, 256, 512) == 40 * 512 * 2
+    # 128-row matrix-core arm (M > 40, or K or N not a multiple of 256): h for
     # one block of 128 rows and the partial slots
-    ws33 = ffn.workspace_bytes(33, 256, 512)
-    assert ws33 > 33 * 512 * 2 and ws33 % 256 == 0
+    ws41 = ffn.workspace_bytes(41, 256, 512)
+    assert ws41 > 41 * 512 * 2 and ws41 % 256 == 0 and ws41 > 32 << 20
     assert ffn.workspace_bytes(16, 640, 1024) > 32 << 20
     assert ffn.workspace_bytes(128, 5120, 17408) == ffn.workspace_bytes(4096, 5120, 17408)
     assert ffn.workspace_bytes(128, 5120, 17408) >= 128 * 17408 * 2

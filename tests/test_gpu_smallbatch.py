@@ -1,4 +1,4 @@
-"""GPU parity of the small-batch matrix-core arm (9 <= M <= 32 token rows,
+"""GPU parity of the small-batch matrix-core arm (9 <= M <= 40 token rows,
 K and N multiples of 256) against the CPU oracle, with the
 bounds of the other arms: |out - out_ref| <= 1e-2 rms(out_ref) + 1 bf16 ulp(out_ref); the dual
 entry's fp32 gate/up within 1e-4 rms(ref) + 1e-6 |ref|.
@@ -46,6 +46,18 @@ SMALL_BATCH = [
     (12, 512, 21504, fi.ACT_GELU_TANH, 69),
     (20, 256, 21504, fi.ACT_SILU, 70),
     (9, 256, 65536, fi.ACT_SILU, 71),
+    # three token groups (33 <= M <= 40): one row of the third group to a
+    # full batch; the dual projection in one part (2 rounds, its most),
+    # two (K = 4096) and three (K = 5120, the activation epilogue after the
+    # parts); the down projection in one part (3 rounds, its most), three
+    # (N = 8192), seven (N = 21504) and 22 (N = 65536) parts
+    (33, 256, 512, fi.ACT_SILU, 81),
+    (40, 1280, 2048, fi.ACT_GELU_TANH, 82),
+    (36, 5120, 2048, fi.ACT_SILU, 83),
+    (40, 4096, 8192, fi.ACT_GELU_TANH, 84),
+    (34, 2048, 3072, fi.ACT_SILU, 85),
+    (39, 256, 21504, fi.ACT_GELU_TANH, 86),
+    (35, 256, 65536, fi.ACT_SILU, 87),
 ]
 IDS = [f"m{m}_k{k}_n{n}_a{a}" for m, k, n, a, _ in SMALL_BATCH]
 
@@ -90,9 +102,14 @@ def test_smallbatch_workspace():
     assert ffn.workspace_bytes(17, 5120, 17408) == (r256(17 * 17408 * 2) + 4 * 17 * 5120 * 4
                                                     + 2 * 2 * 17 * 17408 * 4
                                                     + r256(8 * max(2 * (cus // 2), 4 * (cus // 4))))
-    # M = 33, or K or N not a multiple of 256: the 128-row arm with its
+    # three token groups: the dual projection's reduction in 3 parts
+    # (K = 5120), the down projection's in 6
+    assert ffn.workspace_bytes(40, 5120, 17408) == (r256(40 * 17408 * 2) + 6 * 40 * 5120 * 4
+                                                    + 2 * 3 * 40 * 17408 * 4
+                                                    + r256(8 * max(3 * (cus // 3), 6 * (cus // 6))))
+    # M = 41, or K or N not a multiple of 256: the 128-row arm with its
     # partial slots
-    assert ffn.workspace_bytes(33, 5120, 17408) > 32 << 20
+    assert ffn.workspace_bytes(41, 5120, 17408) > 32 << 20
     assert ffn.workspace_bytes(16, 640, 1024) > 32 << 20
 
 
@@ -130,10 +147,21 @@ def test_smallbatch_two_groups_rows_independent():
         assert torch.equal(part, full[lo:hi]), (lo, hi)
 
 
-@pytest.mark.parametrize("M", [9, 16, 17, 32, 48, 64])
+def test_smallbatch_three_groups_rows_independent():
+    """The same for three token groups (33 to 40 rows), with both
+    reductions split in parts (K = 5120: 3 parts; N = 8192: 3 parts)."""
+    case = fi.make_small(40, 5120, 8192, act=fi.ACT_GELU_TANH, seed=88)
+    L = loaded(case.name, lambda: case)
+    full = L.forward()
+    for lo, hi in ((0, 33), (7, 40), (3, 38), (1, 35)):
+        part = L.forward(L.x[lo:hi].contiguous())
+        assert torch.equal(part, full[lo:hi]), (lo, hi)
+
+
+@pytest.mark.parametrize("M", [9, 16, 17, 32, 33, 40, 48, 64])
 def test_config_smallbatch(M):
     """The prefill shapes (hidden 5120, intermediate 17408, SiLU) at 9 to 64
-    token rows (above 32 the 128-row arm, with one or two token tiles), the
+    token rows (above 40 the 128-row arm, with one or two token tiles), the
     launch configuration the bench times: the forward and the dual entry
     against the oracle on every token row."""
     case = fi.make_config(4, M=M)

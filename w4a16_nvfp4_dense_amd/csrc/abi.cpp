@@ -76,7 +76,7 @@ struct PrefillLayout {
     size_t h, partials, total;
 };
 
-// Batches of 9 to 32 rows take the small-batch arm when it covers the shape;
+// Batches of 9 to 40 rows take the small-batch arm when it covers the shape;
 // its workspace is h, the down projection's partial sums and, when the dual
 // projection's reduction is split in parts, its partial sums, then the ready
 // words of the split reductions.

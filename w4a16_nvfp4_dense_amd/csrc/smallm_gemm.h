@@ -1,5 +1,5 @@
 // smallm_gemm.h -- the small-batch matrix-core arm of the NVFP4 gated FFN
-// (9 <= M <= 32 token rows): the dual gate+up projection and the down
+// (9 <= M <= 40 token rows): the dual gate+up projection and the down
 // projection as skinny GEMMs on bf16 matrix cores, for the batch sizes between
 // the batched GEMV and the 128-row prefill tiles (dense_ffn.rs page, the
 // prefill GEMM dispatch by token count, whose small-M tiles exist because
@@ -16,9 +16,12 @@
 // accumulators through LDS in a fixed order (waves 0-7 and 8-15 in wave
 // order, then the two halves). At M <= 16 this MFMA shape reads each
 // weight once per 16 cycles, twice the rate of the 32x32x16 shape. Batches
-// of 17 to 32 rows run two token groups of 16 (TG = 2): each dequantised
-// weight fragment feeds the products of both, so a weight is still read and
-// dequantised once.
+// of 17 to 32 rows run two token groups of 16 (TG = 2), and 33 to 40 rows
+// three (TG = 3): each dequantised weight fragment feeds the products of every
+// group, so a weight is still read and dequantised once. (Above 40 rows the
+// 128-row arm is as fast: measured at 48 rows, 89.7 us with three groups
+// against 89.0 us there, while 33 and 40 rows take 81.1 and 84.8 us against
+// 88.3 us.)
 //
 // Dequantisation. As in the prefill arm: FP4 pair -> fp32 pair (unit-scale
 // hardware conversion) times the E4M3 block scale, rounded to bf16, which is
@@ -46,8 +49,8 @@
 //
 // Work split. Workgroup w takes part w % P of the reduction (P consecutive
 // ranges of 256-column blocks, each at most as many rounds as a wave's
-// activations fit in registers: 5 rounds, 4 for the dual GEMM with two token
-// groups) and
+// activations fit in registers: 5 rounds; with two token groups 4 for the
+// dual GEMM; with three, 2 for the dual GEMM and 3 for the down GEMM) and
 // tiles [g T / G, (g + 1) T / G) with g = w / P, T tiles and G = gridDim / P
 // groups. With P = 1 the epilogue writes finished outputs. With P > 1
 // (SPLIT) every workgroup stores its part's fp32 sums of its tiles with
@@ -75,9 +78,9 @@ constexpr int kSmRows = 16;                   // weight rows per tile
 constexpr int kSmUnit = 64;                   // reduction columns per wave and round
 constexpr int kSmRound = kSmWaves * kSmUnit;  // reduction columns per round
 constexpr int kSmMaxRounds = 5;               // rounds per tile and part (activations kept in registers)
-constexpr int kSmStages = 3;
-constexpr int kSmMaxGroups = 2;               // token groups of 16 (M <= 32)
-constexpr int kSmMaxRoundsTwoGroups = 4;      // rounds per tile and part of the dual GEMM with two token groups                  // LDS ring stages (deeper measured slower: the arm is bound by its arithmetic, not by load latency)
+constexpr int kSmStages = 3;                  // LDS ring stages (deeper measured slower: the arm is bound by its arithmetic, not by load latency)
+constexpr int kSmMaxGroups = 3;               // token groups of 16 (M <= 48; the arm takes M <= 40)
+constexpr int kSmMaxRoundsTwoGroups = 4;      // rounds per tile and part of the dual GEMM with two token groups
 
 struct SmallParams {
     const void *in0;  // bf16 [M, cols]
@@ -293,19 +296,20 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
     // Tile tt's sums from the 16 waves' accumulators in the reduction area,
     // and its epilogue. Thread pair (2 j, 2 j + 1) takes output j = (t, o),
     // o = 16 m + rr (accumulator m % 4 of lane 16 (m / 4) + rr of every
-    // wave): each thread adds waves 8 h .. 8 h + 7 in order (h = tid % 2),
-    // and the even thread adds the two halves, half 0 first.
+    // wave), and j + 512 with three token groups: each thread adds waves
+    // 8 h .. 8 h + 7 in order (h = tid % 2), and the even thread adds the two
+    // halves, half 0 first.
     const FFN_LDS float *redf = reinterpret_cast<const FFN_LDS float *>(red);
     auto finish_tile = [&](int tt) {
-        const int j = tid >> 1;
-        const int h = tid & 1;
+      const int h = tid & 1;
+      for (int j = tid >> 1; j < TG * 256; j += kSmWaves * 32) {
         const int t = j >> 8;
         const int o = j & 255;
         const int ml = o >> 4;
         const int rr = o & 15;
         const int m = 16 * t + ml;
-        if (j >= TG * 256 || (PARTIAL && m >= M))  // (the pair of threads leaves together)
-            return;
+        if (PARTIAL && m >= M)  // (the pair of threads skips together)
+            continue;
         const int at = (16 * (ml >> 2) + rr) * 4 + (ml & 3);
         float y[NMAT];
 #pragma unroll
@@ -320,7 +324,7 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
             y[f] = a + b;  // in the even thread: half 0 + half 1
         }
         if (h != 0)
-            return;
+            continue;
         const int row = (ta + tt) * kSmRows + rr;
         const size_t o_out = static_cast<size_t>(m) * p.rows + row;
         if constexpr (SPLIT) {
@@ -339,6 +343,7 @@ __global__ __launch_bounds__(kSmWaves * 64) void smallm_gemm_kernel(const SmallP
         } else {
             static_cast<uint16_t *>(p.out0)[o_out] = to_bf16_bits(y[0] * p.s2_0);
         }
+      }
     };
 
     int st = 0;  // ring stage of the round being multiplied

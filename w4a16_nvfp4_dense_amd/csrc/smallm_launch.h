@@ -1,5 +1,5 @@
 // smallm_launch.h -- host interface of the small-batch matrix-core arm
-// (9 <= M <= 32 token rows).
+// (9 <= M <= 40 token rows).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -9,7 +9,7 @@
 
 namespace ffn {
 
-constexpr int kSmallMaxM = 32;
+constexpr int kSmallMaxM = 40;
 
 // Whether the small-batch arm covers the dual GEMM (rows = N, cols = K) and
 // the down GEMM (rows = K, cols = N) of an M-row batch.

@@ -19,11 +19,14 @@ int token_groups(int M)
 
 // Rounds a wave may take per tile and part: its activations (8 registers per
 // round and token group) and accumulators must fit the 128 registers a lane
-// has with 16 waves per compute unit (compiled, the two-group dual GEMM needs
-// 122 at 4 rounds and spills at 5; the two-group down GEMM fits 5).
-int max_rounds(int tg, int nmat)
+// has with 16 waves per compute unit. Compiled: two groups, the dual GEMM
+// needs 124-128 at 4 rounds (16 bytes per lane spilled without PARTIAL) and the
+// down GEMM 127-128 at 5 (8 bytes spilled without PARTIAL; 4 rounds, which fit,
+// measured slower: 61.5 vs 59.9 us at 17 rows, 67.2 vs 66.9 us at 32); three
+// groups, the dual GEMM 120-122 at 2 rounds and the down GEMM 127-128 at 3.
+constexpr int max_rounds(int tg, int nmat)
 {
-    return (tg == 1 || nmat == 1) ? kSmMaxRounds : kSmMaxRoundsTwoGroups;
+    return tg == 1 ? kSmMaxRounds : tg == 2 ? (nmat == 1 ? kSmMaxRounds : kSmMaxRoundsTwoGroups) : (nmat == 1 ? 3 : 2);
 }
 
 // Split of one GEMM: P parts of the reduction (each at most max_rounds(tg)
@@ -59,13 +62,25 @@ template <int NMAT, int OUT, int TG, bool SPLIT, bool PARTIAL>
 hipError_t launch_tg(const SmallParams &p, int rounds, hipStream_t stream)
 {
     const void *kern = nullptr;
+    if (rounds > max_rounds(TG, NMAT))
+        return hipErrorNotSupported;
     switch (rounds) {
     case 1: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 1, TG, SPLIT, PARTIAL>); break;
     case 2: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 2, TG, SPLIT, PARTIAL>); break;
-    case 3: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 3, TG, SPLIT, PARTIAL>); break;
-    case 4: kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 4, TG, SPLIT, PARTIAL>); break;
+    case 3:
+        if constexpr (max_rounds(TG, NMAT) >= 3) {
+            kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 3, TG, SPLIT, PARTIAL>);
+            break;
+        }
+        return hipErrorNotSupported;
+    case 4:
+        if constexpr (max_rounds(TG, NMAT) >= 4) {
+            kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 4, TG, SPLIT, PARTIAL>);
+            break;
+        }
+        return hipErrorNotSupported;
     case 5:
-        if constexpr (TG == 1 || NMAT == 1) {
+        if constexpr (max_rounds(TG, NMAT) >= 5) {
             kern = reinterpret_cast<const void *>(smallm_gemm_kernel<NMAT, OUT, 5, TG, SPLIT, PARTIAL>);
             break;
         }
@@ -95,6 +110,7 @@ hipError_t launch_t(const SmallParams &p, const SmallPlan &s, hipStream_t stream
     switch (s.tg) {
     case 1: return split ? launch_split<NMAT, OUT, 1, true>(p, s.rounds, stream) : launch_split<NMAT, OUT, 1, false>(p, s.rounds, stream);
     case 2: return split ? launch_split<NMAT, OUT, 2, true>(p, s.rounds, stream) : launch_split<NMAT, OUT, 2, false>(p, s.rounds, stream);
+    case 3: return split ? launch_split<NMAT, OUT, 3, true>(p, s.rounds, stream) : launch_split<NMAT, OUT, 3, false>(p, s.rounds, stream);
     default: return hipErrorNotSupported;
     }
 }
