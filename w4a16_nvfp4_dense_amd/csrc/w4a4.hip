@@ -87,27 +87,35 @@ __device__ __forceinline__ void mx_store_block(const float (&v)[kMxBlock], uint8
     *e8m0 = static_cast<uint8_t>(se + 127);
 }
 
-// bf16 [rows, cols] -> MXFP4: one thread per 32-element block (64 bytes in,
-// 17 bytes out; neighbouring threads take neighbouring blocks).
-__global__ __launch_bounds__(256) void mx_quant_bf16_kernel(const uint16_t *x, int rows, int cols, uint8_t *codes,
+// bf16 [rows, cols] -> MXFP4: four threads per 32-element block, each with 8
+// consecutive elements (one 16-byte load; a wave reads 1 KB contiguously and
+// writes 256 code bytes), the block maximum taken over the quad with DPP (max
+// is exact in any order, so every code and exponent equals that of one thread
+// per block). rows * cols / 8 threads; cols is a multiple of 32, so a quad is
+// wholly inside or past the end.
+__global__ __launch_bounds__(256) void mx_quant_bf16_kernel(const uint16_t *x, long pieces, uint8_t *codes,
                                                            uint8_t *e8m0)
 {
-    const int nb = cols / kMxBlock;
-    const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (t >= static_cast<long>(rows) * nb)
+    const long t = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;  // 8-element piece
+    if (t >= pieces)
         return;
-    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + t * kMxBlock);
-    float v[kMxBlock];
+    const u32x4_t w = *reinterpret_cast<const u32x4_t *>(x + t * 8);
+    float v[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const u32x4_t w = src[q];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[8 * q + 2 * k] = __uint_as_float(w[k] << 16);
-            v[8 * q + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-        }
+    for (int k = 0; k < 4; ++k) {
+        v[2 * k] = __uint_as_float(w[k] << 16);
+        v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
     }
-    mx_store_block(v, codes + t * (kMxBlock / 2), e8m0 + t);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        amax = fmaxf(amax, fabsf(v[j]));
+    amax = fmaxf(amax, dpp_move<0xB1>(amax));  // quad_perm [1,0,3,2]
+    amax = fmaxf(amax, dpp_move<0x4E>(amax));  // quad_perm [2,3,0,1]
+    const int se = mx_exponent(amax);
+    reinterpret_cast<uint32_t *>(codes)[t] = e2m1_pack8(v, mx_inverse_scale(se));
+    if ((t & 3) == 0)
+        e8m0[t >> 2] = static_cast<uint8_t>(se + 127);
 }
 
 // NVFP4 [rows, cols] (codes, scales; scale2 left out) -> MXFP4: one thread per
@@ -519,10 +527,10 @@ hipError_t launch_mx_quant_bf16(const void *x, int rows, int cols, uint8_t *code
 {
     if (rows < 1 || cols < kMxBlock || cols % kMxBlock != 0)
         return hipErrorNotSupported;
-    const long blocks = static_cast<long>(rows) * (cols / kMxBlock);
-    const int grid = static_cast<int>((blocks + 255) / 256);
-    hipLaunchKernelGGL(mx_quant_bf16_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const uint16_t *>(x), rows,
-                       cols, codes, e8m0);
+    const long pieces = static_cast<long>(rows) * (cols / 8);
+    const int grid = static_cast<int>((pieces + 255) / 256);
+    hipLaunchKernelGGL(mx_quant_bf16_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const uint16_t *>(x), pieces,
+                       codes, e8m0);
     return hipGetLastError();
 }
 
