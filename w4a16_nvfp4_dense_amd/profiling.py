@@ -52,13 +52,20 @@ def _one(pattern: str) -> str:
     return found[0]
 
 
+def short_name(name: str) -> str:
+    """A kernel's name without its parameter list (and without the
+    anonymous-namespace qualifier, which would otherwise be cut at its own
+    parenthesis)."""
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    return name.split("(")[0]
+
+
 def stats_summary(trace_dir: str, top: int = 8) -> str:
     path = _one(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
     rows = list(csv.DictReader(open(path)))
     out = ["kernel | calls | average us | min us | max us | share %", "---|---|---|---|---|---"]
     for r in rows[:top]:
-        name = r["Name"].replace("void ", "")
-        name = name.split("(")[0] if "ffn::" in name else name[:60]
+        name = short_name(r["Name"]) if "ffn::" in r["Name"] else r["Name"].replace("void ", "")[:60]
         out.append(f"{name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
                    f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.2f}")
     return "\n".join(out)
@@ -124,7 +131,7 @@ def counters_summary(run_dirs: List[str]) -> str:
             names[int(r["Dispatch_Id"])] = r["Kernel_Name"]
         byk: Dict[str, Dict[str, List[float]]] = {}
         for (disp, ctr), v in per.items():
-            k = names[disp].replace("void ", "").split("(")[0]
+            k = short_name(names[disp])
             byk.setdefault(k, {}).setdefault(ctr, []).append(v)
         for k, cs in byk.items():
             for ctr, vals in cs.items():
