@@ -31,9 +31,9 @@
 //                    that delays every workgroup's stream), then each thread
 //                    encodes one 16-element block at a time: 32 bytes in (two
 //                    16-byte loads, issued one block ahead so the first ones
-//                    overlap the prologue), 8 code bytes and 1 scale byte out,
-//                    so a wave reads 2 KB and writes 512 + 64 bytes
-//                    contiguously.
+//                    overlap the prologue), 8 code bytes and 1 scale byte out
+//                    (non-temporal stores), so a wave reads 2 KB and writes
+//                    512 + 64 bytes contiguously.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -47,6 +47,8 @@ namespace ffn {
 namespace {
 
 constexpr int kThreads = 256;
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));  // a block's 8 code bytes
 constexpr int kAbsmaxInFlight = 4;  // 16-element blocks per thread and step of the absmax pass
 constexpr int kAbsmaxGroupsPerCu = 2;
 
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void quantize_absmax_kernel(const u32x4_t
 }
 
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t *w, size_t nblocks, const uint32_t *partial,
-                                                            int npartial, uint2 *codes, uint8_t *scales,
+                                                            int npartial, u32x2_t *codes, uint8_t *scales,
                                                             float *scale2_out)
 {
     __shared__ uint32_t sh[kThreads / 64];
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t *w, si
             sb = e4m3_encode(bf16_bits_to_float(bm) / d);
             denom = e4m3_decode(sb) * scale2;
         }
-        uint2 packed = {0u, 0u};
+        u32x2_t packed = {0u, 0u};
         if (denom != 0.0f) {
             const float inv = 1.0f / denom;
             float f[16];
@@ -181,8 +183,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const u32x4_t *w, si
             packed.x = e2m1_encode4(f[0], f[1], f[2], f[3], inv) | (e2m1_encode4(f[4], f[5], f[6], f[7], inv) << 16);
             packed.y = e2m1_encode4(f[8], f[9], f[10], f[11], inv) | (e2m1_encode4(f[12], f[13], f[14], f[15], inv) << 16);
         }
-        codes[b] = packed;
-        scales[b] = static_cast<uint8_t>(sb);
+        // non-temporal: the 50 MB of codes and scales are not read back here,
+        // and stores that stream out at once leave less to write back while
+        // the next quantise reads (73.4 -> 67.1 us per 17408 x 5120 weight)
+        __builtin_nontemporal_store(packed, codes + b);
+        __builtin_nontemporal_store(static_cast<uint8_t>(sb), scales + b);
     }
 }
 
@@ -221,7 +226,7 @@ hipError_t launch_quantize(const void *w, int rows, int cols, uint8_t *codes, ui
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(quantize_kernel, dim3(g), dim3(kThreads), 0, stream, static_cast<const u32x4_t *>(w), nblocks,
-                       partial, ga, reinterpret_cast<uint2 *>(codes), scales, scale2);
+                       partial, ga, reinterpret_cast<u32x2_t *>(codes), scales, scale2);
     return hipGetLastError();
 }
 
