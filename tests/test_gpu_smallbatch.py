@@ -58,6 +58,10 @@ SMALL_BATCH = [
     (34, 2048, 3072, fi.ACT_SILU, 85),
     (39, 256, 21504, fi.ACT_GELU_TANH, 86),
     (35, 256, 65536, fi.ACT_SILU, 87),
+    # K = 5376 (21 blocks of 256 columns): parts of unequal length, 10 and 11
+    # blocks with two token groups, 7 each with three (1.75 rounds)
+    (20, 5376, 1024, fi.ACT_SILU, 89),
+    (37, 5376, 1024, fi.ACT_GELU_TANH, 90),
 ]
 IDS = [f"m{m}_k{k}_n{n}_a{a}" for m, k, n, a, _ in SMALL_BATCH]
 

@@ -2,7 +2,8 @@
 in place of a workspace) against ffn_nvfp4_forward, through the C ABI: the
 same kernels, so the outputs must be bit-identical (which also meets the
 oracle bound the forward is held to). Two calls in a row, the second on a
-smaller input, then the small-batch matrix-core arm, and the rejection of a
+smaller input, then the small-batch matrix-core arm (also with three token
+groups and split reductions), and the rejection of a
 shape whose workspace exceeds the scratch."""
 import ctypes
 
@@ -45,6 +46,17 @@ def test_noalloc_small_batch_arm():
     assert ffn.workspace_bytes(16, 1024, 2048) <= 4 << 20
     out, ref = _run(case)
     assert torch.equal(out, ref)
+
+
+def test_noalloc_three_token_groups_split():
+    """Three token groups with the dual reduction split in 3 parts (K = 5120):
+    the partial sums and the ready words live in the static scratch, and a
+    second call finds the words the first one cleared."""
+    case = fi.make_small(36, 5120, 2048, seed=73)
+    assert ffn.workspace_bytes(36, 5120, 2048) <= 4 << 20
+    for _ in range(2):
+        out, ref = _run(case)
+        assert torch.equal(out, ref)
 
 
 def test_noalloc_rejects_oversized_workspace():
