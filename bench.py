@@ -132,11 +132,12 @@ def algorithmic_bytes(M, K, N):
     }
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the dual GEMV from the committed counter
-    summary (profiles/traffic_dual_gemv_<workload>.json), or None when there is
-    none or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_dual_gemv_{workload}.json")
+def measured_traffic(workload, what="dual_gemv"):
+    """HBM bytes per launch of the dual GEMV (or, with what="forward", per
+    forward summed over its kernels) from the committed counter summary
+    (profiles/traffic_<what>_<workload>.json), or None when there is none or
+    the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{what}_{workload}.json")
     if not os.path.exists(path):
         return None
     from w4a16_nvfp4_dense_amd import profiling
@@ -736,6 +737,10 @@ def bench_nvfp4(args):
         arm = "small-batch GEMMs" if M <= SMALL_BATCH_MAX_M else "128-row GEMMs"
         log(f"[bench] {args.workload}: {tflops:.1f} TFLOP/s ({100 * tflops / MFMA_BF16_PEAK_TFLOPS:.1f}% of "
             f"{MFMA_BF16_PEAK_TFLOPS:.0f}); bound by {bound}")
+        traffic = measured_traffic(args.workload, "forward")
+        if traffic is not None:
+            log(f"[bench] measured HBM traffic of the forward's kernels: {traffic['bytes'] / 1e6:.2f} MB per forward "
+                f"({traffic['bytes'] / nbytes['forward']:.4f} x algorithmic)")
         result["roofline"] = {
             "kernel": f"whole forward ({arm}: dual GEMM + down GEMM on bf16 matrix cores)",
             "bound": bound,
@@ -743,7 +748,8 @@ def bench_nvfp4(args):
             "peak": HBM_PEAK_GBS if bound == "hbm" else MFMA_BF16_PEAK_TFLOPS,
             "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
             "frac": round(gbs / HBM_PEAK_GBS if bound == "hbm" else tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None, "flops_per_forward": flops, "tflops": round(tflops, 2),
+            "traffic": None if traffic is None else round(traffic["bytes"]), "flops_per_forward": flops,
+            "tflops": round(tflops, 2),
             "intensity_flop_per_byte": round(flops / nbytes["forward"], 1)}
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
