@@ -486,6 +486,8 @@ def bench_quantize(args):
         outs.append((codes.clone(), scales.clone(), s2.clone()))
     torch.cuda.synchronize()
     assert all(all(torch.equal(a, b) for a, b in zip(o, outs[0])) for o in outs), "input copies disagree"
+    if args.calibrate_copy:
+        calibration_copy(dev)
     steps = min(args.steps, 1000)
     t0 = time.perf_counter()
     ms_per_step = timed_ms(step, steps, stream, args.warmup) / steps
@@ -493,6 +495,10 @@ def bench_quantize(args):
     us = ms_per_step * 1e3
     nbytes = quant_bytes(rows, cols)
     gbs = nbytes / (us * 1e-6) / 1e9
+    traffic = measured_traffic(args.workload, "quantize")
+    if traffic is not None:
+        log(f"[bench] measured HBM traffic of both passes: {traffic['bytes'] / 1e6:.2f} MB per quantise "
+            f"({traffic['bytes'] / nbytes:.4f} x algorithmic)")
     log(f"[bench] {args.workload}: {us:.2f} us/quantise, {gbs:.1f} GB/s algorithmic "
         f"({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f}); host wall {wall * 1e3 / steps * 1e3:.2f} us/step")
     result = {
@@ -505,7 +511,8 @@ def bench_quantize(args):
                    "rows": rows, "cols": cols, "algorithmic_bytes_per_quantise": nbytes},
         "roofline": {"kernel": "whole quantise (absmax pass + quantise pass)", "bound": "hbm",
                      "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "us_per_launch": round(us, 3),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic["bytes"]), "us_per_launch": round(us, 3),
                      "algorithmic_bytes_per_launch": nbytes},
     }
     if not args.no_cpu_baseline:
